@@ -1,0 +1,245 @@
+/*
+ * mi_prefill.h - C ABI of the gfx950 (MI355X) Q8_0 prefill library.
+ *
+ * One call runs the prefill forward of a Qwen2/Qwen3-style decoder over all prompt
+ * tokens together, writes every token's K/V row into persistent per-layer KV regions
+ * at the row its position names, and returns the logits of the last token only.
+ * Sources for what each call computes (the "minfer Inference E2E Walkthrough"
+ * pages):
+ *   - "09 - Prefill: the first forward": the prefill call, positions as data
+ *     (section 2.2), last-token logits (2.4), KV regions sized by n_ctx (2.5),
+ *     one owned copy of the logits (2.6), the position check (3.4);
+ *   - "05 - Graph build - the IR and the builder": the layer node by node (2.5),
+ *     GQA (2.5), the tail rows (2.8), inline matmul bias and the KV store (3.2);
+ *   - the walkthrough index, stages 10 and 11: Q8_0 activations quantized on the
+ *     fly against quantized weights; RMSNorm, RoPE, softmax, SiLU, GQA attention.
+ *
+ * Conventions for every entry point
+ *   - All functions return an mi_status (0 = MI_OK).  On error nothing has been
+ *     enqueued or written, except for MI_ERR_HIP (a runtime failure after launch);
+ *     mi_last_error() then describes the failure (thread-local, valid until the
+ *     next call on the same thread).
+ *   - Pointers marked "device" are HIP device memory owned by the caller; the
+ *     library never allocates, frees or retains them.  "host" pointers are read
+ *     before the call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is asynchronous on that stream; the caller synchronizes before reading.
+ *   - Matrices are row-major.  A Q8_0 matrix [rows][cols] is stored as two
+ *     planes: int8 codes [rows][cols] and fp16 scales [rows][cols/32] (bits in a
+ *     uint16).  Value (r, c) = scale[r][c/32] * code[r][c].  cols % 32 == 0.
+ *     Weights use rows = output features, cols = input features ([out][in]).
+ *   - Activations are token-major f32: [n_tokens][features].
+ *   - Numerics: every node computes to f64 accuracy from its f32 inputs and
+ *     rounds its result once to f32 (round to nearest even); the Q8_0 quantizer
+ *     runs in f32 exactly as specified below.
+ */
+#ifndef MI_PREFILL_H
+#define MI_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MI_OK = 0,
+  MI_ERR_INVALID_ARG = 1,     /* null pointer, bad size, dims not multiples of 32, ... */
+  MI_ERR_POSITION_RANGE = 2,  /* a position < 0 or >= n_ctx ("09", section 3.4)       */
+  MI_ERR_DUP_POSITION = 3,    /* two tokens of one call name the same KV row           */
+  MI_ERR_KV_MISMATCH = 4,     /* KV descriptor disagrees with the model or the call   */
+  MI_ERR_WORKSPACE = 5,       /* workspace too small                                   */
+  MI_ERR_HIP = 6,             /* HIP runtime error                                     */
+  MI_ERR_UNSUPPORTED = 7      /* shape outside what the kernels implement              */
+} mi_status;
+
+/* Model shape.  n_head % n_head_kv == 0; head_dim even and <= 128; hidden, ffn,
+ * n_head*head_dim multiples of 32.  rms_eps is used for every RMSNorm (and the
+ * Qwen3 per-head QK norm); rope_theta is the NeoX RoPE base. */
+typedef struct {
+  int32_t n_layers, hidden, n_head, n_head_kv, head_dim, ffn, vocab;
+  float rms_eps, rope_theta;
+  int32_t qkv_bias;  /* 1: Q/K/V matmuls add a bias (Qwen2)            */
+  int32_t qk_norm;   /* 1: per-head RMSNorm of Q and K before RoPE (Qwen3) */
+  int32_t tied;      /* 1: lm_head reuses token_embd                      */
+} mi_hparams;
+
+/* A Q8_0 matrix in device memory (layout above). */
+typedef struct {
+  const int8_t* codes;     /* device [rows][cols]      */
+  const uint16_t* scales;  /* device [rows][cols / 32] */
+  int32_t rows, cols;
+} mi_q8_matrix;
+
+/* One decoder layer, in the library's weight layout (the binding builds it once at load):
+ *   wqkv      rows of Wq, then Wk, then Wv stacked: [nh*hd + 2*nkv*hd][hidden].  One matmul
+ *             computes Q, K and V; each output element is the same dot product as in three
+ *             separate matmuls.
+ *   bqkv      device f32 [nh*hd + 2*nkv*hd] (bq, bk, bv stacked), NULL unless hp.qkv_bias.
+ *   wo        [hidden][nh*hd].
+ *   w_gate_up gate and up rows interleaved in groups of 32: rows 64p..64p+31 are gate rows
+ *             32p..32p+31, rows 64p+32..64p+63 are up rows 32p..32p+31; [2*ffn][hidden], so
+ *             one tile of the matmul holds matching gate and up columns and SwiGLU plus the
+ *             Q8_0 of its result run in the matmul epilogue.
+ *   w_down    [hidden][ffn].
+ *   attn_norm, ffn_norm device f32 [hidden]; q_norm, k_norm device f32 [head_dim] (NULL unless
+ *   hp.qk_norm). */
+typedef struct {
+  mi_q8_matrix wqkv, wo, w_gate_up, w_down;
+  const float* bqkv;
+  const float *attn_norm, *ffn_norm;
+  const float *q_norm, *k_norm;
+} mi_layer_weights;
+
+/* A loaded model plus the per-model buffers one forward uses.  Not thread-safe:
+ * calls that share one mi_model (its workspace) must be serialized. */
+typedef struct {
+  mi_hparams hp;
+  mi_q8_matrix token_embd;          /* [vocab][hidden]                       */
+  mi_q8_matrix output;              /* [vocab][hidden]; ignored when tied    */
+  const float* output_norm;         /* device [hidden]                       */
+  const mi_layer_weights* layers;   /* host array [n_layers]                 */
+  const double* rope_table;         /* device, filled by mi_rope_table_init  */
+  int32_t rope_rows;                /* positions the table covers (>= n_ctx) */
+  void* workspace;                  /* device scratch                        */
+  size_t workspace_bytes;           /* >= mi_prefill_workspace_bytes(...)    */
+  int32_t max_tokens;               /* largest n_tokens the workspace serves */
+  void* stream;                     /* hipStream_t                           */
+} mi_model;
+
+/* Persistent KV regions ("09", section 2.5): for each layer one K and one V
+ * region, device f32 [n_ctx][n_head_kv*head_dim]; row p holds the position-p
+ * token (K after RoPE, and after the QK norm for Qwen3; V raw plus bias).  The
+ * caller owns them; they persist across calls so a later call can continue at
+ * later positions. */
+typedef struct {
+  float* const* k;   /* host array [n_layers] of device pointers */
+  float* const* v;
+  int32_t n_layers, n_ctx, n_kv_embd;
+} mi_kv_regions;
+
+/* ------------------------------------------------------------------ forward */
+
+/* Bytes of workspace one forward needs for up to max_tokens tokens. */
+size_t mi_prefill_workspace_bytes(const mi_hparams* hp, int32_t max_tokens);
+
+/* Bytes of the RoPE table for positions [0, rows): rows x (head_dim/2) x {cos, sin} f64. */
+size_t mi_rope_table_bytes(const mi_hparams* hp, int32_t rows);
+
+/* Fill a device RoPE table: entry (p, i) = cos/sin(p * theta^(-2i/head_dim)), computed
+ * on the host in f64 and copied to `table` (device) on `stream` (synchronously). */
+int mi_rope_table_init(const mi_hparams* hp, int32_t rows, double* table, void* stream);
+
+/* The prefill forward ("09", sections 2.2-2.6; "05", sections 2.5 and 2.8).
+ *   token_ids  host int32 [n_tokens], each in [0, vocab)
+ *   positions  host int32 [n_tokens]: the KV row each token writes, the causal
+ *              limit (token t sees rows 0..=positions[t]) and the RoPE angle
+ *   n_ctx      rows of every KV region; must equal kv->n_ctx
+ *   kv         the persistent regions; rows named by `positions` are overwritten;
+ *              rows <= max(positions) not written by this call must hold earlier
+ *              calls' rows (the caller's contract)
+ *   logits_out device f32 [vocab]: logits of token n_tokens-1
+ * Checks before enqueueing: every position in [0, n_ctx) (MI_ERR_POSITION_RANGE),
+ * no position repeated (MI_ERR_DUP_POSITION), descriptor shapes
+ * (MI_ERR_KV_MISMATCH), n_tokens <= model->max_tokens and workspace size
+ * (MI_ERR_WORKSPACE), rope table rows >= n_ctx. */
+int mi_prefill_forward(const mi_model* model, const int32_t* token_ids, const int32_t* positions,
+                       int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv, float* logits_out);
+
+/* ------------------------------------------------------------------ per-op calls */
+
+/* Q8_0 quantize rows of f32 ("CPU matmul kernels" stage of the walkthrough index;
+ * format as the workload defines it): for each block of 32 values
+ * amax = max|x|, d = f32(amax/127), id = d ? f32(1/d) : 0,
+ * code = round-half-away(f32(x*id)) clamped to [-127,127], stored scale fp16(d) RNE.
+ *   x      device f32 [rows][cols], cols % 32 == 0
+ *   codes  device int8 [rows][cols]; scales device uint16 (fp16 bits) [rows][cols/32] */
+int mi_quantize_q8_0(const float* x, int64_t rows, int32_t cols, int8_t* codes, uint16_t* scales,
+                     void* stream);
+
+/* Q8_0 x Q8_0 matmul with inline bias and optional residual ("05", sections 2.5, 3.2):
+ *   out[t][n] = residual[t][n] + f32( sum_kb da[t][kb] dw[n][kb] sum_32 qa qw + bias[n] )
+ * a_codes/a_scales: device, the activations already in Q8_0 [m][k];
+ * w: the weight [n][k]; bias device f32 [n] or NULL; residual device f32 [m][n] or
+ * NULL (may alias out); out device f32 [m][n].  The block sums are exact (int8
+ * MFMA, int32) and the scaled sum is accumulated in f64. */
+int mi_gemm_q8_0(const int8_t* a_codes, const uint16_t* a_scales, int32_t m, const mi_q8_matrix* w,
+                 const float* bias, const float* residual, float* out, void* stream);
+
+/* The same matmul with a caller workspace for split-K partials (f64 [split][m][n], reduced in
+ * a fixed order afterwards).  split_k = 0 lets the library choose; the split is lowered when the
+ * workspace is too small.  mi_gemm_q8_0_workspace_bytes gives the bytes for its own choice. */
+int mi_gemm_q8_0_ws(const int8_t* a_codes, const uint16_t* a_scales, int32_t m, const mi_q8_matrix* w,
+                    const float* bias, const float* residual, float* out, void* workspace,
+                    size_t workspace_bytes, int32_t split_k, void* stream);
+size_t mi_gemm_q8_0_workspace_bytes(int32_t m, int32_t n, int32_t k);
+
+/* gate|up matmul with SwiGLU and Q8_0 in the epilogue ("05", section 2.5 gate, up, SwiGLU):
+ *   g = f32(x.Wgate), u = f32(x.Wup), s = f32(silu(g) * u), then s -> Q8_0.
+ *   w_gate_up in the interleaved layout of mi_layer_weights ([2*ffn][k], rows % 64 == 0);
+ *   s_codes device int8 [m][ffn], s_scales device uint16 [m][ffn/32]; workspace as above. */
+int mi_gemm_swiglu_q8_0(const int8_t* a_codes, const uint16_t* a_scales, int32_t m,
+                        const mi_q8_matrix* w_gate_up, int8_t* s_codes, uint16_t* s_scales,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* RMSNorm then Q8_0 ("05", section 2.5 attn_norm / ffn_norm / output_norm):
+ * y = f32(x / sqrt(mean(x^2) + eps) * gamma) per row, then quantized as above.
+ *   x device f32 [rows][cols]; gamma device f32 [cols]; codes/scales as above.
+ *   y_out optional device f32 [rows][cols] (NULL to skip). */
+int mi_rmsnorm_quant(const float* x, const float* gamma, int64_t rows, int32_t cols, float eps,
+                     int8_t* codes, uint16_t* scales, float* y_out, void* stream);
+
+/* Per-head RMSNorm of Q and K over head_dim (Qwen3 QkNorm, "05", sections 2.3, 2.6),
+ * in place.  x device f32 [rows][n_heads*head_dim]; gamma device f32 [head_dim]. */
+int mi_qk_norm(float* x, const float* gamma, int64_t rows, int32_t n_heads, int32_t head_dim,
+               float eps, void* stream);
+
+/* NeoX RoPE of Q (in place) and K, then the KV store ("09", section 2.2: row p of the
+ * layer's K and V regions <- the position-p token; "05", section 3.2: rotated K, raw V):
+ *   q device f32 [n_tokens][n_head*head_dim], rotated in place
+ *   k, v device f32 [n_tokens][n_head_kv*head_dim] (k is not modified)
+ *   positions device int32 [n_tokens] (validated by the caller; see mi_prefill_forward)
+ *   rope_table from mi_rope_table_init with rope_rows > max position
+ *   k_region, v_region device f32 [n_ctx][n_head_kv*head_dim] */
+int mi_rope_kvstore(float* q, const float* k, const float* v, const int32_t* positions,
+                    int32_t n_tokens, int32_t n_head, int32_t n_head_kv, int32_t head_dim,
+                    const double* rope_table, int32_t rope_rows, float* k_region, float* v_region,
+                    int32_t n_ctx, void* stream);
+
+/* Causal GQA attention over a layer's regions ("09", section 2.2; "05", section 2.5):
+ *   out[t][h] = sum_{j<=pos[t]} softmax_j(q[t][h].K[j][g] / sqrt(hd)) V[j][g],
+ *   g = h / (n_head/n_head_kv).  q device f32 [n_tokens][n_head*head_dim];
+ *   positions device int32 [n_tokens], each < n_ctx; out device f32 like q.
+ *   max_pos: host copy of max(positions) (bounds the rows read). */
+int mi_attention_gqa(const float* q, const float* k_region, const float* v_region,
+                     const int32_t* positions, int32_t n_tokens, int32_t max_pos, int32_t n_head,
+                     int32_t n_head_kv, int32_t head_dim, int32_t n_ctx, float* out, void* stream);
+
+/* SwiGLU then Q8_0 ("05", section 2.5): s = f32(silu(g) * u), silu(x) = x*sigmoid(x),
+ * quantized as above.  gate, up device f32 [rows][cols]. */
+int mi_swiglu_quant(const float* gate, const float* up, int64_t rows, int32_t cols, int8_t* codes,
+                    uint16_t* scales, void* stream);
+
+/* Embedding rows: out[t] = dequant(table row ids[t]) ("05", section 2.5, GetRows).
+ *   ids device int32 [n_tokens] in [0, table->rows); out device f32 [n_tokens][cols]. */
+int mi_embed_q8_0(const mi_q8_matrix* table, const int32_t* ids, int32_t n_tokens, float* out,
+                  void* stream);
+
+/* Last-row lm_head ("09", section 2.4): RMSNorm of one hidden row, Q8_0, then the
+ * matvec against the head matrix: logits[v] = f32(sum_kb dx dw sum qx qw).
+ *   x device f32 [cols] (the last token's hidden state); gamma device f32 [cols];
+ *   head [vocab][cols]; logits device f32 [vocab]; scratch device >= cols + 2*cols/32 bytes. */
+int mi_lm_head_row(const float* x, const float* gamma, float eps, const mi_q8_matrix* head,
+                   float* logits, void* scratch, void* stream);
+
+/* Description of the last error on this thread ("" if none). */
+const char* mi_last_error(void);
+
+/* Library version string. */
+const char* mi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MI_PREFILL_H */

@@ -1,0 +1,344 @@
+// C ABI: argument validation, the per-op entry points and the prefill forward.
+//
+// The forward is the Qwen2/Qwen3 layer sequence of the graph-build page (section 2.5):
+// embedding -> per layer [attn RMSNorm+Q8_0 -> fused Q|K|V matmul (+bias) -> (Qwen3) per-head QK
+// norm -> RoPE + KV store at positions -> causal GQA attention -> Q8_0 -> output projection +
+// residual -> ffn RMSNorm+Q8_0 -> gate|up matmul with SwiGLU+Q8_0 fused in its epilogue -> down
+// projection + residual] -> final RMSNorm+Q8_0 -> lm_head on the last row.  In the last layer only
+// the last token's row continues after the attention output projection (the tail rows of the
+// prefill page, section 2.4): its FFN, the final norm and the lm_head run on one row.
+//
+// Everything is validated on the host before anything is enqueued; nothing is allocated.
+#include <cstdarg>
+#include <cstring>
+#include <vector>
+#include <algorithm>
+
+#include "common.h"
+
+namespace mi {
+
+static thread_local char g_err[512] = "";
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  return set_error(MI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static bool q8_ok(const mi_q8_matrix& w, int rows, int cols) {
+  return w.codes && w.scales && w.rows == rows && w.cols == cols && cols % QK == 0;
+}
+
+// ---------------------------------------------------------------- workspace layout
+struct Ws {
+  int32_t* ids; int32_t* pos;
+  float* h;          // [T][hidden]
+  int8_t* xq;        // [T][max(hidden, nq, ffn)]
+  uint16_t* xs;      // [T][max(...)/32]
+  float* qkv;        // [T][nq + 2 nkv]
+  float* attn;       // [T][nq]
+  int8_t* sq;        // [T][ffn] SwiGLU output codes
+  uint16_t* ss;      // [T][ffn/32]
+  int8_t* lm_q; uint16_t* lm_s;  // final row quantized
+  void* gemm_ws; size_t gemm_ws_bytes;
+  size_t total;
+};
+
+static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static Ws carve(const mi_hparams& hp, int T, char* base) {
+  Ws w{};
+  const size_t nq = (size_t)hp.n_head * hp.head_dim, nkv = (size_t)hp.n_head_kv * hp.head_dim;
+  const size_t wide = std::max({(size_t)hp.hidden, nq, (size_t)hp.ffn});
+  size_t off = 0;
+  auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += align_up(bytes); return p; };
+  w.ids = (int32_t*)take(sizeof(int32_t) * T);
+  w.pos = (int32_t*)take(sizeof(int32_t) * T);
+  w.h = (float*)take(sizeof(float) * T * (size_t)hp.hidden);
+  w.xq = (int8_t*)take((size_t)T * wide);
+  w.xs = (uint16_t*)take(sizeof(uint16_t) * (size_t)T * (wide / QK));
+  w.qkv = (float*)take(sizeof(float) * (size_t)T * (nq + 2 * nkv));
+  w.attn = (float*)take(sizeof(float) * (size_t)T * nq);
+  w.sq = (int8_t*)take((size_t)T * hp.ffn);
+  w.ss = (uint16_t*)take(sizeof(uint16_t) * (size_t)T * (hp.ffn / QK));
+  w.lm_q = (int8_t*)take((size_t)hp.hidden);
+  w.lm_s = (uint16_t*)take(sizeof(uint16_t) * (size_t)(hp.hidden / QK));
+  size_t g = 0;
+  g = std::max(g, gemm_workspace_bytes(T, (int)(nq + 2 * nkv), hp.hidden));
+  g = std::max(g, gemm_workspace_bytes(T, hp.hidden, (int)nq));
+  g = std::max(g, gemm_workspace_bytes(T, 2 * hp.ffn, hp.hidden));
+  g = std::max(g, gemm_workspace_bytes(T, hp.hidden, hp.ffn));
+  g = std::max(g, gemm_workspace_bytes(1, hp.hidden, (int)nq));
+  g = std::max(g, gemm_workspace_bytes(1, 2 * hp.ffn, hp.hidden));
+  g = std::max(g, gemm_workspace_bytes(1, hp.hidden, hp.ffn));
+  w.gemm_ws = take(g);
+  w.gemm_ws_bytes = g;
+  w.total = off;
+  return w;
+}
+
+static int check_hparams(const mi_hparams* hp) {
+  if (!hp) return set_error(MI_ERR_INVALID_ARG, "hparams is NULL");
+  if (hp->n_layers < 0 || hp->hidden <= 0 || hp->n_head <= 0 || hp->n_head_kv <= 0 || hp->head_dim <= 0 ||
+      hp->ffn <= 0 || hp->vocab <= 0)
+    return set_error(MI_ERR_INVALID_ARG, "hparams: sizes must be positive");
+  if (hp->n_head % hp->n_head_kv) return set_error(MI_ERR_INVALID_ARG, "n_head %% n_head_kv != 0");
+  if (hp->hidden % QK || hp->ffn % QK || (hp->n_head * hp->head_dim) % QK)
+    return set_error(MI_ERR_INVALID_ARG, "hidden, ffn and n_head*head_dim must be multiples of 32");
+  if (hp->head_dim != 64 && hp->head_dim != 128)
+    return set_error(MI_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", hp->head_dim);
+  if (hp->hidden > 4096) return set_error(MI_ERR_UNSUPPORTED, "hidden %d > 4096", hp->hidden);
+  if (hp->ffn % 32) return set_error(MI_ERR_INVALID_ARG, "ffn %% 32 != 0");
+  return MI_OK;
+}
+
+}  // namespace mi
+
+using namespace mi;
+
+extern "C" const char* mi_last_error(void) { return g_err; }
+extern "C" const char* mi_version(void) { return "mi_prefill 0.1 gfx950"; }
+
+extern "C" size_t mi_prefill_workspace_bytes(const mi_hparams* hp, int32_t max_tokens) {
+  if (check_hparams(hp) != MI_OK || max_tokens <= 0) return 0;
+  return carve(*hp, max_tokens, nullptr).total;
+}
+
+// ---------------------------------------------------------------- per-op entry points
+extern "C" int mi_quantize_q8_0(const float* x, int64_t rows, int32_t cols, int8_t* codes, uint16_t* scales,
+                                void* stream) {
+  if (!x || !codes || !scales || rows < 0 || cols <= 0 || cols % QK)
+    return set_error(MI_ERR_INVALID_ARG, "mi_quantize_q8_0: bad arguments (cols must be a positive multiple of 32)");
+  return launch_quantize(x, rows, cols, cols, codes, scales, as_stream(stream));
+}
+
+extern "C" int mi_gemm_q8_0(const int8_t* a_codes, const uint16_t* a_scales, int32_t m, const mi_q8_matrix* w,
+                            const float* bias, const float* residual, float* out, void* stream) {
+  if (!a_codes || !a_scales || !w || !w->codes || !w->scales || !out || m < 0 || w->rows <= 0 || w->cols <= 0 ||
+      w->cols % QK || w->rows % QK)
+    return set_error(MI_ERR_INVALID_ARG, "mi_gemm_q8_0: bad arguments (k and n multiples of 32)");
+  GemmArgs g{};
+  g.a_codes = a_codes; g.a_scales = a_scales; g.m = m;
+  g.w_codes = w->codes; g.w_scales = w->scales; g.n = w->rows; g.k = w->cols;
+  g.bias = bias; g.residual = residual; g.out = out; g.ld_out = w->rows;
+  g.split_k = 1;
+  return launch_gemm_q8(g, as_stream(stream));
+}
+
+extern "C" int mi_gemm_q8_0_ws(const int8_t* a_codes, const uint16_t* a_scales, int32_t m, const mi_q8_matrix* w,
+                               const float* bias, const float* residual, float* out, void* workspace,
+                               size_t workspace_bytes, int32_t split_k, void* stream) {
+  if (!a_codes || !a_scales || !w || !w->codes || !w->scales || !out || m < 0 || w->rows <= 0 || w->cols <= 0 ||
+      w->cols % QK || w->rows % QK || split_k < 0)
+    return set_error(MI_ERR_INVALID_ARG, "mi_gemm_q8_0_ws: bad arguments");
+  GemmArgs g{};
+  g.a_codes = a_codes; g.a_scales = a_scales; g.m = m;
+  g.w_codes = w->codes; g.w_scales = w->scales; g.n = w->rows; g.k = w->cols;
+  g.bias = bias; g.residual = residual; g.out = out; g.ld_out = w->rows;
+  g.workspace = workspace; g.workspace_bytes = workspace_bytes; g.split_k = split_k;
+  return launch_gemm_q8(g, as_stream(stream));
+}
+
+extern "C" size_t mi_gemm_q8_0_workspace_bytes(int32_t m, int32_t n, int32_t k) {
+  if (m <= 0 || n <= 0 || k <= 0) return 0;
+  return gemm_workspace_bytes(m, n, k);
+}
+
+extern "C" int mi_gemm_swiglu_q8_0(const int8_t* a_codes, const uint16_t* a_scales, int32_t m,
+                                   const mi_q8_matrix* w_gate_up, int8_t* s_codes, uint16_t* s_scales,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!a_codes || !a_scales || !w_gate_up || !w_gate_up->codes || !w_gate_up->scales || !s_codes || !s_scales ||
+      m < 0 || w_gate_up->rows <= 0 || w_gate_up->rows % 64 || w_gate_up->cols % QK)
+    return set_error(MI_ERR_INVALID_ARG, "mi_gemm_swiglu_q8_0: bad arguments (rows a multiple of 64)");
+  GemmArgs g{};
+  g.a_codes = a_codes; g.a_scales = a_scales; g.m = m;
+  g.w_codes = w_gate_up->codes; g.w_scales = w_gate_up->scales; g.n = w_gate_up->rows; g.k = w_gate_up->cols;
+  g.q_codes = s_codes; g.q_scales = s_scales;
+  g.workspace = workspace; g.workspace_bytes = workspace_bytes;
+  return launch_gemm_q8(g, as_stream(stream));
+}
+
+extern "C" int mi_rmsnorm_quant(const float* x, const float* gamma, int64_t rows, int32_t cols, float eps,
+                                int8_t* codes, uint16_t* scales, float* y_out, void* stream) {
+  if (!x || !gamma || !codes || !scales || rows < 0 || cols <= 0 || cols % QK)
+    return set_error(MI_ERR_INVALID_ARG, "mi_rmsnorm_quant: bad arguments");
+  return launch_rmsnorm_quant(x, gamma, rows, cols, eps, codes, scales, y_out, as_stream(stream));
+}
+
+extern "C" int mi_qk_norm(float* x, const float* gamma, int64_t rows, int32_t n_heads, int32_t head_dim, float eps,
+                          void* stream) {
+  if (!x || !gamma || rows < 0 || n_heads <= 0 || head_dim <= 0 || head_dim > 128)
+    return set_error(MI_ERR_INVALID_ARG, "mi_qk_norm: bad arguments (head_dim <= 128)");
+  return launch_qk_norm(x, (int64_t)n_heads * head_dim, gamma, rows, n_heads, head_dim, eps, as_stream(stream));
+}
+
+extern "C" int mi_rope_kvstore(float* q, const float* k, const float* v, const int32_t* positions, int32_t n_tokens,
+                               int32_t n_head, int32_t n_head_kv, int32_t head_dim, const double* rope_table,
+                               int32_t rope_rows, float* k_region, float* v_region, int32_t n_ctx, void* stream) {
+  if (!q || !k || !v || !positions || !rope_table || !k_region || !v_region || n_tokens < 0 || n_head <= 0 ||
+      n_head_kv <= 0 || head_dim <= 0 || (head_dim & 1) || n_ctx <= 0 || rope_rows < n_ctx)
+    return set_error(MI_ERR_INVALID_ARG, "mi_rope_kvstore: bad arguments (rope_rows must cover n_ctx)");
+  return launch_rope_kvstore(q, (int64_t)n_head * head_dim, k, v, (int64_t)n_head_kv * head_dim, positions, n_tokens,
+                             n_head, n_head_kv, head_dim, rope_table, k_region, v_region, as_stream(stream));
+}
+
+extern "C" int mi_attention_gqa(const float* q, const float* k_region, const float* v_region,
+                                const int32_t* positions, int32_t n_tokens, int32_t max_pos, int32_t n_head,
+                                int32_t n_head_kv, int32_t head_dim, int32_t n_ctx, float* out, void* stream) {
+  if (!q || !k_region || !v_region || !positions || !out || n_tokens < 0 || n_head <= 0 || n_head_kv <= 0 ||
+      n_head % n_head_kv || n_ctx <= 0)
+    return set_error(MI_ERR_INVALID_ARG, "mi_attention_gqa: bad arguments");
+  if (max_pos < 0 || max_pos >= n_ctx) return set_error(MI_ERR_POSITION_RANGE, "max_pos %d outside [0, %d)", max_pos, n_ctx);
+  return launch_attention(q, (int64_t)n_head * head_dim, k_region, v_region, positions, n_tokens, max_pos, n_head,
+                          n_head_kv, head_dim, out, (int64_t)n_head * head_dim, as_stream(stream));
+}
+
+extern "C" int mi_swiglu_quant(const float* gate, const float* up, int64_t rows, int32_t cols, int8_t* codes,
+                               uint16_t* scales, void* stream) {
+  if (!gate || !up || !codes || !scales || rows < 0 || cols <= 0 || cols % QK)
+    return set_error(MI_ERR_INVALID_ARG, "mi_swiglu_quant: bad arguments");
+  return launch_swiglu_quant(gate, up, rows, cols, cols, codes, scales, as_stream(stream));
+}
+
+extern "C" int mi_embed_q8_0(const mi_q8_matrix* table, const int32_t* ids, int32_t n_tokens, float* out,
+                             void* stream) {
+  if (!table || !table->codes || !table->scales || !ids || !out || n_tokens < 0 || table->cols % QK)
+    return set_error(MI_ERR_INVALID_ARG, "mi_embed_q8_0: bad arguments");
+  return launch_embed(table->codes, table->scales, table->cols, ids, n_tokens, out, as_stream(stream));
+}
+
+extern "C" int mi_lm_head_row(const float* x, const float* gamma, float eps, const mi_q8_matrix* head, float* logits,
+                              void* scratch, void* stream) {
+  if (!x || !gamma || !head || !head->codes || !head->scales || !logits || !scratch || head->cols % QK)
+    return set_error(MI_ERR_INVALID_ARG, "mi_lm_head_row: bad arguments");
+  int8_t* xq = (int8_t*)scratch;
+  uint16_t* xs = (uint16_t*)((char*)scratch + align_up(head->cols));
+  hipStream_t s = as_stream(stream);
+  int rc = launch_rmsnorm_quant(x, gamma, 1, head->cols, eps, xq, xs, nullptr, s);
+  if (rc) return rc;
+  return launch_lm_head(xq, xs, head->cols, head->codes, head->scales, head->rows, logits, s);
+}
+
+// ---------------------------------------------------------------- the forward
+static int validate_forward(const mi_model* md, const int32_t* ids, const int32_t* pos, int32_t nt, int32_t n_ctx,
+                            const mi_kv_regions* kv, const float* logits) {
+  if (!md || !ids || !pos || !kv || !logits) return set_error(MI_ERR_INVALID_ARG, "forward: NULL argument");
+  int rc = check_hparams(&md->hp);
+  if (rc) return rc;
+  const mi_hparams& hp = md->hp;
+  if (nt < 1) return set_error(MI_ERR_INVALID_ARG, "forward: n_tokens must be >= 1");
+  if (n_ctx < 1) return set_error(MI_ERR_INVALID_ARG, "forward: n_ctx must be >= 1");
+  if (kv->n_ctx != n_ctx) return set_error(MI_ERR_KV_MISMATCH, "forward: kv n_ctx %d != call n_ctx %d", kv->n_ctx, n_ctx);
+  if (kv->n_layers != hp.n_layers || kv->n_kv_embd != hp.n_head_kv * hp.head_dim || !kv->k || !kv->v)
+    return set_error(MI_ERR_KV_MISMATCH, "forward: kv descriptor does not match the model");
+  for (int l = 0; l < hp.n_layers; ++l)
+    if (!kv->k[l] || !kv->v[l]) return set_error(MI_ERR_KV_MISMATCH, "forward: kv region of layer %d is NULL", l);
+  if (nt > md->max_tokens) return set_error(MI_ERR_WORKSPACE, "forward: n_tokens %d > max_tokens %d", nt, md->max_tokens);
+  if (!md->workspace || md->workspace_bytes < carve(hp, md->max_tokens, nullptr).total)
+    return set_error(MI_ERR_WORKSPACE, "forward: workspace smaller than mi_prefill_workspace_bytes(max_tokens)");
+  if (!md->rope_table || md->rope_rows < n_ctx) return set_error(MI_ERR_INVALID_ARG, "forward: rope table rows < n_ctx");
+  for (int t = 0; t < nt; ++t) {
+    if (pos[t] < 0 || pos[t] >= n_ctx)
+      return set_error(MI_ERR_POSITION_RANGE, "forward: position %d of token %d outside [0, %d)", pos[t], t, n_ctx);
+    if (ids[t] < 0 || ids[t] >= hp.vocab)
+      return set_error(MI_ERR_INVALID_ARG, "forward: token id %d of token %d outside [0, %d)", ids[t], t, hp.vocab);
+  }
+  std::vector<int32_t> sorted(pos, pos + nt);
+  std::sort(sorted.begin(), sorted.end());
+  for (int t = 1; t < nt; ++t)
+    if (sorted[t] == sorted[t - 1]) return set_error(MI_ERR_DUP_POSITION, "forward: position %d repeated", sorted[t]);
+  const int nq = hp.n_head * hp.head_dim, nkv = hp.n_head_kv * hp.head_dim;
+  if (!q8_ok(md->token_embd, hp.vocab, hp.hidden)) return set_error(MI_ERR_INVALID_ARG, "forward: token_embd shape");
+  if (!hp.tied && !q8_ok(md->output, hp.vocab, hp.hidden)) return set_error(MI_ERR_INVALID_ARG, "forward: output shape");
+  if (!md->output_norm || (hp.n_layers && !md->layers)) return set_error(MI_ERR_INVALID_ARG, "forward: missing tensors");
+  for (int l = 0; l < hp.n_layers; ++l) {
+    const mi_layer_weights& L = md->layers[l];
+    if (!q8_ok(L.wqkv, nq + 2 * nkv, hp.hidden) || !q8_ok(L.wo, hp.hidden, nq) ||
+        !q8_ok(L.w_gate_up, 2 * hp.ffn, hp.hidden) || !q8_ok(L.w_down, hp.hidden, hp.ffn) || !L.attn_norm ||
+        !L.ffn_norm || (hp.qkv_bias && !L.bqkv) || (hp.qk_norm && (!L.q_norm || !L.k_norm)))
+      return set_error(MI_ERR_INVALID_ARG, "forward: layer %d tensors missing or mis-shaped", l);
+  }
+  if (hp.ffn % 32) return set_error(MI_ERR_INVALID_ARG, "forward: ffn %% 32");
+  return MI_OK;
+}
+
+extern "C" int mi_prefill_forward(const mi_model* md, const int32_t* token_ids, const int32_t* positions,
+                                  int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv, float* logits_out) {
+  int rc = validate_forward(md, token_ids, positions, n_tokens, n_ctx, kv, logits_out);
+  if (rc) return rc;
+  const mi_hparams& hp = md->hp;
+  const int nt = n_tokens, H = hp.hidden, F = hp.ffn;
+  const int nq = hp.n_head * hp.head_dim, nkv = hp.n_head_kv * hp.head_dim, nqkv = nq + 2 * nkv;
+  const float eps = hp.rms_eps;
+  hipStream_t s = as_stream(md->stream);
+  Ws w = carve(hp, md->max_tokens, (char*)md->workspace);
+  // boundary staging: token ids and positions to the device
+  MI_HIP(hipMemcpyAsync(w.ids, token_ids, sizeof(int32_t) * nt, hipMemcpyHostToDevice, s));
+  MI_HIP(hipMemcpyAsync(w.pos, positions, sizeof(int32_t) * nt, hipMemcpyHostToDevice, s));
+  int max_pos = 0;
+  for (int t = 0; t < nt; ++t) max_pos = std::max(max_pos, positions[t]);
+
+  if ((rc = launch_embed(md->token_embd.codes, md->token_embd.scales, H, w.ids, nt, w.h, s))) return rc;
+  float* h_last = w.h + (size_t)(nt - 1) * H;  // the tail row
+  for (int l = 0; l < hp.n_layers; ++l) {
+    const mi_layer_weights& L = md->layers[l];
+    const bool last = l == hp.n_layers - 1;
+    if ((rc = launch_rmsnorm_quant(w.h, L.attn_norm, nt, H, eps, w.xq, w.xs, nullptr, s))) return rc;
+    GemmArgs g{};
+    g.a_codes = w.xq; g.a_scales = w.xs; g.m = nt;
+    g.w_codes = L.wqkv.codes; g.w_scales = L.wqkv.scales; g.n = nqkv; g.k = H;
+    g.bias = hp.qkv_bias ? L.bqkv : nullptr; g.out = w.qkv; g.ld_out = nqkv;
+    g.workspace = w.gemm_ws; g.workspace_bytes = w.gemm_ws_bytes;
+    if ((rc = launch_gemm_q8(g, s))) return rc;
+    float* q = w.qkv;
+    float* k = w.qkv + nq;
+    float* v = w.qkv + nq + nkv;
+    if (hp.qk_norm) {
+      if ((rc = launch_qk_norm(q, nqkv, L.q_norm, nt, hp.n_head, hp.head_dim, eps, s))) return rc;
+      if ((rc = launch_qk_norm(k, nqkv, L.k_norm, nt, hp.n_head_kv, hp.head_dim, eps, s))) return rc;
+    }
+    if ((rc = launch_rope_kvstore(q, nqkv, k, v, nqkv, w.pos, nt, hp.n_head, hp.n_head_kv, hp.head_dim,
+                                  md->rope_table, kv->k[l], kv->v[l], s)))
+      return rc;
+    if ((rc = launch_attention(q, nqkv, kv->k[l], kv->v[l], w.pos, nt, max_pos, hp.n_head, hp.n_head_kv,
+                               hp.head_dim, w.attn, nq, s)))
+      return rc;
+    // attention output [nt][nq] back to Q8_0
+    const int rows = last ? 1 : nt;                       // tail: only the last token continues
+    const float* o_src = last ? w.attn + (size_t)(nt - 1) * nq : w.attn;
+    float* h_rows = last ? h_last : w.h;
+    if ((rc = launch_quantize(o_src, rows, nq, nq, w.xq, w.xs, s))) return rc;
+    GemmArgs go{};
+    go.a_codes = w.xq; go.a_scales = w.xs; go.m = rows;
+    go.w_codes = L.wo.codes; go.w_scales = L.wo.scales; go.n = H; go.k = nq;
+    go.residual = h_rows; go.out = h_rows; go.ld_out = H;
+    go.workspace = w.gemm_ws; go.workspace_bytes = w.gemm_ws_bytes;
+    if ((rc = launch_gemm_q8(go, s))) return rc;
+    if ((rc = launch_rmsnorm_quant(h_rows, L.ffn_norm, rows, H, eps, w.xq, w.xs, nullptr, s))) return rc;
+    GemmArgs gg{};
+    gg.a_codes = w.xq; gg.a_scales = w.xs; gg.m = rows;
+    gg.w_codes = L.w_gate_up.codes; gg.w_scales = L.w_gate_up.scales; gg.n = 2 * F; gg.k = H;
+    int8_t* s_codes = w.sq;
+    uint16_t* s_scales = w.ss;
+    gg.q_codes = s_codes; gg.q_scales = s_scales;
+    gg.workspace = w.gemm_ws; gg.workspace_bytes = w.gemm_ws_bytes;
+    if ((rc = launch_gemm_q8(gg, s))) return rc;
+    GemmArgs gd{};
+    gd.a_codes = s_codes; gd.a_scales = s_scales; gd.m = rows;
+    gd.w_codes = L.w_down.codes; gd.w_scales = L.w_down.scales; gd.n = H; gd.k = F;
+    gd.residual = h_rows; gd.out = h_rows; gd.ld_out = H;
+    gd.workspace = w.gemm_ws; gd.workspace_bytes = w.gemm_ws_bytes;
+    if ((rc = launch_gemm_q8(gd, s))) return rc;
+  }
+  const mi_q8_matrix& head = hp.tied ? md->token_embd : md->output;
+  if ((rc = launch_rmsnorm_quant(h_last, md->output_norm, 1, H, eps, w.lm_q, w.lm_s, nullptr, s))) return rc;
+  if ((rc = launch_lm_head(w.lm_q, w.lm_s, H, head.codes, head.scales, head.rows, logits_out, s))) return rc;
+  return MI_OK;
+}

@@ -1,0 +1,232 @@
+// Elementwise and row-wise kernels that end in (or feed) Q8_0:
+//   quantize, RMSNorm + quantize, SwiGLU + quantize, embedding rows, per-head QK RMSNorm.
+//
+// Every kernel reads each input element once and writes each output once, with
+// 16-byte accesses laid out so that consecutive lanes touch consecutive addresses
+// (these kernels are HBM-bound).  Floating-point node math runs in f64 and rounds
+// once to f32; the Q8_0 step is the bit-exact f32 quantizer of common.h.
+#include "common.h"
+
+namespace mi {
+
+// ---------------------------------------------------------------- plain quantizer
+// One lane per 4 values; 8 lanes per Q8_0 block; flat grid over all float4 of the
+// matrix (cols % 32 == 0 so a block never straddles rows).
+__global__ void __launch_bounds__(256) k_quantize(const float* __restrict__ x, int64_t rows, int cols,
+                                                  int64_t ld_x, int8_t* __restrict__ codes,
+                                                  uint16_t* __restrict__ scales) {
+  const int64_t nvec_row = cols / 4;
+  const int64_t total = rows * nvec_row;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total + 0; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / nvec_row, c4 = i - r * nvec_row;
+    const float4 v = *reinterpret_cast<const float4*>(x + r * ld_x + c4 * 4);
+    float d;
+    const uint32_t q = q8_block_quant4(v, d);
+    reinterpret_cast<uint32_t*>(codes + r * cols)[c4] = q;
+    if ((c4 & 7) == 0) scales[r * (cols / QK) + c4 / 8] = f32_to_f16_bits(d);
+  }
+}
+
+// The shuffle inside q8_block_quant4 needs all 8 lanes of a block active, so grid-stride
+// loops must keep whole lane groups together: total % 8 == 0 always holds (cols % 32 == 0)
+// and the stride is a multiple of 64, so a group is either fully in range or fully out.
+
+int launch_quantize(const float* x, int64_t rows, int cols, int64_t ld_x, int8_t* codes,
+                    uint16_t* scales, hipStream_t s) {
+  if (rows == 0) return MI_OK;
+  const int64_t total = rows * (cols / 4);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_quantize, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, cols, ld_x, codes, scales);
+  MI_LAUNCH_CHECK("k_quantize");
+  return MI_OK;
+}
+
+// ---------------------------------------------------------------- block reductions
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <int NT>
+__device__ double block_sum_f64(double v, double* sh) {
+  v = wave_sum_f64(v);
+  const int w = threadIdx.x / 64, l = threadIdx.x % 64;
+  if (l == 0) sh[w] = v;
+  __syncthreads();
+  double t = 0;
+  if (threadIdx.x < NT / 64) t = sh[threadIdx.x];
+  if (threadIdx.x < 64) {
+    t = wave_sum_f64(t);
+    if (threadIdx.x == 0) sh[NT / 64] = t;
+  }
+  __syncthreads();
+  return sh[NT / 64];
+}
+
+// ---------------------------------------------------------------- RMSNorm + quantize
+// One workgroup per row.  y = f32(x / sqrt(mean(x^2) + eps) * gamma) with the mean,
+// sqrt, divide and gain in f64; then Q8_0 per 32-block.  Rows of up to 16 float4 per
+// thread stay in registers (cols <= 16384), longer rows are re-read.
+constexpr int RN_THREADS = 256;
+constexpr int RN_MAXV = 8;  // float4 per thread kept in registers
+
+__global__ void __launch_bounds__(RN_THREADS) k_rmsnorm_quant(const float* __restrict__ x,
+                                                             const float* __restrict__ gamma, int cols,
+                                                             float eps, int8_t* __restrict__ codes,
+                                                             uint16_t* __restrict__ scales,
+                                                             float* __restrict__ y_out) {
+  __shared__ double sh[RN_THREADS / 64 + 1];
+  const int64_t r = blockIdx.x;
+  const float* xr = x + r * cols;
+  const int nvec = cols / 4;
+  float4 keep[RN_MAXV];
+  double ss = 0.0;
+#pragma unroll
+  for (int j = 0; j < RN_MAXV; ++j) {
+    const int c4 = threadIdx.x + j * RN_THREADS;
+    if (c4 < nvec) {
+      keep[j] = reinterpret_cast<const float4*>(xr)[c4];
+      const double a = keep[j].x, b = keep[j].y, c = keep[j].z, d = keep[j].w;
+      ss += a * a + b * b + c * c + d * d;
+    }
+  }
+  for (int c4 = threadIdx.x + RN_MAXV * RN_THREADS; c4 < nvec; c4 += RN_THREADS) {
+    const float4 v = reinterpret_cast<const float4*>(xr)[c4];
+    const double a = v.x, b = v.y, c = v.z, d = v.w;
+    ss += a * a + b * b + c * c + d * d;
+  }
+  const double total = block_sum_f64<RN_THREADS>(ss, sh);
+  const double rms = sqrt(total / (double)cols + (double)eps);
+  // rows are a multiple of 32 values; lane groups of 8 cover one block, and all 8 lanes of
+  // a group share the same loop trip count, so the shuffles see a full group.
+  for (int c4 = threadIdx.x, j = 0; c4 < nvec; c4 += RN_THREADS, ++j) {
+    const float4 v = (j < RN_MAXV) ? keep[j] : reinterpret_cast<const float4*>(xr)[c4];
+    const float4 g = reinterpret_cast<const float4*>(gamma)[c4];
+    float4 o;
+    o.x = (float)((double)v.x / rms * (double)g.x);
+    o.y = (float)((double)v.y / rms * (double)g.y);
+    o.z = (float)((double)v.z / rms * (double)g.z);
+    o.w = (float)((double)v.w / rms * (double)g.w);
+    if (y_out) reinterpret_cast<float4*>(y_out + r * cols)[c4] = o;
+    float d;
+    const uint32_t q = q8_block_quant4(o, d);
+    reinterpret_cast<uint32_t*>(codes + r * cols)[c4] = q;
+    if ((c4 & 7) == 0) scales[r * (cols / QK) + c4 / 8] = f32_to_f16_bits(d);
+  }
+}
+
+int launch_rmsnorm_quant(const float* x, const float* gamma, int64_t rows, int cols, float eps,
+                         int8_t* codes, uint16_t* scales, float* y, hipStream_t s) {
+  if (rows == 0) return MI_OK;
+  hipLaunchKernelGGL(k_rmsnorm_quant, dim3((unsigned)rows), dim3(RN_THREADS), 0, s, x, gamma, cols, eps,
+                     codes, scales, y);
+  MI_LAUNCH_CHECK("k_rmsnorm_quant");
+  return MI_OK;
+}
+
+// ---------------------------------------------------------------- SwiGLU + quantize
+// s = f32(g / (1 + exp(-g)) * u) in f64, then Q8_0.  Flat grid over float4s.
+__device__ __forceinline__ float swiglu1(float g, float u) {
+  const double gd = g;
+  const double sg = gd / (1.0 + exp(-gd));
+  return (float)(sg * (double)u);
+}
+
+__global__ void __launch_bounds__(256) k_swiglu_quant(const float* __restrict__ gate,
+                                                      const float* __restrict__ up, int64_t rows, int cols,
+                                                      int64_t ld_in, int8_t* __restrict__ codes,
+                                                      uint16_t* __restrict__ scales) {
+  const int64_t nvec_row = cols / 4;
+  const int64_t total = rows * nvec_row;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / nvec_row, c4 = i - r * nvec_row;
+    const float4 g = *reinterpret_cast<const float4*>(gate + r * ld_in + c4 * 4);
+    const float4 u = *reinterpret_cast<const float4*>(up + r * ld_in + c4 * 4);
+    float4 o;
+    o.x = swiglu1(g.x, u.x);
+    o.y = swiglu1(g.y, u.y);
+    o.z = swiglu1(g.z, u.z);
+    o.w = swiglu1(g.w, u.w);
+    float d;
+    const uint32_t q = q8_block_quant4(o, d);
+    reinterpret_cast<uint32_t*>(codes + r * cols)[c4] = q;
+    if ((c4 & 7) == 0) scales[r * (cols / QK) + c4 / 8] = f32_to_f16_bits(d);
+  }
+}
+
+int launch_swiglu_quant(const float* gate, const float* up, int64_t rows, int cols, int64_t ld_in,
+                        int8_t* codes, uint16_t* scales, hipStream_t s) {
+  if (rows == 0) return MI_OK;
+  const int64_t total = rows * (cols / 4);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_swiglu_quant, dim3((unsigned)blocks), dim3(256), 0, s, gate, up, rows, cols, ld_in,
+                     codes, scales);
+  MI_LAUNCH_CHECK("k_swiglu_quant");
+  return MI_OK;
+}
+
+// ---------------------------------------------------------------- embedding rows
+// out[t][c] = scale[id][c/32] * code[id][c]  (exact in f32).  One lane per 4 values.
+__global__ void __launch_bounds__(256) k_embed(const int8_t* __restrict__ codes,
+                                               const uint16_t* __restrict__ scales, int cols,
+                                               const int32_t* __restrict__ ids, int n, float* __restrict__ out) {
+  const int64_t nvec_row = cols / 4;
+  const int64_t total = (int64_t)n * nvec_row;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / nvec_row, c4 = i - t * nvec_row;
+    const int64_t row = ids[t];
+    const uint32_t q = reinterpret_cast<const uint32_t*>(codes + row * cols)[c4];
+    const float d = f16_bits_to_f32(scales[row * (cols / QK) + c4 / 8]);
+    float4 o;
+    o.x = d * (float)(int8_t)(q & 0xff);
+    o.y = d * (float)(int8_t)((q >> 8) & 0xff);
+    o.z = d * (float)(int8_t)((q >> 16) & 0xff);
+    o.w = d * (float)(int8_t)(q >> 24);
+    reinterpret_cast<float4*>(out + t * cols)[c4] = o;
+  }
+}
+
+int launch_embed(const int8_t* codes, const uint16_t* scales, int cols, const int32_t* ids, int n,
+                 float* out, hipStream_t s) {
+  if (n == 0) return MI_OK;
+  const int64_t total = (int64_t)n * (cols / 4);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_embed, dim3((unsigned)blocks), dim3(256), 0, s, codes, scales, cols, ids, n, out);
+  MI_LAUNCH_CHECK("k_embed");
+  return MI_OK;
+}
+
+// ---------------------------------------------------------------- per-head QK RMSNorm
+// One wave per (row, head); head_dim <= 128 so each lane holds at most 2 values.
+__global__ void __launch_bounds__(256) k_qk_norm(float* __restrict__ x, int64_t ld, const float* __restrict__ gamma,
+                                                 int64_t rows, int n_heads, int head_dim, float eps) {
+  const int64_t wave = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / 64;
+  const int lane = threadIdx.x % 64;
+  if (wave >= rows * n_heads) return;  // whole waves exit together
+  const int64_t r = wave / n_heads;
+  const int h = (int)(wave - r * n_heads);
+  float* p = x + r * ld + (int64_t)h * head_dim;
+  const bool has0 = lane < head_dim, has1 = lane + 64 < head_dim;
+  const float v0 = has0 ? p[lane] : 0.0f, v1 = has1 ? p[lane + 64] : 0.0f;
+  double ss = (double)v0 * v0 + (double)v1 * v1;
+  ss = wave_sum_f64(ss);
+  const double rms = sqrt(ss / (double)head_dim + (double)eps);
+  if (has0) p[lane] = (float)((double)v0 / rms * (double)gamma[lane]);
+  if (has1) p[lane + 64] = (float)((double)v1 / rms * (double)gamma[lane + 64]);
+}
+
+int launch_qk_norm(float* x, int64_t ld, const float* gamma, int64_t rows, int n_heads, int head_dim,
+                   float eps, hipStream_t s) {
+  if (rows == 0) return MI_OK;
+  const int64_t waves = rows * n_heads;
+  const int64_t blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL(k_qk_norm, dim3((unsigned)blocks), dim3(256), 0, s, x, ld, gamma, rows, n_heads,
+                     head_dim, eps);
+  MI_LAUNCH_CHECK("k_qk_norm");
+  return MI_OK;
+}
+
+}  // namespace mi

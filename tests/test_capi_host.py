@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, and rejects
+bad calls with the documented error codes before touching a device (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from quantized_transformer_prefill_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mi_prefill.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(mi_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 15, names
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in mi_prefill.h but not exported"
+        assert n in B.SIGNATURES, f"{n} has no binding signature"
+    assert lib.mi_version().startswith(b"mi_prefill")
+
+
+FAKE = 0x10000  # a non-null pointer value that is never dereferenced on these paths
+
+
+def _fake_q8(rows, cols):
+    return B.Q8Matrix(FAKE, FAKE, rows, cols)
+
+
+def make_model(n_layers=2, hidden=64, nh=4, nkv=2, hd=64, ffn=96, vocab=50, max_tokens=8, n_ctx=16,
+               ws_bytes=None):
+    hp = B.Hparams(n_layers, hidden, nh, nkv, hd, ffn, vocab, 1e-6, 1e6, 1, 0, 0)
+    layers = (B.LayerWeights * n_layers)()
+    for L in layers:
+        L.wqkv = _fake_q8(nh * hd + 2 * nkv * hd, hidden)
+        L.wo = _fake_q8(hidden, nh * hd)
+        L.w_gate_up = _fake_q8(2 * ffn, hidden)
+        L.w_down = _fake_q8(hidden, ffn)
+        L.bqkv = L.attn_norm = L.ffn_norm = FAKE
+    need = B.lib().mi_prefill_workspace_bytes(C.byref(hp), max_tokens)
+    model = B.Model(hp, _fake_q8(vocab, hidden), _fake_q8(vocab, hidden), FAKE,
+                    C.cast(layers, C.POINTER(B.LayerWeights)), FAKE, n_ctx, FAKE,
+                    need if ws_bytes is None else ws_bytes, max_tokens, None)
+    kk = (C.c_void_p * n_layers)(*([FAKE] * n_layers))
+    kv = B.KvRegions(kk, kk, n_layers, n_ctx, nkv * hd)
+    return model, kv, (layers, kk)
+
+
+def call_forward(model, kv, ids, pos, n_ctx=16):
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    return B.lib().mi_prefill_forward(C.byref(model), ids.ctypes.data, pos.ctypes.data, ids.shape[0], n_ctx,
+                                      C.byref(kv), FAKE)
+
+
+def test_forward_rejects_out_of_range_positions():
+    model, kv, keep = make_model()
+    assert call_forward(model, kv, [1, 2, 3], [0, 1, 16]) == B.MI_ERR_POSITION_RANGE
+    assert b"position 16" in B.lib().mi_last_error()
+    assert call_forward(model, kv, [1, 2, 3], [0, -1, 2]) == B.MI_ERR_POSITION_RANGE
+
+
+def test_forward_rejects_duplicate_positions():
+    model, kv, keep = make_model()
+    assert call_forward(model, kv, [1, 2, 3], [4, 1, 4]) == B.MI_ERR_DUP_POSITION
+
+
+def test_forward_rejects_kv_mismatch_and_sizes():
+    model, kv, keep = make_model()
+    assert call_forward(model, kv, [1, 2], [0, 1], n_ctx=15) == B.MI_ERR_KV_MISMATCH
+    kv.n_kv_embd = 64
+    assert call_forward(model, kv, [1, 2], [0, 1]) == B.MI_ERR_KV_MISMATCH
+    model, kv, keep = make_model()
+    assert call_forward(model, kv, list(range(9)), list(range(9))) == B.MI_ERR_WORKSPACE
+    model, kv, keep = make_model(ws_bytes=100)
+    assert call_forward(model, kv, [1], [0]) == B.MI_ERR_WORKSPACE
+    model, kv, keep = make_model()
+    assert call_forward(model, kv, [], []) == B.MI_ERR_INVALID_ARG
+    assert call_forward(model, kv, [50], [0]) == B.MI_ERR_INVALID_ARG  # id outside vocab
+
+
+def test_forward_rejects_bad_shapes():
+    model, kv, keep = make_model()
+    keep[0][1].w_down = _fake_q8(64, 64)  # ffn mismatch
+    assert call_forward(model, kv, [1], [0]) == B.MI_ERR_INVALID_ARG
+    hp = B.Hparams(1, 64, 4, 3, 64, 96, 50, 1e-6, 1e6, 0, 0, 0)  # 4 % 3 != 0
+    assert B.lib().mi_prefill_workspace_bytes(C.byref(hp), 8) == 0
+    hp = B.Hparams(1, 64, 4, 2, 96, 96, 50, 1e-6, 1e6, 0, 0, 0)  # head_dim 96 unsupported
+    assert B.lib().mi_prefill_workspace_bytes(C.byref(hp), 8) == 0
+
+
+def test_per_op_argument_checks():
+    L = B.lib()
+    assert L.mi_quantize_q8_0(FAKE, 2, 48, FAKE, FAKE, None) == B.MI_ERR_INVALID_ARG
+    w = _fake_q8(64, 48)
+    assert L.mi_gemm_q8_0(FAKE, FAKE, 4, C.byref(w), None, None, FAKE, None) == B.MI_ERR_INVALID_ARG
+    assert L.mi_attention_gqa(FAKE, FAKE, FAKE, FAKE, 3, 16, 4, 2, 64, 16, FAKE, None) == B.MI_ERR_POSITION_RANGE
+    assert L.mi_rope_kvstore(FAKE, FAKE, FAKE, FAKE, 3, 4, 2, 64, FAKE, 8, FAKE, FAKE, 16, None) == \
+        B.MI_ERR_INVALID_ARG  # rope table shorter than n_ctx
+    gu = _fake_q8(96, 64)  # rows not a multiple of 64
+    assert L.mi_gemm_swiglu_q8_0(FAKE, FAKE, 2, C.byref(gu), FAKE, FAKE, None, 0, None) == B.MI_ERR_INVALID_ARG
+
+
+def test_workspace_grows_with_tokens():
+    hp = B.Hparams(24, 896, 14, 2, 64, 4864, 151936, 1e-6, 1e6, 1, 0, 1)
+    a = B.lib().mi_prefill_workspace_bytes(C.byref(hp), 16)
+    b = B.lib().mi_prefill_workspace_bytes(C.byref(hp), 512)
+    assert 0 < a < b
+    assert B.lib().mi_rope_table_bytes(C.byref(hp), 4096) == 4096 * 32 * 2 * 8

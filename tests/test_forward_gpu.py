@@ -1,0 +1,155 @@
+"""End-to-end parity of mi_prefill_forward with the oracle, plus the forward's invariants on GPU."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from quantized_transformer_prefill_amd import binding as B
+from quantized_transformer_prefill_amd.model import PrefillModel
+from tests.gpu_util import assert_f32_match, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = -777.25
+
+# spec bar for last-token logits
+MAX_ABS, REL_L2 = 2e-2, 1e-3
+
+
+def load_pair(cfg, dev, max_tokens=None):
+    """GPU model and oracle weights from the same seeded draws (drawn once, on the device)."""
+    host = {}
+
+    def tensors():
+        for name, kind, t in synth.iter_tensors(cfg, device=dev):
+            host[name] = t.cpu().numpy()
+            yield name, kind, t
+
+    m = PrefillModel(cfg, tensors(), max_tokens or cfg.prefix_tokens + cfg.n_tokens, cfg.n_ctx, device=dev,
+                     kv_fill=SENTINEL)
+    q8 = [n for n, s, k in synth.tensor_specs(cfg) if k == "q8"]
+    return m, oracle.weights_from_arrays(host, q8)
+
+
+def compare_logits(got, want, what):
+    got = np.asarray(got, np.float32)
+    d = got.astype(np.float64) - want
+    rel = np.linalg.norm(d) / np.linalg.norm(want)
+    say(f"  {what}: max-abs {np.abs(d).max():.3e} rel-L2 {rel:.3e} identical {np.mean(got == want):.6f}")
+    assert np.abs(d).max() <= MAX_ABS and rel <= REL_L2, what
+
+
+def run_pair(cfg, dev):
+    m, w = load_pair(cfg, dev)
+    pre_ids, ids = synth.gen_token_ids(cfg)
+    pre_pos, pos = synth.positions_for(cfg)
+    kk, vv = oracle.new_kv_regions(cfg, cfg.n_ctx, fill=SENTINEL)
+    if cfg.prefix_tokens:
+        m.forward(pre_ids, pre_pos)
+        oracle.prefill_forward(cfg, w, pre_ids, pre_pos, cfg.n_ctx, kk, vv)
+    logits = m.forward(ids, pos).cpu().numpy()
+    want = oracle.prefill_forward(cfg, w, ids, pos, cfg.n_ctx, kk, vv)[0]
+    return m, logits, want, kk, vv
+
+
+TINY_Q3 = synth.ModelConfig(name="tiny_qwen3", n_layers=3, hidden=256, n_head=8, n_head_kv=2, head_dim=128,
+                            ffn=384, vocab=1000, n_tokens=45, n_ctx=96, seed=7, qkv_bias=False, qk_norm=True,
+                            tied=True)
+TINY_Q2 = synth.ModelConfig(name="tiny_qwen2_ctx", n_layers=2, hidden=128, n_head=4, n_head_kv=1, head_dim=64,
+                            ffn=192, vocab=700, n_tokens=20, n_ctx=50, seed=8, qkv_bias=True, prefix_tokens=17)
+
+
+@pytest.mark.parametrize("cfg", [synth.LAYER1, TINY_Q3, TINY_Q2], ids=lambda c: c.name)
+def test_forward_matches_oracle(cfg):
+    dev = need_gpu()
+    say(f"forward {cfg.name}")
+    m, logits, want, kk, vv = run_pair(cfg, dev)
+    compare_logits(logits, want, f"{cfg.name} logits")
+    assert_f32_match(logits, want, max_ulp=64, max_frac_inexact=0.05, what=f"{cfg.name} logits ulp")
+    gk, gv = m.kv_k.cpu().numpy(), m.kv_v.cpu().numpy()
+    used = np.arange(cfg.prefix_tokens + cfg.n_tokens)
+    free = np.arange(used.size, cfg.n_ctx)
+    assert np.all(gk[:, free] == SENTINEL) and np.all(gv[:, free] == SENTINEL), "stray KV writes"
+    assert_f32_match(gk[:, used], kk[:, used], max_ulp=64, max_frac_inexact=0.05, what="K regions")
+    assert_f32_match(gv[:, used], vv[:, used], max_ulp=64, max_frac_inexact=0.05, what="V regions")
+
+
+def test_prefill_equals_replay_and_chunks_on_gpu():
+    dev = need_gpu()
+    cfg = synth.LAYER1
+    m, _ = load_pair(cfg, dev)
+    _, ids = synth.gen_token_ids(cfg)
+    pos = np.arange(cfg.n_tokens, dtype=np.int32)
+    full = m.forward(ids, pos).cpu().numpy().copy()
+    k_full = m.kv_k.cpu().numpy().copy()
+    m.kv_k.fill_(SENTINEL)
+    m.kv_v.fill_(SENTINEL)
+    for t in range(cfg.n_tokens):                       # token by token through the same regions
+        step = m.forward(ids[t:t + 1], pos[t:t + 1]).cpu().numpy().copy()
+    assert_f32_match(step, full, max_ulp=4, max_frac_inexact=0.01, what="replay logits")
+    assert_f32_match(m.kv_k.cpu().numpy(), k_full, max_ulp=4, max_frac_inexact=0.01, what="replay K")
+    m.kv_k.fill_(SENTINEL)
+    m.kv_v.fill_(SENTINEL)
+    m.forward(ids[:5], pos[:5])                         # prefix, then the rest at later positions
+    two = m.forward(ids[5:], pos[5:]).cpu().numpy().copy()
+    assert_f32_match(two, full, max_ulp=4, max_frac_inexact=0.01, what="chunked logits")
+
+
+def test_future_tokens_leave_earlier_kv_rows_bit_identical():
+    dev = need_gpu()
+    cfg = synth.LAYER1
+    m, _ = load_pair(cfg, dev)
+    _, ids = synth.gen_token_ids(cfg)
+    pos = np.arange(cfg.n_tokens, dtype=np.int32)
+    m.forward(ids, pos)
+    k1 = m.kv_k.cpu().numpy().copy()
+    ids2 = ids.copy()
+    ids2[10:] = (ids2[10:] + 1) % cfg.vocab
+    m.forward(ids2, pos)
+    k2 = m.kv_k.cpu().numpy()
+    np.testing.assert_array_equal(k1[:, :10], k2[:, :10])
+    assert not np.array_equal(k1[:, 10:16], k2[:, 10:16])
+
+
+def test_forward_errors_leave_state_untouched():
+    dev = need_gpu()
+    cfg = synth.LAYER1
+    m, _ = load_pair(cfg, dev)
+    before = m.kv_k.cpu().numpy().copy()
+    with pytest.raises(B.MiError) as e:
+        m.forward([1, 2], [0, cfg.n_ctx])
+    assert e.value.code == B.MI_ERR_POSITION_RANGE
+    with pytest.raises(B.MiError) as e:
+        m.forward([1, 2], [3, 3])
+    assert e.value.code == B.MI_ERR_DUP_POSITION
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(m.kv_k.cpu().numpy(), before)
+
+
+def test_headline_config_matches_oracle():
+    """The 24-layer 0.5B-shaped model on its 512-token prompt, logits and all KV rows."""
+    dev = need_gpu()
+    cfg = synth.QWEN2_0P5B
+    say(f"forward {cfg.name}")
+    m, logits, want, kk, vv = run_pair(cfg, dev)
+    compare_logits(logits, want, f"{cfg.name} logits")
+    gk = m.kv_k.cpu().numpy()
+    n = cfg.n_tokens
+    assert np.all(gk[:, n:] == SENTINEL)
+    d = np.linalg.norm(gk[:, :n] - kk[:, :n]) / np.linalg.norm(kk[:, :n])
+    say(f"  K regions rel-L2 {d:.3e}, identical {np.mean(gk[:, :n] == kk[:, :n]):.6f}")
+    assert d <= 1e-3
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["qwen2p5_7b_pp2048", "qwen3_8b_chunk3072at1024"])
+def test_large_configs_match_oracle(name):
+    if not os.environ.get("MI_RUN_SLOW"):
+        pytest.skip("set MI_RUN_SLOW=1 (the oracle needs tens of TFLOP on the host)")
+    dev = need_gpu()
+    cfg = synth.MODEL_CONFIGS[name]
+    m, logits, want, kk, vv = run_pair(cfg, dev)
+    compare_logits(logits, want, f"{cfg.name} logits")

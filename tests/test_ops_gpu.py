@@ -1,0 +1,271 @@
+"""Per-op parity: every C-ABI entry point against the oracle on the same seeded inputs."""
+import ctypes as C
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ops
+from oracle.q8_0 import quantize_q8_0
+from quantized_transformer_prefill_amd import binding as B
+from quantized_transformer_prefill_amd.model import interleave_gate_up
+from tests.gpu_util import assert_codes_match, assert_f32_match, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+f32 = np.float32
+
+
+def outlier_acts(m, k, seed, dev):
+    x, _ = synth.gen_gemm_inputs(synth.GemmCase(m, k, 32, seed=seed), device=dev)
+    return x.contiguous()
+
+
+# ---------------------------------------------------------------- quantizer
+def test_quantize_bit_exact_worked_blocks_and_c2_activations():
+    dev = need_gpu()
+    from tests.test_oracle_q8_0 import load_worked_blocks
+    rows = []
+    for case in load_worked_blocks():
+        r = np.zeros(32, dtype=f32)
+        for i, v in case["x"].items():
+            r[i] = v
+        rows.append(r)
+    x = torch.tensor(np.stack(rows), device=dev)
+    gc, gs = B.quantize_q8_0(x)
+    oc, os_ = quantize_q8_0(x.cpu().numpy())
+    assert_codes_match(gc, gs, oc, os_, what="worked blocks")
+    for case in synth.GEMM_SWEEP:  # the activation matrices of the GEMM sweep at full size
+        x = outlier_acts(case.m, case.k, case.seed, dev)
+        say(f"quantize {case.name}")
+        gc, gs = B.quantize_q8_0(x)
+        oc, os_ = quantize_q8_0(x.cpu().numpy())
+        assert_codes_match(gc, gs, oc, os_, what=case.name)
+
+
+def test_quantize_extreme_ranges():
+    dev = need_gpu()
+    g = torch.Generator(device=dev).manual_seed(5)
+    parts = [torch.randn(40, 96, generator=g, device=dev) * s for s in (1e-7, 1e-3, 1.0, 1e4)]
+    x = torch.cat(parts).contiguous()
+    x[3, :32] = 0.0
+    gc, gs = B.quantize_q8_0(x)
+    oc, os_ = quantize_q8_0(x.cpu().numpy())
+    assert_codes_match(gc, gs, oc, os_, what="scales 1e-7..1e4")
+
+
+# ---------------------------------------------------------------- matmul
+def q8_pair(w_dev):
+    gc, gs = B.quantize_q8_0(w_dev)
+    oc, os_ = quantize_q8_0(w_dev.cpu().numpy())
+    return (gc, gs), (oc, os_)
+
+
+GEMM_CASES = [  # m, k, n, bias, residual, split
+    (77, 320, 192, True, False, 1),
+    (64, 896, 1152, True, False, 1),
+    (130, 4864, 896, False, True, 0),
+    (1, 896, 896, False, True, 1),
+    (5, 3584, 512, True, True, 0),
+    (200, 128, 64, False, False, 1),
+    (33, 1024, 256, True, False, 4),
+]
+
+
+@pytest.mark.parametrize("m,k,n,use_bias,use_res,split", GEMM_CASES,
+                         ids=[f"m{c[0]}_k{c[1]}_n{c[2]}_s{c[5]}" for c in GEMM_CASES])
+def test_gemm_matches_oracle(m, k, n, use_bias, use_res, split):
+    dev = need_gpu()
+    say(f"gemm m={m} k={k} n={n} bias={use_bias} res={use_res} split={split}")
+    x = outlier_acts(m, k, 11, dev)
+    w = synth.gen_normal(12, f"w{n}x{k}", (n, k), std=0.02, device=dev)
+    bias = synth.gen_normal(13, f"b{n}", (n,), std=0.02, device=dev) if use_bias else None
+    res = synth.gen_normal(14, f"r{m}x{n}", (m, n), device=dev) if use_res else None
+    (wc, ws), (owc, ows) = q8_pair(w)
+    xc, xs = B.quantize_q8_0(x)
+    out = B.gemm_q8_0(xc, xs, wc, ws, bias=bias, residual=res, split_k=split)
+    torch.cuda.synchronize()
+    want = ops.matmul_q8_0(x.cpu().numpy(), owc, ows, None if bias is None else bias.cpu().numpy())
+    if res is not None:
+        want = ops.add_f32(res.cpu().numpy(), want)
+    assert_f32_match(out.cpu().numpy(), want, what="gemm out")
+
+
+def test_gemm_in_place_residual():
+    dev = need_gpu()
+    x = outlier_acts(40, 896, 21, dev)
+    w = synth.gen_normal(22, "w", (896, 896), std=0.02, device=dev)
+    h = synth.gen_normal(23, "h", (40, 896), device=dev)
+    h0 = h.cpu().numpy()
+    (wc, ws), (owc, ows) = q8_pair(w)
+    xc, xs = B.quantize_q8_0(x)
+    B.gemm_q8_0(xc, xs, wc, ws, residual=h, out=h)
+    want = ops.add_f32(h0, ops.matmul_q8_0(x.cpu().numpy(), owc, ows))
+    assert_f32_match(h.cpu().numpy(), want, what="h += x W")
+
+
+@pytest.mark.parametrize("case", synth.GEMM_SWEEP, ids=lambda c: c.name)
+def test_gemm_full_size_sampled(case):
+    """The GEMM sweep at full size, in the launch configuration the benchmark uses (library's own
+    split choice); the oracle computes 512 sampled outputs one by one."""
+    dev = need_gpu()
+    say(f"gemm full size {case.name}")
+    x, w = synth.gen_gemm_inputs(case, device=dev)
+    xc, xs = B.quantize_q8_0(x)
+    wc, ws = B.quantize_q8_0(w)
+    out = B.gemm_q8_0(xc, xs, wc, ws, split_k=0)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(case.m + case.n)
+    rows = rng.integers(0, case.m, 512)
+    cols = rng.integers(0, case.n, 512)
+    rows[:2], cols[:2] = [0, case.m - 1], [0, case.n - 1]
+    xr = x[torch.as_tensor(rows, device=dev)].cpu().numpy()
+    wr = w[torch.as_tensor(cols, device=dev)].cpu().numpy()
+    oq, od = quantize_q8_0(wr)
+    want = np.array([ops.matmul_q8_0(xr[i:i + 1], oq[i:i + 1], od[i:i + 1])[0, 0] for i in range(512)], dtype=f32)
+    got = out.cpu().numpy()[rows, cols]
+    assert_f32_match(got, want, what=f"{case.name} sampled")
+
+
+def test_gemm_swiglu_matches_oracle():
+    dev = need_gpu()
+    for m, k, f in [(100, 896, 320), (16, 3584, 512), (1, 896, 4864)]:
+        say(f"gemm+swiglu m={m} k={k} ffn={f}")
+        x = synth.gen_normal(31, f"x{m}", (m, k), device=dev)
+        wg = synth.gen_normal(32, f"g{f}", (f, k), std=0.02, device=dev)
+        wu = synth.gen_normal(33, f"u{f}", (f, k), std=0.02, device=dev)
+        (gc, gs), (ogc, ogs) = q8_pair(wg)
+        (uc, us), (ouc, ous) = q8_pair(wu)
+        wgu_c = interleave_gate_up(gc, uc).contiguous()
+        wgu_s = interleave_gate_up(gs, us).contiguous()
+        xc, xs = B.quantize_q8_0(x)
+        ws_bytes = B.lib().mi_gemm_q8_0_workspace_bytes(m, 2 * f, k)
+        wsp = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=dev)
+        sc, ss = B.gemm_swiglu_q8_0(xc, xs, wgu_c, wgu_s, workspace=wsp)
+        xh = x.cpu().numpy()
+        s = ops.swiglu(ops.matmul_q8_0(xh, ogc, ogs), ops.matmul_q8_0(xh, ouc, ous))
+        oc, os_ = quantize_q8_0(s)
+        assert_codes_match(sc, ss, oc, os_, max_frac_code_diff=1e-4, what=f"swiglu codes m={m}")
+
+
+# ---------------------------------------------------------------- row / elementwise ops
+def test_rmsnorm_quant_matches_oracle():
+    dev = need_gpu()
+    for rows, cols in [(37, 896), (5, 4096), (3, 3584), (2, 18944), (1, 64)]:
+        x = synth.gen_normal(41, f"x{rows}", (rows, cols), std=0.7, device=dev)
+        gam = (1 + synth.gen_normal(42, f"g{cols}", (cols,), std=0.02, device=dev)).contiguous()
+        gc, gs, y = B.rmsnorm_quant(x, gam, 1e-6, want_y=True)
+        want_y = ops.rms_norm(x.cpu().numpy(), gam.cpu().numpy(), 1e-6)
+        assert_f32_match(y.cpu().numpy(), want_y, what=f"rmsnorm y {rows}x{cols}")
+        oc, os_ = quantize_q8_0(want_y)
+        assert_codes_match(gc, gs, oc, os_, max_frac_code_diff=1e-4, what=f"rmsnorm codes {rows}x{cols}")
+
+
+def test_swiglu_quant_matches_oracle():
+    dev = need_gpu()
+    g = synth.gen_normal(51, "g", (29, 4864), std=2.0, device=dev)
+    u = synth.gen_normal(52, "u", (29, 4864), device=dev)
+    gc, gs = B.swiglu_quant(g, u)
+    s = ops.swiglu(g.cpu().numpy(), u.cpu().numpy())
+    oc, os_ = quantize_q8_0(s)
+    assert_codes_match(gc, gs, oc, os_, max_frac_code_diff=1e-4, what="swiglu_quant")
+
+
+def test_embed_exact():
+    dev = need_gpu()
+    w = synth.gen_normal(61, "emb", (500, 896), std=0.02, device=dev)
+    (wc, ws), (oc, os_) = q8_pair(w)
+    ids = np.array([499, 0, 7, 7, 250], dtype=np.int32)
+    out = B.embed_q8_0(wc, ws, torch.as_tensor(ids, device=dev))
+    np.testing.assert_array_equal(out.cpu().numpy(), ops.embed_q8_0(oc, os_, ids))
+
+
+def test_qk_norm_matches_oracle():
+    dev = need_gpu()
+    for nh, hd in [(32, 128), (8, 128), (14, 64)]:
+        x = synth.gen_normal(71, f"q{nh}", (19, nh * hd), std=0.5, device=dev)
+        gam = (1 + synth.gen_normal(72, f"g{hd}", (hd,), std=0.02, device=dev)).contiguous()
+        x0 = x.cpu().numpy()
+        B.qk_norm_(x, gam, nh, hd, 1e-6)
+        want = ops.qk_norm(x0.reshape(19, nh, hd), gam.cpu().numpy(), 1e-6).reshape(19, nh * hd)
+        assert_f32_match(x.cpu().numpy(), want, what=f"qk_norm nh={nh} hd={hd}")
+
+
+def _rope_table(nh, nkv, hd, rows, dev):
+    hp = B.Hparams(1, 64, nh, nkv, hd, 64, 64, 1e-6, 1e6, 0, 0, 0)
+    t = torch.empty(B.lib().mi_rope_table_bytes(C.byref(hp), rows) // 8, dtype=torch.float64, device=dev)
+    B.check(B.lib().mi_rope_table_init(C.byref(hp), rows, t.data_ptr(), B.stream_ptr()))
+    return t
+
+
+@pytest.mark.parametrize("nh,nkv,hd", [(14, 2, 64), (32, 8, 128)])
+def test_rope_kvstore_rows_and_values(nh, nkv, hd):
+    dev = need_gpu()
+    n_ctx, n = 4096, 23
+    rng = np.random.default_rng(hd)
+    pos = rng.choice(n_ctx, size=n, replace=False).astype(np.int32)
+    pos[0] = n_ctx - 1
+    q = synth.gen_normal(81, "q", (n, nh * hd), device=dev)
+    k = synth.gen_normal(82, "k", (n, nkv * hd), device=dev)
+    v = synth.gen_normal(83, "v", (n, nkv * hd), device=dev)
+    q0, k0, v0 = q.cpu().numpy(), k.cpu().numpy(), v.cpu().numpy()
+    sentinel = -12345.5
+    kr = torch.full((n_ctx, nkv * hd), sentinel, device=dev)
+    vr = torch.full((n_ctx, nkv * hd), sentinel, device=dev)
+    table = _rope_table(nh, nkv, hd, n_ctx, dev)
+    B.rope_kvstore(q, k, v, torch.as_tensor(pos, device=dev), nh, nkv, hd, table, n_ctx, kr, vr)
+    qw = ops.rope_neox(q0.reshape(n, nh, hd), pos, 1e6).reshape(n, nh * hd)
+    kw = ops.rope_neox(k0.reshape(n, nkv, hd), pos, 1e6).reshape(n, nkv * hd)
+    assert_f32_match(q.cpu().numpy(), qw, what="rope q")
+    krh, vrh = kr.cpu().numpy(), vr.cpu().numpy()
+    assert_f32_match(krh[pos], kw, what="rope k -> region rows")
+    np.testing.assert_array_equal(vrh[pos], v0)
+    untouched = np.setdiff1d(np.arange(n_ctx), pos)
+    assert np.all(krh[untouched] == sentinel) and np.all(vrh[untouched] == sentinel)
+    np.testing.assert_array_equal(k.cpu().numpy(), k0)  # k itself is not modified
+
+
+@pytest.mark.parametrize("nh,nkv,hd,n,n_ctx", [(14, 2, 64, 37, 300), (28, 4, 128, 21, 200), (32, 8, 128, 50, 700),
+                                               (4, 4, 64, 1, 5)])
+def test_attention_matches_oracle(nh, nkv, hd, n, n_ctx):
+    dev = need_gpu()
+    say(f"attention nh={nh} nkv={nkv} hd={hd} n={n} n_ctx={n_ctx}")
+    rng = np.random.default_rng(n)
+    pos = rng.choice(n_ctx, size=n, replace=False).astype(np.int32)  # unsorted, gaps
+    q = synth.gen_normal(91, "q", (n, nh * hd), std=0.6, device=dev)
+    kr = synth.gen_normal(92, "k", (n_ctx, nkv * hd), std=0.6, device=dev)
+    vr = synth.gen_normal(93, "v", (n_ctx, nkv * hd), device=dev)
+    out = B.attention_gqa(q, kr, vr, torch.as_tensor(pos, device=dev), int(pos.max()), nh, nkv, hd)
+    want = ops.attention_gqa(q.cpu().numpy(), kr.cpu().numpy(), vr.cpu().numpy(), pos, nh, nkv, hd)
+    assert_f32_match(out.cpu().numpy(), want, what="attention")
+
+
+def test_attention_invariants():
+    dev = need_gpu()
+    nh, nkv, hd, n = 14, 2, 64, 9
+    pos = np.arange(n, dtype=np.int32)
+    q = synth.gen_normal(95, "q", (n, nh * hd), device=dev)
+    kr = synth.gen_normal(96, "k", (16, nkv * hd), device=dev)
+    ones = torch.ones(16, nkv * hd, device=dev)
+    out = B.attention_gqa(q, kr, ones, torch.as_tensor(pos, device=dev), n - 1, nh, nkv, hd)
+    np.testing.assert_array_equal(out.cpu().numpy(), np.ones((n, nh * hd), f32))   # V = 1 gives 1
+    vr = synth.gen_normal(97, "v", (16, nkv * hd), device=dev)
+    out = B.attention_gqa(q[:1].contiguous(), kr, vr, torch.as_tensor(pos[:1], device=dev), 0, nh, nkv, hd)
+    v0 = vr[0].cpu().numpy()
+    for h in range(nh):                                                             # one row gives v_0
+        g = h // 7
+        np.testing.assert_array_equal(out[0, h * hd:(h + 1) * hd].cpu().numpy(), v0[g * hd:(g + 1) * hd])
+
+
+def test_lm_head_row_matches_oracle():
+    dev = need_gpu()
+    for vocab, hidden in [(8192, 896), (151936, 896), (4000, 4096), (3000, 3584)]:
+        say(f"lm_head vocab={vocab} hidden={hidden}")
+        w = synth.gen_normal(101, f"o{vocab}", (vocab, hidden), std=0.02, device=dev)
+        x = synth.gen_normal(102, f"h{hidden}", (hidden,), std=1.5, device=dev)
+        gam = (1 + synth.gen_normal(103, f"g{hidden}", (hidden,), std=0.02, device=dev)).contiguous()
+        (wc, ws), (oc, os_) = q8_pair(w)
+        logits = B.lm_head_row(x, gam, 1e-6, wc, ws)
+        xn = ops.rms_norm(x.cpu().numpy()[None, :], gam.cpu().numpy(), 1e-6)
+        want = ops.matmul_q8_0(xn, oc, os_)[0]
+        assert_f32_match(logits.cpu().numpy(), want, what=f"logits v={vocab}")
