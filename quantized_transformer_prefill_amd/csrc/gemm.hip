@@ -16,9 +16,10 @@
 // * The VALU f64 epilogue (2 f64 FMAs per output per block) bounds this kernel, not the
 //   MFMA: half-used MFMAs cost nothing extra.
 //
-// Tiling: 256 threads = 4 waves (2 x 2); workgroup tile 64 real rows x 128 weight rows; wave
-// tile 32 x 64 = 2 x 2 MFMAs per block.  A/B codes and the f64 scales of each block are
-// staged through LDS, double-buffered.  Split-K writes f64 partials that a second kernel
+// Tiling: 256 threads = 4 waves (2 x 2).  Wave tile RG x CG MFMAs of 16 real rows x 32 columns:
+// 2 x 2 (workgroup 64 x 128) for large problems, 1 x 1 (workgroup 32 x 64) for small ones.  A
+// stage of 4 blocks (128 K values) of codes and f64 scales goes through LDS, double-buffered,
+// with the next stage's global loads in flight while the current one computes.  Split-K writes f64 partials that a second kernel
 // reduces in a fixed order (deterministic).
 #include "common.h"
 
@@ -28,16 +29,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int G_THREADS = 256;
-constexpr int G_BM = 64;    // real activation rows per workgroup
-constexpr int G_BN = 128;   // weight rows (output columns) per workgroup
+constexpr int G_KS = 4;     // Q8_0 blocks per LDS stage (128 K values)
 constexpr double G_MAGIC = 0x1.8p+52 + 0x1p+31;  // 1.5*2^52 + 2^31, exact
-
-struct GemmSmem {
-  int8_t a[2][G_BM][QK];     // 4 KB
-  int8_t b[2][G_BN][QK];     // 8 KB
-  double as[2][G_BM];        // 1 KB
-  double bs[2][G_BN];        // 2 KB
-};
 
 __device__ __forceinline__ double pair_f64(int lo, int hi) {
   return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
@@ -49,135 +42,196 @@ __device__ __forceinline__ float swiglu_f32(float g, float u) {
   return (float)(sg * (double)u);
 }
 
-template <int EPI, bool SPLIT>
+// Wave tile = RG x CG MFMAs (16 real rows x 32 columns each); workgroup = 2 x 2 waves.
+// LDS rows hold the 4 blocks of a stage back to back (128 bytes) plus 16 bytes of padding, so a
+// row stride of 144 bytes spreads the 16-byte fragment reads of 16 consecutive rows over all
+// banks; one extra all-zero row feeds the odd (dummy) MFMA rows.
+constexpr int G_ROWB = G_KS * QK + 16;  // bytes per LDS row
+
+template <int RG, int CG>
+struct GemmTile {
+  static constexpr int BM = 2 * 16 * RG;   // real activation rows per workgroup
+  static constexpr int BN = 2 * 32 * CG;   // weight rows (output columns) per workgroup
+  static constexpr int A_CHUNKS = BM * G_KS * 2 / G_THREADS;  // 16-byte chunks per thread per stage
+  static constexpr int B_CHUNKS = BN * G_KS * 2 / G_THREADS;
+  static constexpr int AS_PER_T = (BM * G_KS + G_THREADS - 1) / G_THREADS;
+  static constexpr int BS_PER_T = (BN * G_KS + G_THREADS - 1) / G_THREADS;
+  int8_t a[2][BM + 1][G_ROWB];   // row BM is all zeros
+  int8_t b[2][BN][G_ROWB];
+  double as[2][G_KS][BM];
+  double bs[2][G_KS][BN];
+};
+
+template <int RG, int CG, int EPI, bool SPLIT>
 __global__ void __launch_bounds__(G_THREADS, 2)
 k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales, int M,
           const int8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales, int N, int K,
           const float* __restrict__ bias, const float* residual, float* out, int64_t ld_out,
           int8_t* __restrict__ q_codes, uint16_t* __restrict__ q_scales,
           double* __restrict__ partial, int kb_per_split) {
-  __shared__ __align__(16) GemmSmem sm;
+  using T = GemmTile<RG, CG>;
+  constexpr int BM = T::BM, BN = T::BN;
+  __shared__ __align__(16) T sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * G_BN, m0 = blockIdx.y * G_BM;
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
   const int KB = K / QK;
   const int kb0 = blockIdx.z * kb_per_split;
   const int kb1 = min(KB, kb0 + kb_per_split);
 
-  // ---- global -> register prefetch mapping
-  const int ld_row = tid >> 1, ld_half = tid & 1;  // 128 rows x 2 halves of 16 bytes
-  const bool a_ld = tid < 2 * G_BM;
-  const int a_row = m0 + ld_row;
-  const bool a_ok = a_ld && a_row < M;
-  const int b_row = n0 + ld_row;  // N % 32 == 0 and n0 + 128 may exceed N
-  const bool b_ok = b_row < N;
-  const int8_t* a_src = a_codes + (int64_t)(a_ok ? a_row : 0) * K + ld_half * 16;
-  const int8_t* b_src = w_codes + (int64_t)(b_ok ? b_row : 0) * K + ld_half * 16;
-  const uint16_t* as_src = a_scales + (int64_t)(m0 + tid < M ? m0 + tid : 0) * KB;
-  const uint16_t* bs_src = w_scales + (int64_t)(n0 + tid < N ? n0 + tid : 0) * KB;
-  const bool as_ok = tid < G_BM && m0 + tid < M;
-  const bool bs_ok = tid < G_BN && n0 + tid < N;
+  // zero row for the dummy MFMA rows (both stages)
+  if (tid < 2 * G_ROWB / 16) *reinterpret_cast<v4i*>(&sm.a[tid / (G_ROWB / 16)][BM][(tid % (G_ROWB / 16)) * 16]) =
+      v4i{0, 0, 0, 0};
 
-  v4i pa = {0, 0, 0, 0}, pb = {0, 0, 0, 0};
-  uint16_t pas = 0, pbs = 0;
-  auto fetch = [&](int kb) {
-    if (a_ok) pa = *reinterpret_cast<const v4i*>(a_src + (int64_t)kb * QK);
-    if (b_ok) pb = *reinterpret_cast<const v4i*>(b_src + (int64_t)kb * QK);
-    if (as_ok) pas = as_src[kb];
-    if (bs_ok) pbs = bs_src[kb];
+  // ---- prefetch registers for one stage (G_KS blocks).  Codes: chunk c -> row c/8, 16-byte
+  // piece c%8 of the row's 128 stage bytes (8 consecutive threads read 128 contiguous bytes).
+  // Scales: element e -> block e / R, row e % R (consecutive threads fill consecutive LDS slots).
+  v4i pa[T::A_CHUNKS], pb[T::B_CHUNKS];
+  uint16_t pas[T::AS_PER_T], pbs[T::BS_PER_T];
+  auto fetch = [&](int kbs) {
+    const int nb = min(G_KS, kb1 - kbs) * 2;  // 16-byte pieces present in this stage
+#pragma unroll
+    for (int i = 0; i < T::A_CHUNKS; ++i) {
+      const int c = tid + i * G_THREADS, row = c >> 3, piece = c & 7;
+      const int gr = m0 + row;
+      pa[i] = (gr < M && piece < nb)
+                  ? *reinterpret_cast<const v4i*>(a_codes + (int64_t)gr * K + (int64_t)kbs * QK + piece * 16)
+                  : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_CHUNKS; ++i) {
+      const int c = tid + i * G_THREADS, row = c >> 3, piece = c & 7;
+      const int gr = n0 + row;
+      pb[i] = (gr < N && piece < nb)
+                  ? *reinterpret_cast<const v4i*>(w_codes + (int64_t)gr * K + (int64_t)kbs * QK + piece * 16)
+                  : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < T::AS_PER_T; ++i) {
+      const int e = tid + i * G_THREADS, j = e / BM, row = e % BM;
+      const int gr = m0 + row, kb = kbs + j;
+      pas[i] = (e < BM * G_KS && gr < M && kb < kb1) ? a_scales[(int64_t)gr * KB + kb] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int i = 0; i < T::BS_PER_T; ++i) {
+      const int e = tid + i * G_THREADS, j = e / BN, row = e % BN;
+      const int gr = n0 + row, kb = kbs + j;
+      pbs[i] = (e < BN * G_KS && gr < N && kb < kb1) ? w_scales[(int64_t)gr * KB + kb] : (uint16_t)0;
+    }
   };
   auto stash = [&](int st) {
-    if (a_ld) *reinterpret_cast<v4i*>(&sm.a[st][ld_row][ld_half * 16]) = pa;
-    *reinterpret_cast<v4i*>(&sm.b[st][ld_row][ld_half * 16]) = pb;
-    if (tid < G_BM) sm.as[st][tid] = as_ok ? (double)f16_bits_to_f32(pas) : 0.0;
-    if (tid < G_BN) sm.bs[st][tid] = bs_ok ? (double)f16_bits_to_f32(pbs) : 0.0;
+#pragma unroll
+    for (int i = 0; i < T::A_CHUNKS; ++i) {
+      const int c = tid + i * G_THREADS;
+      *reinterpret_cast<v4i*>(&sm.a[st][c >> 3][(c & 7) * 16]) = pa[i];
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_CHUNKS; ++i) {
+      const int c = tid + i * G_THREADS;
+      *reinterpret_cast<v4i*>(&sm.b[st][c >> 3][(c & 7) * 16]) = pb[i];
+    }
+#pragma unroll
+    for (int i = 0; i < T::AS_PER_T; ++i) {
+      const int e = tid + i * G_THREADS;
+      if (e < BM * G_KS) sm.as[st][e / BM][e % BM] = (double)f16_bits_to_f32(pas[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < T::BS_PER_T; ++i) {
+      const int e = tid + i * G_THREADS;
+      if (e < BN * G_KS) sm.bs[st][e / BN][e % BN] = (double)f16_bits_to_f32(pbs[i]);
+    }
   };
 
   v16i cinit;
 #pragma unroll
   for (int i = 0; i < 16; ++i) cinit[i] = (i & 1) ? 0x43380000 : (int)0x80000000;
 
-  double acc[2][2][8];
+  double acc[RG][CG][8];
 #pragma unroll
-  for (int rg = 0; rg < 2; ++rg)
+  for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg)
+    for (int cg = 0; cg < CG; ++cg)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[rg][cg][j] = 0.0;
 
-  const bool a_lane = (lane & 1) == 0;          // even MFMA rows carry data
-  const int a_rrow = wm * 32 + ((lane & 31) >> 1);  // + rg*16
+  const bool a_lane = (lane & 1) == 0;                   // even MFMA rows carry data
+  const int a_rrow = wm * 16 * RG + ((lane & 31) >> 1);   // + rg*16
   const int koff = (lane >> 5) * 16;
-  const int b_rrow = wn * 64 + (lane & 31);         // + cg*32
-  const int da_row = wm * 32 + 2 * (lane >> 5);     // + rg*16 + 4c + e
+  const int b_rrow = wn * 32 * CG + (lane & 31);          // + cg*32
+  const int da_row = wm * 16 * RG + 2 * (lane >> 5);      // + rg*16 + 4c + e
 
   if (kb0 < kb1) {
     fetch(kb0);
     stash(0);
   }
   __syncthreads();
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const int st = (kb - kb0) & 1;
-    if (kb + 1 < kb1) fetch(kb + 1);
-    v4i fa[2], fb[2];
+  for (int kbs = kb0; kbs < kb1; kbs += G_KS) {
+    const int st = ((kbs - kb0) / G_KS) & 1;
+    const bool more = kbs + G_KS < kb1;
+    if (more) fetch(kbs + G_KS);
+#pragma unroll 1
+    for (int jb = 0; jb < G_KS; ++jb) {
+      v4i fa[RG], fb[CG];
 #pragma unroll
-    for (int rg = 0; rg < 2; ++rg)
-      fa[rg] = a_lane ? *reinterpret_cast<const v4i*>(&sm.a[st][a_rrow + rg * 16][koff]) : v4i{0, 0, 0, 0};
+      for (int rg = 0; rg < RG; ++rg)
+        fa[rg] = *reinterpret_cast<const v4i*>(&sm.a[st][a_lane ? a_rrow + rg * 16 : BM][jb * QK + koff]);
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg) fb[cg] = *reinterpret_cast<const v4i*>(&sm.b[st][b_rrow + cg * 32][koff]);
-    v16i d[2][2];
+      for (int cg = 0; cg < CG; ++cg)
+        fb[cg] = *reinterpret_cast<const v4i*>(&sm.b[st][b_rrow + cg * 32][jb * QK + koff]);
+      v16i d[RG][CG];
 #pragma unroll
-    for (int rg = 0; rg < 2; ++rg)
+      for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-      for (int cg = 0; cg < 2; ++cg) d[rg][cg] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[rg], fb[cg], cinit, 0, 0, 0);
-    double dw[2], cdw[2];
+        for (int cg = 0; cg < CG; ++cg) d[rg][cg] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[rg], fb[cg], cinit, 0, 0, 0);
+      double dw[CG], cdw[CG];
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg) {
-      dw[cg] = sm.bs[st][b_rrow + cg * 32];
-      cdw[cg] = -G_MAGIC * dw[cg];
-    }
-#pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-      double da[8];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const double2 v2 = *reinterpret_cast<const double2*>(&sm.as[st][da_row + rg * 16 + 4 * c]);
-        da[2 * c] = v2.x;
-        da[2 * c + 1] = v2.y;
+      for (int cg = 0; cg < CG; ++cg) {
+        dw[cg] = sm.bs[st][jb][b_rrow + cg * 32];
+        cdw[cg] = -G_MAGIC * dw[cg];
       }
 #pragma unroll
-      for (int cg = 0; cg < 2; ++cg)
+      for (int rg = 0; rg < RG; ++rg) {
+        double da[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const double x = pair_f64(d[rg][cg][2 * j], d[rg][cg][2 * j + 1]);
-          const double t = fma(x, dw[cg], cdw[cg]);
-          acc[rg][cg][j] = fma(t, da[j], acc[rg][cg][j]);
+        for (int c = 0; c < 4; ++c) {
+          const double2 v2 = *reinterpret_cast<const double2*>(&sm.as[st][jb][da_row + rg * 16 + 4 * c]);
+          da[2 * c] = v2.x;
+          da[2 * c + 1] = v2.y;
         }
+#pragma unroll
+        for (int cg = 0; cg < CG; ++cg)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const double x = pair_f64(d[rg][cg][2 * j], d[rg][cg][2 * j + 1]);
+            const double t = fma(x, dw[cg], cdw[cg]);
+            acc[rg][cg][j] = fma(t, da[j], acc[rg][cg][j]);
+          }
+      }
     }
-    if (kb + 1 < kb1) stash(st ^ 1);
+    if (more) stash(st ^ 1);
     __syncthreads();
   }
 
-  // ---- epilogue.  Lane holds, for each (rg, cg, j): real row rr, column cc.
+  // ---- epilogue.  Lane holds, for each (rg, cg, j): real row, column.
 #pragma unroll
-  for (int rg = 0; rg < 2; ++rg)
+  for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int row = m0 + wm * 32 + rg * 16 + 4 * (j >> 1) + 2 * (lane >> 5) + (j & 1);
+      const int row = m0 + wm * 16 * RG + rg * 16 + 4 * (j >> 1) + 2 * (lane >> 5) + (j & 1);
       if (SPLIT) {
         if (row < M) {
 #pragma unroll
-          for (int cg = 0; cg < 2; ++cg) {
-            const int col = n0 + wn * 64 + cg * 32 + (lane & 31);
+          for (int cg = 0; cg < CG; ++cg) {
+            const int col = n0 + wn * 32 * CG + cg * 32 + (lane & 31);
             if (col < N) partial[((int64_t)blockIdx.z * M + row) * N + col] = acc[rg][cg][j];
           }
         }
       } else if (EPI == EPI_F32) {
         if (row < M) {
 #pragma unroll
-          for (int cg = 0; cg < 2; ++cg) {
-            const int col = n0 + wn * 64 + cg * 32 + (lane & 31);
+          for (int cg = 0; cg < CG; ++cg) {
+            const int col = n0 + wn * 32 * CG + cg * 32 + (lane & 31);
             if (col < N) {
               double v = acc[rg][cg][j];
               if (bias) v += (double)bias[col];
@@ -188,23 +242,26 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
             }
           }
         }
-      } else {  // EPI_SWIGLU_Q8: cg 0 = gate, cg 1 = up of the same ffn column
-        const int gcol = n0 + wn * 64;               // multiple of 64: 32 gate rows, 32 up rows
-        const float g = (float)acc[rg][0][j];
-        const float u = (float)acc[rg][1][j];
-        const float sv = swiglu_f32(g, u);
-        float m = fabsf(sv);
+      } else {  // EPI_SWIGLU_Q8: column group pairs (2p, 2p+1) = 32 gate rows, 32 up rows
 #pragma unroll
-        for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-        const float dq = m / 127.0f;
-        const float id = (dq != 0.0f) ? 1.0f / dq : 0.0f;
-        float r = roundf(sv * id);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        const int ncols = N / 2;
-        const int scol = gcol / 2 + (lane & 31);
-        if (row < M && gcol < N) {
-          q_codes[(int64_t)row * ncols + scol] = (int8_t)(int)r;
-          if ((lane & 31) == 0) q_scales[(int64_t)row * (ncols / QK) + scol / QK] = f32_to_f16_bits(dq);
+        for (int cp = 0; cp < CG / 2; ++cp) {
+          const int gcol = n0 + wn * 32 * CG + cp * 64;
+          const float gv = (float)acc[rg][2 * cp][j];
+          const float uv = (float)acc[rg][2 * cp + 1][j];
+          const float sv = swiglu_f32(gv, uv);
+          float m = fabsf(sv);
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+          const float dq = m / 127.0f;
+          const float id = (dq != 0.0f) ? 1.0f / dq : 0.0f;
+          float r = roundf(sv * id);
+          r = fminf(fmaxf(r, -127.0f), 127.0f);
+          const int ncols = N / 2;
+          const int scol = gcol / 2 + (lane & 31);
+          if (row < M && gcol < N) {
+            q_codes[(int64_t)row * ncols + scol] = (int8_t)(int)r;
+            if ((lane & 31) == 0) q_scales[(int64_t)row * (ncols / QK) + scol / QK] = f32_to_f16_bits(dq);
+          }
         }
       }
     }
@@ -256,47 +313,79 @@ __global__ void __launch_bounds__(256) k_splitk_swiglu(const double* __restrict_
   }
 }
 
-static int choose_split(int m, int n, int k) {
-  const int tiles = ((m + G_BM - 1) / G_BM) * ((n + G_BN - 1) / G_BN);
+// Tile and split choice: aim for at least ~4 waves per CU of independent work; split K only when
+// the output tiles alone cannot fill the chip, keeping >= 2 stages (8 blocks) per split.
+// Tile shapes: 0 = 1x1 MFMA wave tile (workgroup 32 x 64), 1 = 2x2 (64 x 128), 2 = 1x2 (32 x 128).
+struct GemmPlan { int shape; int split; };
+
+static GemmPlan plan_gemm(int m, int n, int k, bool swiglu) {
   const int KB = k / QK;
-  int split = 1;
-  const int target = 2 * 256;  // two workgroups per CU
-  while (split < 16 && tiles * split < target && KB / (split * 2) >= 8) split *= 2;
-  return split;
+  GemmPlan p{1, 1};
+  const int tiles_big = ((m + 63) / 64) * ((n + 127) / 128);
+  if (swiglu) {
+    // gate/up pairs live in column-group pairs: 2x2 or 1x2; prefer enough workgroups for 2 per CU
+    p.shape = tiles_big >= 1024 ? 1 : 2;
+  } else if (tiles_big < 512) {
+    p.shape = 0;
+  }
+  const int tiles = p.shape == 1 ? tiles_big : p.shape == 2 ? ((m + 31) / 32) * ((n + 127) / 128)
+                                                           : ((m + 31) / 32) * ((n + 63) / 64);
+  // Split K only for long reductions whose output tiles cannot fill the chip, keeping the f64
+  // partials (written once, read once) at most 8 MB.
+  const int target = 512;
+  const size_t max_partial = (size_t)8 << 20;
+  if (KB > 64)
+    while (p.split < 16 && tiles * p.split < target && KB / (p.split * 2) >= 2 * G_KS &&
+           (size_t)(p.split * 2) * m * n * sizeof(double) <= max_partial)
+      p.split *= 2;
+  return p;
 }
 
 size_t gemm_workspace_bytes(int m, int n, int k) {
-  const int s = choose_split(m, n, k);
+  const GemmPlan p = plan_gemm(m, n, k, false);
+  const GemmPlan q = plan_gemm(m, n, k, true);
+  const int s = std::max(p.split, q.split);
   return s > 1 ? (size_t)s * m * n * sizeof(double) : 0;
+}
+
+template <int RG, int CG>
+static void launch_tiles(const GemmArgs& g, int split, int kb_per, hipStream_t s) {
+  using T = GemmTile<RG, CG>;
+  dim3 grid((g.n + T::BN - 1) / T::BN, (g.m + T::BM - 1) / T::BM, split);
+  double* partial = reinterpret_cast<double*>(g.workspace);
+  if (split > 1)
+    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, true>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
+                       g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
+                       partial, kb_per);
+  else if (g.q_codes) {
+    if constexpr (CG >= 2)
+      hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_SWIGLU_Q8, false>), grid, dim3(G_THREADS), 0, s, g.a_codes,
+                         g.a_scales, g.m, g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out,
+                         g.q_codes, g.q_scales, nullptr, kb_per);
+  } else
+    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, false>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
+                       g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
+                       nullptr, kb_per);
 }
 
 int launch_gemm_q8(const GemmArgs& g, hipStream_t s) {
   if (g.m == 0) return MI_OK;
   const int KB = g.k / QK;
-  int split = g.split_k > 0 ? g.split_k : choose_split(g.m, g.n, g.k);
-  if (split > KB) split = KB;
+  GemmPlan p = plan_gemm(g.m, g.n, g.k, g.q_codes != nullptr);
+  if (g.split_k > 0) p.split = g.split_k;
+  int split = std::min(p.split, KB);
   const size_t need = split > 1 ? (size_t)split * g.m * g.n * sizeof(double) : 0;
   if (need > g.workspace_bytes || (need && !g.workspace)) split = 1;
-  const int kb_per = (KB + split - 1) / split;
+  // splits cover whole stages where possible
+  int kb_per = (KB + split - 1) / split;
+  kb_per = ((kb_per + G_KS - 1) / G_KS) * G_KS;
   split = (KB + kb_per - 1) / kb_per;
-  dim3 grid((g.n + G_BN - 1) / G_BN, (g.m + G_BM - 1) / G_BM, split);
+  if (p.shape == 1) launch_tiles<2, 2>(g, split, kb_per, s);
+  else if (p.shape == 2) launch_tiles<1, 2>(g, split, kb_per, s);
+  else launch_tiles<1, 1>(g, split, kb_per, s);
+  MI_LAUNCH_CHECK("k_gemm_q8");
+  if (split == 1) return MI_OK;
   double* partial = reinterpret_cast<double*>(g.workspace);
-  if (split == 1) {
-    if (g.q_codes)
-      hipLaunchKernelGGL((k_gemm_q8<EPI_SWIGLU_Q8, false>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales,
-                         g.m, g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes,
-                         g.q_scales, nullptr, kb_per);
-    else
-      hipLaunchKernelGGL((k_gemm_q8<EPI_F32, false>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
-                         g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes,
-                         g.q_scales, nullptr, kb_per);
-    MI_LAUNCH_CHECK("k_gemm_q8");
-    return MI_OK;
-  }
-  hipLaunchKernelGGL((k_gemm_q8<EPI_F32, true>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
-                     g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes,
-                     g.q_scales, partial, kb_per);
-  MI_LAUNCH_CHECK("k_gemm_q8 (split)");
   if (g.q_codes) {
     const int64_t total = (int64_t)g.m * (g.n / 2 / 4);
     const int64_t blocks = std::min<int64_t>((total + 255) / 256, 65536);
