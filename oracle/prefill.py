@@ -69,12 +69,13 @@ def _mm(w, x, name, bias=None):
 
 
 def prefill_forward(cfg, w, token_ids, positions, n_ctx: int, kv_k, kv_v,
-                    n_out: int = 1) -> np.ndarray:
+                    n_out: int = 1, progress=None) -> np.ndarray:
     """Run one prefill call; returns logits f32 [n_out][vocab] and fills kv_k/kv_v.
 
     cfg: an object with n_layers, hidden, n_head, n_head_kv, head_dim, ffn, vocab,
     rms_eps, rope_theta, qkv_bias, qk_norm, tied.  kv_k / kv_v: per-layer f32 regions
     [n_ctx][n_head_kv * head_dim], updated in place (the caller owns them).
+    progress: optional callable(layer_index) invoked after each layer (long runs report liveness).
     """
     ids = np.asarray(token_ids, dtype=np.int64)
     pos = np.asarray(positions, dtype=np.int64)
@@ -114,6 +115,8 @@ def prefill_forward(cfg, w, token_ids, positions, n_ctx: int, kv_k, kv_v,
         u = _mm(w, x, p + "ffn_up.weight")
         s = ops.swiglu(g, u)
         h = ops.add_f32(h, _mm(w, s, p + "ffn_down.weight"))
+        if progress is not None:
+            progress(il)
     if cfg.n_layers == 0:
         h = h[nt - n_out:]
     x = ops.rms_norm(h, w["output_norm.weight"], eps)

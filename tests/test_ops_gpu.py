@@ -69,6 +69,7 @@ GEMM_CASES = [  # m, k, n, bias, residual, split
     (5, 3584, 512, True, True, 0),
     (200, 128, 64, False, False, 1),
     (33, 1024, 256, True, False, 4),
+    (256, 512, 16384, True, False, 0),   # 2x2 wave tiles (64 x 128 workgroups)
 ]
 
 
@@ -129,7 +130,8 @@ def test_gemm_full_size_sampled(case):
 
 def test_gemm_swiglu_matches_oracle():
     dev = need_gpu()
-    for m, k, f in [(100, 896, 320), (16, 3584, 512), (1, 896, 4864)]:
+    # 1x2 wave tiles for the first three, 2x2 for the last (>= 1024 workgroup tiles)
+    for m, k, f in [(100, 896, 320), (16, 3584, 512), (1, 896, 4864), (512, 256, 8192)]:
         say(f"gemm+swiglu m={m} k={k} ffn={f}")
         x = synth.gen_normal(31, f"x{m}", (m, k), device=dev)
         wg = synth.gen_normal(32, f"g{f}", (f, k), std=0.02, device=dev)
