@@ -23,7 +23,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, tera-ops/s
+F64_VALU_PEAK_TFLOPS = 78.6  # MI355X fp64 vector: 256 CUs x 2.4 GHz x 128 flop/clk
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = "traffic_gemm_swiglu_qwen2_0p5b.json"
+COPY_BYTES = 256 << 20       # the calibration kernel reads and writes this many bytes
 
 
 def parse():
@@ -33,6 +36,15 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--traffic-run", action="store_true",
+                   help="launch only the dominant kernel (20x) and a 256 MiB streaming kernel (5x), for a "
+                        "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE pass")
+    p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="turn the two counter passes of --traffic-run into profiles/" + TRAFFIC_FILE)
+    p.add_argument("--workload", default=None,
+                   help="model workload name (default: the 512-token 0.5B-shaped headline); the others "
+                        "are reported for context: " + ", ".join(["layer1_896", "qwen2_0p5b_pp512",
+                                                                   "qwen2p5_7b_pp2048", "qwen3_8b_chunk3072at1024"]))
     return p.parse_args()
 
 
@@ -59,6 +71,9 @@ def timed_loop(fn, reps: int, torch) -> float:
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -73,14 +88,20 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     B.lib()  # fail loudly if the HIP library is not built
-    cfg = synth.HEADLINE
+    cfg = synth.MODEL_CONFIGS[args.workload] if args.workload else synth.HEADLINE
     dev = torch.device("cuda:0")
+    if args.traffic_run:
+        traffic_run(cfg, dev)
+        return
     t0 = time.time()
-    model = PrefillModel(cfg, synth.iter_tensors(cfg, device=dev), cfg.n_tokens, cfg.n_ctx, device=dev)
+    model = PrefillModel(cfg, synth.iter_tensors(cfg, device=dev), cfg.prefix_tokens + cfg.n_tokens, cfg.n_ctx,
+                         device=dev)
     torch.cuda.synchronize()
     load_s = time.time() - t0
-    _, ids = synth.gen_token_ids(cfg)
-    _, pos = synth.positions_for(cfg)
+    pre_ids, ids = synth.gen_token_ids(cfg)
+    pre_pos, pos = synth.positions_for(cfg)
+    if cfg.prefix_tokens:  # untimed: the KV rows of the earlier positions; each timed chunk call
+        model.forward(pre_ids, pre_pos)  # rewrites the same chunk rows with the same values
 
     for _ in range(args.warmup):
         model.forward(ids, pos)
@@ -95,26 +116,28 @@ def main():
     tok_s = cfg.n_tokens / (ms / 1e3)
 
     # ---- dominant kernel: fused gate|up matmul + SwiGLU + Q8_0 at the forward's shape
-    H, F, M = cfg.hidden, cfg.ffn, cfg.n_tokens
-    x = synth.gen_normal(1, "bench.x", (M, H), device=dev)
-    xc, xs = B.quantize_q8_0(x)
-    gu_codes, gu_scales = model.layer_tensors[0]["w_gate_up"]
-    ws_bytes = B.lib().mi_gemm_q8_0_workspace_bytes(M, 2 * F, H)
-    wsp = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=dev)
+    run_gu, (M, N2, H) = dominant_kernel(cfg, dev, model.layer_tensors[0]["w_gate_up"])
     reps = 200
-    k_ms = timed_loop(lambda: B.gemm_swiglu_q8_0(xc, xs, gu_codes, gu_scales, workspace=wsp), reps, torch)
-    ops = 2.0 * M * (2 * F) * H
+    k_ms = timed_loop(run_gu, reps, torch)
+    ops = 2.0 * M * N2 * H
     achieved = ops / (k_ms / 1e3) / 1e12
+    # the exact scale epilogue: 2 f64 FMAs (4 flops) per output per Q8_0 block, on the VALU
+    f64_flops = 4.0 * M * N2 * (H // 32)
+    f64_achieved = f64_flops / (k_ms / 1e3) / 1e12
     traffic = None
-    tf = os.path.join(ROOT, "profiles", "traffic_gemm_swiglu_qwen2_0p5b.json")
+    tf = os.path.join(ROOT, "profiles", TRAFFIC_FILE)
     if os.path.exists(tf):
         rec = json.load(open(tf))
         if rec.get("kernel_source_hash") == kernel_source_hash():
             traffic = rec.get("bytes_per_launch")
     roofline = {"bound": "mfma", "kernel": "k_gemm_q8<EPI_SWIGLU_Q8> (gate|up + SwiGLU + Q8_0)",
-                "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS (int8)",
+                "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8)",
                 "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
-                "avg_launch_ms": round(k_ms, 5), "shape_mnk": [M, 2 * F, H], "launches_timed": reps}
+                "algorithmic_ops_per_launch": ops, "avg_launch_ms": round(k_ms, 5), "shape_mnk": [M, N2, H],
+                "launches_timed": reps,
+                "f64_epilogue": {"bound": "alu", "achieved": round(f64_achieved, 2), "peak": F64_VALU_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s (f64 vector)", "frac": round(f64_achieved / F64_VALU_PEAK_TFLOPS, 4),
+                                 "flops_per_launch": f64_flops}}
 
     # ---- the Q8_0 GEMM sweep shapes (quantized activations x Q8_0 weights -> f32)
     sweep = []
@@ -142,7 +165,7 @@ def main():
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, model_tensors=None)
+        cpu = cpu_baseline(cfg)
 
     line = {
         "metric": "prefill tokens/sec (512-tok prompt) + Q8_0 GEMM % of int8 MFMA peak, 1 GPU",
@@ -160,34 +183,127 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(cfg, model_tensors=None):
-    """Time the oracle (numpy, f64 GEMMs) on the first layers of the same model and prompt."""
+def dominant_kernel(cfg, dev, w_gate_up=None):
+    """A callable launching the fused gate|up matmul + SwiGLU + Q8_0 of layer 0 on the forward's
+    shape (M = prompt tokens, N = 2 x ffn interleaved rows, K = hidden), and that shape."""
+    import torch
+
+    import synth
+    from quantized_transformer_prefill_amd import binding as B
+    from quantized_transformer_prefill_amd.model import interleave_gate_up
+
+    H, F, M = cfg.hidden, cfg.ffn, cfg.n_tokens
+    if w_gate_up is None:
+        g = B.quantize_q8_0(synth.gen_tensor(cfg.seed, "blk.0.ffn_gate.weight", (F, H), "q8", device=dev))
+        u = B.quantize_q8_0(synth.gen_tensor(cfg.seed, "blk.0.ffn_up.weight", (F, H), "q8", device=dev))
+        w_gate_up = (interleave_gate_up(g[0], u[0]).contiguous(), interleave_gate_up(g[1], u[1]).contiguous())
+    x = synth.gen_normal(1, "bench.x", (M, H), device=dev)
+    xc, xs = B.quantize_q8_0(x)
+    ws_bytes = B.lib().mi_gemm_q8_0_workspace_bytes(M, 2 * F, H)
+    wsp = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=dev)
+    gu_codes, gu_scales = w_gate_up
+    return (lambda: B.gemm_swiglu_q8_0(xc, xs, gu_codes, gu_scales, workspace=wsp)), (M, 2 * F, H)
+
+
+def traffic_run(cfg, dev):
+    """Launches for the HBM-traffic counters: the dominant kernel 20 times, then a streaming kernel
+    that reads and writes COPY_BYTES (torch's elementwise multiply) 5 times, to calibrate the
+    counters against a known byte count."""
+    import torch
+
+    run, shape = dominant_kernel(cfg, dev)
+    for _ in range(20):
+        run()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_run": cfg.name, "shape_mnk": list(shape), "copy_bytes": COPY_BYTES}), flush=True)
+
+
+def _counter_rows(d, counter):
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def write_traffic(fetch_dir, write_dir):
+    """HBM bytes per launch of the dominant kernel from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled by the factor that maps the same counter onto the known bytes of the streaming kernel."""
+    out = {}
+    for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _counter_rows(d, counter)
+        gemm = [v for n, v in rows if "k_gemm_q8" in n]
+        copy = [v for n, v in rows if "MulFunctor" in n or "mul_kernel" in n]
+        if not gemm or not copy:
+            raise SystemExit(f"{counter}: gemm dispatches {len(gemm)}, calibration dispatches {len(copy)}")
+        copy_kib = float(np.median(copy))
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        out[key] = {"counter": counter, "kernel_kib_median": float(np.median(gemm)), "dispatches": len(gemm),
+                    "calibration_kib_median": copy_kib, "calibration_bytes": COPY_BYTES, "factor": factor,
+                    "bytes_per_launch": float(np.median(gemm)) * 1024.0 * factor}
+    rec = {"kernel": "k_gemm_q8<EPI_SWIGLU_Q8> (gate|up + SwiGLU + Q8_0), 512 x 9728 x 896",
+           "kernel_source_hash": kernel_source_hash(),
+           "bytes_per_launch": round(out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]),
+           "fetch": out["fetch"], "write": out["write"],
+           "commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o p -- "
+                        "python3 bench.py --traffic-run",
+                        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o p -- "
+                        "python3 bench.py --traffic-run",
+                        "python3 bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write"]}
+    path = os.path.join(ROOT, "profiles", TRAFFIC_FILE)
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
+def cpu_baseline(cfg, min_seconds: float = 10.0, max_reps: int = 3):
+    """Time the oracle (numpy, f64 GEMMs) on whole forwards of the same model and prompt.
+
+    The sample is the full prefill call (every layer, the KV stores, the last-token lm_head),
+    repeated until min_seconds of CPU time have passed or max_reps calls ran; weight
+    quantization happens before the timed region, as the GPU side loads its weights untimed.
+    """
     import threadpoolctl
     import torch
 
     import oracle
     import synth
 
-    n_layers = 2
-    sample = cfg.with_(n_layers=n_layers)
-    q8 = [n for n, s, k in synth.tensor_specs(sample) if k == "q8"]
+    q8 = [n for n, s, k in synth.tensor_specs(cfg) if k == "q8"]
     dev = torch.device("cuda:0")
-    arrays = {n: t.cpu().numpy() for n, k, t in synth.iter_tensors(sample, device=dev)}
+    arrays = {n: t.cpu().numpy() for n, k, t in synth.iter_tensors(cfg, device=dev)}
     w = oracle.weights_from_arrays(arrays, q8)
     for n in q8:
         w[n]  # quantize outside the timed region
-    _, ids = synth.gen_token_ids(cfg)
-    _, pos = synth.positions_for(cfg)
-    kk, vv = oracle.new_kv_regions(sample, cfg.n_ctx)
+        del arrays[n]  # the f32 originals of quantized weights are no longer read
+    pre_ids, ids = synth.gen_token_ids(cfg)
+    pre_pos, pos = synth.positions_for(cfg)
+    kk, vv = oracle.new_kv_regions(cfg, cfg.n_ctx)
+    if cfg.prefix_tokens:
+        oracle.prefill_forward(cfg, w, pre_ids, pre_pos, cfg.n_ctx, kk, vv)
     threads = sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info() if i.get("internal_api") == "openblas")
-    t0 = time.time()
-    oracle.prefill_forward(sample, w, ids, pos, cfg.n_ctx, kk, vv)
-    t = time.time() - t0
-    scaled = t * cfg.n_layers / n_layers  # lm_head counted n_layers/2 times: a conservative rate
-    return {"value": round(cfg.n_tokens / scaled, 2), "unit": "tokens/s", "cores": threads or os.cpu_count(),
+    reps, t = 0, 0.0
+    while reps < max_reps and (reps == 0 or t < min_seconds):
+        t0 = time.time()
+        oracle.prefill_forward(cfg, w, ids, pos, cfg.n_ctx, kk, vv)
+        t += time.time() - t0
+        reps += 1
+    return {"value": round(reps * cfg.n_tokens / t, 2), "unit": "tokens/s", "cores": threads or os.cpu_count(),
             "kind": "oracle",
-            "sample": f"{cfg.n_tokens}-token prompt through {n_layers} of {cfg.n_layers} layers plus the "
-                      f"lm_head ({t:.1f} s), time scaled by {cfg.n_layers}/{n_layers}",
+            "sample": f"{reps} whole prefill call(s) of the {cfg.n_tokens}-token prompt through all {cfg.n_layers} "
+                      f"layers and the lm_head ({t:.1f} s of CPU time; weights quantized beforehand)",
             "host_cpus": os.cpu_count()}
 
 

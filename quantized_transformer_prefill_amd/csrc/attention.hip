@@ -6,12 +6,19 @@
 // scores, softmax and the weighted sum run in f64 on v_mfma_f64_16x16x4f64; the online-softmax
 // bookkeeping (running max, running sum, rescale) is f64 on the VALU.
 //
-// Work split: a workgroup of 4 waves serves 16 query tokens x 1 head.  The key tiles (16 rows
-// each, from row 0 to the largest position among the 16 queries) are dealt round-robin to the 4
+// Work split: a workgroup of NW waves serves 16 query tokens x 1 head.  The key tiles (16 rows
+// each, from row 0 to the largest position among the 16 queries) are dealt round-robin to the
 // waves, so every wave sees early and late tiles alike.  Each wave keeps its own running max,
-// sum and output; at the end the four partial states are merged in f64 through LDS
-// (o = sum_w O_w e^(m_w - m) / sum_w l_w e^(m_w - m)).  The next tile's K and V are loaded while
-// the current tile computes.
+// sum and output; at the end the partial states are merged in f64 through LDS, pairwise in a
+// fixed order (o = sum_w O_w e^(m_w - m) / sum_w l_w e^(m_w - m)).  The next tile's K and V are
+// loaded while the current tile computes.
+//
+// Softmax bookkeeping per tile, kept off the critical path:
+//  * the running max is raised lazily: a query's reference m moves only when a score exceeds it
+//    by more than LAZY_MAX (softmax is invariant to the reference, and e^(s - m) <= e^LAZY_MAX is
+//    harmless in f64), so most tiles need neither the cross-lane max nor the rescale of O;
+//  * the running sum is kept per lane (each lane sums its own keys) and reduced once at the end;
+//  * the causal mask is applied only on tiles that some query of the 16 does not fully see.
 //
 // MFMA 16x16x4 f64 lane layout: A lane l -> (m = l%16, k = l/16), B lane l -> (k = l/16, n =
 // l%16), D register i lane l -> (m = 4i + l/16, n = l%16).
@@ -19,8 +26,8 @@
 //    contraction is free, so lane slot g = l/16 owns the contiguous dims [g*hd/4, (g+1)*hd/4) and
 //    MFMA s uses dim g*hd/4 + s: K and Q are read as float4s.  Two accumulators (even/odd s) keep
 //    the MFMA dependency chain short.
-//  * lane l then holds the scores of query l%16 against keys 4i + l/16 (i = 0..3); row max and
-//    row sum reduce over the 4 registers and the lanes l^16, l^32.
+//  * lane l then holds the scores of query l%16 against keys 4i + l/16 (i = 0..3); the max over
+//    a query's keys reduces over the 4 registers and the lanes l^16, l^32.
 //  * O^T += V^T . P^T  (m = output dim, n = query, k = key): MFMA c takes key slot s = l/16 as key
 //    4c + s, which is exactly register c of the lane's P; the output dim of row m in dim block b is
 //    m*(hd/16) + b, so V reads and O stores are contiguous per lane.
@@ -30,7 +37,7 @@ namespace mi {
 
 typedef double v4d __attribute__((ext_vector_type(4)));
 
-constexpr int AT_WAVES = 4;
+constexpr double LAZY_MAX = 16.0;  // natural-log units
 
 template <int HD>
 struct AttnTile {
@@ -38,52 +45,64 @@ struct AttnTile {
   float4 v[4][HD / 64];       // V rows key0 + 4c + slot, dims (l%16)*HD/16 .. +HD/16
 };
 
+// Loads of one key tile.  Rows are clamped to max_pos (the largest position of the call, a row
+// this call wrote), so every load is in bounds; rows past a query's position are masked later:
+// their scores are replaced by -inf, and their V values (which may be anything) are zeroed on the
+// tile that straddles the largest position of the 16 queries (mask_tile_v).
 template <int HD>
 __device__ __forceinline__ void load_tile(AttnTile<HD>& t, const float* kbase, const float* vbase, int kv_embd,
-                                          int key0, int pmax, int qi, int slot) {
+                                          int key0, int max_pos, int qi, int slot) {
   constexpr int Q4 = HD / 4, NB = HD / 16;
-  const int krow = key0 + qi;
-  const bool kok = krow <= pmax;
-  const float* kp = kbase + (int64_t)(kok ? krow : 0) * kv_embd + slot * Q4;
+  const float* kp = kbase + (int64_t)min(key0 + qi, max_pos) * kv_embd + slot * Q4;
 #pragma unroll
-  for (int s = 0; s < Q4 / 4; ++s)
-    t.k[s] = kok ? *reinterpret_cast<const float4*>(kp + 4 * s) : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < Q4 / 4; ++s) t.k[s] = *reinterpret_cast<const float4*>(kp + 4 * s);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int vrow = key0 + 4 * c + slot;
-    const bool vok = vrow <= pmax;
-    const float* vp = vbase + (int64_t)(vok ? vrow : 0) * kv_embd + qi * NB;
+    const float* vp = vbase + (int64_t)min(key0 + 4 * c + slot, max_pos) * kv_embd + qi * NB;
 #pragma unroll
-    for (int b = 0; b < NB / 4; ++b)
-      t.v[c][b] = vok ? *reinterpret_cast<const float4*>(vp + 4 * b) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int b = 0; b < NB / 4; ++b) t.v[c][b] = *reinterpret_cast<const float4*>(vp + 4 * b);
   }
+}
+
+template <int HD>
+__device__ __forceinline__ void mask_tile_v(AttnTile<HD>& t, int key0, int pmax, int slot) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (key0 + 4 * c + slot > pmax)
+#pragma unroll
+      for (int b = 0; b < HD / 64; ++b) t.v[c][b] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 __device__ __forceinline__ double f4get(const float4& v, int e) {
   return e == 0 ? (double)v.x : e == 1 ? (double)v.y : e == 2 ? (double)v.z : (double)v.w;
 }
 
-template <int HD>
-__global__ void __launch_bounds__(64 * AT_WAVES) k_attention(const float* __restrict__ q, int64_t ld_q,
-                                                             const float* __restrict__ k_region,
-                                                             const float* __restrict__ v_region,
-                                                             const int32_t* __restrict__ pos, int n_tokens,
-                                                             int n_head, int n_head_kv, float* __restrict__ out,
-                                                             int64_t ld_out) {
+template <int HD, int NW>
+__global__ void __launch_bounds__(64 * NW) k_attention(const float* __restrict__ q, int64_t ld_q,
+                                                       const float* __restrict__ k_region,
+                                                       const float* __restrict__ v_region,
+                                                       const int32_t* __restrict__ pos, int n_tokens, int max_pos,
+                                                       int n_head, int n_head_kv, float* __restrict__ out,
+                                                       int64_t ld_out) {
   constexpr int Q4 = HD / 4;    // dims per lane slot (scores) = MFMAs per score tile
   constexpr int NB = HD / 16;   // output dim blocks
-  __shared__ double sh_m[AT_WAVES][64], sh_l[AT_WAVES][64];
-  __shared__ double sh_o[AT_WAVES - 1][NB * 4][64];
+  __shared__ double exp_tab[64];
+  __shared__ double sh_m[NW][64], sh_l[NW][64];
+  __shared__ double sh_o[NW / 2][NB * 4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int qi = lane & 15, slot = lane >> 4;
+  exp2_table_fill(exp_tab, threadIdx.x);
   const int h = blockIdx.y;
   const int g = h / (n_head / n_head_kv);
   const int kv_embd = n_head_kv * HD;
   const int t = blockIdx.x * 16 + qi;
   const bool valid = t < n_tokens;
   const int p = valid ? pos[t] : 0;
-  int pmax = p;
-  for (int o = 1; o < 16; o <<= 1) pmax = max(pmax, __shfl_xor(pmax, o));
+  int pmax = p, pmin = valid ? p : 0x7fffffff;
+  for (int o = 1; o < 16; o <<= 1) {
+    pmax = max(pmax, __shfl_xor(pmax, o));
+    pmin = min(pmin, __shfl_xor(pmin, o));
+  }
 
   // query fragment: dims slot*Q4 + s, pre-scaled by 1/sqrt(hd) in f64
   const double scale = 1.0 / sqrt((double)HD);
@@ -103,18 +122,15 @@ __global__ void __launch_bounds__(64 * AT_WAVES) k_attention(const float* __rest
   v4d acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = v4d{0.0, 0.0, 0.0, 0.0};
-  double m_run = -INFINITY, l_run = 0.0;
+  double m_run = -INFINITY, l_run = 0.0;   // l_run: this lane's keys only
 
   const float* kbase = k_region + (int64_t)g * HD;
   const float* vbase = v_region + (int64_t)g * HD;
   const int ntiles = pmax / 16 + 1;
-  AttnTile<HD> cur, nxt;
-  int tile = wave;
-  if (tile < ntiles) load_tile<HD>(cur, kbase, vbase, kv_embd, tile * 16, pmax, qi, slot);
-  for (; tile < ntiles; tile += AT_WAVES) {
-    const int key0 = tile * 16;
-    if (tile + AT_WAVES < ntiles) load_tile<HD>(nxt, kbase, vbase, kv_embd, key0 + 16 * AT_WAVES, pmax, qi, slot);
-    // ---- scores
+
+  // one key tile: scores, online softmax, O += V^T P^T
+  auto tile_step = [&](AttnTile<HD>& cur, int key0) {
+    if (key0 + 15 > pmax) mask_tile_v<HD>(cur, key0, pmax, slot);
     v4d sc0 = {0.0, 0.0, 0.0, 0.0}, sc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int s = 0; s < Q4; s += 2) {
@@ -122,71 +138,93 @@ __global__ void __launch_bounds__(64 * AT_WAVES) k_attention(const float* __rest
       sc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(cur.k[(s + 1) / 4], (s + 1) % 4), qf[s + 1], sc1, 0, 0, 0);
     }
     // ---- online softmax for query l%16 over keys key0 + 4i + slot
+    const bool full = key0 + 15 <= pmin;  // every query of the 16 sees every key of the tile
     double sv[4];
     double tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = key0 + 4 * i + slot;
-      sv[i] = (key <= p) ? sc0[i] + sc1[i] : -INFINITY;
+      sv[i] = sc0[i] + sc1[i];
+      if (!full && key0 + 4 * i + slot > p) sv[i] = -INFINITY;
       tmax = fmax(tmax, sv[i]);
     }
-    tmax = fmax(tmax, __shfl_xor(tmax, 16));
-    tmax = fmax(tmax, __shfl_xor(tmax, 32));
-    const double m_new = fmax(m_run, tmax);
-    // a wave whose tiles so far are all masked for this query keeps m = -inf and p = 0
-    const double corr = (m_run == -INFINITY) ? 0.0 : exp(m_run - m_new);
-    double pv[4], psum = 0.0;
+    if (__any(tmax > m_run + LAZY_MAX)) {
+      tmax = fmax(tmax, __shfl_xor(tmax, 16));
+      tmax = fmax(tmax, __shfl_xor(tmax, 32));
+      if (tmax > m_run) {  // the same decision on the 4 lanes of a query
+        // a query whose keys so far were all masked has m = -inf and nothing to rescale
+        const double corr = (m_run == -INFINITY) ? 0.0 : exp_f64(m_run - tmax, exp_tab);
+        l_run *= corr;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b] *= corr;
+        m_run = tmax;
+      }
+    }
+    double pv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pv[i] = (sv[i] == -INFINITY) ? 0.0 : exp(sv[i] - m_new);
-      psum += pv[i];
+      pv[i] = (sv[i] == -INFINITY) ? 0.0 : exp_f64(sv[i] - m_run, exp_tab);
+      l_run += pv[i];
     }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    l_run = l_run * corr + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] *= corr;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int b = 0; b < NB; ++b)
         acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(cur.v[c][b / 4], b % 4), pv[c], acc[b], 0, 0, 0);
-    cur = nxt;
+  };
+
+  // tiles wave, wave + NW, ...; two tile buffers alternate (the loop body handles two tiles), the
+  // next tile's loads in flight while the current one computes.  The first tile is requested
+  // before the positions arrive.
+  AttnTile<HD> ta, tb;
+  load_tile<HD>(ta, kbase, vbase, kv_embd, wave * 16, max_pos, qi, slot);
+  __syncthreads();  // exp_tab
+  for (int tile = wave; tile < ntiles; tile += 2 * NW) {
+    if (tile + NW < ntiles) load_tile<HD>(tb, kbase, vbase, kv_embd, (tile + NW) * 16, max_pos, qi, slot);
+    tile_step(ta, tile * 16);
+    if (tile + NW >= ntiles) break;
+    if (tile + 2 * NW < ntiles) load_tile<HD>(ta, kbase, vbase, kv_embd, (tile + 2 * NW) * 16, max_pos, qi, slot);
+    tile_step(tb, (tile + NW) * 16);
   }
 
-  // ---- merge the four waves' partial softmax states (f64, fixed order)
+  // ---- merge: the query's sum over its 4 lanes, then the waves' partial states (f64, fixed order)
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
   sh_m[wave][lane] = m_run;
   sh_l[wave][lane] = l_run;
-  if (wave > 0) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sh_o[wave - 1][b * 4 + i][lane] = acc[b][i];
-  }
   __syncthreads();
+  double m_all = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) m_all = fmax(m_all, sh_m[w][lane]);
+  {
+    const double f_self = (m_run == -INFINITY) ? 0.0 : exp_f64(m_run - m_all, exp_tab);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] *= f_self;
+  }
+#pragma unroll
+  for (int half = NW / 2; half >= 1; half /= 2) {
+    if (wave >= half && wave < 2 * half) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sh_o[wave - half][b * 4 + i][lane] = acc[b][i];
+    }
+    __syncthreads();
+    if (wave < half) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[b][i] += sh_o[wave][b * 4 + i][lane];
+    }
+    if (half > 1) __syncthreads();
+  }
   if (wave == 0) {
-    double mw[AT_WAVES], m_all = -INFINITY;
+    double l_all = 0.0;
 #pragma unroll
-    for (int w = 0; w < AT_WAVES; ++w) {
-      mw[w] = sh_m[w][lane];
-      m_all = fmax(m_all, mw[w]);
+    for (int w = 0; w < NW; ++w) {
+      const double mw = sh_m[w][lane];
+      l_all += (mw == -INFINITY) ? 0.0 : sh_l[w][lane] * exp_f64(mw - m_all, exp_tab);
     }
-    double fw[AT_WAVES], l_all = 0.0;
-#pragma unroll
-    for (int w = 0; w < AT_WAVES; ++w) {
-      fw[w] = (mw[w] == -INFINITY) ? 0.0 : exp(mw[w] - m_all);
-      l_all += sh_l[w][lane] * fw[w];
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        double o = acc[b][i] * fw[0];
-#pragma unroll
-        for (int w = 1; w < AT_WAVES; ++w) o += sh_o[w - 1][b * 4 + i][lane] * fw[w];
-        acc[b][i] = o;
-      }
+    const double inv = recip_f64(l_all);
     if (valid) {
       float* op = out + (int64_t)t * ld_out + (int64_t)h * HD;
 #pragma unroll
@@ -195,10 +233,10 @@ __global__ void __launch_bounds__(64 * AT_WAVES) k_attention(const float* __rest
 #pragma unroll
         for (int b = 0; b < NB; b += 4) {
           float4 o;
-          o.x = (float)(acc[b][i] / l_all);
-          o.y = (float)(acc[b + 1][i] / l_all);
-          o.z = (float)(acc[b + 2][i] / l_all);
-          o.w = (float)(acc[b + 3][i] / l_all);
+          o.x = (float)(acc[b][i] * inv);
+          o.y = (float)(acc[b + 1][i] * inv);
+          o.z = (float)(acc[b + 2][i] * inv);
+          o.w = (float)(acc[b + 3][i] * inv);
           *reinterpret_cast<float4*>(dst + b) = o;
         }
       }
@@ -209,15 +247,14 @@ __global__ void __launch_bounds__(64 * AT_WAVES) k_attention(const float* __rest
 int launch_attention(const float* q, int64_t ld_q, const float* k_region, const float* v_region,
                      const int32_t* pos, int n_tokens, int max_pos, int n_head, int n_head_kv,
                      int head_dim, float* out, int64_t ld_out, hipStream_t s) {
-  (void)max_pos;
   if (n_tokens == 0) return MI_OK;
   dim3 grid((n_tokens + 15) / 16, n_head);
   if (head_dim == 64)
-    hipLaunchKernelGGL(k_attention<64>, grid, dim3(64 * AT_WAVES), 0, s, q, ld_q, k_region, v_region, pos, n_tokens,
-                       n_head, n_head_kv, out, ld_out);
+    hipLaunchKernelGGL((k_attention<64, 4>), grid, dim3(64 * 4), 0, s, q, ld_q, k_region, v_region, pos, n_tokens,
+                       max_pos, n_head, n_head_kv, out, ld_out);
   else if (head_dim == 128)
-    hipLaunchKernelGGL(k_attention<128>, grid, dim3(64 * AT_WAVES), 0, s, q, ld_q, k_region, v_region, pos, n_tokens,
-                       n_head, n_head_kv, out, ld_out);
+    hipLaunchKernelGGL((k_attention<128, 4>), grid, dim3(64 * 4), 0, s, q, ld_q, k_region, v_region, pos,
+                       n_tokens, max_pos, n_head, n_head_kv, out, ld_out);
   else
     return set_error(MI_ERR_UNSUPPORTED, "attention: head_dim %d (supported: 64, 128)", head_dim);
   MI_LAUNCH_CHECK("k_attention");

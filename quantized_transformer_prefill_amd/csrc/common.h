@@ -40,24 +40,115 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
 }
 
+// ---- cross-lane maxima of non-negative f32 values without LDS round trips: DPP row
+// permutations inside 16-lane rows, one bit-mode swizzle across the two rows of a 32-lane half.
+// Lanes whose DPP source is unavailable read 0, which leaves a maximum of non-negative values
+// unchanged.
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_MIRROR = 0x140;  // lane i <- 15 - i within a row of 16
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <- 7 - i within each 8 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
+  return fmaxf(v, __builtin_bit_cast(float, o));
+}
+
+// max over each aligned group of 8 lanes
+__device__ __forceinline__ float max8_nonneg(float v) {
+  v = dpp_max<DPP_XOR1>(v);
+  v = dpp_max<DPP_XOR2>(v);
+  return dpp_max<DPP_HALF_MIRROR>(v);  // quad 0 <-> quad 1 of the 8
+}
+
+// max over each aligned group of 32 lanes
+__device__ __forceinline__ float max32_nonneg(float v) {
+  v = max8_nonneg(v);
+  v = dpp_max<DPP_ROW_MIRROR>(v);  // 8-lane halves of a row
+  // ds_swizzle bit mode (offset bit 15 = 0): lane <- ((lane & 0x1F) | 0) ^ 0x10 within 32 lanes
+  const int o = __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F);
+  return fmaxf(v, __builtin_bit_cast(float, o));
+}
+
+// f32(m / 127), correctly rounded, from one f64 product.  The f64 result is within 2^-52
+// (relative) of m/127, while m/127 for an f32 m is never closer than about 2^-32 (relative) to a
+// rounding midpoint of the f32 grid (m - 127*midpoint is a nonzero multiple of the midpoint
+// spacing), so rounding the f64 value to f32 gives the correctly rounded quotient.
+__device__ __forceinline__ float div127_f32(float m) { return (float)((double)m * (1.0 / 127.0)); }
+
+// f32(1 / d), correctly rounded, for an f32 d != 0: the hardware f64 reciprocal refined by two
+// Newton steps (error below 2^-52 relative), rounded to f32; 1/d is never closer than 2^-46
+// (relative) to an f32 rounding midpoint, so the result equals the IEEE f32 division.
+__device__ __forceinline__ float recip_f32(float d) {
+  const double x = d;
+  double r = __builtin_amdgcn_rcp(x);
+  r = fma(r, fma(-x, r, 1.0), r);
+  r = fma(r, fma(-x, r, 1.0), r);
+  return (float)r;
+}
+
 // Q8_0 of one block of 32 f32 values spread over 8 consecutive lanes (lane group
 // aligned to 8), 4 consecutive values per lane.  amax exact; d = f32(amax/127);
 // id = f32(1/d) or 0; code = round half away from zero of f32(x*id), clamped.
 // Returns the 4 codes packed little-endian; d_out = f32 scale (before fp16).
+__device__ __forceinline__ int q8_code(float x, float id) {
+  float r = roundf(x * id);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
 __device__ __forceinline__ uint32_t q8_block_quant4(float4 v, float& d_out) {
   float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  m = fmaxf(m, __shfl_xor(m, 1));
-  m = fmaxf(m, __shfl_xor(m, 2));
-  m = fmaxf(m, __shfl_xor(m, 4));
-  const float d = m / 127.0f;
-  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
-  auto code = [&](float x) -> uint32_t {
-    float r = roundf(x * id);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (uint32_t)(uint8_t)(int8_t)(int)r;
-  };
+  m = max8_nonneg(m);
+  const float d = div127_f32(m);
+  const float id = (d != 0.0f) ? recip_f32(d) : 0.0f;
   d_out = d;
-  return code(v.x) | (code(v.y) << 8) | (code(v.z) << 16) | (code(v.w) << 24);
+  return (uint32_t)(uint8_t)q8_code(v.x, id) | ((uint32_t)(uint8_t)q8_code(v.y, id) << 8) |
+         ((uint32_t)(uint8_t)q8_code(v.z, id) << 16) | ((uint32_t)(uint8_t)q8_code(v.w, id) << 24);
+}
+
+// ---- e^x and SiLU in f64: the softmax of the attention node and the activation of the SwiGLU
+// node, silu(g) = g / (1 + e^-g).  e^x by Tang's table-driven method: x = (64k + j) ln2/64 + r
+// with |r| <= ln2/128, so e^x = 2^k * 2^(j/64) * e^r; e^r from its degree-5 Taylor polynomial
+// (truncation below 4e-17 relative).  ln2/64 is split into a 36-bit head (k * head exact for
+// |64k + j| < 2^17) and a tail.  Quotients use the f64 reciprocal with two Newton steps.  Error: a
+// few f64 ulps, far below the f32 rounding the callers apply.  `tab` holds 2^(j/64), j = 0..63
+// (exp2_table_fill, in LDS).
+__device__ __forceinline__ void exp2_table_fill(double* tab, int tid) {
+  if (tid < 64) tab[tid] = exp2((double)tid * (1.0 / 64.0));
+}
+
+// e^x for x <= 709 (x below -745 gives 0 or a subnormal), from the 2^(j/64) table `tab`.
+__device__ __forceinline__ double exp_f64(double x, const double* tab) {
+  constexpr double INV_LN2_64 = 0x1.71547652b82fep+6;   // 64 / ln2
+  constexpr double LN2_64_HI = 0x1.62e42fefa0000p-7;    // ln2/64, first 36 bits
+  constexpr double LN2_64_LO = 0x1.cf79abc9e3b3ap-46;   // ln2/64 - LN2_64_HI
+  x = fmin(fmax(x, -746.0), 709.0);
+  const double kf = rint(x * INV_LN2_64);
+  double r = fma(-kf, LN2_64_HI, x);
+  r = fma(-kf, LN2_64_LO, r);
+  const double p = fma(fma(fma(fma(fma(1.0 / 120.0, r, 1.0 / 24.0), r, 1.0 / 6.0), r, 0.5), r, 1.0), r, 1.0);
+  const int k = (int)kf;
+  return ldexp(tab[k & 63] * p, k >> 6);
+}
+
+// 1/x for x >= 1 (or any normal x): hardware f64 reciprocal plus two Newton steps.
+__device__ __forceinline__ double recip_f64(double x) {
+  double rc = __builtin_amdgcn_rcp(x);
+  rc = fma(rc, fma(-x, rc, 1.0), rc);
+  return fma(rc, fma(-x, rc, 1.0), rc);
+}
+
+__device__ __forceinline__ double silu_f64(double g, const double* tab) {
+  // e^-g overflows past 709.78 (silu(g) is then -0 or a tiny negative that rounds to 0 in f32)
+  // and underflows below -745 (silu(g) = g): exp_f64's clamp keeps every step finite
+  return g * recip_f64(1.0 + exp_f64(-g, tab));
+}
+
+// SwiGLU of one element: f32(silu(g) * u), silu and the product in f64.
+__device__ __forceinline__ float swiglu_f32(float g, float u, const double* tab) {
+  return (float)(silu_f64((double)g, tab) * (double)u);
 }
 
 // ------------------------------------------------------------------ launchers (internal)

@@ -27,20 +27,11 @@ namespace mi {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef double v8d __attribute__((ext_vector_type(8)));
 
 constexpr int G_THREADS = 256;
 constexpr int G_KS = 4;     // Q8_0 blocks per LDS stage (128 K values)
 constexpr double G_MAGIC = 0x1.8p+52 + 0x1p+31;  // 1.5*2^52 + 2^31, exact
-
-__device__ __forceinline__ double pair_f64(int lo, int hi) {
-  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
-}
-
-__device__ __forceinline__ float swiglu_f32(float g, float u) {
-  const double gd = g;
-  const double sg = gd / (1.0 + exp(-gd));
-  return (float)(sg * (double)u);
-}
 
 // Wave tile = RG x CG MFMAs (16 real rows x 32 columns each); workgroup = 2 x 2 waves.
 // LDS rows hold the 4 blocks of a stage back to back (128 bytes) plus 16 bytes of padding, so a
@@ -68,16 +59,29 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
           const int8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales, int N, int K,
           const float* __restrict__ bias, const float* residual, float* out, int64_t ld_out,
           int8_t* __restrict__ q_codes, uint16_t* __restrict__ q_scales,
-          double* __restrict__ partial, int kb_per_split) {
+          double* __restrict__ partial, int kb_per_split, int xcd_order) {
   using T = GemmTile<RG, CG>;
   constexpr int BM = T::BM, BN = T::BN;
   __shared__ __align__(16) T sm;
+  __shared__ double exp_tab[EPI == EPI_SWIGLU_Q8 ? 64 : 1];  // 2^(j/64) for the SiLU
   const int tid = threadIdx.x;
+  if constexpr (EPI == EPI_SWIGLU_Q8) exp2_table_fill(exp_tab, tid);
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  // XCD-aware tile order.  Workgroups are dispatched round-robin over the 8 XCDs, each with its
+  // own L2; workgroup L is given tile t so that every XCD owns one contiguous range of tiles, and
+  // t walks the row tiles fastest, so the workgroups of an XCD share the weight tiles they read.
+  // Applied when the weight matrix exceeds what one XCD's L2 holds (xcd_order != 0).
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int n_all = gx * gy * gridDim.z;
+  const int L = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int xq = n_all >> 3, xr = n_all & 7, xcd = L & 7;
+  const int t = xcd_order ? xcd * xq + min(xcd, xr) + (L >> 3)
+                          : blockIdx.y + gy * (blockIdx.x + gx * blockIdx.z);
+  const int n0 = ((t / gy) % gx) * BN, m0 = (t % gy) * BM;
+  const int kz = t / (gx * gy);  // K split
   const int KB = K / QK;
-  const int kb0 = blockIdx.z * kb_per_split;
+  const int kb0 = kz * kb_per_split;
   const int kb1 = min(KB, kb0 + kb_per_split);
 
   // zero row for the dummy MFMA rows (both stages)
@@ -87,15 +91,41 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
   // ---- prefetch registers for one stage (G_KS blocks).  Codes: chunk c -> row c/8, 16-byte
   // piece c%8 of the row's 128 stage bytes (8 consecutive threads read 128 contiguous bytes).
   // Scales: element e -> block e / R, row e % R (consecutive threads fill consecutive LDS slots).
-  v4i pa[T::A_CHUNKS], pb[T::B_CHUNKS];
-  uint16_t pas[T::AS_PER_T], pbs[T::BS_PER_T];
-  auto fetch = [&](int kbs) {
+  struct Pre {
+    v4i a[T::A_CHUNKS], b[T::B_CHUNKS];
+    uint16_t as[T::AS_PER_T], bs[T::BS_PER_T];
+  };
+  const bool a_full = m0 + BM <= M, b_full = n0 + BN <= N;
+  auto fetch = [&](Pre& p, int kbs) {
+    if (kbs + G_KS <= kb1 && a_full && b_full) {  // common case: no bounds checks
+#pragma unroll
+      for (int i = 0; i < T::A_CHUNKS; ++i) {
+        const int c = tid + i * G_THREADS;
+        p.a[i] = *reinterpret_cast<const v4i*>(a_codes + (int64_t)(m0 + (c >> 3)) * K + (int64_t)kbs * QK + (c & 7) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < T::B_CHUNKS; ++i) {
+        const int c = tid + i * G_THREADS;
+        p.b[i] = *reinterpret_cast<const v4i*>(w_codes + (int64_t)(n0 + (c >> 3)) * K + (int64_t)kbs * QK + (c & 7) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < T::AS_PER_T; ++i) {
+        const int e = tid + i * G_THREADS;
+        if (e < BM * G_KS) p.as[i] = a_scales[(int64_t)(m0 + e % BM) * KB + kbs + e / BM];
+      }
+#pragma unroll
+      for (int i = 0; i < T::BS_PER_T; ++i) {
+        const int e = tid + i * G_THREADS;
+        if (e < BN * G_KS) p.bs[i] = w_scales[(int64_t)(n0 + e % BN) * KB + kbs + e / BN];
+      }
+      return;
+    }
     const int nb = min(G_KS, kb1 - kbs) * 2;  // 16-byte pieces present in this stage
 #pragma unroll
     for (int i = 0; i < T::A_CHUNKS; ++i) {
       const int c = tid + i * G_THREADS, row = c >> 3, piece = c & 7;
       const int gr = m0 + row;
-      pa[i] = (gr < M && piece < nb)
+      p.a[i] = (gr < M && piece < nb)
                   ? *reinterpret_cast<const v4i*>(a_codes + (int64_t)gr * K + (int64_t)kbs * QK + piece * 16)
                   : v4i{0, 0, 0, 0};
     }
@@ -103,7 +133,7 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
     for (int i = 0; i < T::B_CHUNKS; ++i) {
       const int c = tid + i * G_THREADS, row = c >> 3, piece = c & 7;
       const int gr = n0 + row;
-      pb[i] = (gr < N && piece < nb)
+      p.b[i] = (gr < N && piece < nb)
                   ? *reinterpret_cast<const v4i*>(w_codes + (int64_t)gr * K + (int64_t)kbs * QK + piece * 16)
                   : v4i{0, 0, 0, 0};
     }
@@ -111,35 +141,35 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
     for (int i = 0; i < T::AS_PER_T; ++i) {
       const int e = tid + i * G_THREADS, j = e / BM, row = e % BM;
       const int gr = m0 + row, kb = kbs + j;
-      pas[i] = (e < BM * G_KS && gr < M && kb < kb1) ? a_scales[(int64_t)gr * KB + kb] : (uint16_t)0;
+      p.as[i] = (e < BM * G_KS && gr < M && kb < kb1) ? a_scales[(int64_t)gr * KB + kb] : (uint16_t)0;
     }
 #pragma unroll
     for (int i = 0; i < T::BS_PER_T; ++i) {
       const int e = tid + i * G_THREADS, j = e / BN, row = e % BN;
       const int gr = n0 + row, kb = kbs + j;
-      pbs[i] = (e < BN * G_KS && gr < N && kb < kb1) ? w_scales[(int64_t)gr * KB + kb] : (uint16_t)0;
+      p.bs[i] = (e < BN * G_KS && gr < N && kb < kb1) ? w_scales[(int64_t)gr * KB + kb] : (uint16_t)0;
     }
   };
-  auto stash = [&](int st) {
+  auto stash = [&](const Pre& p, int st) {
 #pragma unroll
     for (int i = 0; i < T::A_CHUNKS; ++i) {
       const int c = tid + i * G_THREADS;
-      *reinterpret_cast<v4i*>(&sm.a[st][c >> 3][(c & 7) * 16]) = pa[i];
+      *reinterpret_cast<v4i*>(&sm.a[st][c >> 3][(c & 7) * 16]) = p.a[i];
     }
 #pragma unroll
     for (int i = 0; i < T::B_CHUNKS; ++i) {
       const int c = tid + i * G_THREADS;
-      *reinterpret_cast<v4i*>(&sm.b[st][c >> 3][(c & 7) * 16]) = pb[i];
+      *reinterpret_cast<v4i*>(&sm.b[st][c >> 3][(c & 7) * 16]) = p.b[i];
     }
 #pragma unroll
     for (int i = 0; i < T::AS_PER_T; ++i) {
       const int e = tid + i * G_THREADS;
-      if (e < BM * G_KS) sm.as[st][e / BM][e % BM] = (double)f16_bits_to_f32(pas[i]);
+      if (e < BM * G_KS) sm.as[st][e / BM][e % BM] = (double)f16_bits_to_f32(p.as[i]);
     }
 #pragma unroll
     for (int i = 0; i < T::BS_PER_T; ++i) {
       const int e = tid + i * G_THREADS;
-      if (e < BN * G_KS) sm.bs[st][e / BN][e % BN] = (double)f16_bits_to_f32(pbs[i]);
+      if (e < BN * G_KS) sm.bs[st][e / BN][e % BN] = (double)f16_bits_to_f32(p.bs[i]);
     }
   };
 
@@ -161,15 +191,9 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
   const int b_rrow = wn * 32 * CG + (lane & 31);          // + cg*32
   const int da_row = wm * 16 * RG + 2 * (lane >> 5);      // + rg*16 + 4c + e
 
-  if (kb0 < kb1) {
-    fetch(kb0);
-    stash(0);
-  }
-  __syncthreads();
-  for (int kbs = kb0; kbs < kb1; kbs += G_KS) {
-    const int st = ((kbs - kb0) / G_KS) & 1;
-    const bool more = kbs + G_KS < kb1;
-    if (more) fetch(kbs + G_KS);
+  // one stage of G_KS blocks from LDS buffer st
+  auto compute = [&](int st) {
+    asm volatile("" : "+v"(cinit));  // keep the accumulator initial value resident in VGPRs
 #pragma unroll 1
     for (int jb = 0; jb < G_KS; ++jb) {
       v4i fa[RG], fb[CG];
@@ -200,17 +224,56 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
           da[2 * c + 1] = v2.y;
         }
 #pragma unroll
-        for (int cg = 0; cg < CG; ++cg)
+        for (int cg = 0; cg < CG; ++cg) {
+          // the 8 (even, odd) register pairs are the f64 values 1.5*2^52 + 2^31 + I
+          v8d x = __builtin_bit_cast(v8d, d[rg][cg]);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const double x = pair_f64(d[rg][cg][2 * j], d[rg][cg][2 * j + 1]);
-            const double t = fma(x, dw[cg], cdw[cg]);
-            acc[rg][cg][j] = fma(t, da[j], acc[rg][cg][j]);
-          }
+          for (int j = 0; j < 8; ++j) x[j] = fma(x[j], dw[cg], cdw[cg]);   // exactly I*dw
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[rg][cg][j] = fma(x[j], da[j], acc[rg][cg][j]);
+        }
       }
     }
-    if (more) stash(st ^ 1);
+  };
+
+  // Stages of G_KS blocks through two LDS buffers.  The 1 x 2 tile keeps two stages of global
+  // loads in flight (two register sets, the loop unrolled by two so the sets stay static); the
+  // others keep one.
+  const int ns = (kb1 - kb0 + G_KS - 1) / G_KS;
+  Pre p0, p1;
+  if constexpr (RG == 1 && CG == 2) {
+    if (ns > 0) {
+      fetch(p0, kb0);
+      if (ns > 1) fetch(p1, kb0 + G_KS);
+      stash(p0, 0);
+    }
     __syncthreads();
+    for (int s = 0; s < ns; s += 2) {
+      if (s + 2 < ns) fetch(p0, kb0 + (s + 2) * G_KS);
+      compute(0);
+      if (s + 1 < ns) stash(p1, 1);
+      __syncthreads();
+      if (s + 1 < ns) {
+        if (s + 3 < ns) fetch(p1, kb0 + (s + 3) * G_KS);
+        compute(1);
+        if (s + 2 < ns) stash(p0, 0);
+        __syncthreads();
+      }
+    }
+  } else {
+    (void)p1;
+    if (ns > 0) {
+      fetch(p0, kb0);
+      stash(p0, 0);
+    }
+    __syncthreads();
+    for (int s = 0; s < ns; ++s) {
+      const bool more = s + 1 < ns;
+      if (more) fetch(p0, kb0 + (s + 1) * G_KS);
+      compute(s & 1);
+      if (more) stash(p0, (s & 1) ^ 1);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue.  Lane holds, for each (rg, cg, j): real row, column.
@@ -224,7 +287,7 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
 #pragma unroll
           for (int cg = 0; cg < CG; ++cg) {
             const int col = n0 + wn * 32 * CG + cg * 32 + (lane & 31);
-            if (col < N) partial[((int64_t)blockIdx.z * M + row) * N + col] = acc[rg][cg][j];
+            if (col < N) partial[((int64_t)kz * M + row) * N + col] = acc[rg][cg][j];
           }
         }
       } else if (EPI == EPI_F32) {
@@ -242,29 +305,37 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
             }
           }
         }
-      } else {  // EPI_SWIGLU_Q8: column group pairs (2p, 2p+1) = 32 gate rows, 32 up rows
+      }
+    }
+
+  if constexpr (EPI == EPI_SWIGLU_Q8 && !SPLIT) {
+    // column group pairs (2p, 2p+1) = 32 gate rows, 32 up rows of the interleaved weight; lane
+    // l%32 holds column l%32 of both, i.e. element l%32 of one Q8_0 block of the SwiGLU output.
+    // The 8 rows of a lane run side by side so their latencies overlap.
+    const int ncols = N / 2;
 #pragma unroll
-        for (int cp = 0; cp < CG / 2; ++cp) {
-          const int gcol = n0 + wn * 32 * CG + cp * 64;
-          const float gv = (float)acc[rg][2 * cp][j];
-          const float uv = (float)acc[rg][2 * cp + 1][j];
-          const float sv = swiglu_f32(gv, uv);
-          float m = fabsf(sv);
+    for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-          for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-          const float dq = m / 127.0f;
-          const float id = (dq != 0.0f) ? 1.0f / dq : 0.0f;
-          float r = roundf(sv * id);
-          r = fminf(fmaxf(r, -127.0f), 127.0f);
-          const int ncols = N / 2;
-          const int scol = gcol / 2 + (lane & 31);
+      for (int cp = 0; cp < CG / 2; ++cp) {
+        const int gcol = n0 + wn * 32 * CG + cp * 64;
+        const int scol = gcol / 2 + (lane & 31);
+        float sv[8], am[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sv[j] = swiglu_f32((float)acc[rg][2 * cp][j], (float)acc[rg][2 * cp + 1][j], exp_tab);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) am[j] = max32_nonneg(fabsf(sv[j]));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int row = m0 + wm * 16 * RG + rg * 16 + 4 * (j >> 1) + 2 * (lane >> 5) + (j & 1);
+          const float dq = div127_f32(am[j]);
+          const float id = (dq != 0.0f) ? recip_f32(dq) : 0.0f;
           if (row < M && gcol < N) {
-            q_codes[(int64_t)row * ncols + scol] = (int8_t)(int)r;
+            q_codes[(int64_t)row * ncols + scol] = (int8_t)q8_code(sv[j], id);
             if ((lane & 31) == 0) q_scales[(int64_t)row * (ncols / QK) + scol / QK] = f32_to_f16_bits(dq);
           }
         }
       }
-    }
+  }
 }
 
 // ---- split-K reductions (fixed order over the splits)
@@ -287,6 +358,9 @@ __global__ void __launch_bounds__(256) k_splitk_f32(const double* __restrict__ p
 
 __global__ void __launch_bounds__(256) k_splitk_swiglu(const double* __restrict__ partial, int S, int M, int N,
                                                        int8_t* __restrict__ q_codes, uint16_t* __restrict__ q_scales) {
+  __shared__ double exp_tab[64];
+  exp2_table_fill(exp_tab, threadIdx.x);
+  __syncthreads();
   const int ncols = N / 2;
   const int64_t nvec_row = ncols / 4;
   const int64_t total = (int64_t)M * nvec_row;
@@ -304,7 +378,7 @@ __global__ void __launch_bounds__(256) k_splitk_swiglu(const double* __restrict_
         g += partial[z * plane + row * N + gcol];
         u += partial[z * plane + row * N + gcol + 32];
       }
-      s[e] = swiglu_f32((float)g, (float)u);
+      s[e] = swiglu_f32((float)g, (float)u, exp_tab);
     }
     float d;
     const uint32_t q = q8_block_quant4(make_float4(s[0], s[1], s[2], s[3]), d);
@@ -333,9 +407,11 @@ static GemmPlan plan_gemm(int m, int n, int k, bool swiglu) {
   // Split K only for long reductions whose output tiles cannot fill the chip, keeping the f64
   // partials (written once, read once) at most 8 MB.
   const int target = 512;
-  const size_t max_partial = (size_t)8 << 20;
+  const size_t max_partial = KB >= 256 ? ((size_t)64 << 20) : ((size_t)8 << 20);
+  if (KB >= 256 && tiles_big >= 128 && !swiglu) p.shape = 1;  // long reductions: big tiles, split K
+  const int tiles2 = p.shape == 1 ? tiles_big : tiles;
   if (KB > 64)
-    while (p.split < 16 && tiles * p.split < target && KB / (p.split * 2) >= 2 * G_KS &&
+    while (p.split < 16 && tiles2 * p.split < target && KB / (p.split * 2) >= 2 * G_KS &&
            (size_t)(p.split * 2) * m * n * sizeof(double) <= max_partial)
       p.split *= 2;
   return p;
@@ -352,20 +428,22 @@ template <int RG, int CG>
 static void launch_tiles(const GemmArgs& g, int split, int kb_per, hipStream_t s) {
   using T = GemmTile<RG, CG>;
   dim3 grid((g.n + T::BN - 1) / T::BN, (g.m + T::BM - 1) / T::BM, split);
+  // XCD-aware order once the weights outgrow one XCD's 4 MB L2 several times over
+  const int xcd = (int64_t)g.n * g.k > ((int64_t)16 << 20) ? 1 : 0;
   double* partial = reinterpret_cast<double*>(g.workspace);
   if (split > 1)
     hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, true>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
                        g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
-                       partial, kb_per);
+                       partial, kb_per, xcd);
   else if (g.q_codes) {
     if constexpr (CG >= 2)
       hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_SWIGLU_Q8, false>), grid, dim3(G_THREADS), 0, s, g.a_codes,
                          g.a_scales, g.m, g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out,
-                         g.q_codes, g.q_scales, nullptr, kb_per);
+                         g.q_codes, g.q_scales, nullptr, kb_per, xcd);
   } else
     hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, false>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
                        g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
-                       nullptr, kb_per);
+                       nullptr, kb_per, xcd);
 }
 
 int launch_gemm_q8(const GemmArgs& g, hipStream_t s) {

@@ -126,17 +126,14 @@ int launch_rmsnorm_quant(const float* x, const float* gamma, int64_t rows, int c
 }
 
 // ---------------------------------------------------------------- SwiGLU + quantize
-// s = f32(g / (1 + exp(-g)) * u) in f64, then Q8_0.  Flat grid over float4s.
-__device__ __forceinline__ float swiglu1(float g, float u) {
-  const double gd = g;
-  const double sg = gd / (1.0 + exp(-gd));
-  return (float)(sg * (double)u);
-}
-
+// s = f32(silu(g) * u) in f64 (common.h), then Q8_0.  Flat grid over float4s.
 __global__ void __launch_bounds__(256) k_swiglu_quant(const float* __restrict__ gate,
                                                       const float* __restrict__ up, int64_t rows, int cols,
                                                       int64_t ld_in, int8_t* __restrict__ codes,
                                                       uint16_t* __restrict__ scales) {
+  __shared__ double exp_tab[64];
+  exp2_table_fill(exp_tab, threadIdx.x);
+  __syncthreads();
   const int64_t nvec_row = cols / 4;
   const int64_t total = rows * nvec_row;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
@@ -144,10 +141,10 @@ __global__ void __launch_bounds__(256) k_swiglu_quant(const float* __restrict__ 
     const float4 g = *reinterpret_cast<const float4*>(gate + r * ld_in + c4 * 4);
     const float4 u = *reinterpret_cast<const float4*>(up + r * ld_in + c4 * 4);
     float4 o;
-    o.x = swiglu1(g.x, u.x);
-    o.y = swiglu1(g.y, u.y);
-    o.z = swiglu1(g.z, u.z);
-    o.w = swiglu1(g.w, u.w);
+    o.x = swiglu_f32(g.x, u.x, exp_tab);
+    o.y = swiglu_f32(g.y, u.y, exp_tab);
+    o.z = swiglu_f32(g.z, u.z, exp_tab);
+    o.w = swiglu_f32(g.w, u.w, exp_tab);
     float d;
     const uint32_t q = q8_block_quant4(o, d);
     reinterpret_cast<uint32_t*>(codes + r * cols)[c4] = q;
