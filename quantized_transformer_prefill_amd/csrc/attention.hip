@@ -83,7 +83,8 @@ __global__ void __launch_bounds__(64 * NW) k_attention(const float* __restrict__
                                                        const float* __restrict__ v_region,
                                                        const int32_t* __restrict__ pos, int n_tokens, int max_pos,
                                                        int n_head, int n_head_kv, float* __restrict__ out,
-                                                       int64_t ld_out) {
+                                                       int64_t ld_out, int8_t* __restrict__ q_codes,
+                                                       uint16_t* __restrict__ q_scales) {
   constexpr int Q4 = HD / 4;    // dims per lane slot (scores) = MFMAs per score tile
   constexpr int NB = HD / 16;   // output dim blocks
   __shared__ double exp_tab[64];
@@ -225,19 +226,53 @@ __global__ void __launch_bounds__(64 * NW) k_attention(const float* __restrict__
       l_all += (mw == -INFINITY) ? 0.0 : sh_l[w][lane] * exp_f64(mw - m_all, exp_tab);
     }
     const double inv = recip_f64(l_all);
-    if (valid) {
-      float* op = out + (int64_t)t * ld_out + (int64_t)h * HD;
+    // lane holds dims (4i + slot)*NB + b of query l%16 (i = 0..3, b = 0..NB-1)
+    float o[4][NB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float* dst = op + (4 * i + slot) * NB;  // dims (4i + slot)*NB + b
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int b = 0; b < NB; b += 4) {
-          float4 o;
-          o.x = (float)(acc[b][i] * inv);
-          o.y = (float)(acc[b + 1][i] * inv);
-          o.z = (float)(acc[b + 2][i] * inv);
-          o.w = (float)(acc[b + 3][i] * inv);
-          *reinterpret_cast<float4*>(dst + b) = o;
+      for (int b = 0; b < NB; ++b) o[i][b] = (float)(acc[b][i] * inv);
+    if (!q_codes) {
+      if (valid) {
+        float* op = out + (int64_t)t * ld_out + (int64_t)h * HD;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float* dst = op + (4 * i + slot) * NB;
+#pragma unroll
+          for (int b = 0; b < NB; b += 4) *reinterpret_cast<float4*>(dst + b) = make_float4(o[i][b], o[i][b + 1], o[i][b + 2], o[i][b + 3]);
+        }
+      }
+    } else {
+      // Q8_0 of the output row: block kb of the head covers dims 32kb..32kb+31, i.e. the registers
+      // i with i*NB/8 == kb of the query's 4 lanes (slots) -- 8 values per lane
+      constexpr int IPB = 8 / NB;  // registers i per block
+      const int64_t nq = (int64_t)n_head * HD;
+#pragma unroll
+      for (int kb = 0; kb < HD / 32; ++kb) {
+        float m = 0.0f;
+#pragma unroll
+        for (int ii = 0; ii < IPB; ++ii)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) m = fmaxf(m, fabsf(o[kb * IPB + ii][b]));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const float d = div127_f32(m);
+        const float id = (d != 0.0f) ? recip_f32(d) : 0.0f;
+        if (valid) {
+          int8_t* cp = q_codes + (int64_t)t * nq + (int64_t)h * HD;
+#pragma unroll
+          for (int ii = 0; ii < IPB; ++ii) {
+            const int i = kb * IPB + ii;
+#pragma unroll
+            for (int b = 0; b < NB; b += 4) {
+              const uint32_t w4 = (uint32_t)(uint8_t)q8_code(o[i][b], id) |
+                                  ((uint32_t)(uint8_t)q8_code(o[i][b + 1], id) << 8) |
+                                  ((uint32_t)(uint8_t)q8_code(o[i][b + 2], id) << 16) |
+                                  ((uint32_t)(uint8_t)q8_code(o[i][b + 3], id) << 24);
+              *reinterpret_cast<uint32_t*>(cp + (4 * i + slot) * NB + b) = w4;
+            }
+          }
+          if (slot == 0) q_scales[(int64_t)t * (nq / QK) + (int64_t)h * (HD / QK) + kb] = f32_to_f16_bits(d);
         }
       }
     }
@@ -246,15 +281,16 @@ __global__ void __launch_bounds__(64 * NW) k_attention(const float* __restrict__
 
 int launch_attention(const float* q, int64_t ld_q, const float* k_region, const float* v_region,
                      const int32_t* pos, int n_tokens, int max_pos, int n_head, int n_head_kv,
-                     int head_dim, float* out, int64_t ld_out, hipStream_t s) {
+                     int head_dim, float* out, int64_t ld_out, hipStream_t s, int8_t* q_codes,
+                     uint16_t* q_scales) {
   if (n_tokens == 0) return MI_OK;
   dim3 grid((n_tokens + 15) / 16, n_head);
   if (head_dim == 64)
     hipLaunchKernelGGL((k_attention<64, 4>), grid, dim3(64 * 4), 0, s, q, ld_q, k_region, v_region, pos, n_tokens,
-                       max_pos, n_head, n_head_kv, out, ld_out);
+                       max_pos, n_head, n_head_kv, out, ld_out, q_codes, q_scales);
   else if (head_dim == 128)
     hipLaunchKernelGGL((k_attention<128, 4>), grid, dim3(64 * 4), 0, s, q, ld_q, k_region, v_region, pos,
-                       n_tokens, max_pos, n_head, n_head_kv, out, ld_out);
+                       n_tokens, max_pos, n_head, n_head_kv, out, ld_out, q_codes, q_scales);
   else
     return set_error(MI_ERR_UNSUPPORTED, "attention: head_dim %d (supported: 64, 128)", head_dim);
   MI_LAUNCH_CHECK("k_attention");

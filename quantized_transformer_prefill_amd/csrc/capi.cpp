@@ -169,7 +169,8 @@ extern "C" int mi_rmsnorm_quant(const float* x, const float* gamma, int64_t rows
                                 int8_t* codes, uint16_t* scales, float* y_out, void* stream) {
   if (!x || !gamma || !codes || !scales || rows < 0 || cols <= 0 || cols % QK)
     return set_error(MI_ERR_INVALID_ARG, "mi_rmsnorm_quant: bad arguments");
-  return launch_rmsnorm_quant(x, gamma, rows, cols, eps, codes, scales, y_out, as_stream(stream));
+  // no pending partials: x is only read
+  return launch_rmsnorm_quant(const_cast<float*>(x), gamma, rows, cols, eps, codes, scales, y_out, as_stream(stream));
 }
 
 extern "C" int mi_qk_norm(float* x, const float* gamma, int64_t rows, int32_t n_heads, int32_t head_dim, float eps,
@@ -221,7 +222,7 @@ extern "C" int mi_lm_head_row(const float* x, const float* gamma, float eps, con
   int8_t* xq = (int8_t*)scratch;
   uint16_t* xs = (uint16_t*)((char*)scratch + align_up(head->cols));
   hipStream_t s = as_stream(stream);
-  int rc = launch_rmsnorm_quant(x, gamma, 1, head->cols, eps, xq, xs, nullptr, s);
+  int rc = launch_rmsnorm_quant(const_cast<float*>(x), gamma, 1, head->cols, eps, xq, xs, nullptr, s);
   if (rc) return rc;
   return launch_lm_head(xq, xs, head->cols, head->codes, head->scales, head->rows, logits, s);
 }
@@ -287,10 +288,14 @@ extern "C" int mi_prefill_forward(const mi_model* md, const int32_t* token_ids, 
 
   if ((rc = launch_embed(md->token_embd.codes, md->token_embd.scales, H, w.ids, nt, w.h, s))) return rc;
   float* h_last = w.h + (size_t)(nt - 1) * H;  // the tail row
+  // the down projection's split-K partials, reduced (with its residual add) by the next RMSNorm
+  int pending = 1;
   for (int l = 0; l < hp.n_layers; ++l) {
     const mi_layer_weights& L = md->layers[l];
     const bool last = l == hp.n_layers - 1;
-    if ((rc = launch_rmsnorm_quant(w.h, L.attn_norm, nt, H, eps, w.xq, w.xs, nullptr, s))) return rc;
+    if ((rc = launch_rmsnorm_quant(w.h, L.attn_norm, nt, H, eps, w.xq, w.xs, nullptr, s, (const double*)w.gemm_ws,
+                                   pending)))
+      return rc;
     GemmArgs g{};
     g.a_codes = w.xq; g.a_scales = w.xs; g.m = nt;
     g.w_codes = L.wqkv.codes; g.w_scales = L.wqkv.scales; g.n = nqkv; g.k = H;
@@ -307,14 +312,15 @@ extern "C" int mi_prefill_forward(const mi_model* md, const int32_t* token_ids, 
     if ((rc = launch_rope_kvstore(q, nqkv, k, v, nqkv, w.pos, nt, hp.n_head, hp.n_head_kv, hp.head_dim,
                                   md->rope_table, kv->k[l], kv->v[l], s)))
       return rc;
-    if ((rc = launch_attention(q, nqkv, kv->k[l], kv->v[l], w.pos, nt, max_pos, hp.n_head, hp.n_head_kv,
-                               hp.head_dim, w.attn, nq, s)))
-      return rc;
-    // attention output [nt][nq] back to Q8_0
-    const int rows = last ? 1 : nt;                       // tail: only the last token continues
-    const float* o_src = last ? w.attn + (size_t)(nt - 1) * nq : w.attn;
+    // attention, its output rows quantized to Q8_0 in the same kernel.  In the last layer only the
+    // last token continues past the output projection, so only its row is computed (the KV store
+    // above covered every token).
+    const int rows = last ? 1 : nt;
+    const int t0 = nt - rows;
     float* h_rows = last ? h_last : w.h;
-    if ((rc = launch_quantize(o_src, rows, nq, nq, w.xq, w.xs, s))) return rc;
+    if ((rc = launch_attention(q + (size_t)t0 * nqkv, nqkv, kv->k[l], kv->v[l], w.pos + t0, rows, max_pos, hp.n_head,
+                               hp.n_head_kv, hp.head_dim, nullptr, nq, s, w.xq, w.xs)))
+      return rc;
     GemmArgs go{};
     go.a_codes = w.xq; go.a_scales = w.xs; go.m = rows;
     go.w_codes = L.wo.codes; go.w_scales = L.wo.scales; go.n = H; go.k = nq;
@@ -335,10 +341,13 @@ extern "C" int mi_prefill_forward(const mi_model* md, const int32_t* token_ids, 
     gd.w_codes = L.w_down.codes; gd.w_scales = L.w_down.scales; gd.n = H; gd.k = F;
     gd.residual = h_rows; gd.out = h_rows; gd.ld_out = H;
     gd.workspace = w.gemm_ws; gd.workspace_bytes = w.gemm_ws_bytes;
+    gd.split_out = &pending;
     if ((rc = launch_gemm_q8(gd, s))) return rc;
   }
   const mi_q8_matrix& head = hp.tied ? md->token_embd : md->output;
-  if ((rc = launch_rmsnorm_quant(h_last, md->output_norm, 1, H, eps, w.lm_q, w.lm_s, nullptr, s))) return rc;
+  if ((rc = launch_rmsnorm_quant(h_last, md->output_norm, 1, H, eps, w.lm_q, w.lm_s, nullptr, s,
+                                 (const double*)w.gemm_ws, pending)))
+    return rc;
   if ((rc = launch_lm_head(w.lm_q, w.lm_s, H, head.codes, head.scales, head.rows, logits_out, s))) return rc;
   return MI_OK;
 }

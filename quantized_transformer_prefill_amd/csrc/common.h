@@ -155,8 +155,11 @@ __device__ __forceinline__ float swiglu_f32(float g, float u, const double* tab)
 // All take device pointers, assume validated shapes, launch on `s`.
 int launch_quantize(const float* x, int64_t rows, int cols, int64_t ld_x, int8_t* codes,
                     uint16_t* scales, hipStream_t s);
-int launch_rmsnorm_quant(const float* x, const float* gamma, int64_t rows, int cols, float eps,
-                         int8_t* codes, uint16_t* scales, float* y, hipStream_t s);
+// x [rows][cols]; with n_split > 1, x += f32(sum of the split-K partials [n_split][rows][cols]) first
+// (written back), as the deferred reduction of the matmul that produced them.
+int launch_rmsnorm_quant(float* x, const float* gamma, int64_t rows, int cols, float eps,
+                         int8_t* codes, uint16_t* scales, float* y, hipStream_t s,
+                         const double* partial = nullptr, int n_split = 0);
 int launch_swiglu_quant(const float* gate, const float* up, int64_t rows, int cols, int64_t ld_in,
                         int8_t* codes, uint16_t* scales, hipStream_t s);
 int launch_embed(const int8_t* codes, const uint16_t* scales, int cols, const int32_t* ids, int n,
@@ -166,9 +169,12 @@ int launch_qk_norm(float* x, int64_t ld, const float* gamma, int64_t rows, int n
 int launch_rope_kvstore(float* q, int64_t ld_q, const float* k, const float* v, int64_t ld_kv,
                         const int32_t* pos, int n_tokens, int n_head, int n_head_kv, int head_dim,
                         const double* table, float* k_region, float* v_region, hipStream_t s);
+// out f32 [n_tokens][ld_out], or, with q_codes non-null, the output rows quantized to Q8_0
+// (codes [n_tokens][n_head*head_dim], scales [n_tokens][n_head*head_dim/32]) and out unused.
 int launch_attention(const float* q, int64_t ld_q, const float* k_region, const float* v_region,
                      const int32_t* pos, int n_tokens, int max_pos, int n_head, int n_head_kv,
-                     int head_dim, float* out, int64_t ld_out, hipStream_t s);
+                     int head_dim, float* out, int64_t ld_out, hipStream_t s,
+                     int8_t* q_codes = nullptr, uint16_t* q_scales = nullptr);
 
 // Exact Q8_0 GEMM.  Epilogue modes:
 enum GemmEpi { EPI_F32 = 0, EPI_SWIGLU_Q8 = 1 };
@@ -182,6 +188,9 @@ struct GemmArgs {
   int8_t* q_codes; uint16_t* q_scales;                       // EPI_SWIGLU_Q8 output [m][n/2]
   void* workspace; size_t workspace_bytes;                   // split-K partials
   int split_k;            // 0 = choose
+  // EPI_F32 only: when split K is used, leave the f64 partials [split][m][n] in workspace
+  // and skip the reduction (the consumer reduces them); *split_out receives the split (1 = none)
+  int* split_out;
 };
 int launch_gemm_q8(const GemmArgs& a, hipStream_t s);
 size_t gemm_workspace_bytes(int m, int n, int k);

@@ -462,7 +462,9 @@ int launch_gemm_q8(const GemmArgs& g, hipStream_t s) {
   else if (p.shape == 2) launch_tiles<1, 2>(g, split, kb_per, s);
   else launch_tiles<1, 1>(g, split, kb_per, s);
   MI_LAUNCH_CHECK("k_gemm_q8");
-  if (split == 1) return MI_OK;
+  const bool defer = g.split_out && !g.q_codes && !g.bias && split > 1;  // the consumer reduces the partials
+  if (g.split_out) *g.split_out = defer ? split : 1;
+  if (split == 1 || defer) return MI_OK;
   double* partial = reinterpret_cast<double*>(g.workspace);
   if (g.q_codes) {
     const int64_t total = (int64_t)g.m * (g.n / 2 / 4);

@@ -65,49 +65,71 @@ __device__ double block_sum_f64(double v, double* sh) {
 }
 
 // ---------------------------------------------------------------- RMSNorm + quantize
-// One workgroup per row.  y = f32(x / sqrt(mean(x^2) + eps) * gamma) with the mean,
-// sqrt, divide and gain in f64; then Q8_0 per 32-block.  Rows of up to 16 float4 per
-// thread stay in registers (cols <= 16384), longer rows are re-read.
+// One workgroup per row.  y = f32(x / sqrt(mean(x^2) + eps) * gamma) with the mean, sqrt,
+// reciprocal and gain in f64; then Q8_0 per 32-block.  Rows of up to RN_MAXV float4 per thread
+// stay in registers, longer rows are re-read.
+//
+// Pending split-K partials (partial != null): the row first becomes
+// x + f32(sum_z partial[z][r]) (the residual add of the matmul that produced the partials, summed
+// in the fixed order z = 0..n_split-1 exactly as the split-K reduction would), which is written
+// back to x before the norm.
 constexpr int RN_THREADS = 256;
 constexpr int RN_MAXV = 8;  // float4 per thread kept in registers
 
-__global__ void __launch_bounds__(RN_THREADS) k_rmsnorm_quant(const float* __restrict__ x,
+__global__ void __launch_bounds__(RN_THREADS) k_rmsnorm_quant(float* __restrict__ x,
                                                              const float* __restrict__ gamma, int cols,
                                                              float eps, int8_t* __restrict__ codes,
                                                              uint16_t* __restrict__ scales,
-                                                             float* __restrict__ y_out) {
+                                                             float* __restrict__ y_out,
+                                                             const double* __restrict__ partial, int n_split,
+                                                             int64_t rows) {
   __shared__ double sh[RN_THREADS / 64 + 1];
   const int64_t r = blockIdx.x;
-  const float* xr = x + r * cols;
+  float* xr = x + r * cols;
   const int nvec = cols / 4;
+  auto load = [&](int c4) -> float4 {
+    float4 v = reinterpret_cast<const float4*>(xr)[c4];
+    if (partial) {
+      double a = 0.0, b = 0.0, c = 0.0, d = 0.0;
+      for (int z = 0; z < n_split; ++z) {
+        const double* pz = partial + ((int64_t)z * rows + r) * cols + 4 * c4;
+        const double2 p0 = reinterpret_cast<const double2*>(pz)[0];
+        const double2 p1 = reinterpret_cast<const double2*>(pz)[1];
+        a += p0.x; b += p0.y; c += p1.x; d += p1.y;
+      }
+      v.x = v.x + (float)a; v.y = v.y + (float)b; v.z = v.z + (float)c; v.w = v.w + (float)d;
+      reinterpret_cast<float4*>(xr)[c4] = v;
+    }
+    return v;
+  };
   float4 keep[RN_MAXV];
   double ss = 0.0;
 #pragma unroll
   for (int j = 0; j < RN_MAXV; ++j) {
     const int c4 = threadIdx.x + j * RN_THREADS;
     if (c4 < nvec) {
-      keep[j] = reinterpret_cast<const float4*>(xr)[c4];
+      keep[j] = load(c4);
       const double a = keep[j].x, b = keep[j].y, c = keep[j].z, d = keep[j].w;
       ss += a * a + b * b + c * c + d * d;
     }
   }
   for (int c4 = threadIdx.x + RN_MAXV * RN_THREADS; c4 < nvec; c4 += RN_THREADS) {
-    const float4 v = reinterpret_cast<const float4*>(xr)[c4];
+    const float4 v = load(c4);
     const double a = v.x, b = v.y, c = v.z, d = v.w;
     ss += a * a + b * b + c * c + d * d;
   }
   const double total = block_sum_f64<RN_THREADS>(ss, sh);
-  const double rms = sqrt(total / (double)cols + (double)eps);
+  const double inv_rms = recip_f64(sqrt(total / (double)cols + (double)eps));
   // rows are a multiple of 32 values; lane groups of 8 cover one block, and all 8 lanes of
-  // a group share the same loop trip count, so the shuffles see a full group.
+  // a group share the same loop trip count, so the cross-lane maxima see a full group.
   for (int c4 = threadIdx.x, j = 0; c4 < nvec; c4 += RN_THREADS, ++j) {
     const float4 v = (j < RN_MAXV) ? keep[j] : reinterpret_cast<const float4*>(xr)[c4];
     const float4 g = reinterpret_cast<const float4*>(gamma)[c4];
     float4 o;
-    o.x = (float)((double)v.x / rms * (double)g.x);
-    o.y = (float)((double)v.y / rms * (double)g.y);
-    o.z = (float)((double)v.z / rms * (double)g.z);
-    o.w = (float)((double)v.w / rms * (double)g.w);
+    o.x = (float)((double)v.x * inv_rms * (double)g.x);
+    o.y = (float)((double)v.y * inv_rms * (double)g.y);
+    o.z = (float)((double)v.z * inv_rms * (double)g.z);
+    o.w = (float)((double)v.w * inv_rms * (double)g.w);
     if (y_out) reinterpret_cast<float4*>(y_out + r * cols)[c4] = o;
     float d;
     const uint32_t q = q8_block_quant4(o, d);
@@ -116,11 +138,12 @@ __global__ void __launch_bounds__(RN_THREADS) k_rmsnorm_quant(const float* __res
   }
 }
 
-int launch_rmsnorm_quant(const float* x, const float* gamma, int64_t rows, int cols, float eps,
-                         int8_t* codes, uint16_t* scales, float* y, hipStream_t s) {
+int launch_rmsnorm_quant(float* x, const float* gamma, int64_t rows, int cols, float eps,
+                         int8_t* codes, uint16_t* scales, float* y, hipStream_t s, const double* partial,
+                         int n_split) {
   if (rows == 0) return MI_OK;
   hipLaunchKernelGGL(k_rmsnorm_quant, dim3((unsigned)rows), dim3(RN_THREADS), 0, s, x, gamma, cols, eps,
-                     codes, scales, y);
+                     codes, scales, y, n_split > 1 ? partial : nullptr, n_split, rows);
   MI_LAUNCH_CHECK("k_rmsnorm_quant");
   return MI_OK;
 }
