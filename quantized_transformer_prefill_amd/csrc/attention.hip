@@ -6,9 +6,10 @@
 // scores, softmax and the weighted sum run in f64 on v_mfma_f64_16x16x4f64; the online-softmax
 // bookkeeping (running max, running sum, rescale) is f64 on the VALU.
 //
-// Work split: a workgroup of NW waves serves 16 query tokens x 1 head.  The key tiles (16 rows
-// each, from row 0 to the largest position among the 16 queries) are dealt round-robin to the
-// waves, so every wave sees early and late tiles alike.  Each wave keeps its own running max,
+// Work split: a group of NW waves serves 16 query tokens x 1 head.  The key tiles (16 rows each,
+// from row 0 to the largest position among the 16 queries) are dealt round-robin to the waves,
+// so every wave sees early and late tiles alike.  For head_dim 64 a workgroup holds two groups,
+// for query tiles x and (last - x), which balances the causal work across workgroups and SIMDs.  Each wave keeps its own running max,
 // sum and output; at the end the partial states are merged in f64 through LDS, pairwise in a
 // fixed order (o = sum_w O_w e^(m_w - m) / sum_w l_w e^(m_w - m)).  The next tile's K and V are
 // loaded while the current tile computes.
@@ -77,8 +78,8 @@ __device__ __forceinline__ double f4get(const float4& v, int e) {
   return e == 0 ? (double)v.x : e == 1 ? (double)v.y : e == 2 ? (double)v.z : (double)v.w;
 }
 
-template <int HD, int NW>
-__global__ void __launch_bounds__(64 * NW) k_attention(const float* __restrict__ q, int64_t ld_q,
+template <int HD, int NW, int NG>
+__global__ void __launch_bounds__(64 * NW * NG) k_attention(const float* __restrict__ q, int64_t ld_q,
                                                        const float* __restrict__ k_region,
                                                        const float* __restrict__ v_region,
                                                        const int32_t* __restrict__ pos, int n_tokens, int max_pos,
@@ -88,16 +89,22 @@ __global__ void __launch_bounds__(64 * NW) k_attention(const float* __restrict__
   constexpr int Q4 = HD / 4;    // dims per lane slot (scores) = MFMAs per score tile
   constexpr int NB = HD / 16;   // output dim blocks
   __shared__ double exp_tab[64];
-  __shared__ double sh_m[NW][64], sh_l[NW][64];
-  __shared__ double sh_o[NW / 2][NB * 4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ double sh_m[NG][NW][64], sh_l[NG][NW][64];
+  __shared__ double sh_o[NG][NW / 2][NB * 4][64];
+  const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) % NW, grp = (threadIdx.x >> 6) / NW;
   const int qi = lane & 15, slot = lane >> 4;
   exp2_table_fill(exp_tab, threadIdx.x);
   const int h = blockIdx.y;
   const int g = h / (n_head / n_head_kv);
   const int kv_embd = n_head_kv * HD;
-  const int t = blockIdx.x * 16 + qi;
-  const bool valid = t < n_tokens;
+  // query tile of this group: with two groups, workgroup x serves tiles x and nqt-1-x, so that
+  // every workgroup (and every SIMD: waves w and w+NW share one) gets about the same number of
+  // key tiles under the causal mask; the middle workgroup of an odd count has one group
+  const int nqt = (n_tokens + 15) / 16;
+  const int qt = grp == 0 ? blockIdx.x : nqt - 1 - blockIdx.x;
+  const bool gactive = grp == 0 || qt != (int)blockIdx.x;
+  const int t = qt * 16 + qi;
+  const bool valid = gactive && t < n_tokens;
   const int p = valid ? pos[t] : 0;
   int pmax = p, pmin = valid ? p : 0x7fffffff;
   for (int o = 1; o < 16; o <<= 1) {
@@ -127,7 +134,7 @@ __global__ void __launch_bounds__(64 * NW) k_attention(const float* __restrict__
 
   const float* kbase = k_region + (int64_t)g * HD;
   const float* vbase = v_region + (int64_t)g * HD;
-  const int ntiles = pmax / 16 + 1;
+  const int ntiles = gactive ? pmax / 16 + 1 : 0;
 
   // one key tile: scores, online softmax, O += V^T P^T
   auto tile_step = [&](AttnTile<HD>& cur, int key0) {
@@ -190,12 +197,12 @@ __global__ void __launch_bounds__(64 * NW) k_attention(const float* __restrict__
   // ---- merge: the query's sum over its 4 lanes, then the waves' partial states (f64, fixed order)
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  sh_m[wave][lane] = m_run;
-  sh_l[wave][lane] = l_run;
+  sh_m[grp][wave][lane] = m_run;
+  sh_l[grp][wave][lane] = l_run;
   __syncthreads();
   double m_all = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) m_all = fmax(m_all, sh_m[w][lane]);
+  for (int w = 0; w < NW; ++w) m_all = fmax(m_all, sh_m[grp][w][lane]);
   {
     const double f_self = (m_run == -INFINITY) ? 0.0 : exp_f64(m_run - m_all, exp_tab);
 #pragma unroll
@@ -207,14 +214,14 @@ __global__ void __launch_bounds__(64 * NW) k_attention(const float* __restrict__
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sh_o[wave - half][b * 4 + i][lane] = acc[b][i];
+        for (int i = 0; i < 4; ++i) sh_o[grp][wave - half][b * 4 + i][lane] = acc[b][i];
     }
     __syncthreads();
     if (wave < half) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[b][i] += sh_o[wave][b * 4 + i][lane];
+        for (int i = 0; i < 4; ++i) acc[b][i] += sh_o[grp][wave][b * 4 + i][lane];
     }
     if (half > 1) __syncthreads();
   }
@@ -222,8 +229,8 @@ __global__ void __launch_bounds__(64 * NW) k_attention(const float* __restrict__
     double l_all = 0.0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const double mw = sh_m[w][lane];
-      l_all += (mw == -INFINITY) ? 0.0 : sh_l[w][lane] * exp_f64(mw - m_all, exp_tab);
+      const double mw = sh_m[grp][w][lane];
+      l_all += (mw == -INFINITY) ? 0.0 : sh_l[grp][w][lane] * exp_f64(mw - m_all, exp_tab);
     }
     const double inv = recip_f64(l_all);
     // lane holds dims (4i + slot)*NB + b of query l%16 (i = 0..3, b = 0..NB-1)
@@ -284,13 +291,13 @@ int launch_attention(const float* q, int64_t ld_q, const float* k_region, const 
                      int head_dim, float* out, int64_t ld_out, hipStream_t s, int8_t* q_codes,
                      uint16_t* q_scales) {
   if (n_tokens == 0) return MI_OK;
-  dim3 grid((n_tokens + 15) / 16, n_head);
+  const int nqt = (n_tokens + 15) / 16;
   if (head_dim == 64)
-    hipLaunchKernelGGL((k_attention<64, 4>), grid, dim3(64 * 4), 0, s, q, ld_q, k_region, v_region, pos, n_tokens,
-                       max_pos, n_head, n_head_kv, out, ld_out, q_codes, q_scales);
+    hipLaunchKernelGGL((k_attention<64, 4, 2>), dim3((nqt + 1) / 2, n_head), dim3(64 * 4 * 2), 0, s, q, ld_q, k_region,
+                       v_region, pos, n_tokens, max_pos, n_head, n_head_kv, out, ld_out, q_codes, q_scales);
   else if (head_dim == 128)
-    hipLaunchKernelGGL((k_attention<128, 4>), grid, dim3(64 * 4), 0, s, q, ld_q, k_region, v_region, pos,
-                       n_tokens, max_pos, n_head, n_head_kv, out, ld_out, q_codes, q_scales);
+    hipLaunchKernelGGL((k_attention<128, 4, 1>), dim3(nqt, n_head), dim3(64 * 4), 0, s, q, ld_q, k_region, v_region,
+                       pos, n_tokens, max_pos, n_head, n_head_kv, out, ld_out, q_codes, q_scales);
   else
     return set_error(MI_ERR_UNSUPPORTED, "attention: head_dim %d (supported: 64, 128)", head_dim);
   MI_LAUNCH_CHECK("k_attention");
