@@ -268,7 +268,7 @@ def write_traffic(fetch_dir, write_dir):
     print(json.dumps(rec))
 
 
-def cpu_baseline(cfg, min_seconds: float = 10.0, max_reps: int = 3):
+def cpu_baseline(cfg, min_seconds: float = 10.0, max_reps: int = 8):
     """Time the oracle (numpy, f64 GEMMs) on whole forwards of the same model and prompt.
 
     The sample is the full prefill call (every layer, the KV stores, the last-token lm_head),

@@ -11,7 +11,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmi_prefill.so")
+# MI_PREFILL_LIB selects another build of the same library (for A/B timing of builds)
+LIB_PATH = os.environ.get("MI_PREFILL_LIB") or os.path.join(_HERE, "libmi_prefill.so")
 
 MI_OK, MI_ERR_INVALID_ARG, MI_ERR_POSITION_RANGE, MI_ERR_DUP_POSITION = 0, 1, 2, 3
 MI_ERR_KV_MISMATCH, MI_ERR_WORKSPACE, MI_ERR_HIP, MI_ERR_UNSUPPORTED = 4, 5, 6, 7
