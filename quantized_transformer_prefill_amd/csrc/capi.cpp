@@ -296,22 +296,18 @@ extern "C" int mi_prefill_forward(const mi_model* md, const int32_t* token_ids, 
     if ((rc = launch_rmsnorm_quant(w.h, L.attn_norm, nt, H, eps, w.xq, w.xs, nullptr, s, (const double*)w.gemm_ws,
                                    pending)))
       return rc;
+    // Q|K|V matmul; its epilogue applies the QK norm (Qwen3) and RoPE, writes Q, and stores the
+    // rotated K and the raw V into the layer's regions at the tokens' positions
     GemmArgs g{};
     g.a_codes = w.xq; g.a_scales = w.xs; g.m = nt;
     g.w_codes = L.wqkv.codes; g.w_scales = L.wqkv.scales; g.n = nqkv; g.k = H;
     g.bias = hp.qkv_bias ? L.bqkv : nullptr; g.out = w.qkv; g.ld_out = nqkv;
     g.workspace = w.gemm_ws; g.workspace_bytes = w.gemm_ws_bytes;
+    g.qkv.pos = w.pos; g.qkv.rope = md->rope_table; g.qkv.n_q = nq; g.qkv.n_kv = nkv; g.qkv.head_dim = hp.head_dim;
+    g.qkv.k_region = kv->k[l]; g.qkv.v_region = kv->v[l];
+    g.qkv.q_norm = hp.qk_norm ? L.q_norm : nullptr; g.qkv.k_norm = hp.qk_norm ? L.k_norm : nullptr; g.qkv.eps = eps;
     if ((rc = launch_gemm_q8(g, s))) return rc;
     float* q = w.qkv;
-    float* k = w.qkv + nq;
-    float* v = w.qkv + nq + nkv;
-    if (hp.qk_norm) {
-      if ((rc = launch_qk_norm(q, nqkv, L.q_norm, nt, hp.n_head, hp.head_dim, eps, s))) return rc;
-      if ((rc = launch_qk_norm(k, nqkv, L.k_norm, nt, hp.n_head_kv, hp.head_dim, eps, s))) return rc;
-    }
-    if ((rc = launch_rope_kvstore(q, nqkv, k, v, nqkv, w.pos, nt, hp.n_head, hp.n_head_kv, hp.head_dim,
-                                  md->rope_table, kv->k[l], kv->v[l], s)))
-      return rc;
     // attention, its output rows quantized to Q8_0 in the same kernel.  In the last layer only the
     // last token continues past the output projection, so only its row is computed (the KV store
     // above covered every token).

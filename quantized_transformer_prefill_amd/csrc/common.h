@@ -177,7 +177,21 @@ int launch_attention(const float* q, int64_t ld_q, const float* k_region, const 
                      int8_t* q_codes = nullptr, uint16_t* q_scales = nullptr);
 
 // Exact Q8_0 GEMM.  Epilogue modes:
-enum GemmEpi { EPI_F32 = 0, EPI_SWIGLU_Q8 = 1 };
+enum GemmEpi { EPI_F32 = 0, EPI_SWIGLU_Q8 = 1, EPI_QKV = 2 };
+
+// EPI_QKV: the stacked Q|K|V matmul of a layer finishes the attention inputs in its epilogue:
+// [per-head QK RMSNorm] and NeoX RoPE of the Q and K heads, Q written to `out`, rotated K and raw
+// V stored into the layer's regions at row pos[t].  Every head lies inside one tile.
+struct QkvEpi {
+  const int32_t* pos;      // device [m]
+  const double* rope;      // device [n_ctx][head_dim/2] of (cos, sin)
+  int n_q, n_kv, head_dim; // Q columns, K (= V) columns, head size
+  float* k_region;         // device [n_ctx][n_kv]
+  float* v_region;
+  const float* q_norm;     // [head_dim] gains of the QK norm, or null (no QK norm)
+  const float* k_norm;
+  float eps;
+};
 struct GemmArgs {
   const int8_t* a_codes; const uint16_t* a_scales; int m;   // activations [m][k]
   const int8_t* w_codes; const uint16_t* w_scales; int n;   // weights [n][k]
@@ -191,6 +205,7 @@ struct GemmArgs {
   // EPI_F32 only: when split K is used, leave the f64 partials [split][m][n] in workspace
   // and skip the reduction (the consumer reduces them); *split_out receives the split (1 = none)
   int* split_out;
+  QkvEpi qkv;             // EPI_QKV parameters (used when qkv.pos is non-null)
 };
 int launch_gemm_q8(const GemmArgs& a, hipStream_t s);
 size_t gemm_workspace_bytes(int m, int n, int k);

@@ -59,7 +59,7 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
           const int8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales, int N, int K,
           const float* __restrict__ bias, const float* residual, float* out, int64_t ld_out,
           int8_t* __restrict__ q_codes, uint16_t* __restrict__ q_scales,
-          double* __restrict__ partial, int kb_per_split, int xcd_order) {
+          double* __restrict__ partial, int kb_per_split, int xcd_order, QkvEpi qe) {
   using T = GemmTile<RG, CG>;
   constexpr int BM = T::BM, BN = T::BN;
   __shared__ __align__(16) T sm;
@@ -83,6 +83,24 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
   const int KB = K / QK;
   const int kb0 = kz * kb_per_split;
   const int kb1 = min(KB, kb0 + kb_per_split);
+
+  // QKV epilogue of the smallest tile: the positions and (cos, sin) of this thread's RoPE pairs
+  // are requested now, so they arrive while the K loop runs
+  constexpr int QPRE = (EPI == EPI_QKV && RG == 1 && CG == 1) ? GemmTile<RG, CG>::BM * GemmTile<RG, CG>::BN / 2 / G_THREADS : 0;
+  double2 qcs[QPRE > 0 ? QPRE : 1];
+  int64_t qpos[QPRE > 0 ? QPRE : 1];
+  if constexpr (QPRE > 0) {
+    const int half = qe.head_dim / 2;
+#pragma unroll
+    for (int k = 0; k < QPRE; ++k) {
+      const int e = tid + k * G_THREADS;
+      const int row_l = e / (BN / 2), r2 = e - row_l * (BN / 2);
+      const int i = r2 % half;
+      const int row = m0 + row_l;
+      qpos[k] = row < M ? qe.pos[row] : 0;
+      qcs[k] = reinterpret_cast<const double2*>(qe.rope)[qpos[k] * half + i];
+    }
+  }
 
   // zero row for the dummy MFMA rows (both stages)
   if (tid < 2 * G_ROWB / 16) *reinterpret_cast<v4i*>(&sm.a[tid / (G_ROWB / 16)][BM][(tid % (G_ROWB / 16)) * 16]) =
@@ -290,8 +308,8 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
             if (col < N) partial[((int64_t)kz * M + row) * N + col] = acc[rg][cg][j];
           }
         }
-      } else if (EPI == EPI_F32) {
-        if (row < M) {
+      } else if (EPI == EPI_F32 || EPI == EPI_QKV) {
+        if (EPI == EPI_F32 && row < M) {
 #pragma unroll
           for (int cg = 0; cg < CG; ++cg) {
             const int col = n0 + wn * 32 * CG + cg * 32 + (lane & 31);
@@ -307,6 +325,83 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
         }
       }
     }
+
+  if constexpr (EPI == EPI_QKV && !SPLIT) {
+    // Stage the tile's outputs (bias added in f64, one rounding to f32) in LDS -- the staging
+    // buffers are free after the K loop's last barrier -- so that each RoPE pair (i, i + hd/2) and
+    // each head's QK-norm sum meet in one thread.  Tiles hold whole heads (BN % head_dim == 0).
+    float* tb = reinterpret_cast<float*>(&sm);
+    static_assert(sizeof(T) >= sizeof(float) * BM * BN + sizeof(double) * BM * 4, "QKV staging");
+    double* inv_rms = reinterpret_cast<double*>(tb + BM * BN);   // [BM][BN / head_dim]
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row_l = wm * 16 * RG + rg * 16 + 4 * (j >> 1) + 2 * (lane >> 5) + (j & 1);
+#pragma unroll
+        for (int cg = 0; cg < CG; ++cg) {
+          const int col_l = wn * 32 * CG + cg * 32 + (lane & 31);
+          double v = acc[rg][cg][j];
+          if (bias && n0 + col_l < N) v += (double)bias[n0 + col_l];
+          tb[row_l * BN + col_l] = (float)v;
+        }
+      }
+    __syncthreads();
+    const int hd = qe.head_dim, half = hd / 2, heads = BN / hd;
+    if (qe.q_norm) {
+      // f64 sum of squares per (row, head) of the Q and K heads: one thread per pair
+      for (int gidx = tid; gidx < BM * heads; gidx += G_THREADS) {
+        const int row_l = gidx / heads, hh = gidx - row_l * heads;
+        const float* xr = tb + row_l * BN + hh * hd;
+        double ss = 0.0;
+        for (int i = 0; i < hd; ++i) ss += (double)xr[i] * (double)xr[i];
+        inv_rms[gidx] = recip_f64(sqrt(ss / (double)hd + (double)qe.eps));
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < BM * BN / 2 / G_THREADS; ++k) {
+      const int e = tid + k * G_THREADS;
+      const int row_l = e / (BN / 2), r2 = e - row_l * (BN / 2);
+      const int hh = r2 / half, i = r2 - hh * half;
+      const int col0 = hh * hd + i;
+      const int row = m0 + row_l, gcol = n0 + col0;
+      if (row >= M || gcol >= N) continue;
+      float a = tb[row_l * BN + col0], b = tb[row_l * BN + col0 + half];
+      int64_t p;
+      double2 cs;
+      if constexpr (QPRE > 0) {
+        p = qpos[k];
+        cs = qcs[k];
+      } else {
+        p = qe.pos[row];
+        cs = reinterpret_cast<const double2*>(qe.rope)[p * half + i];
+      }
+      if (gcol < qe.n_q + qe.n_kv) {
+        const bool isq = gcol < qe.n_q;
+        if (qe.q_norm) {
+          const float* gam = isq ? qe.q_norm : qe.k_norm;
+          const double ir = inv_rms[row_l * heads + hh];
+          a = (float)((double)a * ir * (double)gam[i]);
+          b = (float)((double)b * ir * (double)gam[i + half]);
+        }
+        const float r0 = (float)((double)a * cs.x - (double)b * cs.y);
+        const float r1 = (float)((double)a * cs.y + (double)b * cs.x);
+        if (isq) {
+          out[(int64_t)row * ld_out + gcol] = r0;
+          out[(int64_t)row * ld_out + gcol + half] = r1;
+        } else {
+          float* kr = qe.k_region + p * qe.n_kv + (gcol - qe.n_q);
+          kr[0] = r0;
+          kr[half] = r1;
+        }
+      } else {
+        float* vr = qe.v_region + p * qe.n_kv + (gcol - qe.n_q - qe.n_kv);
+        vr[0] = a;
+        vr[half] = b;
+      }
+    }
+  }
 
   if constexpr (EPI == EPI_SWIGLU_Q8 && !SPLIT) {
     // column group pairs (2p, 2p+1) = 32 gate rows, 32 up rows of the interleaved weight; lane
@@ -434,16 +529,20 @@ static void launch_tiles(const GemmArgs& g, int split, int kb_per, hipStream_t s
   if (split > 1)
     hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, true>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
                        g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
-                       partial, kb_per, xcd);
+                       partial, kb_per, xcd, g.qkv);
+  else if (g.qkv.pos)
+    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_QKV, false>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
+                       g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
+                       nullptr, kb_per, xcd, g.qkv);
   else if (g.q_codes) {
     if constexpr (CG >= 2)
       hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_SWIGLU_Q8, false>), grid, dim3(G_THREADS), 0, s, g.a_codes,
                          g.a_scales, g.m, g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out,
-                         g.q_codes, g.q_scales, nullptr, kb_per, xcd);
+                         g.q_codes, g.q_scales, nullptr, kb_per, xcd, g.qkv);
   } else
     hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, false>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
                        g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
-                       nullptr, kb_per, xcd);
+                       nullptr, kb_per, xcd, g.qkv);
 }
 
 int launch_gemm_q8(const GemmArgs& g, hipStream_t s) {
@@ -451,6 +550,14 @@ int launch_gemm_q8(const GemmArgs& g, hipStream_t s) {
   const int KB = g.k / QK;
   GemmPlan p = plan_gemm(g.m, g.n, g.k, g.q_codes != nullptr);
   if (g.split_k > 0) p.split = g.split_k;
+  if (g.qkv.pos) {  // whole heads per tile, no split
+    p.split = 1;
+    if (g.qkv.head_dim > 64 && p.shape == 0) p.shape = 2;
+    const int bn = p.shape == 0 ? 64 : 128;
+    if (g.qkv.head_dim <= 0 || bn % g.qkv.head_dim || (g.qkv.head_dim & 1))
+      return set_error(MI_ERR_UNSUPPORTED, "gemm: QKV epilogue needs head_dim dividing %d (got %d)", bn,
+                       g.qkv.head_dim);
+  }
   int split = std::min(p.split, KB);
   const size_t need = split > 1 ? (size_t)split * g.m * g.n * sizeof(double) : 0;
   if (need > g.workspace_bytes || (need && !g.workspace)) split = 1;
