@@ -42,33 +42,36 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
 
 // ---- cross-lane maxima of non-negative f32 values without LDS round trips: DPP row
 // permutations inside 16-lane rows, one bit-mode swizzle across the two rows of a 32-lane half.
-// Lanes whose DPP source is unavailable read 0, which leaves a maximum of non-negative values
-// unchanged.
+// For non-negative floats the unsigned order of the bit patterns is the numeric order, so the
+// maxima run as integer maxima (no NaN canonicalization, and the DPP move folds into the max).
+// Lanes whose DPP source is unavailable read 0, which leaves the maximum unchanged.
 constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int DPP_ROW_MIRROR = 0x140;  // lane i <- 15 - i within a row of 16
 constexpr int DPP_HALF_MIRROR = 0x141; // lane i <- 7 - i within each 8 lanes
 
 template <int CTRL>
-__device__ __forceinline__ float dpp_max(float v) {
-  const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
-  return fmaxf(v, __builtin_bit_cast(float, o));
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return v > o ? v : o;
 }
 
-// max over each aligned group of 8 lanes
+// max over each aligned group of 8 lanes (v >= 0)
 __device__ __forceinline__ float max8_nonneg(float v) {
-  v = dpp_max<DPP_XOR1>(v);
-  v = dpp_max<DPP_XOR2>(v);
-  return dpp_max<DPP_HALF_MIRROR>(v);  // quad 0 <-> quad 1 of the 8
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  u = dpp_umax<DPP_XOR1>(u);
+  u = dpp_umax<DPP_XOR2>(u);
+  u = dpp_umax<DPP_HALF_MIRROR>(u);  // quad 0 <-> quad 1 of the 8
+  return __builtin_bit_cast(float, u);
 }
 
-// max over each aligned group of 32 lanes
+// max over each aligned group of 32 lanes (v >= 0)
 __device__ __forceinline__ float max32_nonneg(float v) {
-  v = max8_nonneg(v);
-  v = dpp_max<DPP_ROW_MIRROR>(v);  // 8-lane halves of a row
+  uint32_t u = __builtin_bit_cast(uint32_t, max8_nonneg(v));
+  u = dpp_umax<DPP_ROW_MIRROR>(u);  // 8-lane halves of a row
   // ds_swizzle bit mode (offset bit 15 = 0): lane <- ((lane & 0x1F) | 0) ^ 0x10 within 32 lanes
-  const int o = __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F);
-  return fmaxf(v, __builtin_bit_cast(float, o));
+  const uint32_t o = (uint32_t)__builtin_amdgcn_ds_swizzle((int)u, 0x401F);
+  return __builtin_bit_cast(float, u > o ? u : o);
 }
 
 // f32(m / 127), correctly rounded, from one f64 product.  The f64 result is within 2^-52

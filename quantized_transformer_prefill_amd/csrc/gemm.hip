@@ -424,9 +424,9 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
           const int row = m0 + wm * 16 * RG + rg * 16 + 4 * (j >> 1) + 2 * (lane >> 5) + (j & 1);
           const float dq = div127_f32(am[j]);
           const float id = (dq != 0.0f) ? recip_f32(dq) : 0.0f;
-          if (row < M && gcol < N) {
-            q_codes[(int64_t)row * ncols + scol] = (int8_t)q8_code(sv[j], id);
-            if ((lane & 31) == 0) q_scales[(int64_t)row * (ncols / QK) + scol / QK] = f32_to_f16_bits(dq);
+          if (row < M && gcol < N) {  // offsets below 2^31: M * N / 2 codes
+            q_codes[(uint32_t)(row * ncols + scol)] = (int8_t)q8_code(sv[j], id);
+            if ((lane & 31) == 0) q_scales[(uint32_t)(row * (ncols / QK) + scol / QK)] = f32_to_f16_bits(dq);
           }
         }
       }
