@@ -404,29 +404,35 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
   }
 
   if constexpr (EPI == EPI_SWIGLU_Q8 && !SPLIT) {
-    // column group pairs (2p, 2p+1) = 32 gate rows, 32 up rows of the interleaved weight; lane
-    // l%32 holds column l%32 of both, i.e. element l%32 of one Q8_0 block of the SwiGLU output.
-    // The 8 rows of a lane run side by side so their latencies overlap.
+    // Column group pairs (2p, 2p+1) = 32 gate rows, 32 up rows of the interleaved weight; lane
+    // l%32 holds column l%32 of both, so the SwiGLU runs per element in registers.  The results
+    // then pass through a wave-private LDS tile (16 rows x 32 columns) so that 8 lanes x 4 values
+    // cover one Q8_0 block: the block maximum, scale and reciprocal are computed once per 4
+    // values instead of once per value.  The staging buffers are free after the K loop's last
+    // barrier, and a wave's own LDS accesses complete in order.
     const int ncols = N / 2;
+    constexpr int TS = 36;  // floats per tile row: 144-byte stride spreads the float4 reads
+    float* ts = reinterpret_cast<float*>(&sm) + wave * 16 * TS;
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
       for (int cp = 0; cp < CG / 2; ++cp) {
         const int gcol = n0 + wn * 32 * CG + cp * 64;
-        const int scol = gcol / 2 + (lane & 31);
-        float sv[8], am[8];
+        const int scol0 = gcol / 2;  // first SwiGLU column of this 32-wide block
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sv[j] = swiglu_f32((float)acc[rg][2 * cp][j], (float)acc[rg][2 * cp + 1][j], exp_tab);
+        for (int j = 0; j < 8; ++j)
+          ts[(4 * (j >> 1) + 2 * (lane >> 5) + (j & 1)) * TS + (lane & 31)] =
+              swiglu_f32((float)acc[rg][2 * cp][j], (float)acc[rg][2 * cp + 1][j], exp_tab);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) am[j] = max32_nonneg(fabsf(sv[j]));
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int row = m0 + wm * 16 * RG + rg * 16 + 4 * (j >> 1) + 2 * (lane >> 5) + (j & 1);
-          const float dq = div127_f32(am[j]);
-          const float id = (dq != 0.0f) ? recip_f32(dq) : 0.0f;
+        for (int hr = 0; hr < 2; ++hr) {
+          const int r = hr * 8 + (lane >> 3), c4 = lane & 7;
+          const float4 v = *reinterpret_cast<const float4*>(ts + r * TS + c4 * 4);
+          float d;
+          const uint32_t q = q8_block_quant4(v, d);
+          const int row = m0 + wm * 16 * RG + rg * 16 + r;
           if (row < M && gcol < N) {  // offsets below 2^31: M * N / 2 codes
-            q_codes[(uint32_t)(row * ncols + scol)] = (int8_t)q8_code(sv[j], id);
-            if ((lane & 31) == 0) q_scales[(uint32_t)(row * (ncols / QK) + scol / QK)] = f32_to_f16_bits(dq);
+            *reinterpret_cast<uint32_t*>(q_codes + (uint32_t)(row * ncols + scol0 + c4 * 4)) = q;
+            if (c4 == 0) q_scales[(uint32_t)(row * (ncols / QK) + scol0 / QK)] = f32_to_f16_bits(d);
           }
         }
       }
