@@ -147,6 +147,16 @@ int mi_rope_table_init(const mi_hparams* hp, int32_t rows, double* table, void* 
 int mi_prefill_forward(const mi_model* model, const int32_t* token_ids, const int32_t* positions,
                        int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv, float* logits_out);
 
+/* The same forward with the logits of the last n_out tokens ("09", section 2.4: the tail rows
+ * [n_tokens - n_out, n_tokens) continue past the last layer's output projection; "05",
+ * section 2.8).  1 <= n_out <= n_tokens (MI_ERR_INVALID_ARG otherwise); n_out = n_tokens gives
+ * the logits of every token.
+ *   logits_out device f32 [n_out][vocab], row r = token n_tokens - n_out + r
+ * mi_prefill_forward is this call with n_out = 1. */
+int mi_prefill_forward_n(const mi_model* model, const int32_t* token_ids, const int32_t* positions,
+                         int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv, int32_t n_out,
+                         float* logits_out);
+
 /* ------------------------------------------------------------------ per-op calls */
 
 /* Q8_0 quantize rows of f32 ("CPU matmul kernels" stage of the walkthrough index;

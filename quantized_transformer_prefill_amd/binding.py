@@ -61,6 +61,7 @@ SIGNATURES = {
     "mi_rope_table_bytes": (_SZ, [C.POINTER(Hparams), _I32]),
     "mi_rope_table_init": (C.c_int, [C.POINTER(Hparams), _I32, _P, _P]),
     "mi_prefill_forward": (C.c_int, [C.POINTER(Model), _P, _P, _I32, _I32, C.POINTER(KvRegions), _P]),
+    "mi_prefill_forward_n": (C.c_int, [C.POINTER(Model), _P, _P, _I32, _I32, C.POINTER(KvRegions), _I32, _P]),
     "mi_quantize_q8_0": (C.c_int, [_P, _I64, _I32, _P, _P, _P]),
     "mi_gemm_q8_0": (C.c_int, [_P, _P, _I32, C.POINTER(Q8Matrix), _P, _P, _P, _P]),
     "mi_gemm_q8_0_ws": (C.c_int, [_P, _P, _I32, C.POINTER(Q8Matrix), _P, _P, _P, _P, _SZ, _I32, _P]),

@@ -272,8 +272,16 @@ static int validate_forward(const mi_model* md, const int32_t* ids, const int32_
 
 extern "C" int mi_prefill_forward(const mi_model* md, const int32_t* token_ids, const int32_t* positions,
                                   int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv, float* logits_out) {
+  return mi_prefill_forward_n(md, token_ids, positions, n_tokens, n_ctx, kv, 1, logits_out);
+}
+
+extern "C" int mi_prefill_forward_n(const mi_model* md, const int32_t* token_ids, const int32_t* positions,
+                                    int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv, int32_t n_out,
+                                    float* logits_out) {
   int rc = validate_forward(md, token_ids, positions, n_tokens, n_ctx, kv, logits_out);
   if (rc) return rc;
+  if (n_out < 1 || n_out > n_tokens)
+    return set_error(MI_ERR_INVALID_ARG, "forward: n_out %d outside [1, n_tokens = %d]", n_out, n_tokens);
   const mi_hparams& hp = md->hp;
   const int nt = n_tokens, H = hp.hidden, F = hp.ffn;
   const int nq = hp.n_head * hp.head_dim, nkv = hp.n_head_kv * hp.head_dim, nqkv = nq + 2 * nkv;
@@ -287,7 +295,7 @@ extern "C" int mi_prefill_forward(const mi_model* md, const int32_t* token_ids, 
   for (int t = 0; t < nt; ++t) max_pos = std::max(max_pos, positions[t]);
 
   if ((rc = launch_embed(md->token_embd.codes, md->token_embd.scales, H, w.ids, nt, w.h, s))) return rc;
-  float* h_last = w.h + (size_t)(nt - 1) * H;  // the tail row
+  float* h_tail = w.h + (size_t)(nt - n_out) * H;  // the tail rows [nt - n_out, nt)
   // the down projection's split-K partials, reduced (with its residual add) by the next RMSNorm
   int pending = 1;
   for (int l = 0; l < hp.n_layers; ++l) {
@@ -309,11 +317,11 @@ extern "C" int mi_prefill_forward(const mi_model* md, const int32_t* token_ids, 
     if ((rc = launch_gemm_q8(g, s))) return rc;
     float* q = w.qkv;
     // attention, its output rows quantized to Q8_0 in the same kernel.  In the last layer only the
-    // last token continues past the output projection, so only its row is computed (the KV store
-    // above covered every token).
-    const int rows = last ? 1 : nt;
+    // last n_out tokens continue past the output projection, so only their rows are computed (the
+    // KV store above covered every token).
+    const int rows = last ? n_out : nt;
     const int t0 = nt - rows;
-    float* h_rows = last ? h_last : w.h;
+    float* h_rows = last ? h_tail : w.h;
     if ((rc = launch_attention(q + (size_t)t0 * nqkv, nqkv, kv->k[l], kv->v[l], w.pos + t0, rows, max_pos, hp.n_head,
                                hp.n_head_kv, hp.head_dim, nullptr, nq, s, w.xq, w.xs)))
       return rc;
@@ -341,9 +349,21 @@ extern "C" int mi_prefill_forward(const mi_model* md, const int32_t* token_ids, 
     if ((rc = launch_gemm_q8(gd, s))) return rc;
   }
   const mi_q8_matrix& head = hp.tied ? md->token_embd : md->output;
-  if ((rc = launch_rmsnorm_quant(h_last, md->output_norm, 1, H, eps, w.lm_q, w.lm_s, nullptr, s,
-                                 (const double*)w.gemm_ws, pending)))
-    return rc;
-  if ((rc = launch_lm_head(w.lm_q, w.lm_s, H, head.codes, head.scales, head.rows, logits_out, s))) return rc;
+  if (n_out == 1) {  // one row: the HBM-bound row kernel
+    if ((rc = launch_rmsnorm_quant(h_tail, md->output_norm, 1, H, eps, w.lm_q, w.lm_s, nullptr, s,
+                                   (const double*)w.gemm_ws, pending)))
+      return rc;
+    if ((rc = launch_lm_head(w.lm_q, w.lm_s, H, head.codes, head.scales, head.rows, logits_out, s))) return rc;
+  } else {  // several rows: the MFMA matmul, logits [n_out][vocab]
+    if ((rc = launch_rmsnorm_quant(h_tail, md->output_norm, n_out, H, eps, w.xq, w.xs, nullptr, s,
+                                   (const double*)w.gemm_ws, pending)))
+      return rc;
+    GemmArgs gl{};
+    gl.a_codes = w.xq; gl.a_scales = w.xs; gl.m = n_out;
+    gl.w_codes = head.codes; gl.w_scales = head.scales; gl.n = head.rows; gl.k = H;
+    gl.out = logits_out; gl.ld_out = head.rows;
+    gl.split_k = 1;
+    if ((rc = launch_gemm_q8(gl, s))) return rc;
+  }
   return MI_OK;
 }

@@ -101,3 +101,14 @@ class PrefillModel:
                                            self.n_ctx if n_ctx is None else n_ctx, C.byref(self.kv),
                                            out.data_ptr()))
         return out
+
+    def forward_n(self, token_ids, positions, n_out: int, n_ctx: Optional[int] = None):
+        """One prefill call; returns device logits f32 [n_out][vocab] of the last n_out tokens."""
+        ids = np.ascontiguousarray(token_ids, dtype=np.int32)
+        pos = np.ascontiguousarray(positions, dtype=np.int32)
+        out = torch.empty(max(n_out, 1), self.cfg.vocab, dtype=torch.float32, device=self.device)
+        self.model.stream = B.stream_ptr()
+        B.check(B.lib().mi_prefill_forward_n(C.byref(self.model), ids.ctypes.data, pos.ctypes.data, ids.shape[0],
+                                             self.n_ctx if n_ctx is None else n_ctx, C.byref(self.kv), n_out,
+                                             out.data_ptr()))
+        return out

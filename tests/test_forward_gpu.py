@@ -77,6 +77,43 @@ def test_forward_matches_oracle(cfg):
     assert_f32_match(gv[:, used], vv[:, used], max_ulp=64, max_frac_inexact=0.05, what="V regions")
 
 
+@pytest.mark.parametrize("cfg,n_outs", [(synth.LAYER1, (1, 3, 16)), (TINY_Q3, (2, 45)), (TINY_Q2, (20,))],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_forward_n_out_matches_oracle(cfg, n_outs):
+    """Logits of the last n_out tokens (the tail rows of the last layer), against the oracle."""
+    dev = need_gpu()
+    m, w = load_pair(cfg, dev)
+    pre_ids, ids = synth.gen_token_ids(cfg)
+    pre_pos, pos = synth.positions_for(cfg)
+    for n_out in n_outs:
+        say(f"forward_n {cfg.name} n_out={n_out}")
+        m.kv_k.fill_(SENTINEL)
+        m.kv_v.fill_(SENTINEL)
+        kk, vv = oracle.new_kv_regions(cfg, cfg.n_ctx, fill=SENTINEL)
+        if cfg.prefix_tokens:
+            m.forward(pre_ids, pre_pos)
+            oracle.prefill_forward(cfg, w, pre_ids, pre_pos, cfg.n_ctx, kk, vv)
+        got = m.forward_n(ids, pos, n_out).cpu().numpy()
+        want = oracle.prefill_forward(cfg, w, ids, pos, cfg.n_ctx, kk, vv, n_out=n_out)
+        assert got.shape == want.shape == (n_out, cfg.vocab)
+        compare_logits(got, want, f"{cfg.name} n_out={n_out} logits")
+        assert_f32_match(got, want, max_ulp=64, max_frac_inexact=0.05, what=f"{cfg.name} n_out={n_out} ulp")
+        one = m.forward(ids, pos).cpu().numpy()
+        np.testing.assert_array_equal(got[-1], one)   # the last row is the n_out = 1 logits
+
+
+def test_forward_n_out_bounds():
+    dev = need_gpu()
+    cfg = synth.LAYER1
+    m, _ = load_pair(cfg, dev)
+    _, ids = synth.gen_token_ids(cfg)
+    pos = np.arange(cfg.n_tokens, dtype=np.int32)
+    for bad in (0, cfg.n_tokens + 1):
+        with pytest.raises(B.MiError) as e:
+            m.forward_n(ids, pos, bad)
+        assert e.value.code == B.MI_ERR_INVALID_ARG
+
+
 def test_prefill_equals_replay_and_chunks_on_gpu():
     dev = need_gpu()
     cfg = synth.LAYER1
