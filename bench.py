@@ -2,8 +2,10 @@
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
 
-A step is one mi_prefill_forward over the whole 512-token prompt (all layers, the KV stores,
-the last-token lm_head) on seeded synthetic Q8_0 weights resident in HBM.  The dominant kernel
+A step is one forward over the whole 512-token prompt (all layers, the KV stores, the last-token
+lm_head) on seeded synthetic Q8_0 weights resident in HBM, launched as a replay of the captured
+forward (mi_prefill_graph_launch: host validation, H2D of ids and positions, graph replay); the
+eager call (mi_prefill_forward) is timed too and reported as eager_ms_per_step.  The dominant kernel
 (the fused gate|up matmul with the SwiGLU+Q8_0 epilogue) is timed again on its own, at the same
 shape and launch configuration, to report its roofline fraction; the GEMM sweep shapes are timed
 the same way.  The oracle (CPU) is timed on a bounded sample as a reported baseline.
@@ -103,16 +105,32 @@ def main():
     if cfg.prefix_tokens:  # untimed: the KV rows of the earlier positions; each timed chunk call
         model.forward(pre_ids, pre_pos)  # rewrites the same chunk rows with the same values
 
-    for _ in range(args.warmup):
-        model.forward(ids, pos)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        model.forward(ids, pos)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    # eager calls (mi_prefill_forward), then the same forward captured once and replayed
+    # (mi_prefill_graph_launch: validation, H2D of ids and positions, graph replay) -- the timed
+    # steps; both on one side stream, events recorded on it
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            model.forward(ids, pos)
+        stream.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            model.forward(ids, pos)
+        e1.record(stream)
+        stream.synchronize()
+        eager_ms = e0.elapsed_time(e1) / args.steps
+        graph = model.graph(cfg.n_tokens)
+        for _ in range(args.warmup):
+            graph.launch(ids, pos)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            graph.launch(ids, pos)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        graph.close()
     tok_s = cfg.n_tokens / (ms / 1e3)
 
     # ---- dominant kernel: fused gate|up matmul + SwiGLU + Q8_0 at the forward's shape
@@ -175,6 +193,7 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights quantized to Q8_0, uniform token ids)",
         "config": {"workload": cfg.name, "description": cfg.description, "n_tokens": cfg.n_tokens,
                    "n_ctx": cfg.n_ctx, "parallelism": "single GPU"},
+        "eager_ms_per_step": round(eager_ms, 4),
         "roofline": roofline,
         "gemm_sweep": sweep,
         "cpu_baseline": cpu,

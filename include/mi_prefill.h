@@ -157,6 +157,23 @@ int mi_prefill_forward_n(const mi_model* model, const int32_t* token_ids, const 
                          int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv, int32_t n_out,
                          float* logits_out);
 
+/* Graph replay of the forward for callers that repeat one shape (HIP graphs).
+ * mi_prefill_graph_create validates the shapes like mi_prefill_forward_n, then captures the
+ * forward's kernel sequence on model->stream (which must be a non-default stream) into a graph;
+ * nothing runs and nothing is allocated on the device.  The graph keeps the pointers of `model`
+ * (weights, workspace, RoPE table), of `kv` and of `logits_out` as they are now: the caller keeps
+ * them alive and unchanged until mi_prefill_graph_destroy.
+ * mi_prefill_graph_launch validates token ids and positions (as mi_prefill_forward_n: errors leave
+ * everything untouched), stages them into the workspace and replays the graph on the captured
+ * stream; it computes exactly what mi_prefill_forward_n computes for the same arguments.
+ * Launches of one graph run in stream order; different graphs sharing a workspace must not
+ * overlap.  *out is set to NULL on error. */
+typedef struct mi_prefill_graph mi_prefill_graph;
+int mi_prefill_graph_create(const mi_model* model, int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv,
+                            int32_t n_out, float* logits_out, mi_prefill_graph** out);
+int mi_prefill_graph_launch(mi_prefill_graph* graph, const int32_t* token_ids, const int32_t* positions);
+void mi_prefill_graph_destroy(mi_prefill_graph* graph);
+
 /* ------------------------------------------------------------------ per-op calls */
 
 /* Q8_0 quantize rows of f32 ("CPU matmul kernels" stage of the walkthrough index;

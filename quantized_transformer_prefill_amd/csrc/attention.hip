@@ -82,12 +82,14 @@ template <int HD, int NW, int NG>
 __global__ void __launch_bounds__(64 * NW * NG) k_attention(const float* __restrict__ q, int64_t ld_q,
                                                        const float* __restrict__ k_region,
                                                        const float* __restrict__ v_region,
-                                                       const int32_t* __restrict__ pos, int n_tokens, int max_pos,
+                                                       const int32_t* __restrict__ pos, int n_tokens,
+                                                       const int32_t* __restrict__ max_pos_p, int max_pos_v,
                                                        int n_head, int n_head_kv, float* __restrict__ out,
                                                        int64_t ld_out, int8_t* __restrict__ q_codes,
                                                        uint16_t* __restrict__ q_scales) {
   constexpr int Q4 = HD / 4;    // dims per lane slot (scores) = MFMAs per score tile
   constexpr int NB = HD / 16;   // output dim blocks
+  const int max_pos = max_pos_p ? *max_pos_p : max_pos_v;
   __shared__ double exp_tab[64];
   __shared__ double sh_m[NG][NW][64], sh_l[NG][NW][64];
   __shared__ double sh_o[NG][NW / 2][NB * 4][64];
@@ -287,17 +289,17 @@ __global__ void __launch_bounds__(64 * NW * NG) k_attention(const float* __restr
 }
 
 int launch_attention(const float* q, int64_t ld_q, const float* k_region, const float* v_region,
-                     const int32_t* pos, int n_tokens, int max_pos, int n_head, int n_head_kv,
+                     const int32_t* pos, int n_tokens, const int32_t* max_pos_dev, int max_pos, int n_head, int n_head_kv,
                      int head_dim, float* out, int64_t ld_out, hipStream_t s, int8_t* q_codes,
                      uint16_t* q_scales) {
   if (n_tokens == 0) return MI_OK;
   const int nqt = (n_tokens + 15) / 16;
   if (head_dim == 64)
     hipLaunchKernelGGL((k_attention<64, 4, 2>), dim3((nqt + 1) / 2, n_head), dim3(64 * 4 * 2), 0, s, q, ld_q, k_region,
-                       v_region, pos, n_tokens, max_pos, n_head, n_head_kv, out, ld_out, q_codes, q_scales);
+                       v_region, pos, n_tokens, max_pos_dev, max_pos, n_head, n_head_kv, out, ld_out, q_codes, q_scales);
   else if (head_dim == 128)
     hipLaunchKernelGGL((k_attention<128, 4, 1>), dim3(nqt, n_head), dim3(64 * 4), 0, s, q, ld_q, k_region, v_region,
-                       pos, n_tokens, max_pos, n_head, n_head_kv, out, ld_out, q_codes, q_scales);
+                       pos, n_tokens, max_pos_dev, max_pos, n_head, n_head_kv, out, ld_out, q_codes, q_scales);
   else
     return set_error(MI_ERR_UNSUPPORTED, "attention: head_dim %d (supported: 64, 128)", head_dim);
   MI_LAUNCH_CHECK("k_attention");

@@ -39,6 +39,7 @@ static bool q8_ok(const mi_q8_matrix& w, int rows, int cols) {
 // ---------------------------------------------------------------- workspace layout
 struct Ws {
   int32_t* ids; int32_t* pos;
+  int32_t* maxpos;   // [1] largest position of the call
   float* h;          // [T][hidden]
   int8_t* xq;        // [T][max(hidden, nq, ffn)]
   uint16_t* xs;      // [T][max(...)/32]
@@ -61,6 +62,7 @@ static Ws carve(const mi_hparams& hp, int T, char* base) {
   auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += align_up(bytes); return p; };
   w.ids = (int32_t*)take(sizeof(int32_t) * T);
   w.pos = (int32_t*)take(sizeof(int32_t) * T);
+  w.maxpos = (int32_t*)take(sizeof(int32_t));
   w.h = (float*)take(sizeof(float) * T * (size_t)hp.hidden);
   w.xq = (int8_t*)take((size_t)T * wide);
   w.xs = (uint16_t*)take(sizeof(uint16_t) * (size_t)T * (wide / QK));
@@ -197,8 +199,8 @@ extern "C" int mi_attention_gqa(const float* q, const float* k_region, const flo
       n_head % n_head_kv || n_ctx <= 0)
     return set_error(MI_ERR_INVALID_ARG, "mi_attention_gqa: bad arguments");
   if (max_pos < 0 || max_pos >= n_ctx) return set_error(MI_ERR_POSITION_RANGE, "max_pos %d outside [0, %d)", max_pos, n_ctx);
-  return launch_attention(q, (int64_t)n_head * head_dim, k_region, v_region, positions, n_tokens, max_pos, n_head,
-                          n_head_kv, head_dim, out, (int64_t)n_head * head_dim, as_stream(stream));
+  return launch_attention(q, (int64_t)n_head * head_dim, k_region, v_region, positions, n_tokens, nullptr, max_pos,
+                          n_head, n_head_kv, head_dim, out, (int64_t)n_head * head_dim, as_stream(stream));
 }
 
 extern "C" int mi_swiglu_quant(const float* gate, const float* up, int64_t rows, int32_t cols, int8_t* codes,
@@ -228,13 +230,14 @@ extern "C" int mi_lm_head_row(const float* x, const float* gamma, float eps, con
 }
 
 // ---------------------------------------------------------------- the forward
-static int validate_forward(const mi_model* md, const int32_t* ids, const int32_t* pos, int32_t nt, int32_t n_ctx,
-                            const mi_kv_regions* kv, const float* logits) {
-  if (!md || !ids || !pos || !kv || !logits) return set_error(MI_ERR_INVALID_ARG, "forward: NULL argument");
+static int validate_static(const mi_model* md, int32_t nt, int32_t n_ctx, const mi_kv_regions* kv,
+                           const float* logits, int32_t n_out) {
+  if (!md || !kv || !logits) return set_error(MI_ERR_INVALID_ARG, "forward: NULL argument");
   int rc = check_hparams(&md->hp);
   if (rc) return rc;
   const mi_hparams& hp = md->hp;
   if (nt < 1) return set_error(MI_ERR_INVALID_ARG, "forward: n_tokens must be >= 1");
+  if (n_out < 1 || n_out > nt) return set_error(MI_ERR_INVALID_ARG, "forward: n_out %d outside [1, n_tokens = %d]", n_out, nt);
   if (n_ctx < 1) return set_error(MI_ERR_INVALID_ARG, "forward: n_ctx must be >= 1");
   if (kv->n_ctx != n_ctx) return set_error(MI_ERR_KV_MISMATCH, "forward: kv n_ctx %d != call n_ctx %d", kv->n_ctx, n_ctx);
   if (kv->n_layers != hp.n_layers || kv->n_kv_embd != hp.n_head_kv * hp.head_dim || !kv->k || !kv->v)
@@ -245,16 +248,6 @@ static int validate_forward(const mi_model* md, const int32_t* ids, const int32_
   if (!md->workspace || md->workspace_bytes < carve(hp, md->max_tokens, nullptr).total)
     return set_error(MI_ERR_WORKSPACE, "forward: workspace smaller than mi_prefill_workspace_bytes(max_tokens)");
   if (!md->rope_table || md->rope_rows < n_ctx) return set_error(MI_ERR_INVALID_ARG, "forward: rope table rows < n_ctx");
-  for (int t = 0; t < nt; ++t) {
-    if (pos[t] < 0 || pos[t] >= n_ctx)
-      return set_error(MI_ERR_POSITION_RANGE, "forward: position %d of token %d outside [0, %d)", pos[t], t, n_ctx);
-    if (ids[t] < 0 || ids[t] >= hp.vocab)
-      return set_error(MI_ERR_INVALID_ARG, "forward: token id %d of token %d outside [0, %d)", ids[t], t, hp.vocab);
-  }
-  std::vector<int32_t> sorted(pos, pos + nt);
-  std::sort(sorted.begin(), sorted.end());
-  for (int t = 1; t < nt; ++t)
-    if (sorted[t] == sorted[t - 1]) return set_error(MI_ERR_DUP_POSITION, "forward: position %d repeated", sorted[t]);
   const int nq = hp.n_head * hp.head_dim, nkv = hp.n_head_kv * hp.head_dim;
   if (!q8_ok(md->token_embd, hp.vocab, hp.hidden)) return set_error(MI_ERR_INVALID_ARG, "forward: token_embd shape");
   if (!hp.tied && !q8_ok(md->output, hp.vocab, hp.hidden)) return set_error(MI_ERR_INVALID_ARG, "forward: output shape");
@@ -270,30 +263,46 @@ static int validate_forward(const mi_model* md, const int32_t* ids, const int32_
   return MI_OK;
 }
 
-extern "C" int mi_prefill_forward(const mi_model* md, const int32_t* token_ids, const int32_t* positions,
-                                  int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv, float* logits_out) {
-  return mi_prefill_forward_n(md, token_ids, positions, n_tokens, n_ctx, kv, 1, logits_out);
+// token ids and positions: ranges, no repeated position; returns the largest position
+static int validate_tokens(const mi_hparams& hp, const int32_t* ids, const int32_t* pos, int32_t nt, int32_t n_ctx,
+                           int* max_pos) {
+  if (!ids || !pos) return set_error(MI_ERR_INVALID_ARG, "forward: NULL token ids or positions");
+  int mp = 0;
+  for (int t = 0; t < nt; ++t) {
+    if (pos[t] < 0 || pos[t] >= n_ctx)
+      return set_error(MI_ERR_POSITION_RANGE, "forward: position %d of token %d outside [0, %d)", pos[t], t, n_ctx);
+    if (ids[t] < 0 || ids[t] >= hp.vocab)
+      return set_error(MI_ERR_INVALID_ARG, "forward: token id %d of token %d outside [0, %d)", ids[t], t, hp.vocab);
+    mp = std::max(mp, pos[t]);
+  }
+  std::vector<int32_t> sorted(pos, pos + nt);
+  std::sort(sorted.begin(), sorted.end());
+  for (int t = 1; t < nt; ++t)
+    if (sorted[t] == sorted[t - 1]) return set_error(MI_ERR_DUP_POSITION, "forward: position %d repeated", sorted[t]);
+  *max_pos = mp;
+  return MI_OK;
 }
 
-extern "C" int mi_prefill_forward_n(const mi_model* md, const int32_t* token_ids, const int32_t* positions,
-                                    int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv, int32_t n_out,
-                                    float* logits_out) {
-  int rc = validate_forward(md, token_ids, positions, n_tokens, n_ctx, kv, logits_out);
-  if (rc) return rc;
-  if (n_out < 1 || n_out > n_tokens)
-    return set_error(MI_ERR_INVALID_ARG, "forward: n_out %d outside [1, n_tokens = %d]", n_out, n_tokens);
+// boundary staging: token ids, positions and the largest position to the device
+static int stage_tokens(const Ws& w, const int32_t* ids, const int32_t* pos, int32_t nt, const int32_t* max_pos,
+                        hipStream_t s) {
+  MI_HIP(hipMemcpyAsync(w.ids, ids, sizeof(int32_t) * nt, hipMemcpyHostToDevice, s));
+  MI_HIP(hipMemcpyAsync(w.pos, pos, sizeof(int32_t) * nt, hipMemcpyHostToDevice, s));
+  MI_HIP(hipMemcpyAsync(w.maxpos, max_pos, sizeof(int32_t), hipMemcpyHostToDevice, s));
+  return MI_OK;
+}
+
+// Every kernel of one forward, in order, on stream s.  Reads the staged ids, positions and largest
+// position from the workspace; the sequence depends only on the shapes, so it can be captured
+// once into a HIP graph and replayed.
+static int enqueue_forward(const mi_model* md, const Ws& w, int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv,
+                           int32_t n_out, float* logits_out, hipStream_t s) {
   const mi_hparams& hp = md->hp;
   const int nt = n_tokens, H = hp.hidden, F = hp.ffn;
   const int nq = hp.n_head * hp.head_dim, nkv = hp.n_head_kv * hp.head_dim, nqkv = nq + 2 * nkv;
   const float eps = hp.rms_eps;
-  hipStream_t s = as_stream(md->stream);
-  Ws w = carve(hp, md->max_tokens, (char*)md->workspace);
-  // boundary staging: token ids and positions to the device
-  MI_HIP(hipMemcpyAsync(w.ids, token_ids, sizeof(int32_t) * nt, hipMemcpyHostToDevice, s));
-  MI_HIP(hipMemcpyAsync(w.pos, positions, sizeof(int32_t) * nt, hipMemcpyHostToDevice, s));
-  int max_pos = 0;
-  for (int t = 0; t < nt; ++t) max_pos = std::max(max_pos, positions[t]);
-
+  (void)n_ctx;
+  int rc;
   if ((rc = launch_embed(md->token_embd.codes, md->token_embd.scales, H, w.ids, nt, w.h, s))) return rc;
   float* h_tail = w.h + (size_t)(nt - n_out) * H;  // the tail rows [nt - n_out, nt)
   // the down projection's split-K partials, reduced (with its residual add) by the next RMSNorm
@@ -322,8 +331,8 @@ extern "C" int mi_prefill_forward_n(const mi_model* md, const int32_t* token_ids
     const int rows = last ? n_out : nt;
     const int t0 = nt - rows;
     float* h_rows = last ? h_tail : w.h;
-    if ((rc = launch_attention(q + (size_t)t0 * nqkv, nqkv, kv->k[l], kv->v[l], w.pos + t0, rows, max_pos, hp.n_head,
-                               hp.n_head_kv, hp.head_dim, nullptr, nq, s, w.xq, w.xs)))
+    if ((rc = launch_attention(q + (size_t)t0 * nqkv, nqkv, kv->k[l], kv->v[l], w.pos + t0, rows, w.maxpos, 0,
+                               hp.n_head, hp.n_head_kv, hp.head_dim, nullptr, nq, s, w.xq, w.xs)))
       return rc;
     GemmArgs go{};
     go.a_codes = w.xq; go.a_scales = w.xs; go.m = rows;
@@ -366,4 +375,87 @@ extern "C" int mi_prefill_forward_n(const mi_model* md, const int32_t* token_ids
     if ((rc = launch_gemm_q8(gl, s))) return rc;
   }
   return MI_OK;
+}
+
+extern "C" int mi_prefill_forward(const mi_model* md, const int32_t* token_ids, const int32_t* positions,
+                                  int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv, float* logits_out) {
+  return mi_prefill_forward_n(md, token_ids, positions, n_tokens, n_ctx, kv, 1, logits_out);
+}
+
+extern "C" int mi_prefill_forward_n(const mi_model* md, const int32_t* token_ids, const int32_t* positions,
+                                    int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv, int32_t n_out,
+                                    float* logits_out) {
+  int rc = validate_static(md, n_tokens, n_ctx, kv, logits_out, n_out);
+  if (rc) return rc;
+  int max_pos = 0;
+  if ((rc = validate_tokens(md->hp, token_ids, positions, n_tokens, n_ctx, &max_pos))) return rc;
+  hipStream_t s = as_stream(md->stream);
+  const Ws w = carve(md->hp, md->max_tokens, (char*)md->workspace);
+  if ((rc = stage_tokens(w, token_ids, positions, n_tokens, &max_pos, s))) return rc;
+  return enqueue_forward(md, w, n_tokens, n_ctx, kv, n_out, logits_out, s);
+}
+
+// ---------------------------------------------------------------- graph replay
+struct mi_prefill_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipStream_t stream = nullptr;
+  mi_hparams hp{};
+  Ws w{};
+  int32_t n_tokens = 0, n_ctx = 0;
+  int32_t max_pos = 0;  // host copy staged to the device on every launch
+};
+
+extern "C" int mi_prefill_graph_create(const mi_model* md, int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv,
+                                       int32_t n_out, float* logits_out, mi_prefill_graph** out) {
+  if (!out) return set_error(MI_ERR_INVALID_ARG, "graph: NULL output handle");
+  *out = nullptr;
+  int rc = validate_static(md, n_tokens, n_ctx, kv, logits_out, n_out);
+  if (rc) return rc;
+  hipStream_t s = as_stream(md->stream);
+  if (!s) return set_error(MI_ERR_INVALID_ARG, "graph: capture needs a non-default stream in model->stream");
+  mi_prefill_graph* g = new mi_prefill_graph();
+  g->stream = s;
+  g->hp = md->hp;
+  g->w = carve(md->hp, md->max_tokens, (char*)md->workspace);
+  g->n_tokens = n_tokens;
+  g->n_ctx = n_ctx;
+  hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    delete g;
+    return hip_check(e, "hipStreamBeginCapture");
+  }
+  rc = enqueue_forward(md, g->w, n_tokens, n_ctx, kv, n_out, logits_out, s);
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(s, &graph);
+  if (rc || e != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    delete g;
+    return rc ? rc : hip_check(e, "hipStreamEndCapture");
+  }
+  g->graph = graph;
+  e = hipGraphInstantiate(&g->exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    delete g;
+    return hip_check(e, "hipGraphInstantiate");
+  }
+  *out = g;
+  return MI_OK;
+}
+
+extern "C" int mi_prefill_graph_launch(mi_prefill_graph* g, const int32_t* token_ids, const int32_t* positions) {
+  if (!g || !g->exec) return set_error(MI_ERR_INVALID_ARG, "graph: NULL handle");
+  int rc = validate_tokens(g->hp, token_ids, positions, g->n_tokens, g->n_ctx, &g->max_pos);
+  if (rc) return rc;
+  if ((rc = stage_tokens(g->w, token_ids, positions, g->n_tokens, &g->max_pos, g->stream))) return rc;
+  MI_HIP(hipGraphLaunch(g->exec, g->stream));
+  return MI_OK;
+}
+
+extern "C" void mi_prefill_graph_destroy(mi_prefill_graph* g) {
+  if (!g) return;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  delete g;
 }

@@ -174,8 +174,9 @@ int launch_rope_kvstore(float* q, int64_t ld_q, const float* k, const float* v, 
                         const double* table, float* k_region, float* v_region, hipStream_t s);
 // out f32 [n_tokens][ld_out], or, with q_codes non-null, the output rows quantized to Q8_0
 // (codes [n_tokens][n_head*head_dim], scales [n_tokens][n_head*head_dim/32]) and out unused.
+// max_pos: the call's largest position, read from device memory when max_pos_dev is non-null.
 int launch_attention(const float* q, int64_t ld_q, const float* k_region, const float* v_region,
-                     const int32_t* pos, int n_tokens, int max_pos, int n_head, int n_head_kv,
+                     const int32_t* pos, int n_tokens, const int32_t* max_pos_dev, int max_pos, int n_head, int n_head_kv,
                      int head_dim, float* out, int64_t ld_out, hipStream_t s,
                      int8_t* q_codes = nullptr, uint16_t* q_scales = nullptr);
 

@@ -102,6 +102,10 @@ class PrefillModel:
                                            out.data_ptr()))
         return out
 
+    def graph(self, n_tokens: int, n_out: int = 1) -> "PrefillGraph":
+        """A captured forward for n_tokens-token calls on torch's current stream (see PrefillGraph)."""
+        return PrefillGraph(self, n_tokens, n_out)
+
     def forward_n(self, token_ids, positions, n_out: int, n_ctx: Optional[int] = None):
         """One prefill call; returns device logits f32 [n_out][vocab] of the last n_out tokens."""
         ids = np.ascontiguousarray(token_ids, dtype=np.int32)
@@ -112,3 +116,42 @@ class PrefillModel:
                                              self.n_ctx if n_ctx is None else n_ctx, C.byref(self.kv), n_out,
                                              out.data_ptr()))
         return out
+
+
+class PrefillGraph:
+    """mi_prefill_graph_* around a PrefillModel: the forward's kernels captured once, replayed per call.
+
+    Capture happens on torch's current stream, which must not be the default stream; `launch` replays
+    on that stream and returns the logits tensor (the same device buffer every call).
+    """
+
+    def __init__(self, model: PrefillModel, n_tokens: int, n_out: int = 1):
+        self.model = model
+        self.n_tokens, self.n_out = n_tokens, n_out
+        self.logits = torch.empty(n_out, model.cfg.vocab, dtype=torch.float32, device=model.device)
+        model.model.stream = B.stream_ptr()
+        if not model.model.stream:
+            raise ValueError("graph capture needs a non-default stream (use torch.cuda.stream(...))")
+        h = C.c_void_p()
+        B.check(B.lib().mi_prefill_graph_create(C.byref(model.model), n_tokens, model.n_ctx, C.byref(model.kv), n_out,
+                                                self.logits.data_ptr(), C.byref(h)))
+        self.handle = h
+
+    def launch(self, token_ids, positions) -> torch.Tensor:
+        ids = np.ascontiguousarray(token_ids, dtype=np.int32)
+        pos = np.ascontiguousarray(positions, dtype=np.int32)
+        if ids.shape[0] != self.n_tokens or pos.shape[0] != self.n_tokens:
+            raise ValueError(f"graph captured for {self.n_tokens} tokens")
+        B.check(B.lib().mi_prefill_graph_launch(self.handle, ids.ctypes.data, pos.ctypes.data))
+        return self.logits
+
+    def close(self):
+        if self.handle:
+            B.lib().mi_prefill_graph_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

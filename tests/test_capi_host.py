@@ -97,6 +97,26 @@ def test_forward_rejects_bad_shapes():
     assert B.lib().mi_prefill_workspace_bytes(C.byref(hp), 8) == 0
 
 
+def test_forward_n_and_graph_argument_checks():
+    """n_out bounds and the graph entry points' host-side checks (nothing is captured or run)."""
+    L = B.lib()
+    model, kv, keep = make_model()
+    ids = np.array([1, 2, 3], dtype=np.int32)
+    pos = np.array([0, 1, 2], dtype=np.int32)
+    for bad in (0, 4):
+        assert L.mi_prefill_forward_n(C.byref(model), ids.ctypes.data, pos.ctypes.data, 3, 16, C.byref(kv), bad,
+                                      FAKE) == B.MI_ERR_INVALID_ARG
+    h = C.c_void_p(FAKE)
+    assert L.mi_prefill_graph_create(C.byref(model), 3, 16, C.byref(kv), 1, FAKE, None) == B.MI_ERR_INVALID_ARG
+    assert L.mi_prefill_graph_create(C.byref(model), 3, 15, C.byref(kv), 1, FAKE, C.byref(h)) == B.MI_ERR_KV_MISMATCH
+    assert h.value is None  # the handle is cleared on error
+    assert L.mi_prefill_graph_create(C.byref(model), 9, 16, C.byref(kv), 1, FAKE, C.byref(h)) == B.MI_ERR_WORKSPACE
+    assert L.mi_prefill_graph_create(C.byref(model), 3, 16, C.byref(kv), 1, FAKE, C.byref(h)) == B.MI_ERR_INVALID_ARG
+    assert b"non-default stream" in L.mi_last_error()
+    assert L.mi_prefill_graph_launch(None, ids.ctypes.data, pos.ctypes.data) == B.MI_ERR_INVALID_ARG
+    L.mi_prefill_graph_destroy(None)  # a no-op
+
+
 def test_per_op_argument_checks():
     L = B.lib()
     assert L.mi_quantize_q8_0(FAKE, 2, 48, FAKE, FAKE, None) == B.MI_ERR_INVALID_ARG

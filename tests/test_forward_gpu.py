@@ -114,6 +114,47 @@ def test_forward_n_out_bounds():
         assert e.value.code == B.MI_ERR_INVALID_ARG
 
 
+def _reset(m):
+    m.kv_k.fill_(SENTINEL)
+    m.kv_v.fill_(SENTINEL)
+
+
+@pytest.mark.parametrize("cfg,n_out", [(synth.LAYER1, 1), (TINY_Q3, 3), (TINY_Q2, 1)], ids=lambda v: getattr(v, "name", str(v)))
+def test_graph_replay_equals_eager(cfg, n_out):
+    """The captured forward, replayed several times with eager work and synchronizations in between,
+    gives bit-identical logits and KV rows to the eager call on the same ids and positions --
+    including positions that differ between replays (the largest position is staged per launch)."""
+    dev = need_gpu()
+    m, _ = load_pair(cfg, dev)
+    pre_ids, ids = synth.gen_token_ids(cfg)
+    pre_pos, pos = synth.positions_for(cfg)
+    nt = cfg.n_tokens
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        g = m.graph(nt, n_out)
+        shifts = [0, 3, 0] if cfg.prefix_tokens == 0 else [0, 0]
+        for r, shift in enumerate(shifts):
+            say(f"graph {cfg.name} replay {r} shift {shift}")
+            p = pos + shift
+            _reset(m)
+            if cfg.prefix_tokens:
+                m.forward(pre_ids, pre_pos)
+            eager = m.forward_n(ids, p, n_out).cpu().numpy().copy()
+            k_eager = m.kv_k.cpu().numpy().copy()
+            _reset(m)
+            if cfg.prefix_tokens:
+                m.forward(pre_ids, pre_pos)
+            got = g.launch(ids, p).cpu().numpy().copy()
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(got, eager)
+            np.testing.assert_array_equal(m.kv_k.cpu().numpy(), k_eager)
+            _ = torch.ones(1000, device=dev).sum().item()   # unrelated eager work between replays
+        with pytest.raises(B.MiError) as e:
+            g.launch(ids, np.zeros(nt, dtype=np.int32))
+        assert e.value.code == B.MI_ERR_DUP_POSITION
+        g.close()
+
+
 def test_prefill_equals_replay_and_chunks_on_gpu():
     dev = need_gpu()
     cfg = synth.LAYER1
