@@ -53,6 +53,39 @@ struct GemmTile {
   double bs[2][G_KS][BN];
 };
 
+// acc[j] += bcast(da, lane 8*HALF + j of each 16-lane row) * x[j] for j = 0..7: v_fmac_f64 with a
+// DPP row_newbcast source (the one DPP form of the f64 ALU).  da comes from an LDS load; the
+// leading s_nop gives the two wait states a DPP source needs after any VALU write of it.
+template <int HALF>
+__device__ __forceinline__ void fmac8_bcast(double (&acc)[8], const double (&x)[8], double da) {
+  if constexpr (HALF == 0)
+    asm("s_nop 1\n\t"
+        "v_fmac_f64_dpp %0, %8, %9 row_newbcast:0\n\t"
+        "v_fmac_f64_dpp %1, %8, %10 row_newbcast:1\n\t"
+        "v_fmac_f64_dpp %2, %8, %11 row_newbcast:2\n\t"
+        "v_fmac_f64_dpp %3, %8, %12 row_newbcast:3\n\t"
+        "v_fmac_f64_dpp %4, %8, %13 row_newbcast:4\n\t"
+        "v_fmac_f64_dpp %5, %8, %14 row_newbcast:5\n\t"
+        "v_fmac_f64_dpp %6, %8, %15 row_newbcast:6\n\t"
+        "v_fmac_f64_dpp %7, %8, %16 row_newbcast:7"
+        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6]),
+          "+v"(acc[7])
+        : "v"(da), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
+  else
+    asm("s_nop 1\n\t"
+        "v_fmac_f64_dpp %0, %8, %9 row_newbcast:8\n\t"
+        "v_fmac_f64_dpp %1, %8, %10 row_newbcast:9\n\t"
+        "v_fmac_f64_dpp %2, %8, %11 row_newbcast:10\n\t"
+        "v_fmac_f64_dpp %3, %8, %12 row_newbcast:11\n\t"
+        "v_fmac_f64_dpp %4, %8, %13 row_newbcast:12\n\t"
+        "v_fmac_f64_dpp %5, %8, %14 row_newbcast:13\n\t"
+        "v_fmac_f64_dpp %6, %8, %15 row_newbcast:14\n\t"
+        "v_fmac_f64_dpp %7, %8, %16 row_newbcast:15"
+        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6]),
+          "+v"(acc[7])
+        : "v"(da), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
+}
+
 template <int RG, int CG, int EPI, bool SPLIT>
 __global__ void __launch_bounds__(G_THREADS, 2)
 k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales, int M,
@@ -207,12 +240,22 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
   const int a_rrow = wm * 16 * RG + ((lane & 31) >> 1);   // + rg*16
   const int koff = (lane >> 5) * 16;
   const int b_rrow = wn * 32 * CG + (lane & 31);          // + cg*32
-  const int da_row = wm * 16 * RG + 2 * (lane >> 5);      // + rg*16 + 4c + e
+  // Activation scales of a stage, two per lane: register p holds, in each 16-lane row, the 8 rows
+  // this half-wave's MFMA outputs carry (register pair j <-> real row 4(j>>1) + 2(lane>>5) + (j&1))
+  // for blocks 2p (lanes 0-7 of the row) and 2p+1 (lanes 8-15); the accumulate FMA broadcasts
+  // lane 8(jb&1) + j of the row, so the scale is read from LDS once per stage, not once per use.
+  const int da_lrow = wm * 16 * RG + 4 * ((lane & 7) >> 1) + 2 * (lane >> 5) + (lane & 1);  // + rg*16
+  const int da_lblk = (lane & 15) >> 3;
 
   // one stage of G_KS blocks from LDS buffer st
   auto compute = [&](int st) {
     asm volatile("" : "+v"(cinit));  // keep the accumulator initial value resident in VGPRs
-#pragma unroll 1
+    double dav[RG][2];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) dav[rg][p] = sm.as[st][2 * p + da_lblk][da_lrow + rg * 16];
+#pragma unroll
     for (int jb = 0; jb < G_KS; ++jb) {
       v4i fa[RG], fb[CG];
 #pragma unroll
@@ -233,24 +276,17 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
         cdw[cg] = -G_MAGIC * dw[cg];
       }
 #pragma unroll
-      for (int rg = 0; rg < RG; ++rg) {
-        double da[8];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const double2 v2 = *reinterpret_cast<const double2*>(&sm.as[st][jb][da_row + rg * 16 + 4 * c]);
-          da[2 * c] = v2.x;
-          da[2 * c + 1] = v2.y;
-        }
+      for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
         for (int cg = 0; cg < CG; ++cg) {
           // the 8 (even, odd) register pairs are the f64 values 1.5*2^52 + 2^31 + I
-          v8d x = __builtin_bit_cast(v8d, d[rg][cg]);
+          v8d xv = __builtin_bit_cast(v8d, d[rg][cg]);
+          double x[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = fma(x[j], dw[cg], cdw[cg]);   // exactly I*dw
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[rg][cg][j] = fma(x[j], da[j], acc[rg][cg][j]);
+          for (int j = 0; j < 8; ++j) x[j] = fma(xv[j], dw[cg], cdw[cg]);   // exactly I*dw
+          if (jb & 1) fmac8_bcast<1>(acc[rg][cg], x, dav[rg][jb >> 1]);
+          else fmac8_bcast<0>(acc[rg][cg], x, dav[rg][jb >> 1]);
         }
-      }
     }
   };
 
