@@ -34,17 +34,18 @@ constexpr int G_KS = 4;     // Q8_0 blocks per LDS stage (128 K values)
 constexpr double G_MAGIC = 0x1.8p+52 + 0x1p+31;  // 1.5*2^52 + 2^31, exact
 
 // Wave tile = RG x CG MFMAs (16 real rows x 32 columns each); workgroup = 2 x 2 waves.
-// LDS rows hold the 4 blocks of a stage back to back (128 bytes) plus 16 bytes of padding, so a
-// row stride of 144 bytes spreads the 16-byte fragment reads of 16 consecutive rows over all
-// banks; one extra all-zero row feeds the odd (dummy) MFMA rows.
-constexpr int G_ROWB = G_KS * QK + 16;  // bytes per LDS row
+// LDS rows hold the 4 blocks of a stage back to back (128 bytes = 8 chunks of 16).  Chunk c of
+// row r sits at position c ^ (r & 7), so the 16-byte fragment reads of 8 consecutive rows at one
+// chunk hit 8 different 16-byte bank groups; one extra all-zero row feeds the odd (dummy) MFMA
+// rows.
+constexpr int G_ROWB = G_KS * QK;  // bytes per LDS row
+constexpr int VMCNT0 = 0x0f70;      // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima)
+__device__ __forceinline__ int swz(int row, int chunk) { return ((chunk ^ (row & 7)) << 4); }
 
 template <int RG, int CG>
 struct GemmTile {
   static constexpr int BM = 2 * 16 * RG;   // real activation rows per workgroup
   static constexpr int BN = 2 * 32 * CG;   // weight rows (output columns) per workgroup
-  static constexpr int A_CHUNKS = BM * G_KS * 2 / G_THREADS;  // 16-byte chunks per thread per stage
-  static constexpr int B_CHUNKS = BN * G_KS * 2 / G_THREADS;
   static constexpr int AS_PER_T = (BM * G_KS + G_THREADS - 1) / G_THREADS;
   static constexpr int BS_PER_T = (BN * G_KS + G_THREADS - 1) / G_THREADS;
   int8_t a[2][BM + 1][G_ROWB];   // row BM is all zeros
@@ -52,6 +53,18 @@ struct GemmTile {
   double as[2][G_KS][BM];
   double bs[2][G_KS][BN];
 };
+
+// 16 bytes per lane from gbase + voff into LDS at lds + 16 * lane (global_load_lds_dwordx4: M0
+// holds the wave's LDS base; one wait state between writing M0 and the load).  Written as inline
+// assembly so that the compiler does not make every later LDS read wait for these loads: they
+// target the other LDS buffer, and the kernel waits for them (vmcnt) before its barrier.
+__device__ __forceinline__ void lds_dma16(void* lds, const int8_t* gbase, uint32_t voff) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(l), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
 
 // acc[j] += bcast(da, lane 8*HALF + j of each 16-lane row) * x[j] for j = 0..7: v_fmac_f64 with a
 // DPP row_newbcast source (the one DPP form of the f64 ALU).  da comes from an LDS load; the
@@ -87,7 +100,7 @@ __device__ __forceinline__ void fmac8_bcast(double (&acc)[8], const double (&x)[
 }
 
 template <int RG, int CG, int EPI, bool SPLIT>
-__global__ void __launch_bounds__(G_THREADS, 2)
+__global__ void __launch_bounds__(G_THREADS, RG == 1 ? 3 : 2)
 k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales, int M,
           const int8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales, int N, int K,
           const float* __restrict__ bias, const float* residual, float* out, int64_t ld_out,
@@ -139,26 +152,42 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
   if (tid < 2 * G_ROWB / 16) *reinterpret_cast<v4i*>(&sm.a[tid / (G_ROWB / 16)][BM][(tid % (G_ROWB / 16)) * 16]) =
       v4i{0, 0, 0, 0};
 
-  // ---- prefetch registers for one stage (G_KS blocks).  Codes: chunk c -> row c/8, 16-byte
-  // piece c%8 of the row's 128 stage bytes (8 consecutive threads read 128 contiguous bytes).
-  // Scales: element e -> block e / R, row e % R (consecutive threads fill consecutive LDS slots).
+  // ---- codes: global -> LDS directly (global_load_lds_dwordx4).  One wave instruction moves 64
+  // chunks of 16 bytes = 8 whole LDS rows; lane l lands at row 8q + (l >> 3), position l & 7,
+  // which holds chunk (l & 7) ^ (l >> 3) of that row (the XOR layout above).  Instruction q of
+  // wave w covers rows 8(4q + w)..+7.  Rows past M (N) re-read the last valid row: their outputs
+  // are never stored.  The per-lane source offsets do not change from stage to stage; the stage's
+  // K position goes into the uniform base address.
+  constexpr int A_DMA = BM / 32, B_DMA = BN / 32;   // instructions per wave per stage
+  const int lchunk = (lane & 7) ^ (lane >> 3);
+  uint32_t a_off[A_DMA], b_off[B_DMA];
+#pragma unroll
+  for (int q = 0; q < A_DMA; ++q)
+    a_off[q] = (uint32_t)min(m0 + 8 * (4 * q + wave) + (lane >> 3), M - 1) * (uint32_t)K + lchunk * 16;
+#pragma unroll
+  for (int q = 0; q < B_DMA; ++q)
+    b_off[q] = (uint32_t)min(n0 + 8 * (4 * q + wave) + (lane >> 3), N - 1) * (uint32_t)K + lchunk * 16;
+  auto issue_codes = [&](int kbs, int st) {
+    // a stage past the end of the slice (K not a multiple of the stage) re-reads its last block
+    // for the missing ones: their scales are zero, so they add nothing
+    const int nbk = min(G_KS, kb1 - kbs);
+    const uint32_t fix = nbk < G_KS ? (uint32_t)((min(lchunk, 2 * nbk - 1) - lchunk) * 16) : 0u;
+    const int8_t* ga = a_codes + (int64_t)kbs * QK;
+    const int8_t* gb = w_codes + (int64_t)kbs * QK;
+#pragma unroll
+    for (int q = 0; q < A_DMA; ++q) lds_dma16(&sm.a[st][8 * (4 * q + wave)][0], ga, a_off[q] + fix);
+#pragma unroll
+    for (int q = 0; q < B_DMA; ++q) lds_dma16(&sm.b[st][8 * (4 * q + wave)][0], gb, b_off[q] + fix);
+  };
+
+  // ---- scales through registers (converted to f64 on the way into LDS).  Element e -> block
+  // e / R, row e % R (consecutive threads fill consecutive LDS slots).
   struct Pre {
-    v4i a[T::A_CHUNKS], b[T::B_CHUNKS];
     uint16_t as[T::AS_PER_T], bs[T::BS_PER_T];
   };
   const bool a_full = m0 + BM <= M, b_full = n0 + BN <= N;
   auto fetch = [&](Pre& p, int kbs) {
     if (kbs + G_KS <= kb1 && a_full && b_full) {  // common case: no bounds checks
-#pragma unroll
-      for (int i = 0; i < T::A_CHUNKS; ++i) {
-        const int c = tid + i * G_THREADS;
-        p.a[i] = *reinterpret_cast<const v4i*>(a_codes + (int64_t)(m0 + (c >> 3)) * K + (int64_t)kbs * QK + (c & 7) * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < T::B_CHUNKS; ++i) {
-        const int c = tid + i * G_THREADS;
-        p.b[i] = *reinterpret_cast<const v4i*>(w_codes + (int64_t)(n0 + (c >> 3)) * K + (int64_t)kbs * QK + (c & 7) * 16);
-      }
 #pragma unroll
       for (int i = 0; i < T::AS_PER_T; ++i) {
         const int e = tid + i * G_THREADS;
@@ -170,23 +199,6 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
         if (e < BN * G_KS) p.bs[i] = w_scales[(int64_t)(n0 + e % BN) * KB + kbs + e / BN];
       }
       return;
-    }
-    const int nb = min(G_KS, kb1 - kbs) * 2;  // 16-byte pieces present in this stage
-#pragma unroll
-    for (int i = 0; i < T::A_CHUNKS; ++i) {
-      const int c = tid + i * G_THREADS, row = c >> 3, piece = c & 7;
-      const int gr = m0 + row;
-      p.a[i] = (gr < M && piece < nb)
-                  ? *reinterpret_cast<const v4i*>(a_codes + (int64_t)gr * K + (int64_t)kbs * QK + piece * 16)
-                  : v4i{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < T::B_CHUNKS; ++i) {
-      const int c = tid + i * G_THREADS, row = c >> 3, piece = c & 7;
-      const int gr = n0 + row;
-      p.b[i] = (gr < N && piece < nb)
-                  ? *reinterpret_cast<const v4i*>(w_codes + (int64_t)gr * K + (int64_t)kbs * QK + piece * 16)
-                  : v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < T::AS_PER_T; ++i) {
@@ -202,16 +214,6 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
     }
   };
   auto stash = [&](const Pre& p, int st) {
-#pragma unroll
-    for (int i = 0; i < T::A_CHUNKS; ++i) {
-      const int c = tid + i * G_THREADS;
-      *reinterpret_cast<v4i*>(&sm.a[st][c >> 3][(c & 7) * 16]) = p.a[i];
-    }
-#pragma unroll
-    for (int i = 0; i < T::B_CHUNKS; ++i) {
-      const int c = tid + i * G_THREADS;
-      *reinterpret_cast<v4i*>(&sm.b[st][c >> 3][(c & 7) * 16]) = p.b[i];
-    }
 #pragma unroll
     for (int i = 0; i < T::AS_PER_T; ++i) {
       const int e = tid + i * G_THREADS;
@@ -238,7 +240,7 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
 
   const bool a_lane = (lane & 1) == 0;                   // even MFMA rows carry data
   const int a_rrow = wm * 16 * RG + ((lane & 31) >> 1);   // + rg*16
-  const int koff = (lane >> 5) * 16;
+  const int khalf = lane >> 5;                             // 16-byte half of the block
   const int b_rrow = wn * 32 * CG + (lane & 31);          // + cg*32
   // Activation scales of a stage, two per lane: register p holds, in each 16-lane row, the 8 rows
   // this half-wave's MFMA outputs carry (register pair j <-> real row 4(j>>1) + 2(lane>>5) + (j&1))
@@ -259,11 +261,13 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
     for (int jb = 0; jb < G_KS; ++jb) {
       v4i fa[RG], fb[CG];
 #pragma unroll
-      for (int rg = 0; rg < RG; ++rg)
-        fa[rg] = *reinterpret_cast<const v4i*>(&sm.a[st][a_lane ? a_rrow + rg * 16 : BM][jb * QK + koff]);
+      for (int rg = 0; rg < RG; ++rg) {
+        const int r = a_lane ? a_rrow + rg * 16 : BM;
+        fa[rg] = *reinterpret_cast<const v4i*>(&sm.a[st][r][swz(r, 2 * jb + khalf)]);
+      }
 #pragma unroll
       for (int cg = 0; cg < CG; ++cg)
-        fb[cg] = *reinterpret_cast<const v4i*>(&sm.b[st][b_rrow + cg * 32][jb * QK + koff]);
+        fb[cg] = *reinterpret_cast<const v4i*>(&sm.b[st][b_rrow + cg * 32][swz(b_rrow, 2 * jb + khalf)]);
       v16i d[RG][CG];
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg)
@@ -290,44 +294,27 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
     }
   };
 
-  // Stages of G_KS blocks through two LDS buffers.  The 1 x 2 tile keeps two stages of global
-  // loads in flight (two register sets, the loop unrolled by two so the sets stay static); the
-  // others keep one.
+  // Stages of G_KS blocks through two LDS buffers: the next stage's global loads are in flight
+  // while the current one computes.
   const int ns = (kb1 - kb0 + G_KS - 1) / G_KS;
-  Pre p0, p1;
-  if constexpr (RG == 1 && CG == 2) {
-    if (ns > 0) {
-      fetch(p0, kb0);
-      if (ns > 1) fetch(p1, kb0 + G_KS);
-      stash(p0, 0);
+  Pre p0;
+  if (ns > 0) {
+    issue_codes(kb0, 0);
+    fetch(p0, kb0);
+    stash(p0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(VMCNT0);  // this wave's LDS-bound loads have landed
+  __syncthreads();
+  for (int s = 0; s < ns; ++s) {
+    const bool more = s + 1 < ns;
+    if (more) {
+      issue_codes(kb0 + (s + 1) * G_KS, (s & 1) ^ 1);
+      fetch(p0, kb0 + (s + 1) * G_KS);
     }
+    compute(s & 1);
+    if (more) stash(p0, (s & 1) ^ 1);
+    __builtin_amdgcn_s_waitcnt(VMCNT0);
     __syncthreads();
-    for (int s = 0; s < ns; s += 2) {
-      if (s + 2 < ns) fetch(p0, kb0 + (s + 2) * G_KS);
-      compute(0);
-      if (s + 1 < ns) stash(p1, 1);
-      __syncthreads();
-      if (s + 1 < ns) {
-        if (s + 3 < ns) fetch(p1, kb0 + (s + 3) * G_KS);
-        compute(1);
-        if (s + 2 < ns) stash(p0, 0);
-        __syncthreads();
-      }
-    }
-  } else {
-    (void)p1;
-    if (ns > 0) {
-      fetch(p0, kb0);
-      stash(p0, 0);
-    }
-    __syncthreads();
-    for (int s = 0; s < ns; ++s) {
-      const bool more = s + 1 < ns;
-      if (more) fetch(p0, kb0 + (s + 1) * G_KS);
-      compute(s & 1);
-      if (more) stash(p0, (s & 1) ^ 1);
-      __syncthreads();
-    }
   }
 
   // ---- epilogue.  Lane holds, for each (rg, cg, j): real row, column.

@@ -70,6 +70,9 @@ GEMM_CASES = [  # m, k, n, bias, residual, split
     (200, 128, 64, False, False, 1),
     (33, 1024, 256, True, False, 4),
     (256, 512, 16384, True, False, 0),   # 2x2 wave tiles (64 x 128 workgroups)
+    (45, 160, 224, False, False, 1),     # one 1-block stage after a full one; row and column tails
+    (3, 96, 96, True, False, 1),         # K shorter than one 4-block stage
+    (520, 160, 8224, False, True, 0),    # 2x2 tiles with row, column and K-stage tails
 ]
 
 
