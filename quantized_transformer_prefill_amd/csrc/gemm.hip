@@ -39,31 +39,56 @@ constexpr double G_MAGIC = 0x1.8p+52 + 0x1p+31;  // 1.5*2^52 + 2^31, exact
 // chunk hit 8 different 16-byte bank groups; one extra all-zero row feeds the odd (dummy) MFMA
 // rows.
 constexpr int G_ROWB = G_KS * QK;  // bytes per LDS row
-constexpr int VMCNT0 = 0x0f70;      // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima)
+// Ring depth (stages in LDS) per tile shape.  Two: deeper rings cost more in workgroups per CU (LDS)
+// than they gain in latency hiding at the model's shapes (measured for 3 and 4 stages).
+constexpr int G_NS_11 = 2, G_NS_12 = 2, G_NS_22 = 2;
 __device__ __forceinline__ int swz(int row, int chunk) { return ((chunk ^ (row & 7)) << 4); }
 
-template <int RG, int CG>
+// NS stages live in a ring; every load into it is a global->LDS transfer.
+template <int RG, int CG, int NS>
 struct GemmTile {
   static constexpr int BM = 2 * 16 * RG;   // real activation rows per workgroup
   static constexpr int BN = 2 * 32 * CG;   // weight rows (output columns) per workgroup
-  static constexpr int AS_PER_T = (BM * G_KS + G_THREADS - 1) / G_THREADS;
-  static constexpr int BS_PER_T = (BN * G_KS + G_THREADS - 1) / G_THREADS;
-  int8_t a[2][BM + 1][G_ROWB];   // row BM is all zeros
-  int8_t b[2][BN][G_ROWB];
-  double as[2][G_KS][BM];
-  double bs[2][G_KS][BN];
+  int8_t a[NS][BM + 1][G_ROWB];   // row BM is all zeros
+  int8_t b[NS][BN][G_ROWB];
+  uint32_t as[NS][G_KS][BM];      // fp16 scale bits in the low half of each word
+  uint32_t bs[NS][G_KS][BN];
 };
 
 // 16 bytes per lane from gbase + voff into LDS at lds + 16 * lane (global_load_lds_dwordx4: M0
 // holds the wave's LDS base; one wait state between writing M0 and the load).  Written as inline
 // assembly so that the compiler does not make every later LDS read wait for these loads: they
 // target the other LDS buffer, and the kernel waits for them (vmcnt) before its barrier.
+// a wave-uniform pointer, held in SGPRs
+template <typename P>
+__device__ __forceinline__ P* sgpr_ptr(P* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void lds_dma16(void* lds, const int8_t* gbase, uint32_t voff) {
   const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  gbase = sgpr_ptr(gbase);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(l), "v"(voff), "s"(gbase)
                : "memory", "m0");
+}
+// The same for 2 bytes per lane (global_load_lds_ushort): lane l's value lands in the low half of
+// the 4-byte word at lds + 4 * lane, the high half is zeroed.
+__device__ __forceinline__ void lds_dma2(void* lds, const uint16_t* gbase, uint32_t voff) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  gbase = sgpr_ptr(gbase);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, %2"
+               :
+               : "s"(l), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+// s_waitcnt vmcnt(N), expcnt and lgkmcnt left at their maxima
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
 }
 
 // acc[j] += bcast(da, lane 8*HALF + j of each 16-lane row) * x[j] for j = 0..7: v_fmac_f64 with a
@@ -99,20 +124,20 @@ __device__ __forceinline__ void fmac8_bcast(double (&acc)[8], const double (&x)[
         : "v"(da), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
 }
 
-template <int RG, int CG, int EPI, bool SPLIT>
+template <int RG, int CG, int EPI, bool SPLIT, int NS>
 __global__ void __launch_bounds__(G_THREADS, RG == 1 ? 3 : 2)
 k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales, int M,
           const int8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales, int N, int K,
           const float* __restrict__ bias, const float* residual, float* out, int64_t ld_out,
           int8_t* __restrict__ q_codes, uint16_t* __restrict__ q_scales,
           double* __restrict__ partial, int kb_per_split, int xcd_order, QkvEpi qe) {
-  using T = GemmTile<RG, CG>;
+  using T = GemmTile<RG, CG, NS>;
   constexpr int BM = T::BM, BN = T::BN;
   __shared__ __align__(16) T sm;
   __shared__ double exp_tab[EPI == EPI_SWIGLU_Q8 ? 64 : 1];  // 2^(j/64) for the SiLU
   const int tid = threadIdx.x;
   if constexpr (EPI == EPI_SWIGLU_Q8) exp2_table_fill(exp_tab, tid);
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index held in an SGPR
   const int wm = wave >> 1, wn = wave & 1;
   // XCD-aware tile order.  Workgroups are dispatched round-robin over the 8 XCDs, each with its
   // own L2; workgroup L is given tile t so that every XCD owns one contiguous range of tiles, and
@@ -132,25 +157,29 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
 
   // QKV epilogue of the smallest tile: the positions and (cos, sin) of this thread's RoPE pairs
   // are requested now, so they arrive while the K loop runs
-  constexpr int QPRE = (EPI == EPI_QKV && RG == 1 && CG == 1) ? GemmTile<RG, CG>::BM * GemmTile<RG, CG>::BN / 2 / G_THREADS : 0;
+  constexpr int QPRE = (EPI == EPI_QKV && RG == 1 && CG == 1) ? BM * BN / 2 / G_THREADS : 0;
   double2 qcs[QPRE > 0 ? QPRE : 1];
   int64_t qpos[QPRE > 0 ? QPRE : 1];
   if constexpr (QPRE > 0) {
-    const int half = qe.head_dim / 2;
 #pragma unroll
     for (int k = 0; k < QPRE; ++k) {
-      const int e = tid + k * G_THREADS;
-      const int row_l = e / (BN / 2), r2 = e - row_l * (BN / 2);
-      const int i = r2 % half;
-      const int row = m0 + row_l;
+      const int row = m0 + (tid + k * G_THREADS) / (BN / 2);
       qpos[k] = row < M ? qe.pos[row] : 0;
-      qcs[k] = reinterpret_cast<const double2*>(qe.rope)[qpos[k] * half + i];
     }
   }
+  // bias of this lane's output columns (bit patterns), requested before the K loop
+  uint32_t bias_b[CG];
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg) bias_b[cg] = 0u;
+  if (bias) {
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg)
+      bias_b[cg] = reinterpret_cast<const uint32_t*>(bias)[min(n0 + wn * 32 * CG + cg * 32 + (lane & 31), N - 1)];
+  }
 
-  // zero row for the dummy MFMA rows (both stages)
-  if (tid < 2 * G_ROWB / 16) *reinterpret_cast<v4i*>(&sm.a[tid / (G_ROWB / 16)][BM][(tid % (G_ROWB / 16)) * 16]) =
-      v4i{0, 0, 0, 0};
+  // zero row for the dummy MFMA rows (every ring slot)
+  if (tid < NS * G_ROWB / 16)
+    *reinterpret_cast<v4i*>(&sm.a[tid / (G_ROWB / 16)][BM][(tid % (G_ROWB / 16)) * 16]) = v4i{0, 0, 0, 0};
 
   // ---- codes: global -> LDS directly (global_load_lds_dwordx4).  One wave instruction moves 64
   // chunks of 16 bytes = 8 whole LDS rows; lane l lands at row 8q + (l >> 3), position l & 7,
@@ -167,9 +196,20 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
 #pragma unroll
   for (int q = 0; q < B_DMA; ++q)
     b_off[q] = (uint32_t)min(n0 + 8 * (4 * q + wave) + (lane >> 3), N - 1) * (uint32_t)K + lchunk * 16;
-  auto issue_codes = [&](int kbs, int st) {
+  // ---- scales: global -> LDS directly too, 2 bytes per lane.  Per stage, wave w moves the
+  // A-scale elements AS_L*w + l (l < AS_L; AS_L*w / BM = w is the block, l the row) and the
+  // B-scale elements 64(w + 4i) + l (block (64(w + 4i) + l) / BN, row (64(w + 4i) + l) % BN).
+  constexpr int AS_L = BM * G_KS / 4;       // 32 or 64
+  constexpr int BS_I = BN * G_KS / 256;     // 1 or 2
+  static_assert(AS_L * 4 == BM * G_KS && BS_I * 256 == BN * G_KS, "scale transfer shape");
+  constexpr int L_OPS = A_DMA + B_DMA + 1 + BS_I;  // transfers per wave per stage
+  const uint32_t as_off = (uint32_t)min(m0 + lane, M - 1) * (uint32_t)(KB * 2);
+  uint32_t bs_off[BS_I];
+#pragma unroll
+  for (int i = 0; i < BS_I; ++i) bs_off[i] = (uint32_t)min(n0 + (64 * (wave + 4 * i) + lane) % BN, N - 1) * (uint32_t)(KB * 2);
+  auto issue = [&](int kbs, int st) {
     // a stage past the end of the slice (K not a multiple of the stage) re-reads its last block
-    // for the missing ones: their scales are zero, so they add nothing
+    // for the missing ones; compute() skips them
     const int nbk = min(G_KS, kb1 - kbs);
     const uint32_t fix = nbk < G_KS ? (uint32_t)((min(lchunk, 2 * nbk - 1) - lchunk) * 16) : 0u;
     const int8_t* ga = a_codes + (int64_t)kbs * QK;
@@ -178,52 +218,11 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
     for (int q = 0; q < A_DMA; ++q) lds_dma16(&sm.a[st][8 * (4 * q + wave)][0], ga, a_off[q] + fix);
 #pragma unroll
     for (int q = 0; q < B_DMA; ++q) lds_dma16(&sm.b[st][8 * (4 * q + wave)][0], gb, b_off[q] + fix);
-  };
-
-  // ---- scales through registers (converted to f64 on the way into LDS).  Element e -> block
-  // e / R, row e % R (consecutive threads fill consecutive LDS slots).
-  struct Pre {
-    uint16_t as[T::AS_PER_T], bs[T::BS_PER_T];
-  };
-  const bool a_full = m0 + BM <= M, b_full = n0 + BN <= N;
-  auto fetch = [&](Pre& p, int kbs) {
-    if (kbs + G_KS <= kb1 && a_full && b_full) {  // common case: no bounds checks
+    if (lane < AS_L) lds_dma2(&sm.as[st][0][0] + AS_L * wave, a_scales + kbs + min(wave, nbk - 1), as_off);
 #pragma unroll
-      for (int i = 0; i < T::AS_PER_T; ++i) {
-        const int e = tid + i * G_THREADS;
-        if (e < BM * G_KS) p.as[i] = a_scales[(int64_t)(m0 + e % BM) * KB + kbs + e / BM];
-      }
-#pragma unroll
-      for (int i = 0; i < T::BS_PER_T; ++i) {
-        const int e = tid + i * G_THREADS;
-        if (e < BN * G_KS) p.bs[i] = w_scales[(int64_t)(n0 + e % BN) * KB + kbs + e / BN];
-      }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < T::AS_PER_T; ++i) {
-      const int e = tid + i * G_THREADS, j = e / BM, row = e % BM;
-      const int gr = m0 + row, kb = kbs + j;
-      p.as[i] = (e < BM * G_KS && gr < M && kb < kb1) ? a_scales[(int64_t)gr * KB + kb] : (uint16_t)0;
-    }
-#pragma unroll
-    for (int i = 0; i < T::BS_PER_T; ++i) {
-      const int e = tid + i * G_THREADS, j = e / BN, row = e % BN;
-      const int gr = n0 + row, kb = kbs + j;
-      p.bs[i] = (e < BN * G_KS && gr < N && kb < kb1) ? w_scales[(int64_t)gr * KB + kb] : (uint16_t)0;
-    }
-  };
-  auto stash = [&](const Pre& p, int st) {
-#pragma unroll
-    for (int i = 0; i < T::AS_PER_T; ++i) {
-      const int e = tid + i * G_THREADS;
-      if (e < BM * G_KS) sm.as[st][e / BM][e % BM] = (double)f16_bits_to_f32(p.as[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < T::BS_PER_T; ++i) {
-      const int e = tid + i * G_THREADS;
-      if (e < BN * G_KS) sm.bs[st][e / BN][e % BN] = (double)f16_bits_to_f32(p.bs[i]);
-    }
+    for (int i = 0; i < BS_I; ++i)
+      lds_dma2(&sm.bs[st][0][0] + 64 * (wave + 4 * i), w_scales + kbs + min(64 * (wave + 4 * i) / BN, nbk - 1),
+               bs_off[i]);
   };
 
   v16i cinit;
@@ -250,15 +249,17 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
   const int da_lblk = (lane & 15) >> 3;
 
   // one stage of G_KS blocks from LDS buffer st
-  auto compute = [&](int st) {
+  auto compute = [&](int st, int nbk) {
     asm volatile("" : "+v"(cinit));  // keep the accumulator initial value resident in VGPRs
     double dav[RG][2];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-      for (int p = 0; p < 2; ++p) dav[rg][p] = sm.as[st][2 * p + da_lblk][da_lrow + rg * 16];
+      for (int p = 0; p < 2; ++p)
+        dav[rg][p] = (double)f16_bits_to_f32((uint16_t)sm.as[st][2 * p + da_lblk][da_lrow + rg * 16]);
 #pragma unroll
     for (int jb = 0; jb < G_KS; ++jb) {
+      if (jb >= nbk) break;  // past the end of the slice
       v4i fa[RG], fb[CG];
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
@@ -276,7 +277,7 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
       double dw[CG], cdw[CG];
 #pragma unroll
       for (int cg = 0; cg < CG; ++cg) {
-        dw[cg] = sm.bs[st][jb][b_rrow + cg * 32];
+        dw[cg] = (double)f16_bits_to_f32((uint16_t)sm.bs[st][jb][b_rrow + cg * 32]);
         cdw[cg] = -G_MAGIC * dw[cg];
       }
 #pragma unroll
@@ -294,30 +295,37 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
     }
   };
 
-  // Stages of G_KS blocks through two LDS buffers: the next stage's global loads are in flight
-  // while the current one computes.
+  // Stages of G_KS blocks through a ring of NS LDS slots: NS - 1 stages are in flight while one
+  // computes.  Slot (s + NS - 1) % NS is refilled right after the barrier that ends stage s - 1.
   const int ns = (kb1 - kb0 + G_KS - 1) / G_KS;
-  Pre p0;
-  if (ns > 0) {
-    issue_codes(kb0, 0);
-    fetch(p0, kb0);
-    stash(p0, 0);
-  }
-  __builtin_amdgcn_s_waitcnt(VMCNT0);  // this wave's LDS-bound loads have landed
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u)
+    if (u < ns) issue(kb0 + u * G_KS, u);
+  if (ns >= NS - 1) wait_vmcnt<(NS - 2) * L_OPS>();
+  else wait_vmcnt<0>();
   __syncthreads();
-  for (int s = 0; s < ns; ++s) {
-    const bool more = s + 1 < ns;
-    if (more) {
-      issue_codes(kb0 + (s + 1) * G_KS, (s & 1) ^ 1);
-      fetch(p0, kb0 + (s + 1) * G_KS);
+  if constexpr (QPRE > 0) {  // the positions are in; their (cos, sin) rows arrive during the K loop
+    const int half = qe.head_dim / 2;
+#pragma unroll
+    for (int k = 0; k < QPRE; ++k) {
+      const int e = tid + k * G_THREADS;
+      const int i = (e % (BN / 2)) % half;
+      qcs[k] = reinterpret_cast<const double2*>(qe.rope)[qpos[k] * half + i];
     }
-    compute(s & 1);
-    if (more) stash(p0, (s & 1) ^ 1);
-    __builtin_amdgcn_s_waitcnt(VMCNT0);
+  }
+  for (int s = 0; s < ns; ++s) {
+    const bool more = s + NS - 1 < ns;
+    if (more) issue(kb0 + (s + NS - 1) * G_KS, (s + NS - 1) % NS);
+    compute(s % NS, min(G_KS, kb1 - kb0 - s * G_KS));
+    // stage s + 1 has landed once at most the later stages' transfers are outstanding
+    if (more) wait_vmcnt<(NS - 2) * L_OPS>();
+    else wait_vmcnt<0>();
     __syncthreads();
   }
 
   // ---- epilogue.  Lane holds, for each (rg, cg, j): real row, column.
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg) asm volatile("" : "+v"(bias_b[cg]));  // the bias is used from here on
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
@@ -338,7 +346,7 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
             const int col = n0 + wn * 32 * CG + cg * 32 + (lane & 31);
             if (col < N) {
               double v = acc[rg][cg][j];
-              if (bias) v += (double)bias[col];
+              if (bias) v += (double)__uint_as_float(bias_b[cg]);
               float y = (float)v;
               const int64_t o = (int64_t)row * ld_out + col;
               if (residual) y = residual[o] + y;
@@ -365,7 +373,7 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
         for (int cg = 0; cg < CG; ++cg) {
           const int col_l = wn * 32 * CG + cg * 32 + (lane & 31);
           double v = acc[rg][cg][j];
-          if (bias && n0 + col_l < N) v += (double)bias[n0 + col_l];
+          if (bias) v += (double)__uint_as_float(bias_b[cg]);
           tb[row_l * BN + col_l] = (float)v;
         }
       }
@@ -548,28 +556,28 @@ size_t gemm_workspace_bytes(int m, int n, int k) {
   return s > 1 ? (size_t)s * m * n * sizeof(double) : 0;
 }
 
-template <int RG, int CG>
+template <int RG, int CG, int NS>
 static void launch_tiles(const GemmArgs& g, int split, int kb_per, hipStream_t s) {
-  using T = GemmTile<RG, CG>;
+  using T = GemmTile<RG, CG, NS>;
   dim3 grid((g.n + T::BN - 1) / T::BN, (g.m + T::BM - 1) / T::BM, split);
   // XCD-aware order once the weights outgrow one XCD's 4 MB L2 several times over
   const int xcd = (int64_t)g.n * g.k > ((int64_t)16 << 20) ? 1 : 0;
   double* partial = reinterpret_cast<double*>(g.workspace);
   if (split > 1)
-    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, true>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
+    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, true, NS>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
                        g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
                        partial, kb_per, xcd, g.qkv);
   else if (g.qkv.pos)
-    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_QKV, false>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
+    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_QKV, false, NS>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
                        g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
                        nullptr, kb_per, xcd, g.qkv);
   else if (g.q_codes) {
     if constexpr (CG >= 2)
-      hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_SWIGLU_Q8, false>), grid, dim3(G_THREADS), 0, s, g.a_codes,
+      hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_SWIGLU_Q8, false, NS>), grid, dim3(G_THREADS), 0, s, g.a_codes,
                          g.a_scales, g.m, g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out,
                          g.q_codes, g.q_scales, nullptr, kb_per, xcd, g.qkv);
   } else
-    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, false>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
+    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, false, NS>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
                        g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
                        nullptr, kb_per, xcd, g.qkv);
 }
@@ -594,9 +602,9 @@ int launch_gemm_q8(const GemmArgs& g, hipStream_t s) {
   int kb_per = (KB + split - 1) / split;
   kb_per = ((kb_per + G_KS - 1) / G_KS) * G_KS;
   split = (KB + kb_per - 1) / kb_per;
-  if (p.shape == 1) launch_tiles<2, 2>(g, split, kb_per, s);
-  else if (p.shape == 2) launch_tiles<1, 2>(g, split, kb_per, s);
-  else launch_tiles<1, 1>(g, split, kb_per, s);
+  if (p.shape == 1) launch_tiles<2, 2, G_NS_22>(g, split, kb_per, s);
+  else if (p.shape == 2) launch_tiles<1, 2, G_NS_12>(g, split, kb_per, s);
+  else launch_tiles<1, 1, G_NS_11>(g, split, kb_per, s);
   MI_LAUNCH_CHECK("k_gemm_q8");
   const bool defer = g.split_out && !g.q_codes && !g.bias && split > 1;  // the consumer reduces the partials
   if (g.split_out) *g.split_out = defer ? split : 1;
