@@ -157,6 +157,20 @@ int mi_prefill_forward_n(const mi_model* model, const int32_t* token_ids, const 
                          int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv, int32_t n_out,
                          float* logits_out);
 
+/* Decode step: one token `token_id` at `position`, through the same layers and KV regions as the
+ * prefill (the second act of the walkthrough index's two-act engine; the prefill page, section
+ * 2.2, for attention over region rows 0..=position).  Computes exactly what mi_prefill_forward
+ * computes for n_tokens = 1 -- which runs the same one-row kernels: HBM-bound exact Q8_0
+ * matrix-vector products with the RMSNorms in their prologues and the SwiGLU / RoPE / KV-store
+ * work in their epilogues, and a single-query attention split over fixed key ranges.
+ *   token_id, position  host values, 0 <= token_id < vocab, 0 <= position < n_ctx
+ *   logits_out          device f32 [vocab]
+ * Writes K/V row `position` of every layer.  Errors as mi_prefill_forward (nothing written).
+ * A captured graph (mi_prefill_graph_create with n_tokens = 1) replays decode steps at any
+ * position. */
+int mi_decode_step(const mi_model* model, int32_t token_id, int32_t position, int32_t n_ctx,
+                   const mi_kv_regions* kv, float* logits_out);
+
 /* Graph replay of the forward for callers that repeat one shape (HIP graphs).
  * mi_prefill_graph_create validates the shapes like mi_prefill_forward_n, then captures the
  * forward's kernel sequence on model->stream (which must be a non-default stream) into a graph;

@@ -48,6 +48,7 @@ struct Ws {
   int8_t* sq;        // [T][ffn] SwiGLU output codes
   uint16_t* ss;      // [T][ffn/32]
   int8_t* lm_q; uint16_t* lm_s;  // final row quantized
+  double* attn_part; // decode: partial attention states [n_head][AD_MAX_RANGES][head_dim + 2]
   void* gemm_ws; size_t gemm_ws_bytes;
   size_t total;
 };
@@ -72,6 +73,7 @@ static Ws carve(const mi_hparams& hp, int T, char* base) {
   w.ss = (uint16_t*)take(sizeof(uint16_t) * (size_t)T * (hp.ffn / QK));
   w.lm_q = (int8_t*)take((size_t)hp.hidden);
   w.lm_s = (uint16_t*)take(sizeof(uint16_t) * (size_t)(hp.hidden / QK));
+  w.attn_part = (double*)take(sizeof(double) * (size_t)hp.n_head * AD_MAX_RANGES * (hp.head_dim + 2));
   size_t g = 0;
   g = std::max(g, gemm_workspace_bytes(T, (int)(nq + 2 * nkv), hp.hidden));
   g = std::max(g, gemm_workspace_bytes(T, hp.hidden, (int)nq));
@@ -292,6 +294,57 @@ static int stage_tokens(const Ws& w, const int32_t* ids, const int32_t* pos, int
   return MI_OK;
 }
 
+// The decode step: one token through the same layers and regions, with the one-row kernels
+// (decode.hip).  Per layer: Q|K|V matrix-vector product with the attention RMSNorm in its prologue
+// and bias, QK norm, RoPE and the K/V store in its epilogue; single-query attention over the ranges
+// of keys 0..pos, merged into a Q8_0 row; output projection + residual; gate|up with the ffn
+// RMSNorm in its prologue and SwiGLU + Q8_0 in its epilogue; down projection + residual.  Then the
+// lm_head with the final RMSNorm in its prologue.
+static int enqueue_decode(const mi_model* md, const Ws& w, int32_t n_ctx, const mi_kv_regions* kv, float* logits_out,
+                          hipStream_t s) {
+  const mi_hparams& hp = md->hp;
+  const int H = hp.hidden, F = hp.ffn;
+  const int nq = hp.n_head * hp.head_dim, nkv = hp.n_head_kv * hp.head_dim, nqkv = nq + 2 * nkv;
+  const float eps = hp.rms_eps;
+  int rc;
+  if ((rc = launch_embed(md->token_embd.codes, md->token_embd.scales, H, w.ids, 1, w.h, s))) return rc;
+  for (int l = 0; l < hp.n_layers; ++l) {
+    const mi_layer_weights& L = md->layers[l];
+    GemvArgs g{};
+    g.x = w.h; g.gamma = L.attn_norm; g.eps = eps; g.k = H;
+    g.w_codes = L.wqkv.codes; g.w_scales = L.wqkv.scales; g.n = nqkv;
+    g.bias = hp.qkv_bias ? L.bqkv : nullptr; g.epi = GV_QKV;
+    g.qkv.pos = w.pos; g.qkv.rope = md->rope_table; g.qkv.n_q = nq; g.qkv.n_kv = nkv; g.qkv.head_dim = hp.head_dim;
+    g.qkv.q_out = w.qkv; g.qkv.k_region = kv->k[l]; g.qkv.v_region = kv->v[l];
+    g.qkv.q_norm = hp.qk_norm ? L.q_norm : nullptr; g.qkv.k_norm = hp.qk_norm ? L.k_norm : nullptr; g.qkv.eps = eps;
+    if ((rc = launch_gemv_q8(g, s))) return rc;
+    if ((rc = launch_attn_decode(w.qkv, kv->k[l], kv->v[l], w.pos, n_ctx, hp.n_head, hp.n_head_kv, hp.head_dim,
+                                 w.attn_part, w.xq, w.xs, s)))
+      return rc;
+    GemvArgs go{};
+    go.xq = w.xq; go.xs = w.xs; go.k = nq;
+    go.w_codes = L.wo.codes; go.w_scales = L.wo.scales; go.n = H;
+    go.residual = w.h; go.out = w.h; go.epi = GV_RES;
+    if ((rc = launch_gemv_q8(go, s))) return rc;
+    GemvArgs gg{};
+    gg.x = w.h; gg.gamma = L.ffn_norm; gg.eps = eps; gg.k = H;
+    gg.w_codes = L.w_gate_up.codes; gg.w_scales = L.w_gate_up.scales; gg.n = 2 * F;
+    gg.q_codes = w.sq; gg.q_scales = w.ss; gg.epi = GV_SWIGLU;
+    if ((rc = launch_gemv_q8(gg, s))) return rc;
+    GemvArgs gd{};
+    gd.xq = w.sq; gd.xs = w.ss; gd.k = F;
+    gd.w_codes = L.w_down.codes; gd.w_scales = L.w_down.scales; gd.n = H;
+    gd.residual = w.h; gd.out = w.h; gd.epi = GV_RES;
+    if ((rc = launch_gemv_q8(gd, s))) return rc;
+  }
+  const mi_q8_matrix& head = hp.tied ? md->token_embd : md->output;
+  GemvArgs gl{};
+  gl.x = w.h; gl.gamma = md->output_norm; gl.eps = eps; gl.k = H;
+  gl.w_codes = head.codes; gl.w_scales = head.scales; gl.n = head.rows;
+  gl.out = logits_out; gl.epi = GV_F32;
+  return launch_gemv_q8(gl, s);
+}
+
 // Every kernel of one forward, in order, on stream s.  Reads the staged ids, positions and largest
 // position from the workspace; the sequence depends only on the shapes, so it can be captured
 // once into a HIP graph and replayed.
@@ -301,7 +354,7 @@ static int enqueue_forward(const mi_model* md, const Ws& w, int32_t n_tokens, in
   const int nt = n_tokens, H = hp.hidden, F = hp.ffn;
   const int nq = hp.n_head * hp.head_dim, nkv = hp.n_head_kv * hp.head_dim, nqkv = nq + 2 * nkv;
   const float eps = hp.rms_eps;
-  (void)n_ctx;
+  if (nt == 1) return enqueue_decode(md, w, n_ctx, kv, logits_out, s);  // one token: the decode kernels
   int rc;
   if ((rc = launch_embed(md->token_embd.codes, md->token_embd.scales, H, w.ids, nt, w.h, s))) return rc;
   float* h_tail = w.h + (size_t)(nt - n_out) * H;  // the tail rows [nt - n_out, nt)
@@ -380,6 +433,11 @@ static int enqueue_forward(const mi_model* md, const Ws& w, int32_t n_tokens, in
 extern "C" int mi_prefill_forward(const mi_model* md, const int32_t* token_ids, const int32_t* positions,
                                   int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv, float* logits_out) {
   return mi_prefill_forward_n(md, token_ids, positions, n_tokens, n_ctx, kv, 1, logits_out);
+}
+
+extern "C" int mi_decode_step(const mi_model* md, int32_t token_id, int32_t position, int32_t n_ctx,
+                              const mi_kv_regions* kv, float* logits_out) {
+  return mi_prefill_forward_n(md, &token_id, &position, 1, n_ctx, kv, 1, logits_out);
 }
 
 extern "C" int mi_prefill_forward_n(const mi_model* md, const int32_t* token_ids, const int32_t* positions,

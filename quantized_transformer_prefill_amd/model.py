@@ -102,6 +102,15 @@ class PrefillModel:
                                            out.data_ptr()))
         return out
 
+    def decode(self, token_id: int, position: int, n_ctx: Optional[int] = None,
+               logits: Optional[torch.Tensor] = None):
+        """One decode step (mi_decode_step); returns device logits f32 [vocab]."""
+        out = self.logits if logits is None else logits
+        self.model.stream = B.stream_ptr()
+        B.check(B.lib().mi_decode_step(C.byref(self.model), int(token_id), int(position),
+                                       self.n_ctx if n_ctx is None else n_ctx, C.byref(self.kv), out.data_ptr()))
+        return out
+
     def graph(self, n_tokens: int, n_out: int = 1) -> "PrefillGraph":
         """A captured forward for n_tokens-token calls on torch's current stream (see PrefillGraph)."""
         return PrefillGraph(self, n_tokens, n_out)

@@ -1,0 +1,132 @@
+"""Decode step (mi_decode_step: one token at one position) against the oracle's forward of the
+same token at the same position over the same KV regions, after a prefill of the prompt."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from quantized_transformer_prefill_amd import binding as B
+from tests.gpu_util import assert_f32_match, need_gpu, say
+from tests.test_forward_gpu import SENTINEL, TINY_Q2, TINY_Q3, compare_logits, load_pair
+
+pytestmark = pytest.mark.gpu
+
+
+def decode_tokens(cfg, n_steps):
+    """Token ids for the steps after the prompt (seeded, uniform like the prompt)."""
+    rng = np.random.default_rng(cfg.seed + 1000)
+    return rng.integers(0, cfg.vocab, size=n_steps).astype(np.int32)
+
+
+def prefill_then_decode(cfg, dev, n_steps, graph=False):
+    """Prefill the prompt on both sides, then n_steps decode steps at the following positions.
+    Returns per-step (gpu logits, oracle logits) and the final regions of both sides."""
+    m, w = load_pair(cfg, dev, max_tokens=cfg.prefix_tokens + cfg.n_tokens)
+    pre_ids, ids = synth.gen_token_ids(cfg)
+    pre_pos, pos = synth.positions_for(cfg)
+    kk, vv = oracle.new_kv_regions(cfg, cfg.n_ctx, fill=SENTINEL)
+    if cfg.prefix_tokens:
+        m.forward(pre_ids, pre_pos)
+        oracle.prefill_forward(cfg, w, pre_ids, pre_pos, cfg.n_ctx, kk, vv)
+    m.forward(ids, pos)
+    oracle.prefill_forward(cfg, w, ids, pos, cfg.n_ctx, kk, vv)
+    p0 = int(pos[-1]) + 1
+    toks = decode_tokens(cfg, n_steps)
+    steps = []
+    g = None
+    if graph:
+        torch.cuda.synchronize()  # the prefill above ran on the default stream
+        stream = torch.cuda.Stream()
+        torch.cuda.set_stream(stream)
+        g = m.graph(1)
+    try:
+        for i, tok in enumerate(toks):
+            p = p0 + i
+            say(f"decode {cfg.name} step {i} token {int(tok)} position {p}")
+            if graph:
+                got = g.launch([tok], [p]).cpu().numpy().copy()
+                _ = torch.ones(1000, device=dev).sum().item()   # unrelated eager work between replays
+            else:
+                got = m.decode(int(tok), p).cpu().numpy().copy()
+            want = oracle.prefill_forward(cfg, w, np.array([tok], np.int32), np.array([p], np.int32), cfg.n_ctx,
+                                          kk, vv)[0]
+            steps.append((got, want))
+    finally:
+        if g is not None:
+            g.close()
+            torch.cuda.set_stream(torch.cuda.default_stream())
+    torch.cuda.synchronize()
+    return m, steps, kk, vv, p0 + n_steps
+
+
+@pytest.mark.parametrize("cfg", [synth.LAYER1, TINY_Q3, TINY_Q2], ids=lambda c: c.name)
+def test_decode_matches_oracle(cfg):
+    """Head dims 64 and 128, QKV bias, per-head QK norm, tied and separate lm_heads, GQA 7:1, 4:1
+    and 4:1 with one KV head; several steps, each attending to the prompt and the earlier steps."""
+    dev = need_gpu()
+    m, steps, kk, vv, end = prefill_then_decode(cfg, dev, 4)
+    for i, (got, want) in enumerate(steps):
+        compare_logits(got, want, f"{cfg.name} step {i} logits")
+        assert_f32_match(got, want, max_ulp=64, max_frac_inexact=0.05, what=f"{cfg.name} step {i} logits ulp")
+    gk, gv = m.kv_k.cpu().numpy(), m.kv_v.cpu().numpy()
+    assert np.all(gk[:, end:] == SENTINEL) and np.all(gv[:, end:] == SENTINEL), "stray KV writes"
+    assert_f32_match(gk[:, :end], kk[:, :end], max_ulp=64, max_frac_inexact=0.05, what="K regions")
+    assert_f32_match(gv[:, :end], vv[:, :end], max_ulp=64, max_frac_inexact=0.05, what="V regions")
+
+
+def test_decode_graph_replays_at_new_positions():
+    """One captured decode step replayed at successive positions (the position is staged per launch)
+    computes what the eager steps compute."""
+    dev = need_gpu()
+    cfg = TINY_Q3
+    _, steps, _, _, _ = prefill_then_decode(cfg, dev, 5, graph=True)
+    for i, (got, want) in enumerate(steps):
+        compare_logits(got, want, f"graph step {i} logits")
+
+
+def test_decode_equals_prefill_of_one_token():
+    """mi_decode_step and mi_prefill_forward with one token are the same call (bit for bit), and a
+    decode step after a prefill equals the last row of a prefill of prompt + token."""
+    dev = need_gpu()
+    cfg = synth.LAYER1
+    m, _ = load_pair(cfg, dev)
+    _, ids = synth.gen_token_ids(cfg)
+    n = cfg.n_tokens
+    pos = np.arange(n, dtype=np.int32)
+    full = m.forward(ids, pos).cpu().numpy().copy()         # prompt of n tokens at once
+    m.kv_k.fill_(SENTINEL)
+    m.kv_v.fill_(SENTINEL)
+    m.forward(ids[:n - 1], pos[:n - 1])
+    a = m.decode(int(ids[n - 1]), n - 1).cpu().numpy().copy()
+    b = m.forward(ids[n - 1:], pos[n - 1:]).cpu().numpy().copy()
+    np.testing.assert_array_equal(a, b)
+    assert_f32_match(a, full, max_ulp=4, max_frac_inexact=0.01, what="decode vs one-shot prefill")
+
+
+def test_decode_argument_errors_leave_state_untouched():
+    dev = need_gpu()
+    cfg = synth.LAYER1
+    m, _ = load_pair(cfg, dev)
+    before = m.kv_k.cpu().numpy().copy()
+    with pytest.raises(B.MiError) as e:
+        m.decode(1, cfg.n_ctx)
+    assert e.value.code == B.MI_ERR_POSITION_RANGE
+    with pytest.raises(B.MiError) as e:
+        m.decode(cfg.vocab, 0)
+    assert e.value.code == B.MI_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(m.kv_k.cpu().numpy(), before)
+
+
+def test_headline_config_decode_matches_oracle():
+    """The 24-layer 0.5B-shaped model: the 512-token prompt, then 3 decode steps at 512..514."""
+    dev = need_gpu()
+    cfg = synth.QWEN2_0P5B
+    m, steps, kk, vv, end = prefill_then_decode(cfg, dev, 3)
+    for i, (got, want) in enumerate(steps):
+        compare_logits(got, want, f"{cfg.name} step {i} logits")
+    gk = m.kv_k.cpu().numpy()
+    d = np.linalg.norm(gk[:, :end] - kk[:, :end]) / np.linalg.norm(kk[:, :end])
+    say(f"  K regions rel-L2 {d:.3e}, identical {np.mean(gk[:, :end] == kk[:, :end]):.6f}")
+    assert d <= 1e-3 and np.all(gk[:, end:] == SENTINEL)
