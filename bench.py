@@ -43,6 +43,9 @@ def parse():
                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE pass")
     p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn the two counter passes of --traffic-run into profiles/" + TRAFFIC_FILE)
+    p.add_argument("--decode", action="store_true",
+                   help="time decode steps (one token per step, mi_decode_step via a captured graph) after "
+                        "the workload's prompt instead of the prefill; prints its own JSON line")
     p.add_argument("--workload", default=None,
                    help="model workload name (default: the 512-token 0.5B-shaped headline); the others "
                         "are reported for context: " + ", ".join(["layer1_896", "qwen2_0p5b_pp512",
@@ -104,6 +107,9 @@ def main():
     pre_pos, pos = synth.positions_for(cfg)
     if cfg.prefix_tokens:  # untimed: the KV rows of the earlier positions; each timed chunk call
         model.forward(pre_ids, pre_pos)  # rewrites the same chunk rows with the same values
+    if args.decode:
+        decode_bench(args, cfg, model, ids, pos, load_s)
+        return
 
     # eager calls (mi_prefill_forward), then the same forward captured once and replayed
     # (mi_prefill_graph_launch: validation, H2D of ids and positions, graph replay) -- the timed
@@ -200,6 +206,115 @@ def main():
         "load_s": round(load_s, 2),
     }
     print(json.dumps(line), flush=True)
+
+
+def decode_step_bytes(cfg, context: float) -> float:
+    """Algorithmic HBM bytes of one decode step: every Q8_0 weight once (codes + fp16 scales), the
+    K and V rows of `context` positions per layer, the new K/V rows, norm gains and biases."""
+    H, F, V = cfg.hidden, cfg.ffn, cfg.vocab
+    nq, nkv = cfg.n_head * cfg.head_dim, cfg.n_head_kv * cfg.head_dim
+    q8 = 34.0 / 32.0
+    per_layer = ((nq + 2 * nkv) * H + H * nq + 2 * F * H + H * F) * q8
+    per_layer += 2 * context * nkv * 4 + 2 * nkv * 4 + 2 * H * 4 + (nq + 2 * nkv) * 4 * cfg.qkv_bias
+    return cfg.n_layers * per_layer + V * H * q8 + H * 4
+
+
+def decode_bench(args, cfg, model, ids, pos, load_s):
+    """Decode steps after the prompt: the step (mi_prefill_graph_launch of a graph captured for one
+    token: validation, H2D of id and position, replay) at positions after the prompt, on one side
+    stream with HIP events; the eager mi_decode_step is timed too."""
+    import torch
+
+    model.forward(ids, pos)  # the prompt's KV rows (untimed)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cfg.seed + 1000)
+    n = args.warmup + args.steps
+    toks = rng.integers(0, cfg.vocab, size=2 * n).astype(np.int32)
+    p0 = int(pos[-1]) + 1
+    if p0 + 2 * n > cfg.n_ctx:
+        raise SystemExit(f"decode steps run past n_ctx {cfg.n_ctx}")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(args.warmup):
+            model.decode(int(toks[i]), p0 + i)
+        stream.synchronize()
+        e0.record(stream)
+        for i in range(args.warmup, n):
+            model.decode(int(toks[i]), p0 + i)
+        e1.record(stream)
+        stream.synchronize()
+        eager_ms = e0.elapsed_time(e1) / args.steps
+        graph = model.graph(1)
+        for i in range(n, n + args.warmup):
+            graph.launch(toks[i:i + 1], [p0 + i])
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n + args.warmup, 2 * n):
+            graph.launch(toks[i:i + 1], [p0 + i])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        graph.close()
+    context = p0 + n + args.warmup + args.steps / 2.0  # mean attended positions over the timed steps
+    nbytes = decode_step_bytes(cfg, context)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    cpu = None if args.no_cpu_baseline else cpu_baseline_decode(cfg)
+    line = {
+        "metric": "decode tokens/sec (one token per step after the prompt), 1 GPU",
+        "value": round(1e3 / ms, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "q8_0 (sdot4 int8 dot products), f64 accumulation, f32 activations",
+        "data": "synthetic (seeded N(0,0.02) weights quantized to Q8_0, uniform token ids)",
+        "config": {"workload": cfg.name + "_decode", "description": "decode steps after the prompt of " + cfg.description,
+                   "prompt_tokens": cfg.n_tokens, "first_position": p0, "n_ctx": cfg.n_ctx,
+                   "parallelism": "single GPU"},
+        "eager_ms_per_step": round(eager_ms, 4),
+        "roofline": {"bound": "hbm", "kernel": "whole decode step (matrix-vector kernels, attention, lm_head)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_step": round(nbytes), "mean_context": context},
+        "cpu_baseline": cpu,
+        "load_s": round(load_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_decode(cfg, min_seconds: float = 10.0, max_reps: int = 64):
+    """The oracle on decode steps of the same model after the same prompt (the prompt's prefill is
+    untimed); weights quantized beforehand."""
+    import threadpoolctl
+    import torch
+
+    import oracle
+    import synth
+
+    q8 = [n for n, s, k in synth.tensor_specs(cfg) if k == "q8"]
+    dev = torch.device("cuda:0")
+    arrays = {n: t.cpu().numpy() for n, k, t in synth.iter_tensors(cfg, device=dev)}
+    w = oracle.weights_from_arrays(arrays, q8)
+    for n in q8:
+        w[n]
+        del arrays[n]
+    _, ids = synth.gen_token_ids(cfg)
+    _, pos = synth.positions_for(cfg)
+    kk, vv = oracle.new_kv_regions(cfg, cfg.n_ctx)
+    oracle.prefill_forward(cfg, w, ids, pos, cfg.n_ctx, kk, vv)
+    threads = sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info() if i.get("internal_api") == "openblas")
+    rng = np.random.default_rng(cfg.seed + 2000)
+    p0 = int(pos[-1]) + 1
+    reps, t = 0, 0.0
+    while reps < max_reps and (reps == 0 or t < min_seconds) and p0 + reps < cfg.n_ctx:
+        tok = np.array([rng.integers(0, cfg.vocab)], np.int32)
+        t0 = time.time()
+        oracle.prefill_forward(cfg, w, tok, np.array([p0 + reps], np.int32), cfg.n_ctx, kk, vv)
+        t += time.time() - t0
+        reps += 1
+    return {"value": round(reps / t, 2), "unit": "tokens/s", "cores": threads or os.cpu_count(), "kind": "oracle",
+            "sample": f"{reps} decode steps (one token each, all {cfg.n_layers} layers and the lm_head) after the "
+                      f"{cfg.n_tokens}-token prompt ({t:.1f} s of CPU time; prompt prefill and weight "
+                      f"quantization untimed)",
+            "host_cpus": os.cpu_count()}
 
 
 def dominant_kernel(cfg, dev, w_gate_up=None):
