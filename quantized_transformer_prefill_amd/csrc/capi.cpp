@@ -296,8 +296,9 @@ static int stage_tokens(const Ws& w, const int32_t* ids, const int32_t* pos, int
 
 // The decode step: one token through the same layers and regions, with the one-row kernels
 // (decode.hip).  Per layer: Q|K|V matrix-vector product with the attention RMSNorm in its prologue
-// and bias, QK norm, RoPE and the K/V store in its epilogue; single-query attention over the ranges
-// of keys 0..pos, merged into a Q8_0 row; output projection + residual; gate|up with the ffn
+// and bias, QK norm, RoPE and the K/V store in its epilogue; single-query attention over ranges of
+// keys 0..pos; output projection (the ranges merged into a Q8_0 row in its prologue) + residual;
+// gate|up with the ffn
 // RMSNorm in its prologue and SwiGLU + Q8_0 in its epilogue; down projection + residual.  Then the
 // lm_head with the final RMSNorm in its prologue.
 static int enqueue_decode(const mi_model* md, const Ws& w, int32_t n_ctx, const mi_kv_regions* kv, float* logits_out,
@@ -319,10 +320,12 @@ static int enqueue_decode(const mi_model* md, const Ws& w, int32_t n_ctx, const 
     g.qkv.q_norm = hp.qk_norm ? L.q_norm : nullptr; g.qkv.k_norm = hp.qk_norm ? L.k_norm : nullptr; g.qkv.eps = eps;
     if ((rc = launch_gemv_q8(g, s))) return rc;
     if ((rc = launch_attn_decode(w.qkv, kv->k[l], kv->v[l], w.pos, n_ctx, hp.n_head, hp.n_head_kv, hp.head_dim,
-                                 w.attn_part, w.xq, w.xs, s)))
+                                 w.attn_part, s)))
       return rc;
-    GemvArgs go{};
-    go.xq = w.xq; go.xs = w.xs; go.k = nq;
+    GemvArgs go{};  // input: the attention ranges merged in the prologue
+    go.attn.part = w.attn_part; go.attn.pos = w.pos; go.attn.n_head = hp.n_head; go.attn.head_dim = hp.head_dim;
+    go.attn.n_range = attn_decode_ranges(n_ctx, &go.attn.keys_per_range);
+    go.k = nq;
     go.w_codes = L.wo.codes; go.w_scales = L.wo.scales; go.n = H;
     go.residual = w.h; go.out = w.h; go.epi = GV_RES;
     if ((rc = launch_gemv_q8(go, s))) return rc;

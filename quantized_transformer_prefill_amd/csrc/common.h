@@ -231,6 +231,12 @@ struct GemvQkv {
   const float* k_norm;
   float eps;
 };
+// the output projection's input: the per-range attention partial states of k_attn_decode
+struct GemvAttnIn {
+  const double* part;      // [n_head][n_range][head_dim + 2], or null
+  const int32_t* pos;      // device [1]: keys 0..*pos
+  int n_head, head_dim, n_range, keys_per_range;
+};
 struct GemvArgs {
   // input row: with x non-null, RMSNorm(x; gamma, eps) + Q8_0 inside the kernel; else xq/xs
   const float* x; const float* gamma; float eps;
@@ -242,14 +248,14 @@ struct GemvArgs {
   int8_t* q_codes; uint16_t* q_scales;                       // GV_SWIGLU: Q8_0 [n/2]
   int epi;
   GemvQkv qkv;
+  GemvAttnIn attn;         // GV_RES only: with attn.part non-null the input row is the merged attention output
 };
 int launch_gemv_q8(const GemvArgs& g, hipStream_t s);
 // attention of one query per head over keys 0..*pos_dev: partial states per key range in `part`
-// (n_head * AD_MAX_RANGES * (head_dim + 2) f64), then the merged rows as Q8_0 [n_head*head_dim]
+// (n_head * n_range * (head_dim + 2) f64, n_range <= AD_MAX_RANGES), merged by the output projection
 constexpr int AD_MAX_RANGES = 16;
 int attn_decode_ranges(int n_ctx, int* keys_per_range);
 int launch_attn_decode(const float* q, const float* k_region, const float* v_region, const int32_t* pos_dev,
-                       int n_ctx, int n_head, int n_head_kv, int head_dim, double* part, int8_t* q_codes,
-                       uint16_t* q_scales, hipStream_t s);
+                       int n_ctx, int n_head, int n_head_kv, int head_dim, double* part, hipStream_t s);
 
 }  // namespace mi

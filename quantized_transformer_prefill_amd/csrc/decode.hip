@@ -7,20 +7,23 @@
 //    chunks (half a block) of every row, sdot4 gives the integer half-block sums, lane pairs
 //    combine them to the block sum, and the exact f64 epilogue (block sum times dw, times dx,
 //    one rounding per block) accumulates per lane; the lanes' partial sums then reduce in f64.
-//  * The activation row is staged in LDS as codes + f64 scales.  With NORM the workgroup builds
-//    it itself from the f32 residual stream: RMSNorm in f64, one rounding to f32, Q8_0 -- the
-//    same arithmetic as the prefill's k_rmsnorm_quant -- so the decode step has no separate
-//    normalization kernels.
+//  * The activation row is staged in LDS as codes + f64 scales.  The workgroup can build it
+//    itself: from the f32 residual stream (RMSNorm in f64, one rounding to f32, Q8_0 -- the same
+//    arithmetic as the prefill's k_rmsnorm_quant), or, for the output projection, by merging the
+//    attention's per-range partial states -- so the decode step has no normalization or merge
+//    kernels.  The weight loads of the first rows go out before this prologue.
 //  * Epilogues: residual add (output projection, down projection), plain f32 (lm_head), the
 //    attention inputs (bias, per-head QK RMSNorm, NeoX RoPE, K/V rows stored at the position; a
 //    workgroup holds one head), SwiGLU + Q8_0 (a workgroup holds one interleaved group of 32
 //    gate and 32 up rows, i.e. one Q8_0 block of the SwiGLU output).
 //
-// k_attn_decode + k_attn_decode_merge: the query's keys 0..pos are split into fixed ranges (the
-// grid depends only on n_ctx, so the launch can be captured once and replayed for any position);
-// each workgroup computes the partial softmax state (max, sum, unnormalized output) of one head
-// over one range in f64, and the merge combines the ranges in order, normalizes, and writes the
-// head's output row as Q8_0 (the input of the output projection).
+// k_attn_decode: the query's keys 0..pos are split into fixed ranges (the grid depends only on
+// n_ctx, so the launch can be captured once and replayed for any position); each workgroup
+// computes the partial softmax state (max, sum, unnormalized output) of one head over one range in
+// f64.  The output projection's prologue combines the ranges in order, normalizes, and quantizes
+// each head's output row to Q8_0.
+#include <algorithm>
+
 #include "common.h"
 
 namespace mi {
@@ -41,7 +44,16 @@ __device__ __forceinline__ double wave_max_d(double v) {
   return v;
 }
 
-template <int RPW, int EPI, bool NORM>
+// Prologue modes: the activation row comes as Q8_0 (GV_IN_Q8), is built from the f32 residual
+// stream by RMSNorm + Q8_0 (GV_IN_NORM), or is the attention output merged from the per-range
+// partial states of k_attn_decode, normalized and quantized per head (GV_IN_ATTN).
+enum { GV_IN_Q8 = 0, GV_IN_NORM = 1, GV_IN_ATTN = 2 };
+
+template <int HD>
+__device__ __forceinline__ void attn_merge_head(const double* __restrict__ part, int n_range, int n_ne, int h, int lane,
+                                                const double* exp_tab, int8_t* a_codes, double* a_d);
+
+template <int RPW, int EPI, int PRO>
 __global__ void __launch_bounds__(GV_THREADS) k_gemv_q8(const float* __restrict__ x, const float* __restrict__ gamma,
                                                        float eps, const int8_t* __restrict__ xq,
                                                        const uint16_t* __restrict__ xs, int K,
@@ -49,28 +61,69 @@ __global__ void __launch_bounds__(GV_THREADS) k_gemv_q8(const float* __restrict_
                                                        const uint16_t* __restrict__ w_scales, int N,
                                                        const float* __restrict__ bias, const float* residual,
                                                        float* out, int8_t* __restrict__ q_codes,
-                                                       uint16_t* __restrict__ q_scales, GemvQkv qe) {
-  constexpr int RWG = RPW * GV_WAVES;  // weight rows per workgroup
+                                                       uint16_t* __restrict__ q_scales, GemvQkv qe, GemvAttnIn ai) {
+  constexpr int RWG = RPW * GV_WAVES;  // weight rows per group
+  constexpr int B = (RPW >= 8 || EPI == GV_QKV || EPI == GV_SWIGLU) ? 1 : (RPW >= 4 ? 2 : 4);  // 64-chunk steps of K in flight together
   extern __shared__ __align__(16) unsigned char gv_lds[];
   const int KB = K / QK;
   int8_t* a_codes = reinterpret_cast<int8_t*>(gv_lds);                           // [K]
   double* a_d = reinterpret_cast<double*>(gv_lds + ((K + 15) & ~15));             // [KB]
   float* y = reinterpret_cast<float*>(a_d + KB);                                   // [RWG]
   double* red = reinterpret_cast<double*>(y + RWG + (RWG & 1));                    // [GV_WAVES + 1]
-  __shared__ double exp_tab[EPI == GV_SWIGLU ? 64 : 1];
+  __shared__ double exp_tab[(EPI == GV_SWIGLU || PRO == GV_IN_ATTN) ? 64 : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if constexpr (EPI == GV_SWIGLU) exp2_table_fill(exp_tab, tid);
+  const int nchunk = K / 16;
+  const int n_groups = (N + RWG - 1) / RWG;
+
+  // ---- requests that do not depend on the activation row go out first
+  int64_t qpos = 0;
+  if constexpr (EPI == GV_QKV) qpos = *qe.pos;
+  constexpr int RS = RPW < 4 ? RPW : 4;  // rows of a wave whose loads are in flight together
+  v4i wv[B][RS];
+  uint16_t sv[B][RS];
+  float bias_r[RPW];
+  // 32-bit offsets from the uniform matrix bases (rows * K < 2^31 is checked by the launcher);
+  // rows ib..ib+RS-1 of the wave's RPW
+  auto load_batch = [&](int grp, int c0, int ib) {
+    const int r0 = grp * RWG + wave * RPW + ib;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int ch = c0 + 64 * b + lane;
+#pragma unroll
+      for (int i = 0; i < RS; ++i) {
+        const uint32_t r = (uint32_t)min(r0 + i, N - 1);  // rows past N re-read the last row; never stored
+        if (ch < nchunk) {
+          wv[b][i] = *reinterpret_cast<const v4i*>(w_codes + (r * (uint32_t)K + (uint32_t)ch * 16u));
+          sv[b][i] = w_scales[r * (uint32_t)KB + (uint32_t)(ch >> 1)];
+        }
+      }
+    }
+  };
+  load_batch(blockIdx.x, 0, 0);
+  if constexpr (EPI == GV_QKV) {
+    const int r0 = blockIdx.x * RWG + wave * RPW;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) bias_r[i] = bias ? bias[min(r0 + i, N - 1)] : 0.0f;
+  }
+  if constexpr (EPI == GV_SWIGLU || PRO == GV_IN_ATTN) exp2_table_fill(exp_tab, tid);
 
   // ---- the activation row -> LDS (codes, f64 scales)
   const int nvec = K / 4;
-  if constexpr (NORM) {
-    double ss = 0.0;
-    for (int c4 = tid; c4 < nvec; c4 += GV_THREADS) {
-      const float4 v = reinterpret_cast<const float4*>(x)[c4];
-      const double a = v.x, b = v.y, c = v.z, d = v.w;
-      ss += a * a + b * b + c * c + d * d;
+  if constexpr (PRO == GV_IN_ATTN) {  // wave w merges heads w, w + 16, ...
+    __syncthreads();  // exp_tab
+    const int n_ne = (*ai.pos + 1 + ai.keys_per_range - 1) / ai.keys_per_range;
+    for (int h = wave; h < ai.n_head; h += GV_WAVES) {
+      if (ai.head_dim == 64) attn_merge_head<64>(ai.part, ai.n_range, n_ne, h, lane, exp_tab, a_codes, a_d);
+      else attn_merge_head<128>(ai.part, ai.n_range, n_ne, h, lane, exp_tab, a_codes, a_d);
     }
-    ss = wave_sum_d(ss);
+  } else if constexpr (PRO == GV_IN_NORM) {  // K <= GV_THREADS * 4: one float4 of x per thread, kept across both passes
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f), g = v;
+    if (tid < nvec) {
+      v = reinterpret_cast<const float4*>(x)[tid];
+      g = reinterpret_cast<const float4*>(gamma)[tid];
+    }
+    const double a = v.x, b = v.y, c = v.z, d = v.w;
+    double ss = wave_sum_d(a * a + b * b + c * c + d * d);
     if (lane == 0) red[wave] = ss;
     __syncthreads();
     if (wave == 0) {
@@ -80,19 +133,17 @@ __global__ void __launch_bounds__(GV_THREADS) k_gemv_q8(const float* __restrict_
     }
     __syncthreads();
     const double inv_rms = recip_f64(sqrt(red[GV_WAVES] / (double)K + (double)eps));
-    // groups of 8 lanes cover one block; all 8 share the loop trip count (K is a multiple of 32)
-    for (int c4 = tid; c4 < nvec; c4 += GV_THREADS) {
-      const float4 v = reinterpret_cast<const float4*>(x)[c4];
-      const float4 g = reinterpret_cast<const float4*>(gamma)[c4];
+    // groups of 8 lanes cover one block; a group is entirely inside or outside [0, nvec)
+    if (tid < nvec) {
       float4 o;
       o.x = (float)((double)v.x * inv_rms * (double)g.x);
       o.y = (float)((double)v.y * inv_rms * (double)g.y);
       o.z = (float)((double)v.z * inv_rms * (double)g.z);
       o.w = (float)((double)v.w * inv_rms * (double)g.w);
-      float d;
-      const uint32_t q = q8_block_quant4(o, d);
-      reinterpret_cast<uint32_t*>(a_codes)[c4] = q;
-      if ((c4 & 7) == 0) a_d[c4 / 8] = (double)f16_bits_to_f32(f32_to_f16_bits(d));
+      float dq;
+      const uint32_t qv = q8_block_quant4(o, dq);
+      reinterpret_cast<uint32_t*>(a_codes)[tid] = qv;
+      if ((tid & 7) == 0) a_d[tid / 8] = (double)f16_bits_to_f32(f32_to_f16_bits(dq));
     }
   } else {
     for (int c4 = tid; c4 < nvec; c4 += GV_THREADS)
@@ -101,160 +152,177 @@ __global__ void __launch_bounds__(GV_THREADS) k_gemv_q8(const float* __restrict_
   }
   __syncthreads();
 
-  // ---- RPW rows per wave, all of their loads in flight together
-  const int nchunk = K / 16;
-  const int r0 = blockIdx.x * RWG + wave * RPW;
-  const int8_t* wrow[RPW];
-  const uint16_t* srow[RPW];
+  for (int grp = blockIdx.x; grp < n_groups; grp += gridDim.x) {
+    const int r0 = grp * RWG + wave * RPW;
+    double acc[RPW];
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int r = min(r0 + i, N - 1);  // rows past N re-read the last row; never stored
-    wrow[i] = w_codes + (int64_t)r * K;
-    srow[i] = w_scales + (int64_t)r * KB;
-  }
-  double acc[RPW];
+    for (int i = 0; i < RPW; ++i) acc[i] = 0.0;
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) acc[i] = 0.0;
-  for (int c0 = 0; c0 < nchunk; c0 += 64) {
-    const int ch = c0 + lane;
-    const bool on = ch < nchunk;
-    v4i xa = {0, 0, 0, 0};
-    double da = 0.0;
-    int isum[RPW];
-    double dw[RPW];
-    if (on) {
-      xa = *reinterpret_cast<const v4i*>(a_codes + ch * 16);
-      da = a_d[ch >> 1];
-    }
+    for (int ib = 0; ib < RPW; ib += RS) {
+    if (ib || grp != (int)blockIdx.x) load_batch(grp, 0, ib);
+#pragma unroll 1
+    for (int c0 = 0; c0 < nchunk; c0 += 64 * B) {
+      if (c0) load_batch(grp, c0, ib);
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      isum[i] = 0;
-      dw[i] = 0.0;
-      if (on) {
-        const v4i wv = *reinterpret_cast<const v4i*>(wrow[i] + ch * 16);
-        isum[i] = __builtin_amdgcn_sdot4(xa[0], wv[0], 0, false);
-        isum[i] = __builtin_amdgcn_sdot4(xa[1], wv[1], isum[i], false);
-        isum[i] = __builtin_amdgcn_sdot4(xa[2], wv[2], isum[i], false);
-        isum[i] = __builtin_amdgcn_sdot4(xa[3], wv[3], isum[i], false);
-        dw[i] = (double)f16_bits_to_f32(srow[i][ch >> 1]);
+      for (int b = 0; b < B; ++b) {
+        const int ch = c0 + 64 * b + lane;
+        const bool on = ch < nchunk;
+        v4i xa = {0, 0, 0, 0};
+        double da = 0.0;
+        if (on) {
+          xa = *reinterpret_cast<const v4i*>(a_codes + ch * 16);
+          da = a_d[ch >> 1];
+        }
+#pragma unroll
+        for (int i = 0; i < RS; ++i) {
+          int isum = 0;
+          double dw = 0.0;
+          if (on) {
+            isum = __builtin_amdgcn_sdot4(xa[0], wv[b][i][0], 0, false);
+            isum = __builtin_amdgcn_sdot4(xa[1], wv[b][i][1], isum, false);
+            isum = __builtin_amdgcn_sdot4(xa[2], wv[b][i][2], isum, false);
+            isum = __builtin_amdgcn_sdot4(xa[3], wv[b][i][3], isum, false);
+            dw = (double)f16_bits_to_f32(sv[b][i]);
+          }
+          isum += __shfl_xor(isum, 1);  // both lanes of the pair hold the block sum
+          if (on && (lane & 1) == 0) acc[ib + i] = fma((double)isum * dw, da, acc[ib + i]);  // I*dw exact
+        }
       }
     }
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      isum[i] += __shfl_xor(isum[i], 1);  // both lanes of the pair hold the block sum
-      if (on && (lane & 1) == 0) acc[i] = fma((double)isum[i] * dw[i], da, acc[i]);  // I*dw exact
     }
-  }
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) acc[i] = wave_sum_d(acc[i]);
+    for (int i = 0; i < RPW; ++i) acc[i] = wave_sum_d(acc[i]);
 
-  if constexpr (EPI == GV_RES || EPI == GV_F32) {
-    if (lane == 0) {
+    if constexpr (EPI == GV_RES || EPI == GV_F32) {
+      if (lane == 0) {
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) {
-        const int r = r0 + i;
-        if (r < N) {
-          float v = (float)acc[i];
-          if (EPI == GV_RES) v = residual[r] + v;
-          out[r] = v;
-        }
-      }
-    }
-    return;
-  } else {
-    if (lane == 0) {
-#pragma unroll
-      for (int i = 0; i < RPW; ++i) {
-        double v = acc[i];
-        if (EPI == GV_QKV && bias) v += (double)bias[min(r0 + i, N - 1)];
-        y[wave * RPW + i] = (float)v;
-      }
-    }
-    __syncthreads();
-    if constexpr (EPI == GV_SWIGLU) {
-      // rows 64p..64p+31 are gate rows 32p.., rows 64p+32..64p+63 up rows 32p..: one Q8_0 block
-      if (tid < 8) {
-        float4 s;
-        s.x = swiglu_f32(y[4 * tid + 0], y[32 + 4 * tid + 0], exp_tab);
-        s.y = swiglu_f32(y[4 * tid + 1], y[32 + 4 * tid + 1], exp_tab);
-        s.z = swiglu_f32(y[4 * tid + 2], y[32 + 4 * tid + 2], exp_tab);
-        s.w = swiglu_f32(y[4 * tid + 3], y[32 + 4 * tid + 3], exp_tab);
-        float d;
-        const uint32_t q = q8_block_quant4(s, d);
-        reinterpret_cast<uint32_t*>(q_codes + (int64_t)blockIdx.x * QK)[tid] = q;
-        if (tid == 0) q_scales[blockIdx.x] = f32_to_f16_bits(d);
-      }
-    } else {  // GV_QKV: this workgroup's rows are one head of Q, K or V
-      const int hd = qe.head_dim, half = hd / 2;
-      const int c0 = blockIdx.x * RWG;
-      const int64_t p = *qe.pos;
-      if (c0 >= qe.n_q + qe.n_kv) {  // V head: stored as is
-        for (int i = tid; i < hd; i += GV_THREADS) qe.v_region[p * qe.n_kv + (c0 - qe.n_q - qe.n_kv) + i] = y[i];
-        return;
-      }
-      const bool isq = c0 < qe.n_q;
-      const float* gam = isq ? qe.q_norm : qe.k_norm;
-      if (gam) {  // per-head RMSNorm in f64, one rounding (wave 0)
-        if (wave == 0) {
-          double ss = 0.0;
-          for (int i = lane; i < hd; i += 64) ss += (double)y[i] * (double)y[i];
-          ss = wave_sum_d(ss);
-          const double ir = recip_f64(sqrt(ss / (double)hd + (double)qe.eps));
-          float t[2];
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const int i = lane + 64 * k;
-            if (i < hd) t[k] = (float)((double)y[i] * ir * (double)gam[i]);
-          }
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const int i = lane + 64 * k;
-            if (i < hd) y[i] = t[k];
+        for (int i = 0; i < RPW; ++i) {
+          const int r = r0 + i;
+          if (r < N) {
+            float v = (float)acc[i];
+            if (EPI == GV_RES) v = residual[r] + v;
+            out[r] = v;
           }
         }
-        __syncthreads();
       }
-      for (int i = tid; i < half; i += GV_THREADS) {
-        const float a = y[i], b = y[i + half];
-        const double2 cs = reinterpret_cast<const double2*>(qe.rope)[p * half + i];
-        const float o0 = (float)((double)a * cs.x - (double)b * cs.y);
-        const float o1 = (float)((double)a * cs.y + (double)b * cs.x);
-        float* dst = isq ? qe.q_out + c0 : qe.k_region + p * qe.n_kv + (c0 - qe.n_q);
-        dst[i] = o0;
-        dst[i + half] = o1;
+    } else {
+      if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+          double v = acc[i];
+          if (EPI == GV_QKV) v += (double)bias_r[i];
+          y[wave * RPW + i] = (float)v;
+        }
       }
+      __syncthreads();
+      if constexpr (EPI == GV_SWIGLU) {
+        // rows 64p..64p+31 are gate rows 32p.., rows 64p+32..64p+63 up rows 32p..: one Q8_0 block
+        if (tid < 8) {
+          float4 sw;
+          sw.x = swiglu_f32(y[4 * tid + 0], y[32 + 4 * tid + 0], exp_tab);
+          sw.y = swiglu_f32(y[4 * tid + 1], y[32 + 4 * tid + 1], exp_tab);
+          sw.z = swiglu_f32(y[4 * tid + 2], y[32 + 4 * tid + 2], exp_tab);
+          sw.w = swiglu_f32(y[4 * tid + 3], y[32 + 4 * tid + 3], exp_tab);
+          float d;
+          const uint32_t q = q8_block_quant4(sw, d);
+          reinterpret_cast<uint32_t*>(q_codes + (int64_t)grp * QK)[tid] = q;
+          if (tid == 0) q_scales[grp] = f32_to_f16_bits(d);
+        }
+      } else {  // GV_QKV: this group's rows are one head of Q, K or V (one group per workgroup)
+        const int hd = qe.head_dim, half = hd / 2;
+        const int c0 = grp * RWG;
+        if (c0 >= qe.n_q + qe.n_kv) {  // V head: stored as is
+          for (int i = tid; i < hd; i += GV_THREADS) qe.v_region[qpos * qe.n_kv + (c0 - qe.n_q - qe.n_kv) + i] = y[i];
+        } else {
+          const bool isq = c0 < qe.n_q;
+          const float* gam = isq ? qe.q_norm : qe.k_norm;
+          if (gam) {  // per-head RMSNorm in f64, one rounding (wave 0)
+            if (wave == 0) {
+              double ss = 0.0;
+              for (int i = lane; i < hd; i += 64) ss += (double)y[i] * (double)y[i];
+              ss = wave_sum_d(ss);
+              const double ir = recip_f64(sqrt(ss / (double)hd + (double)qe.eps));
+              float t[2];
+#pragma unroll
+              for (int k = 0; k < 2; ++k) {
+                const int i = lane + 64 * k;
+                if (i < hd) t[k] = (float)((double)y[i] * ir * (double)gam[i]);
+              }
+#pragma unroll
+              for (int k = 0; k < 2; ++k) {
+                const int i = lane + 64 * k;
+                if (i < hd) y[i] = t[k];
+              }
+            }
+            __syncthreads();
+          }
+          for (int i = tid; i < half; i += GV_THREADS) {
+            const float a = y[i], b = y[i + half];
+            const double2 cs = reinterpret_cast<const double2*>(qe.rope)[qpos * half + i];
+            const float o0 = (float)((double)a * cs.x - (double)b * cs.y);
+            const float o1 = (float)((double)a * cs.y + (double)b * cs.x);
+            float* dst = isq ? qe.q_out + c0 : qe.k_region + qpos * qe.n_kv + (c0 - qe.n_q);
+            dst[i] = o0;
+            dst[i + half] = o1;
+          }
+        }
+      }
+      __syncthreads();  // y is rewritten by the next group
     }
   }
 }
 
 int launch_gemv_q8(const GemvArgs& g, hipStream_t s) {
   const bool norm = g.x != nullptr;
+  if (g.attn.part) {  // the output projection: its input is the merged attention row
+    if (g.epi != GV_RES || norm || g.k != g.attn.n_head * g.attn.head_dim)
+      return set_error(MI_ERR_INVALID_ARG, "gemv: attention-merge input needs the residual epilogue");
+  }
   const int KB = g.k / QK;
   const size_t lds = (size_t)((g.k + 15) & ~15) + sizeof(double) * KB + sizeof(float) * 130 +
                      sizeof(double) * (GV_WAVES + 1);
-  if (g.k % QK || g.k <= 0 || lds > 64 * 1024)
-    return set_error(MI_ERR_UNSUPPORTED, "gemv: K %d (multiple of 32, LDS %zu bytes)", g.k, lds);
+  if (g.k % QK || g.k <= 0 || lds > 64 * 1024 || ((norm || g.attn.part) && g.k > GV_THREADS * 4) ||
+      (int64_t)g.n * g.k >= ((int64_t)1 << 31))
+    return set_error(MI_ERR_UNSUPPORTED, "gemv: K %d (multiple of 32, LDS %zu bytes, <= %d with the norm)", g.k, lds,
+                     GV_THREADS * 4);
   GemvQkv qe = g.qkv;
-#define GV_LAUNCH(RPW, EPI, NORM)                                                                        \
-  hipLaunchKernelGGL((k_gemv_q8<RPW, EPI, NORM>), dim3((unsigned)((g.n + RPW * GV_WAVES - 1) / (RPW * GV_WAVES))), \
-                     dim3(GV_THREADS), lds, s, g.x, g.gamma, g.eps, g.xq, g.xs, g.k, g.w_codes, g.w_scales, g.n,  \
-                     g.bias, g.residual, g.out, g.q_codes, g.q_scales, qe)
+  // enough workgroups to keep every CU busy, looping over row groups beyond that
+  const int max_wg = 2 * 256;
+  auto grid = [&](int rwg) { return dim3((unsigned)std::min((g.n + rwg - 1) / rwg, max_wg)); };
+#define GV_LAUNCH(RPW, EPI, NORM)                                                                          \
+  hipLaunchKernelGGL((k_gemv_q8<RPW, EPI, NORM>), grid(RPW * GV_WAVES), dim3(GV_THREADS), lds, s, g.x, g.gamma, \
+                     g.eps, g.xq, g.xs, g.k, g.w_codes, g.w_scales, g.n, g.bias, g.residual, g.out, g.q_codes,     \
+                     g.q_scales, qe, g.attn)
   switch (g.epi) {
     case GV_RES:
-      if (norm) GV_LAUNCH(4, GV_RES, true); else GV_LAUNCH(4, GV_RES, false);
+    case GV_F32: {
+      // one row per wave while that gives fewer groups than CUs x 2, else four
+      const bool small = g.n <= 16 * max_wg;
+      if (g.epi == GV_RES) {
+        if (g.attn.part) {
+          if (small) GV_LAUNCH(1, GV_RES, GV_IN_ATTN); else GV_LAUNCH(4, GV_RES, GV_IN_ATTN);
+        } else if (small) {
+          if (norm) GV_LAUNCH(1, GV_RES, GV_IN_NORM); else GV_LAUNCH(1, GV_RES, GV_IN_Q8);
+        } else {
+          if (norm) GV_LAUNCH(4, GV_RES, GV_IN_NORM); else GV_LAUNCH(4, GV_RES, GV_IN_Q8);
+        }
+      } else {
+        if (small) { if (norm) GV_LAUNCH(1, GV_F32, GV_IN_NORM); else GV_LAUNCH(1, GV_F32, GV_IN_Q8); }
+        else { if (norm) GV_LAUNCH(4, GV_F32, GV_IN_NORM); else GV_LAUNCH(4, GV_F32, GV_IN_Q8); }
+      }
       break;
-    case GV_F32:
-      if (norm) GV_LAUNCH(4, GV_F32, true); else GV_LAUNCH(4, GV_F32, false);
-      break;
+    }
     case GV_SWIGLU:
       if (g.n % 64) return set_error(MI_ERR_UNSUPPORTED, "gemv: SwiGLU rows %d not a multiple of 64", g.n);
-      if (norm) GV_LAUNCH(4, GV_SWIGLU, true); else GV_LAUNCH(4, GV_SWIGLU, false);
+      if (norm) GV_LAUNCH(4, GV_SWIGLU, GV_IN_NORM); else GV_LAUNCH(4, GV_SWIGLU, GV_IN_Q8);
       break;
     case GV_QKV:
+      if (g.n / (qe.head_dim > 0 ? qe.head_dim : 1) > max_wg)
+        return set_error(MI_ERR_UNSUPPORTED, "gemv: more than %d heads", max_wg);
       if (qe.head_dim == 64 && g.n % 64 == 0) {
-        if (norm) GV_LAUNCH(4, GV_QKV, true); else GV_LAUNCH(4, GV_QKV, false);
+        if (norm) GV_LAUNCH(4, GV_QKV, GV_IN_NORM); else GV_LAUNCH(4, GV_QKV, GV_IN_Q8);
       } else if (qe.head_dim == 128 && g.n % 128 == 0) {
-        if (norm) GV_LAUNCH(8, GV_QKV, true); else GV_LAUNCH(8, GV_QKV, false);
+        if (norm) GV_LAUNCH(8, GV_QKV, GV_IN_NORM); else GV_LAUNCH(8, GV_QKV, GV_IN_Q8);
       } else {
         return set_error(MI_ERR_UNSUPPORTED, "gemv: attention inputs need head_dim 64 or 128 (got %d)", qe.head_dim);
       }
@@ -268,11 +336,12 @@ int launch_gemv_q8(const GemvArgs& g, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- single-query attention
-constexpr int AD_THREADS = 256;  // 4 waves, 64 keys each per range tile
+constexpr int AD_THREADS = 256;  // 4 waves; a wave takes 64 keys of its range per step
 
-// Partial state of (head h, range r): part[((h * n_range + r) * (HD + 2))] = m, l, o[HD] (f64).
-// m = max of the range's scores (-1e300 for an empty range), l = sum of e^(s - m), o = sum of
-// e^(s - m) v.  Scores s = (q * 1/sqrt(hd)) . k in f64, as in the prefill kernel.
+// Keys 0..pos of head h are split into ranges of keys_per_range; workgroup (h, r) takes range r
+// and writes its partial state to part[(h * n_range + r) * (HD + 2)] = m, l, o[HD] (f64): m the
+// range's largest score, l = sum e^(s - m), o = sum e^(s - m) v, with s = (q * 1/sqrt(hd)) . k as
+// in the prefill kernel.  Ranges past pos write nothing.  The output projection merges the ranges.
 template <int HD>
 __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restrict__ q,
                                                             const float* __restrict__ k_region,
@@ -280,7 +349,8 @@ __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restr
                                                             const int32_t* __restrict__ pos_dev, int n_head,
                                                             int n_head_kv, int keys_per_range,
                                                             double* __restrict__ part) {
-  constexpr int DPL = HD / 64;  // output dims per lane
+  constexpr int DPL = HD / 64;   // output dims per lane
+  constexpr bool V_EARLY = HD == 64;  // V values requested with the K rows (registers allow it)
   __shared__ double qs[HD];
   __shared__ double pw[AD_THREADS / 64][64];
   __shared__ double wst[AD_THREADS / 64][HD + 2];
@@ -291,33 +361,44 @@ __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restr
   const int n_kv = n_head_kv * HD;
   const int n_keys = *pos_dev + 1;
   const int j0 = r * keys_per_range, j1 = min(j0 + keys_per_range, n_keys);
-  double* out = part + ((int64_t)h * n_range + r) * (HD + 2);
-  if (j0 >= j1) {  // empty range (uniform for the workgroup)
-    for (int i = tid; i < HD + 2; i += AD_THREADS) out[i] = i == 0 ? -1e300 : 0.0;
-    return;
-  }
+  if (j0 >= j1) return;  // uniform for the workgroup
   exp2_table_fill(exp_tab, tid);
   const double scale = 1.0 / sqrt((double)HD);
-  for (int i = tid; i < HD; i += AD_THREADS) qs[i] = (double)q[h * HD + i] * scale;
-  __syncthreads();
   double m_w = -1e300, l_w = 0.0, o_w[DPL];
 #pragma unroll
   for (int k = 0; k < DPL; ++k) o_w[k] = 0.0;
-  // wave w takes tiles w, w + 4, ... of 64 keys; lane <-> key for the scores, lane <-> dims for PV
-  for (int t0 = j0 + 64 * wave; t0 < j1; t0 += 64 * (AD_THREADS / 64)) {
-    const int j = t0 + lane;
-    const int nk = min(64, j1 - t0);
+  bool staged = false;
+  // wave w takes the 64-key tiles w, w + 4, ... of the range (one tile each for ranges of 256)
+  for (int t0 = j0 + 64 * wave; t0 < j1 || !staged; t0 += 64 * (AD_THREADS / 64)) {
+    const int nk = t0 < j1 ? min(64, j1 - t0) : 0;
+    // this tile's K row (lane <-> key) and, for HD 64, V values (lane <-> dim) go out together
+    float4 kreg[HD / 4];
+    float vreg[V_EARLY ? 64 : 1];
+    if (lane < nk) {
+      const float4* kr = reinterpret_cast<const float4*>(k_region + (int64_t)(t0 + lane) * n_kv + g * HD);
+#pragma unroll
+      for (int d4 = 0; d4 < HD / 4; ++d4) kreg[d4] = kr[d4];
+    }
+    if constexpr (V_EARLY) {
+#pragma unroll
+      for (int kk = 0; kk < 64; ++kk)
+        if (kk < nk) vreg[kk] = v_region[(int64_t)(t0 + kk) * n_kv + g * HD + lane];
+    }
+    if (!staged) {  // the query, scaled by 1/sqrt(hd) in f64, while the first loads are in flight
+      for (int i = tid; i < HD; i += AD_THREADS) qs[i] = (double)q[h * HD + i] * scale;
+      __syncthreads();
+      staged = true;
+    }
+    if (nk == 0) continue;
     double s = -1e300;
     if (lane < nk) {
-      const float4* kr = reinterpret_cast<const float4*>(k_region + (int64_t)j * n_kv + g * HD);
       double a = 0.0;
-#pragma unroll 8
+#pragma unroll
       for (int d4 = 0; d4 < HD / 4; ++d4) {
-        const float4 kv = kr[d4];
-        a = fma(qs[4 * d4], (double)kv.x, a);
-        a = fma(qs[4 * d4 + 1], (double)kv.y, a);
-        a = fma(qs[4 * d4 + 2], (double)kv.z, a);
-        a = fma(qs[4 * d4 + 3], (double)kv.w, a);
+        a = fma(qs[4 * d4], (double)kreg[d4].x, a);
+        a = fma(qs[4 * d4 + 1], (double)kreg[d4].y, a);
+        a = fma(qs[4 * d4 + 2], (double)kreg[d4].z, a);
+        a = fma(qs[4 * d4 + 3], (double)kreg[d4].w, a);
       }
       s = a;
     }
@@ -330,11 +411,27 @@ __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restr
     for (int k = 0; k < DPL; ++k) o_w[k] *= resc;
     m_w = m_new;
     pw[wave][lane] = p;  // the wave's own LDS row: its accesses complete in order
-    for (int kk = 0; kk < nk; ++kk) {
-      const double pk = pw[wave][kk];
-      const float* vr = v_region + (int64_t)(t0 + kk) * n_kv + g * HD;
+    if constexpr (V_EARLY) {
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) o_w[k] = fma(pk, (double)vr[lane + 64 * k], o_w[k]);
+      for (int kk = 0; kk < 64; ++kk)
+        if (kk < nk) o_w[0] = fma(pw[wave][kk], (double)vreg[kk], o_w[0]);
+    } else {
+      for (int kb = 0; kb < nk; kb += 32) {
+        float vb[32][DPL];
+#pragma unroll
+        for (int kk = 0; kk < 32; ++kk)
+          if (kb + kk < nk) {
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) vb[kk][k] = v_region[(int64_t)(t0 + kb + kk) * n_kv + g * HD + lane + 64 * k];
+          }
+#pragma unroll
+        for (int kk = 0; kk < 32; ++kk)
+          if (kb + kk < nk) {
+            const double pk = pw[wave][kb + kk];
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) o_w[k] = fma(pk, (double)vb[kk][k], o_w[k]);
+          }
+      }
     }
   }
   // merge the waves (fixed order)
@@ -357,6 +454,7 @@ __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restr
 #pragma unroll
       for (int k = 0; k < DPL; ++k) o[k] = fma(wst[w][2 + lane + 64 * k], f, o[k]);
     }
+    double* out = part + ((int64_t)h * n_range + r) * (HD + 2);
     if (lane == 0) {
       out[0] = m;
       out[1] = l;
@@ -366,31 +464,30 @@ __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restr
   }
 }
 
-// Merge the ranges of head h in order, normalize, round to f32, Q8_0 the head's output row.
+// Merge head h's n_ne ranges in order, normalize, round to f32 and Q8_0 into the LDS row (one
+// wave; lane holds dims 4*lane..4*lane+3, HD/4 lanes = whole groups of 8 per block).
 template <int HD>
-__global__ void __launch_bounds__(64) k_attn_decode_merge(const double* __restrict__ part, int n_range,
-                                                          int8_t* __restrict__ q_codes, uint16_t* __restrict__ q_scales) {
-  __shared__ double exp_tab[64];
-  const int h = blockIdx.x, lane = threadIdx.x;
-  exp2_table_fill(exp_tab, lane);
-  __syncthreads();
+__device__ __forceinline__ void attn_merge_head(const double* __restrict__ part, int n_range, int n_ne, int h, int lane,
+                                                const double* exp_tab, int8_t* a_codes, double* a_d) {
   const double* ph = part + (int64_t)h * n_range * (HD + 2);
-  double m = -1e300;
-  for (int r = 0; r < n_range; ++r) m = fmax(m, ph[r * (HD + 2)]);
-  // lane holds dims 4*lane .. 4*lane+3 (HD/4 lanes active)
-  double l = 0.0, o[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int r = 0; r < n_range; ++r) {
-    const double* pr = ph + r * (HD + 2);
-    if (pr[1] == 0.0) continue;  // empty range
-    const double f = exp_f64(pr[0] - m, exp_tab);
-    l = fma(pr[1], f, l);
+  double mr = -1e300, lr = 0.0;
+  if (lane < n_ne) {  // one range per lane (n_ne <= AD_MAX_RANGES <= 64)
+    mr = ph[lane * (HD + 2)];
+    lr = ph[lane * (HD + 2) + 1];
+  }
+  const double m = wave_max_d(mr);
+  const double f_own = lane < n_ne ? exp_f64(mr - m, exp_tab) : 0.0;
+  const double l = wave_sum_d(lr * f_own);
+  double o[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int rr = 0; rr < n_ne; ++rr) {
+    const double f = __shfl(f_own, rr);
     if (lane < HD / 4) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) o[k] = fma(pr[2 + 4 * lane + k], f, o[k]);
+      for (int k = 0; k < 4; ++k) o[k] = fma(ph[rr * (HD + 2) + 2 + 4 * lane + k], f, o[k]);
     }
   }
   const double inv = recip_f64(l);
-  if (lane < HD / 4) {  // HD/4 = 16 or 32 lanes: whole groups of 8 per Q8_0 block
+  if (lane < HD / 4) {
     float4 v;
     v.x = (float)(o[0] * inv);
     v.y = (float)(o[1] * inv);
@@ -398,37 +495,31 @@ __global__ void __launch_bounds__(64) k_attn_decode_merge(const double* __restri
     v.w = (float)(o[3] * inv);
     float d;
     const uint32_t qv = q8_block_quant4(v, d);
-    reinterpret_cast<uint32_t*>(q_codes + (int64_t)h * HD)[lane] = qv;
-    if ((lane & 7) == 0) q_scales[(int64_t)h * (HD / QK) + lane / 8] = f32_to_f16_bits(d);
+    reinterpret_cast<uint32_t*>(a_codes + h * HD)[lane] = qv;
+    if ((lane & 7) == 0) a_d[h * (HD / QK) + lane / 8] = (double)f16_bits_to_f32(f32_to_f16_bits(d));
   }
 }
 
 int attn_decode_ranges(int n_ctx, int* keys_per_range) {
-  int kpr = 256;
+  int kpr = 256;  // one 64-key tile per wave
   while ((n_ctx + kpr - 1) / kpr > AD_MAX_RANGES) kpr *= 2;
   *keys_per_range = kpr;
   return (n_ctx + kpr - 1) / kpr;
 }
 
 int launch_attn_decode(const float* q, const float* k_region, const float* v_region, const int32_t* pos_dev,
-                       int n_ctx, int n_head, int n_head_kv, int head_dim, double* part, int8_t* q_codes,
-                       uint16_t* q_scales, hipStream_t s) {
+                       int n_ctx, int n_head, int n_head_kv, int head_dim, double* part, hipStream_t s) {
   int kpr = 0;
   const int n_range = attn_decode_ranges(n_ctx, &kpr);
-  if (head_dim == 64) {
+  if (head_dim == 64)
     hipLaunchKernelGGL(k_attn_decode<64>, dim3(n_head, n_range), dim3(AD_THREADS), 0, s, q, k_region, v_region,
                        pos_dev, n_head, n_head_kv, kpr, part);
-    MI_LAUNCH_CHECK("k_attn_decode");
-    hipLaunchKernelGGL(k_attn_decode_merge<64>, dim3(n_head), dim3(64), 0, s, part, n_range, q_codes, q_scales);
-  } else if (head_dim == 128) {
+  else if (head_dim == 128)
     hipLaunchKernelGGL(k_attn_decode<128>, dim3(n_head, n_range), dim3(AD_THREADS), 0, s, q, k_region, v_region,
                        pos_dev, n_head, n_head_kv, kpr, part);
-    MI_LAUNCH_CHECK("k_attn_decode");
-    hipLaunchKernelGGL(k_attn_decode_merge<128>, dim3(n_head), dim3(64), 0, s, part, n_range, q_codes, q_scales);
-  } else {
+  else
     return set_error(MI_ERR_UNSUPPORTED, "attention decode: head_dim %d", head_dim);
-  }
-  MI_LAUNCH_CHECK("k_attn_decode_merge");
+  MI_LAUNCH_CHECK("k_attn_decode");
   return MI_OK;
 }
 
