@@ -230,9 +230,9 @@ def decode_bench(args, cfg, model, ids, pos, load_s):
     rng = np.random.default_rng(cfg.seed + 1000)
     n = args.warmup + args.steps
     toks = rng.integers(0, cfg.vocab, size=2 * n).astype(np.int32)
-    p0 = int(pos[-1]) + 1
-    if p0 + 2 * n > cfg.n_ctx:
-        raise SystemExit(f"decode steps run past n_ctx {cfg.n_ctx}")
+    # the steps follow the prompt; a prompt that fills the context (the 8B-shaped chunk ends at
+    # n_ctx - 1) has its last rows rewritten by the steps instead
+    p0 = min(int(pos[-1]) + 1, cfg.n_ctx - 2 * n)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
