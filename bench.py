@@ -225,6 +225,8 @@ def decode_bench(args, cfg, model, ids, pos, load_s):
     stream with HIP events; the eager mi_decode_step is timed too."""
     import torch
 
+    from quantized_transformer_prefill_amd import binding as B
+
     model.forward(ids, pos)  # the prompt's KV rows (untimed)
     torch.cuda.synchronize()
     rng = np.random.default_rng(cfg.seed + 1000)
@@ -256,6 +258,14 @@ def decode_bench(args, cfg, model, ids, pos, load_s):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
         graph.close()
+    # the sampler on the last step's logits (penalties over a 64-token window, top-k 40, top-p 0.9,
+    # temperature 0.8), timed alone on the default stream
+    sp = type("P", (), dict(repeat_penalty=1.1, frequency_penalty=0.0, presence_penalty=0.0, top_k=40, top_p=0.9,
+                            temperature=0.8))
+    ws = torch.empty(B.lib().mi_sampler_workspace_bytes(), dtype=torch.uint8, device=model.device)
+    tok = torch.empty(1, dtype=torch.int32, device=model.device)
+    win = toks[:64]
+    samp_ms = timed_loop(lambda: B.sample(model.logits, win, sp, 1, 0, workspace=ws, token_out=tok), 50, torch)
     context = p0 + n + args.warmup + args.steps / 2.0  # mean attended positions over the timed steps
     nbytes = decode_step_bytes(cfg, context)
     gbs = nbytes / (ms / 1e3) / 1e9
@@ -270,6 +280,7 @@ def decode_bench(args, cfg, model, ids, pos, load_s):
                    "prompt_tokens": cfg.n_tokens, "first_position": p0, "n_ctx": cfg.n_ctx,
                    "parallelism": "single GPU"},
         "eager_ms_per_step": round(eager_ms, 4),
+        "sampler_ms": round(samp_ms, 4),
         "roofline": {"bound": "hbm", "kernel": "whole decode step (matrix-vector kernels, attention, lm_head)",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,

@@ -171,6 +171,43 @@ int mi_prefill_forward_n(const mi_model* model, const int32_t* token_ids, const 
 int mi_decode_step(const mi_model* model, int32_t token_id, int32_t position, int32_t n_ctx,
                    const mi_kv_regions* kv, float* logits_out);
 
+/* ---- sampler: one next token from last-token logits (the sampler row of the walkthrough index:
+ * penalties over the last-64 window -> top-k -> top-p -> temperature -> seeded sample).
+ *   penalties   for token t seen c_t > 0 times in the window, in f64 from its f32 logit:
+ *               l = l / repeat_penalty if l > 0 else l * repeat_penalty; then
+ *               l - c_t * frequency_penalty - presence_penalty
+ *   top-k       the top_k largest penalized logits, ties by the smaller token id
+ *   top-p       softmax of those candidates at temperature 1 (temperature is the next step);
+ *               the shortest prefix whose cumulative probability reaches top_p (at least one)
+ *   temperature kept logits / temperature; temperature 0 picks the first candidate (greedy)
+ *   sample      u = (SplitMix64 output number step+1 of the generator seeded with `seed`) >> 11,
+ *               times 2^-53; weights e^(l_i - l_0); the first candidate whose running weight sum
+ *               exceeds u times the total */
+#define MI_SAMPLER_MAX_K 64
+typedef struct mi_sampler_params {
+  float repeat_penalty;     /* > 0; 1 = off */
+  float frequency_penalty;  /* 0 = off */
+  float presence_penalty;   /* 0 = off */
+  int32_t top_k;            /* 1 .. MI_SAMPLER_MAX_K */
+  float top_p;              /* (0, 1]; 1 = off */
+  float temperature;        /* >= 0; 0 = greedy */
+} mi_sampler_params;
+
+/* Device workspace bytes mi_sample needs (caller-owned, any alignment of 256). */
+size_t mi_sampler_workspace_bytes(void);
+
+/* One token.
+ *   logits     device f32 [vocab], finite or -inf; 1 <= vocab <= 262144
+ *   window     host int32 [n_window], the recent token ids (only the last 64 count), each in
+ *              [0, vocab); may be NULL when n_window is 0
+ *   seed, step the draw's counter (step = the number of tokens sampled before in this sequence)
+ *   token_out  device int32 [1]
+ * Errors (MI_ERR_INVALID_ARG): bad sizes or parameters, window ids out of range; nothing is
+ * written.  Enqueued on `stream`; the window is staged through `workspace`. */
+int mi_sample(const float* logits, int32_t vocab, const int32_t* window, int32_t n_window,
+              const mi_sampler_params* params, uint64_t seed, uint64_t step, void* workspace,
+              size_t workspace_bytes, int32_t* token_out, void* stream);
+
 /* Graph replay of the forward for callers that repeat one shape (HIP graphs).
  * mi_prefill_graph_create validates the shapes like mi_prefill_forward_n, then captures the
  * forward's kernel sequence on model->stream (which must be a non-default stream) into a graph;

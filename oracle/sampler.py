@@ -35,6 +35,11 @@ GOLDEN = 0x9E3779B97F4A7C15
 WINDOW = 64
 
 
+def f32(x) -> float:
+    """The sampler parameters are f32 values (as the library's parameter block holds them)."""
+    return float(np.float32(x))
+
+
 @dataclass
 class SamplerParams:
     repeat_penalty: float = 1.0     # 1 = off
@@ -67,8 +72,9 @@ def penalize(logits, window, p: SamplerParams) -> np.ndarray:
         counts[int(t)] = counts.get(int(t), 0) + 1
     for t, c in counts.items():
         v = out[t]
-        v = v / p.repeat_penalty if v > 0 else v * p.repeat_penalty
-        v = v - c * p.frequency_penalty - p.presence_penalty
+        rp = f32(p.repeat_penalty)
+        v = v / rp if v > 0 else v * rp
+        v = v - c * f32(p.frequency_penalty) - f32(p.presence_penalty)
         out[t] = v
     return out
 
@@ -84,19 +90,19 @@ def sample(logits, window, p: SamplerParams, seed: int, step: int) -> int:
     cand = candidates(pen, min(p.top_k, pen.size))
     lc = pen[cand]
     # top-p on the untempered softmax of the candidates
-    if p.top_p < 1.0:
+    if f32(p.top_p) < 1.0:
         w = np.exp(lc - lc[0])
         prob = w / w.sum()
         keep, run = 0, 0.0
         for i in range(lc.size):
             run += prob[i]
             keep = i + 1
-            if run >= p.top_p:
+            if run >= f32(p.top_p):
                 break
         cand, lc = cand[:keep], lc[:keep]
-    if p.temperature == 0.0:
+    if f32(p.temperature) == 0.0:
         return int(cand[0])
-    lt = lc / p.temperature
+    lt = lc / f32(p.temperature)
     w = np.exp(lt - lt[0])
     total = 0.0
     for x in w:

@@ -8,6 +8,7 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +54,11 @@ class KvRegions(C.Structure):
                 ("n_ctx", C.c_int32), ("n_kv_embd", C.c_int32)]
 
 
+class SamplerParams(C.Structure):
+    _fields_ = [("repeat_penalty", C.c_float), ("frequency_penalty", C.c_float), ("presence_penalty", C.c_float),
+                ("top_k", C.c_int32), ("top_p", C.c_float), ("temperature", C.c_float)]
+
+
 _P, _I32, _I64, _F, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
 
 # name -> (restype, argtypes); mirrors include/mi_prefill.h
@@ -71,6 +77,8 @@ SIGNATURES = {
     "mi_gemm_q8_0": (C.c_int, [_P, _P, _I32, C.POINTER(Q8Matrix), _P, _P, _P, _P]),
     "mi_gemm_q8_0_ws": (C.c_int, [_P, _P, _I32, C.POINTER(Q8Matrix), _P, _P, _P, _P, _SZ, _I32, _P]),
     "mi_gemm_q8_0_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "mi_sampler_workspace_bytes": (_SZ, []),
+    "mi_sample": (C.c_int, [_P, _I32, _P, _I32, C.POINTER(SamplerParams), C.c_uint64, C.c_uint64, _P, _SZ, _P, _P]),
     "mi_gemm_swiglu_q8_0": (C.c_int, [_P, _P, _I32, C.POINTER(Q8Matrix), _P, _P, _P, _SZ, _P]),
     "mi_rmsnorm_quant": (C.c_int, [_P, _P, _I64, _I32, _F, _P, _P, _P, _P]),
     "mi_qk_norm": (C.c_int, [_P, _P, _I64, _I32, _I32, _F, _P]),
@@ -220,3 +228,20 @@ def lm_head_row(x_row, gamma, eps, head_codes, head_scales):
     check(lib().mi_lm_head_row(x_row.data_ptr(), gamma.data_ptr(), eps, C.byref(h), logits.data_ptr(),
                                scratch.data_ptr(), stream_ptr()))
     return logits
+
+
+def sample(logits, window, params, seed: int, step: int, workspace=None, token_out=None) -> torch.Tensor:
+    """mi_sample on device logits f32 [vocab]; `params` has the fields of SamplerParams; returns
+    the device int32 [1] token."""
+    _dev(logits, torch.float32)
+    vocab = logits.numel()
+    if workspace is None:
+        workspace = torch.empty(lib().mi_sampler_workspace_bytes(), dtype=torch.uint8, device=logits.device)
+    if token_out is None:
+        token_out = torch.empty(1, dtype=torch.int32, device=logits.device)
+    w = np.ascontiguousarray(np.asarray(window, dtype=np.int32).reshape(-1))
+    sp = SamplerParams(params.repeat_penalty, params.frequency_penalty, params.presence_penalty, params.top_k,
+                       params.top_p, params.temperature)
+    check(lib().mi_sample(logits.data_ptr(), vocab, w.ctypes.data if w.size else None, w.size, C.byref(sp),
+                          seed, step, workspace.data_ptr(), workspace.numel(), token_out.data_ptr(), stream_ptr()))
+    return token_out

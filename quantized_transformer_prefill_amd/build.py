@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmi_prefill.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["quant.hip", "rope.hip", "gemm.hip", "attention.hip", "decode.hip", "capi.cpp"]
+SOURCES = ["quant.hip", "rope.hip", "gemm.hip", "attention.hip", "decode.hip", "sampler.hip", "capi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

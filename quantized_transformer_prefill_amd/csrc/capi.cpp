@@ -13,6 +13,7 @@
 #include <cstring>
 #include <vector>
 #include <algorithm>
+#include <cmath>
 
 #include "common.h"
 
@@ -229,6 +230,32 @@ extern "C" int mi_lm_head_row(const float* x, const float* gamma, float eps, con
   int rc = launch_rmsnorm_quant(const_cast<float*>(x), gamma, 1, head->cols, eps, xq, xs, nullptr, s);
   if (rc) return rc;
   return launch_lm_head(xq, xs, head->cols, head->codes, head->scales, head->rows, logits, s);
+}
+
+// ---------------------------------------------------------------- sampler
+extern "C" size_t mi_sampler_workspace_bytes(void) { return sampler_workspace_bytes(); }
+
+extern "C" int mi_sample(const float* logits, int32_t vocab, const int32_t* window, int32_t n_window,
+                         const mi_sampler_params* p, uint64_t seed, uint64_t step, void* workspace,
+                         size_t workspace_bytes, int32_t* token_out, void* stream) {
+  if (!logits || !p || !token_out || !workspace || vocab < 1 || vocab > 256 * 1024 || n_window < 0 ||
+      (n_window > 0 && !window))
+    return set_error(MI_ERR_INVALID_ARG, "mi_sample: bad arguments (1 <= vocab <= 262144)");
+  if (workspace_bytes < sampler_workspace_bytes())
+    return set_error(MI_ERR_WORKSPACE, "mi_sample: workspace smaller than mi_sampler_workspace_bytes()");
+  if (p->top_k < 1 || p->top_k > MI_SAMPLER_MAX_K || !(p->top_p > 0.0f && p->top_p <= 1.0f) ||
+      !(p->temperature >= 0.0f) || !(p->repeat_penalty > 0.0f) || !std::isfinite(p->temperature) ||
+      !std::isfinite(p->repeat_penalty) || !std::isfinite(p->frequency_penalty) || !std::isfinite(p->presence_penalty))
+    return set_error(MI_ERR_INVALID_ARG, "mi_sample: parameters out of range (top_k 1..%d, top_p in (0, 1], "
+                     "temperature >= 0, repeat_penalty > 0, all finite)", MI_SAMPLER_MAX_K);
+  const int nw = std::min(n_window, 64);
+  const int32_t* w = window + (n_window - nw);  // the last 64 count
+  for (int i = 0; i < nw; ++i)
+    if (w[i] < 0 || w[i] >= vocab) return set_error(MI_ERR_INVALID_ARG, "mi_sample: window id %d outside [0, %d)", w[i], vocab);
+  hipStream_t s = as_stream(stream);
+  int32_t* window_dev = (int32_t*)((char*)workspace + sampler_workspace_bytes() - 64 * sizeof(int32_t) - 256);
+  if (nw) MI_HIP(hipMemcpyAsync(window_dev, w, sizeof(int32_t) * nw, hipMemcpyHostToDevice, s));
+  return launch_sample(logits, vocab, window_dev, nw, *p, seed, step, workspace, token_out, s);
 }
 
 // ---------------------------------------------------------------- the forward

@@ -258,4 +258,9 @@ int attn_decode_ranges(int n_ctx, int* keys_per_range);
 int launch_attn_decode(const float* q, const float* k_region, const float* v_region, const int32_t* pos_dev,
                        int n_ctx, int n_head, int n_head_kv, int head_dim, double* part, hipStream_t s);
 
+// ---- sampler (sampler.hip)
+size_t sampler_workspace_bytes();
+int launch_sample(const float* logits, int vocab, const int32_t* window_dev, int n_window, const mi_sampler_params& p,
+                  uint64_t seed, uint64_t step, void* workspace, int32_t* token_out, hipStream_t s);
+
 }  // namespace mi

@@ -1,0 +1,82 @@
+"""mi_sample against the oracle sampler: the same token id for every (parameters, seed, step)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sampler as S
+from quantized_transformer_prefill_amd import binding as B
+from tests.gpu_util import need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+PARAM_SETS = [
+    S.SamplerParams(repeat_penalty=1.3, frequency_penalty=0.2, presence_penalty=0.1, top_k=40, top_p=0.9,
+                    temperature=0.8),
+    S.SamplerParams(temperature=0.0),                                    # greedy
+    S.SamplerParams(top_k=1, temperature=1.0),
+    S.SamplerParams(top_k=64, top_p=1.0, temperature=1.5),
+    S.SamplerParams(repeat_penalty=0.7, top_k=8, top_p=0.5, temperature=0.3),
+    S.SamplerParams(frequency_penalty=-0.5, presence_penalty=-0.25, top_k=17, top_p=0.95, temperature=2.0),
+]
+
+
+def synthetic_logits(vocab, seed, scale=3.0):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(vocab) * scale).astype(np.float32)
+    x[rng.integers(0, vocab, 40)] = x.max()          # ties at the top
+    return x
+
+
+@pytest.mark.parametrize("pi", range(len(PARAM_SETS)))
+def test_sample_matches_oracle(pi):
+    dev = need_gpu()
+    p = PARAM_SETS[pi]
+    vocab = 151936
+    logits = synthetic_logits(vocab, 100 + pi)
+    rng = np.random.default_rng(200 + pi)
+    window = rng.integers(0, vocab, 80).astype(np.int32)   # more than 64: only the last 64 count
+    window[-10:] = np.argsort(-logits)[:10]                # penalize some of the top tokens
+    ld = torch.as_tensor(logits, device=dev)
+    ws = torch.empty(B.lib().mi_sampler_workspace_bytes(), dtype=torch.uint8, device=dev)
+    got, want = [], []
+    for step in range(40):
+        seed = 7 + 1000 * pi
+        got.append(int(B.sample(ld, window, p, seed, step, workspace=ws).item()))
+        want.append(S.sample(logits, window, p, seed, step))
+    say(f"  params {pi}: {len(set(want))} distinct tokens over 40 draws")
+    assert got == want
+
+
+def test_sample_edge_cases():
+    dev = need_gpu()
+    p = S.SamplerParams(top_k=64, temperature=1.0, repeat_penalty=1.5, presence_penalty=0.5)
+    cases = [
+        np.array([0.5, -1.0, 2.0, 2.0, -np.inf], np.float32),                 # vocab < top_k, -inf, tie
+        np.full(33, -np.inf, np.float32),                                     # every logit -inf but one
+        synthetic_logits(8192, 3),                                            # one slice per 128 tokens
+        synthetic_logits(1000, 4, scale=0.01),                                # nearly flat
+    ]
+    cases[1][17] = 1.0
+    for ci, x in enumerate(cases):
+        ld = torch.as_tensor(x, device=dev)
+        window = [int(np.argmax(np.where(np.isfinite(x), x, -1e30)))] * 3
+        for step in range(25):
+            g = int(B.sample(ld, window, p, 11, step).item())
+            w = S.sample(x, window, p, 11, step)
+            assert g == w, (ci, step, g, w)
+
+
+def test_sample_argument_errors_write_nothing():
+    dev = need_gpu()
+    ld = torch.zeros(100, device=dev)
+    out = torch.full((1,), -5, dtype=torch.int32, device=dev)
+    bad = [S.SamplerParams(top_k=0), S.SamplerParams(top_k=65), S.SamplerParams(top_p=0.0),
+           S.SamplerParams(temperature=-1.0), S.SamplerParams(repeat_penalty=0.0)]
+    for p in bad:
+        with pytest.raises(B.MiError) as e:
+            B.sample(ld, [], p, 1, 0, token_out=out)
+        assert e.value.code == B.MI_ERR_INVALID_ARG
+    with pytest.raises(B.MiError):
+        B.sample(ld, [3, 100], S.SamplerParams(), 1, 0, token_out=out)   # window id out of range
+    torch.cuda.synchronize()
+    assert int(out.item()) == -5
