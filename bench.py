@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--decode", action="store_true",
                    help="time decode steps (one token per step, mi_decode_step via a captured graph) after "
                         "the workload's prompt instead of the prefill; prints its own JSON line")
+    p.add_argument("--slots", type=int, default=0,
+                   help="time one call of N independent sequences (mi_prefill_forward_slots) that split the "
+                        "workload's prompt evenly, each with its own KV regions; prints its own JSON line")
     p.add_argument("--workload", default=None,
                    help="model workload name (default: the 512-token 0.5B-shaped headline); the others "
                         "are reported for context: " + ", ".join(["layer1_896", "qwen2_0p5b_pp512",
@@ -109,6 +112,9 @@ def main():
         model.forward(pre_ids, pre_pos)  # rewrites the same chunk rows with the same values
     if args.decode:
         decode_bench(args, cfg, model, ids, pos, load_s)
+        return
+    if args.slots:
+        slots_bench(args, cfg, model, ids, load_s)
         return
 
     # eager calls (mi_prefill_forward), then the same forward captured once and replayed
@@ -203,6 +209,43 @@ def main():
         "roofline": roofline,
         "gemm_sweep": sweep,
         "cpu_baseline": cpu,
+        "load_s": round(load_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def slots_bench(args, cfg, model, ids, load_s):
+    """One call of n independent sequences splitting the prompt evenly (tokens n_tokens / n each,
+    positions 0.. in their own regions), eager, HIP events on a side stream."""
+    import torch
+
+    n = args.slots
+    per = cfg.n_tokens // n
+    if n < 1 or per < 1 or n * per != cfg.n_tokens:
+        raise SystemExit(f"--slots must divide the prompt length {cfg.n_tokens}")
+    sets = [model.own_kv_set()] + [model.new_kv_set() for _ in range(n - 1)]
+    slots = [(ids[i * per:(i + 1) * per], np.arange(per, dtype=np.int32), sets[i]) for i in range(n)]
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            model.forward_slots(slots)
+        stream.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            model.forward_slots(slots)
+        e1.record(stream)
+        stream.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+    line = {
+        "metric": "multi-slot prefill tokens/sec (n sequences in one call), 1 GPU",
+        "value": round(cfg.n_tokens / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "q8_0 int8 MFMA, f64 accumulation, f32 activations",
+        "data": "synthetic (seeded N(0,0.02) weights quantized to Q8_0, uniform token ids)",
+        "config": {"workload": f"{cfg.name}_{n}slots", "slots": n, "tokens_per_slot": per, "n_ctx": cfg.n_ctx,
+                   "description": f"{n} sequences of {per} tokens at positions 0..{per - 1}, own regions each, of "
+                                  + cfg.description, "parallelism": "single GPU"},
         "load_s": round(load_s, 2),
     }
     print(json.dumps(line), flush=True)

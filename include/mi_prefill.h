@@ -157,6 +157,26 @@ int mi_prefill_forward_n(const mi_model* model, const int32_t* token_ids, const 
                          int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv, int32_t n_out,
                          float* logits_out);
 
+/* Several independent sequences ("slots") in one prefill call, each with its own KV regions and
+ * positions ("09", section 2.2: positions need not count the tokens before them in the call, and a
+ * server keeps one cache per slot; section 3.2: the slot-scoped cache entry).  One slot is
+ * mi_prefill_forward.  The call computes, for every slot, exactly what mi_prefill_forward computes
+ * for that slot's tokens alone over that slot's regions: the matmuls run over all slots' rows
+ * together, the Q|K|V epilogue stores each row's K/V into its own slot's regions, and one
+ * attention launch per layer covers every slot's query tiles (up to 16 rows of one slot each).
+ *   slot_tokens  host int32 [n_slots]: the token count of each slot (>= 1); the slots' tokens are
+ *                consecutive runs of token_ids / positions, in slot order
+ *   kv           host array [n_slots] of region descriptors (each as for mi_prefill_forward)
+ *   logits_out   device f32 [n_slots][vocab]: the last token of each slot
+ * 1 <= n_slots <= MI_MAX_SLOTS; the total token count <= model->max_tokens; positions must not
+ * repeat within a slot.  The slots' region sets must be distinct (two slots writing one region
+ * set race).  Errors as mi_prefill_forward (nothing written).  Returns after the call's work is
+ * done (the per-call staging buffer is host memory). */
+#define MI_MAX_SLOTS 64
+int mi_prefill_forward_slots(const mi_model* model, const int32_t* token_ids, const int32_t* positions,
+                             const int32_t* slot_tokens, int32_t n_slots, int32_t n_ctx, const mi_kv_regions* kv,
+                             float* logits_out);
+
 /* Decode step: one token `token_id` at `position`, through the same layers and KV regions as the
  * prefill (the second act of the walkthrough index's two-act engine; the prefill page, section
  * 2.2, for attention over region rows 0..=position).  Computes exactly what mi_prefill_forward

@@ -69,6 +69,7 @@ SIGNATURES = {
     "mi_prefill_forward": (C.c_int, [C.POINTER(Model), _P, _P, _I32, _I32, C.POINTER(KvRegions), _P]),
     "mi_prefill_forward_n": (C.c_int, [C.POINTER(Model), _P, _P, _I32, _I32, C.POINTER(KvRegions), _I32, _P]),
     "mi_decode_step": (C.c_int, [C.POINTER(Model), _I32, _I32, _I32, C.POINTER(KvRegions), _P]),
+    "mi_prefill_forward_slots": (C.c_int, [C.POINTER(Model), _P, _P, _P, _I32, _I32, C.POINTER(KvRegions), _P]),
     "mi_prefill_graph_create": (C.c_int, [C.POINTER(Model), _I32, _I32, C.POINTER(KvRegions), _I32, _P,
                                           C.POINTER(C.c_void_p)]),
     "mi_prefill_graph_launch": (C.c_int, [_P, _P, _P]),

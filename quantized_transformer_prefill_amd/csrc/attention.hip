@@ -86,10 +86,10 @@ __global__ void __launch_bounds__(64 * NW * NG) k_attention(const float* __restr
                                                        const int32_t* __restrict__ max_pos_p, int max_pos_v,
                                                        int n_head, int n_head_kv, float* __restrict__ out,
                                                        int64_t ld_out, int8_t* __restrict__ q_codes,
-                                                       uint16_t* __restrict__ q_scales) {
+                                                       uint16_t* __restrict__ q_scales,
+                                                       const AttnSlotTile* __restrict__ tiles, int n_tiles) {
   constexpr int Q4 = HD / 4;    // dims per lane slot (scores) = MFMAs per score tile
   constexpr int NB = HD / 16;   // output dim blocks
-  const int max_pos = max_pos_p ? *max_pos_p : max_pos_v;
   __shared__ double exp_tab[64];
   __shared__ double sh_m[NG][NW][64], sh_l[NG][NW][64];
   __shared__ double sh_o[NG][NW / 2][NB * 4][64];
@@ -101,12 +101,25 @@ __global__ void __launch_bounds__(64 * NW * NG) k_attention(const float* __restr
   const int kv_embd = n_head_kv * HD;
   // query tile of this group: with two groups, workgroup x serves tiles x and nqt-1-x, so that
   // every workgroup (and every SIMD: waves w and w+NW share one) gets about the same number of
-  // key tiles under the causal mask; the middle workgroup of an odd count has one group
-  const int nqt = (n_tokens + 15) / 16;
+  // key tiles under the causal mask; the middle workgroup of an odd count has one group.
+  // With a tile table (several sequences in one call) a query tile is up to 16 rows of one
+  // sequence, with that sequence's regions and largest position.
+  const int nqt = tiles ? n_tiles : (n_tokens + 15) / 16;
   const int qt = grp == 0 ? blockIdx.x : nqt - 1 - blockIdx.x;
   const bool gactive = grp == 0 || qt != (int)blockIdx.x;
-  const int t = qt * 16 + qi;
-  const bool valid = gactive && t < n_tokens;
+  int t0 = qt * 16, tcount = min(16, n_tokens - qt * 16), max_pos = max_pos_p ? *max_pos_p : max_pos_v;
+  const float* k_reg = k_region;
+  const float* v_reg = v_region;
+  if (tiles) {
+    const AttnSlotTile d = tiles[qt];
+    t0 = d.t0;
+    tcount = d.count;
+    k_reg = d.k_region;
+    v_reg = d.v_region;
+    max_pos = d.max_pos;
+  }
+  const int t = t0 + qi;
+  const bool valid = gactive && qi < tcount;
   const int p = valid ? pos[t] : 0;
   int pmax = p, pmin = valid ? p : 0x7fffffff;
   for (int o = 1; o < 16; o <<= 1) {
@@ -134,8 +147,8 @@ __global__ void __launch_bounds__(64 * NW * NG) k_attention(const float* __restr
   for (int b = 0; b < NB; ++b) acc[b] = v4d{0.0, 0.0, 0.0, 0.0};
   double m_run = -INFINITY, l_run = 0.0;   // l_run: this lane's keys only
 
-  const float* kbase = k_region + (int64_t)g * HD;
-  const float* vbase = v_region + (int64_t)g * HD;
+  const float* kbase = k_reg + (int64_t)g * HD;
+  const float* vbase = v_reg + (int64_t)g * HD;
   const int ntiles = gactive ? pmax / 16 + 1 : 0;
 
   // one key tile: scores, online softmax, O += V^T P^T
@@ -291,15 +304,17 @@ __global__ void __launch_bounds__(64 * NW * NG) k_attention(const float* __restr
 int launch_attention(const float* q, int64_t ld_q, const float* k_region, const float* v_region,
                      const int32_t* pos, int n_tokens, const int32_t* max_pos_dev, int max_pos, int n_head, int n_head_kv,
                      int head_dim, float* out, int64_t ld_out, hipStream_t s, int8_t* q_codes,
-                     uint16_t* q_scales) {
-  if (n_tokens == 0) return MI_OK;
-  const int nqt = (n_tokens + 15) / 16;
+                     uint16_t* q_scales, const AttnSlotTile* tiles, int n_tiles) {
+  if (n_tokens == 0 || (tiles && n_tiles == 0)) return MI_OK;
+  const int nqt = tiles ? n_tiles : (n_tokens + 15) / 16;
   if (head_dim == 64)
     hipLaunchKernelGGL((k_attention<64, 4, 2>), dim3((nqt + 1) / 2, n_head), dim3(64 * 4 * 2), 0, s, q, ld_q, k_region,
-                       v_region, pos, n_tokens, max_pos_dev, max_pos, n_head, n_head_kv, out, ld_out, q_codes, q_scales);
+                       v_region, pos, n_tokens, max_pos_dev, max_pos, n_head, n_head_kv, out, ld_out, q_codes, q_scales,
+                       tiles, n_tiles);
   else if (head_dim == 128)
     hipLaunchKernelGGL((k_attention<128, 4, 1>), dim3(nqt, n_head), dim3(64 * 4), 0, s, q, ld_q, k_region, v_region,
-                       pos, n_tokens, max_pos_dev, max_pos, n_head, n_head_kv, out, ld_out, q_codes, q_scales);
+                       pos, n_tokens, max_pos_dev, max_pos, n_head, n_head_kv, out, ld_out, q_codes, q_scales, tiles,
+                       n_tiles);
   else
     return set_error(MI_ERR_UNSUPPORTED, "attention: head_dim %d (supported: 64, 128)", head_dim);
   MI_LAUNCH_CHECK("k_attention");

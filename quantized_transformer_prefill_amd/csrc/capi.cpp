@@ -50,6 +50,13 @@ struct Ws {
   uint16_t* ss;      // [T][ffn/32]
   int8_t* lm_q; uint16_t* lm_s;  // final row quantized
   double* attn_part; // decode: partial attention states [n_head][AD_MAX_RANGES][head_dim + 2]
+  // several sequences: one staging area copied in one transfer per call, holding the attention
+  // query tiles [n_layers][n_tiles], region pointers [2][n_layers][MI_MAX_SLOTS] (K, V), the slot
+  // of each row [T] and the last row of each slot [MI_MAX_SLOTS]
+  char* slot_stage;
+  size_t slot_stage_bytes;
+  int slot_tiles_max;    // per layer: T/16 + MI_MAX_SLOTS
+  float* slot_h;         // several sequences: the slots' last rows gathered [MI_MAX_SLOTS][hidden]
   void* gemm_ws; size_t gemm_ws_bytes;
   size_t total;
 };
@@ -75,6 +82,15 @@ static Ws carve(const mi_hparams& hp, int T, char* base) {
   w.lm_q = (int8_t*)take((size_t)hp.hidden);
   w.lm_s = (uint16_t*)take(sizeof(uint16_t) * (size_t)(hp.hidden / QK));
   w.attn_part = (double*)take(sizeof(double) * (size_t)hp.n_head * AD_MAX_RANGES * (hp.head_dim + 2));
+  w.slot_tiles_max = T / 16 + MI_MAX_SLOTS;
+  {
+    const size_t L = (size_t)std::max(hp.n_layers, 1);
+    w.slot_stage_bytes = align_up(sizeof(AttnSlotTile) * L * w.slot_tiles_max) +
+                         align_up(sizeof(float*) * 2 * L * MI_MAX_SLOTS) + align_up(sizeof(int32_t) * (size_t)T) +
+                         align_up(sizeof(int32_t) * MI_MAX_SLOTS);
+    w.slot_stage = take(w.slot_stage_bytes);
+  }
+  w.slot_h = (float*)take(sizeof(float) * MI_MAX_SLOTS * (size_t)hp.hidden);
   size_t g = 0;
   g = std::max(g, gemm_workspace_bytes(T, (int)(nq + 2 * nkv), hp.hidden));
   g = std::max(g, gemm_workspace_bytes(T, hp.hidden, (int)nq));
@@ -259,6 +275,16 @@ extern "C" int mi_sample(const float* logits, int32_t vocab, const int32_t* wind
 }
 
 // ---------------------------------------------------------------- the forward
+static int validate_kv(const mi_hparams& hp, const mi_kv_regions* kv, int32_t n_ctx) {
+  if (!kv) return set_error(MI_ERR_INVALID_ARG, "forward: NULL kv descriptor");
+  if (kv->n_ctx != n_ctx) return set_error(MI_ERR_KV_MISMATCH, "forward: kv n_ctx %d != call n_ctx %d", kv->n_ctx, n_ctx);
+  if (kv->n_layers != hp.n_layers || kv->n_kv_embd != hp.n_head_kv * hp.head_dim || !kv->k || !kv->v)
+    return set_error(MI_ERR_KV_MISMATCH, "forward: kv descriptor does not match the model");
+  for (int l = 0; l < hp.n_layers; ++l)
+    if (!kv->k[l] || !kv->v[l]) return set_error(MI_ERR_KV_MISMATCH, "forward: kv region of layer %d is NULL", l);
+  return MI_OK;
+}
+
 static int validate_static(const mi_model* md, int32_t nt, int32_t n_ctx, const mi_kv_regions* kv,
                            const float* logits, int32_t n_out) {
   if (!md || !kv || !logits) return set_error(MI_ERR_INVALID_ARG, "forward: NULL argument");
@@ -268,11 +294,7 @@ static int validate_static(const mi_model* md, int32_t nt, int32_t n_ctx, const 
   if (nt < 1) return set_error(MI_ERR_INVALID_ARG, "forward: n_tokens must be >= 1");
   if (n_out < 1 || n_out > nt) return set_error(MI_ERR_INVALID_ARG, "forward: n_out %d outside [1, n_tokens = %d]", n_out, nt);
   if (n_ctx < 1) return set_error(MI_ERR_INVALID_ARG, "forward: n_ctx must be >= 1");
-  if (kv->n_ctx != n_ctx) return set_error(MI_ERR_KV_MISMATCH, "forward: kv n_ctx %d != call n_ctx %d", kv->n_ctx, n_ctx);
-  if (kv->n_layers != hp.n_layers || kv->n_kv_embd != hp.n_head_kv * hp.head_dim || !kv->k || !kv->v)
-    return set_error(MI_ERR_KV_MISMATCH, "forward: kv descriptor does not match the model");
-  for (int l = 0; l < hp.n_layers; ++l)
-    if (!kv->k[l] || !kv->v[l]) return set_error(MI_ERR_KV_MISMATCH, "forward: kv region of layer %d is NULL", l);
+  if ((rc = validate_kv(hp, kv, n_ctx))) return rc;
   if (nt > md->max_tokens) return set_error(MI_ERR_WORKSPACE, "forward: n_tokens %d > max_tokens %d", nt, md->max_tokens);
   if (!md->workspace || md->workspace_bytes < carve(hp, md->max_tokens, nullptr).total)
     return set_error(MI_ERR_WORKSPACE, "forward: workspace smaller than mi_prefill_workspace_bytes(max_tokens)");
@@ -325,9 +347,8 @@ static int stage_tokens(const Ws& w, const int32_t* ids, const int32_t* pos, int
 // (decode.hip).  Per layer: Q|K|V matrix-vector product with the attention RMSNorm in its prologue
 // and bias, QK norm, RoPE and the K/V store in its epilogue; single-query attention over ranges of
 // keys 0..pos; output projection (the ranges merged into a Q8_0 row in its prologue) + residual;
-// gate|up with the ffn
-// RMSNorm in its prologue and SwiGLU + Q8_0 in its epilogue; down projection + residual.  Then the
-// lm_head with the final RMSNorm in its prologue.
+// gate|up with the ffn RMSNorm in its prologue and SwiGLU + Q8_0 in its epilogue; down projection
+// + residual.  Then the lm_head with the final RMSNorm in its prologue.
 static int enqueue_decode(const mi_model* md, const Ws& w, int32_t n_ctx, const mi_kv_regions* kv, float* logits_out,
                           hipStream_t s) {
   const mi_hparams& hp = md->hp;
@@ -481,6 +502,153 @@ extern "C" int mi_prefill_forward_n(const mi_model* md, const int32_t* token_ids
   const Ws w = carve(md->hp, md->max_tokens, (char*)md->workspace);
   if ((rc = stage_tokens(w, token_ids, positions, n_tokens, &max_pos, s))) return rc;
   return enqueue_forward(md, w, n_tokens, n_ctx, kv, n_out, logits_out, s);
+}
+
+// ---------------------------------------------------------------- several sequences in one call
+// Rows of all slots go through the matmuls, norms and activations together; the Q|K|V epilogue
+// stores each row's K/V into its slot's regions; attention runs per slot over that slot's regions;
+// the last layer keeps every row (the tail rows of different slots are not contiguous), and each
+// slot's last row goes through the final norm and the lm_head.
+// device views of the staging area of a call with several sequences
+struct SlotStage {
+  const AttnSlotTile* tiles;  // [n_layers][n_tiles]
+  float* const* regions;      // [2][n_layers][MI_MAX_SLOTS]
+  const int32_t* slot_of_row; // [nt]
+  const int32_t* last;        // [n_slots]
+  int n_tiles;
+};
+
+static int enqueue_slots(const mi_model* md, const Ws& w, const SlotStage& st, int nt, int n_slots,
+                         const mi_kv_regions* kv, float* logits_out, hipStream_t s) {
+  const mi_hparams& hp = md->hp;
+  const int H = hp.hidden, F = hp.ffn;
+  const int nq = hp.n_head * hp.head_dim, nkv = hp.n_head_kv * hp.head_dim, nqkv = nq + 2 * nkv;
+  const float eps = hp.rms_eps;
+  const int L = std::max(hp.n_layers, 1);
+  int rc;
+  if ((rc = launch_embed(md->token_embd.codes, md->token_embd.scales, H, w.ids, nt, w.h, s))) return rc;
+  int pending = 1;
+  for (int l = 0; l < hp.n_layers; ++l) {
+    const mi_layer_weights& Lw = md->layers[l];
+    const bool last = l == hp.n_layers - 1;
+    if ((rc = launch_rmsnorm_quant(w.h, Lw.attn_norm, nt, H, eps, w.xq, w.xs, nullptr, s, (const double*)w.gemm_ws,
+                                   pending)))
+      return rc;
+    GemmArgs g{};
+    g.a_codes = w.xq; g.a_scales = w.xs; g.m = nt;
+    g.w_codes = Lw.wqkv.codes; g.w_scales = Lw.wqkv.scales; g.n = nqkv; g.k = H;
+    g.bias = hp.qkv_bias ? Lw.bqkv : nullptr; g.out = w.qkv; g.ld_out = nqkv;
+    g.workspace = w.gemm_ws; g.workspace_bytes = w.gemm_ws_bytes;
+    g.qkv.pos = w.pos; g.qkv.rope = md->rope_table; g.qkv.n_q = nq; g.qkv.n_kv = nkv; g.qkv.head_dim = hp.head_dim;
+    g.qkv.k_region = kv[0].k[l]; g.qkv.v_region = kv[0].v[l];
+    g.qkv.slot_of_row = st.slot_of_row;
+    g.qkv.k_slots = st.regions + (size_t)l * MI_MAX_SLOTS;
+    g.qkv.v_slots = st.regions + ((size_t)L + l) * MI_MAX_SLOTS;
+    g.qkv.q_norm = hp.qk_norm ? Lw.q_norm : nullptr; g.qkv.k_norm = hp.qk_norm ? Lw.k_norm : nullptr; g.qkv.eps = eps;
+    if ((rc = launch_gemm_q8(g, s))) return rc;
+    // one launch for every slot: the query tiles of this layer's table
+    if ((rc = launch_attention(w.qkv, nqkv, kv[0].k[l], kv[0].v[l], w.pos, nt, nullptr, 0, hp.n_head, hp.n_head_kv,
+                               hp.head_dim, nullptr, nq, s, w.xq, w.xs, st.tiles + (size_t)l * st.n_tiles,
+                               st.n_tiles)))
+      return rc;
+    GemmArgs go{};
+    go.a_codes = w.xq; go.a_scales = w.xs; go.m = nt;
+    go.w_codes = Lw.wo.codes; go.w_scales = Lw.wo.scales; go.n = H; go.k = nq;
+    go.residual = w.h; go.out = w.h; go.ld_out = H;
+    go.workspace = w.gemm_ws; go.workspace_bytes = w.gemm_ws_bytes;
+    if ((rc = launch_gemm_q8(go, s))) return rc;
+    if ((rc = launch_rmsnorm_quant(w.h, Lw.ffn_norm, nt, H, eps, w.xq, w.xs, nullptr, s))) return rc;
+    GemmArgs gg{};
+    gg.a_codes = w.xq; gg.a_scales = w.xs; gg.m = nt;
+    gg.w_codes = Lw.w_gate_up.codes; gg.w_scales = Lw.w_gate_up.scales; gg.n = 2 * F; gg.k = H;
+    gg.q_codes = w.sq; gg.q_scales = w.ss;
+    gg.workspace = w.gemm_ws; gg.workspace_bytes = w.gemm_ws_bytes;
+    if ((rc = launch_gemm_q8(gg, s))) return rc;
+    GemmArgs gd{};
+    gd.a_codes = w.sq; gd.a_scales = w.ss; gd.m = nt;
+    gd.w_codes = Lw.w_down.codes; gd.w_scales = Lw.w_down.scales; gd.n = H; gd.k = F;
+    gd.residual = w.h; gd.out = w.h; gd.ld_out = H;
+    gd.workspace = w.gemm_ws; gd.workspace_bytes = w.gemm_ws_bytes;
+    pending = 1;
+    gd.split_out = last ? nullptr : &pending;  // the last layer reduces its own partials
+    if ((rc = launch_gemm_q8(gd, s))) return rc;
+  }
+  // the slots' last rows, gathered; final norm and the lm_head as one matmul over them
+  const mi_q8_matrix& head = hp.tied ? md->token_embd : md->output;
+  if ((rc = launch_gather_rows(w.h, H, st.last, n_slots, w.slot_h, s))) return rc;
+  if ((rc = launch_rmsnorm_quant(w.slot_h, md->output_norm, n_slots, H, eps, w.xq, w.xs, nullptr, s))) return rc;
+  if (n_slots == 1) return launch_lm_head(w.xq, w.xs, H, head.codes, head.scales, head.rows, logits_out, s);
+  GemmArgs gl{};
+  gl.a_codes = w.xq; gl.a_scales = w.xs; gl.m = n_slots;
+  gl.w_codes = head.codes; gl.w_scales = head.scales; gl.n = head.rows; gl.k = H;
+  gl.out = logits_out; gl.ld_out = head.rows;
+  gl.split_k = 1;
+  return launch_gemm_q8(gl, s);
+}
+
+extern "C" int mi_prefill_forward_slots(const mi_model* md, const int32_t* token_ids, const int32_t* positions,
+                                        const int32_t* slot_tokens, int32_t n_slots, int32_t n_ctx,
+                                        const mi_kv_regions* kv, float* logits_out) {
+  if (!slot_tokens || !kv || n_slots < 1 || n_slots > MI_MAX_SLOTS)
+    return set_error(MI_ERR_INVALID_ARG, "forward_slots: 1 <= n_slots <= %d and non-NULL descriptors", MI_MAX_SLOTS);
+  int32_t off[MI_MAX_SLOTS], maxpos[MI_MAX_SLOTS];
+  int nt = 0;
+  for (int sl = 0; sl < n_slots; ++sl) {
+    if (slot_tokens[sl] < 1) return set_error(MI_ERR_INVALID_ARG, "forward_slots: slot %d has no tokens", sl);
+    off[sl] = nt;
+    nt += slot_tokens[sl];
+  }
+  int rc = validate_static(md, nt, n_ctx, &kv[0], logits_out, 1);
+  if (rc) return rc;
+  for (int sl = 1; sl < n_slots; ++sl)
+    if ((rc = validate_kv(md->hp, &kv[sl], n_ctx))) return rc;
+  for (int sl = 0; sl < n_slots; ++sl)  // positions: ranges; no repeat within a slot
+    if ((rc = validate_tokens(md->hp, token_ids + off[sl], positions + off[sl], slot_tokens[sl], n_ctx, &maxpos[sl])))
+      return rc;
+  hipStream_t s = as_stream(md->stream);
+  const Ws w = carve(md->hp, md->max_tokens, (char*)md->workspace);
+  const int L = std::max(md->hp.n_layers, 1);
+  // attention query tiles: up to 16 rows of one slot each
+  int n_tiles = 0;
+  for (int sl = 0; sl < n_slots; ++sl) n_tiles += (slot_tokens[sl] + 15) / 16;
+  if (n_tiles > w.slot_tiles_max) return set_error(MI_ERR_WORKSPACE, "forward_slots: too many attention tiles");
+  // the staging area, built on the host in the device layout and sent in one copy
+  const size_t o_tiles = 0, o_regions = o_tiles + align_up(sizeof(AttnSlotTile) * (size_t)L * n_tiles),
+               o_rows = o_regions + align_up(sizeof(float*) * 2 * (size_t)L * MI_MAX_SLOTS),
+               o_last = o_rows + align_up(sizeof(int32_t) * (size_t)nt),
+               bytes = o_last + sizeof(int32_t) * MI_MAX_SLOTS;
+  if (bytes > w.slot_stage_bytes) return set_error(MI_ERR_WORKSPACE, "forward_slots: staging area too small");
+  std::vector<char> blob(bytes, 0);
+  AttnSlotTile* tiles = reinterpret_cast<AttnSlotTile*>(blob.data() + o_tiles);
+  float** regions = reinterpret_cast<float**>(blob.data() + o_regions);
+  int32_t* slot_of_row = reinterpret_cast<int32_t*>(blob.data() + o_rows);
+  int32_t* last = reinterpret_cast<int32_t*>(blob.data() + o_last);
+  for (int l = 0; l < md->hp.n_layers; ++l) {
+    int i = 0;
+    for (int sl = 0; sl < n_slots; ++sl) {
+      regions[(size_t)l * MI_MAX_SLOTS + sl] = kv[sl].k[l];
+      regions[((size_t)L + l) * MI_MAX_SLOTS + sl] = kv[sl].v[l];
+      for (int t = 0; t < slot_tokens[sl]; t += 16)
+        tiles[(size_t)l * n_tiles + i++] =
+            AttnSlotTile{kv[sl].k[l], kv[sl].v[l], off[sl] + t, std::min(16, slot_tokens[sl] - t), maxpos[sl], 0};
+    }
+  }
+  for (int sl = 0; sl < n_slots; ++sl) {
+    for (int t = 0; t < slot_tokens[sl]; ++t) slot_of_row[off[sl] + t] = sl;
+    last[sl] = off[sl] + slot_tokens[sl] - 1;
+  }
+  int32_t mp_all = 0;
+  for (int sl = 0; sl < n_slots; ++sl) mp_all = std::max(mp_all, maxpos[sl]);
+  if ((rc = stage_tokens(w, token_ids, positions, nt, &mp_all, s))) return rc;
+  MI_HIP(hipMemcpyAsync(w.slot_stage, blob.data(), bytes, hipMemcpyHostToDevice, s));
+  const SlotStage st{reinterpret_cast<const AttnSlotTile*>(w.slot_stage + o_tiles),
+                     reinterpret_cast<float* const*>(w.slot_stage + o_regions),
+                     reinterpret_cast<const int32_t*>(w.slot_stage + o_rows),
+                     reinterpret_cast<const int32_t*>(w.slot_stage + o_last), n_tiles};
+  rc = enqueue_slots(md, w, st, nt, n_slots, kv, logits_out, s);
+  // the staging buffer above is host heap memory: wait for the copy before returning
+  MI_HIP(hipStreamSynchronize(s));
+  return rc;
 }
 
 // ---------------------------------------------------------------- graph replay

@@ -167,6 +167,8 @@ int launch_swiglu_quant(const float* gate, const float* up, int64_t rows, int co
                         int8_t* codes, uint16_t* scales, hipStream_t s);
 int launch_embed(const int8_t* codes, const uint16_t* scales, int cols, const int32_t* ids, int n,
                  float* out, hipStream_t s);
+// out[r] = x[rows[r]] for r < n (rows of cols floats; rows: device int32 [n])
+int launch_gather_rows(const float* x, int cols, const int32_t* rows, int n, float* out, hipStream_t s);
 int launch_qk_norm(float* x, int64_t ld, const float* gamma, int64_t rows, int n_heads, int head_dim,
                    float eps, hipStream_t s);
 int launch_rope_kvstore(float* q, int64_t ld_q, const float* k, const float* v, int64_t ld_kv,
@@ -175,10 +177,19 @@ int launch_rope_kvstore(float* q, int64_t ld_q, const float* k, const float* v, 
 // out f32 [n_tokens][ld_out], or, with q_codes non-null, the output rows quantized to Q8_0
 // (codes [n_tokens][n_head*head_dim], scales [n_tokens][n_head*head_dim/32]) and out unused.
 // max_pos: the call's largest position, read from device memory when max_pos_dev is non-null.
+// One query tile of a call with several sequences: rows t0 .. t0+count-1 (count <= 16) of one
+// sequence, whose regions and largest position these are.
+struct AttnSlotTile {
+  const float* k_region;
+  const float* v_region;
+  int t0, count, max_pos, pad;
+};
+// tiles: device [n_tiles] (several sequences; n_tokens is then the total row count), or null
 int launch_attention(const float* q, int64_t ld_q, const float* k_region, const float* v_region,
                      const int32_t* pos, int n_tokens, const int32_t* max_pos_dev, int max_pos, int n_head, int n_head_kv,
                      int head_dim, float* out, int64_t ld_out, hipStream_t s,
-                     int8_t* q_codes = nullptr, uint16_t* q_scales = nullptr);
+                     int8_t* q_codes = nullptr, uint16_t* q_scales = nullptr, const AttnSlotTile* tiles = nullptr,
+                     int n_tiles = 0);
 
 // Exact Q8_0 GEMM.  Epilogue modes:
 enum GemmEpi { EPI_F32 = 0, EPI_SWIGLU_Q8 = 1, EPI_QKV = 2 };
@@ -192,6 +203,11 @@ struct QkvEpi {
   int n_q, n_kv, head_dim; // Q columns, K (= V) columns, head size
   float* k_region;         // device [n_ctx][n_kv]
   float* v_region;
+  // several sequences in one call: row t stores into the regions of slot slot_of_row[t]
+  // (k_slots / v_slots: device arrays of region pointers); null = the one region above
+  const int32_t* slot_of_row;
+  float* const* k_slots;
+  float* const* v_slots;
   const float* q_norm;     // [head_dim] gains of the QK norm, or null (no QK norm)
   const float* k_norm;
   float eps;

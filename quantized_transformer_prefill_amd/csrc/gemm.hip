@@ -422,12 +422,13 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
           out[(int64_t)row * ld_out + gcol] = r0;
           out[(int64_t)row * ld_out + gcol + half] = r1;
         } else {
-          float* kr = qe.k_region + p * qe.n_kv + (gcol - qe.n_q);
+          float* kr = (qe.slot_of_row ? qe.k_slots[qe.slot_of_row[row]] : qe.k_region) + p * qe.n_kv + (gcol - qe.n_q);
           kr[0] = r0;
           kr[half] = r1;
         }
       } else {
-        float* vr = qe.v_region + p * qe.n_kv + (gcol - qe.n_q - qe.n_kv);
+        float* vr = (qe.slot_of_row ? qe.v_slots[qe.slot_of_row[row]] : qe.v_region) + p * qe.n_kv +
+                    (gcol - qe.n_q - qe.n_kv);
         vr[0] = a;
         vr[half] = b;
       }

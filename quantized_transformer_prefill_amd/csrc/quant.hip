@@ -5,6 +5,8 @@
 // 16-byte accesses laid out so that consecutive lanes touch consecutive addresses
 // (these kernels are HBM-bound).  Floating-point node math runs in f64 and rounds
 // once to f32; the Q8_0 step is the bit-exact f32 quantizer of common.h.
+#include <algorithm>
+
 #include "common.h"
 
 namespace mi {
@@ -246,6 +248,31 @@ int launch_qk_norm(float* x, int64_t ld, const float* gamma, int64_t rows, int n
   hipLaunchKernelGGL(k_qk_norm, dim3((unsigned)blocks), dim3(256), 0, s, x, ld, gamma, rows, n_heads,
                      head_dim, eps);
   MI_LAUNCH_CHECK("k_qk_norm");
+  return MI_OK;
+}
+
+}  // namespace mi
+
+namespace mi {
+
+// out[r][:] = x[rows[r]][:] (cols a multiple of 4): the last rows of several sequences, gathered
+__global__ void __launch_bounds__(256) k_gather_rows(const float* __restrict__ x, int cols,
+                                                     const int32_t* __restrict__ rows, int n,
+                                                     float* __restrict__ out) {
+  const int nvec = cols / 4;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < (int64_t)n * nvec;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / nvec, c4 = i - r * nvec;
+    reinterpret_cast<float4*>(out + r * cols)[c4] = reinterpret_cast<const float4*>(x + (int64_t)rows[r] * cols)[c4];
+  }
+}
+
+int launch_gather_rows(const float* x, int cols, const int32_t* rows, int n, float* out, hipStream_t s) {
+  if (n == 0) return MI_OK;
+  const int64_t total = (int64_t)n * (cols / 4);
+  const int blocks = (int)std::min<int64_t>((total + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_gather_rows, dim3(blocks), dim3(256), 0, s, x, cols, rows, n, out);
+  MI_LAUNCH_CHECK("k_gather_rows");
   return MI_OK;
 }
 

@@ -102,6 +102,30 @@ class PrefillModel:
                                            out.data_ptr()))
         return out
 
+    def new_kv_set(self, fill: float = 0.0) -> "KvSet":
+        """Another sequence's KV regions (all layers, n_ctx rows), for forward_slots."""
+        return KvSet(self.cfg, self.n_ctx, self.device, fill)
+
+    def own_kv_set(self) -> "KvSet":
+        """The model's own regions (kv_k / kv_v) as a KvSet."""
+        ks = KvSet.__new__(KvSet)
+        ks.k, ks.v, ks.regions, ks._pk, ks._pv = self.kv_k, self.kv_v, self.kv, self._kv_ptrs_k, self._kv_ptrs_v
+        return ks
+
+    def forward_slots(self, slots, n_ctx: Optional[int] = None) -> torch.Tensor:
+        """Several sequences in one call (mi_prefill_forward_slots): `slots` is a list of
+        (token_ids, positions, KvSet); returns device logits f32 [n_slots][vocab]."""
+        ids = np.ascontiguousarray(np.concatenate([np.asarray(a, np.int32) for a, _, _ in slots]))
+        pos = np.ascontiguousarray(np.concatenate([np.asarray(b, np.int32) for _, b, _ in slots]))
+        counts = np.ascontiguousarray(np.array([len(a) for a, _, _ in slots], np.int32))
+        kvs = (B.KvRegions * len(slots))(*[ks.regions for _, _, ks in slots])
+        out = torch.empty(len(slots), self.cfg.vocab, dtype=torch.float32, device=self.device)
+        self.model.stream = B.stream_ptr()
+        B.check(B.lib().mi_prefill_forward_slots(C.byref(self.model), ids.ctypes.data, pos.ctypes.data,
+                                                 counts.ctypes.data, len(slots),
+                                                 self.n_ctx if n_ctx is None else n_ctx, kvs, out.data_ptr()))
+        return out
+
     def decode(self, token_id: int, position: int, n_ctx: Optional[int] = None,
                logits: Optional[torch.Tensor] = None):
         """One decode step (mi_decode_step); returns device logits f32 [vocab]."""
@@ -164,3 +188,15 @@ class PrefillGraph:
             self.close()
         except Exception:
             pass
+
+
+class KvSet:
+    """One sequence's KV regions: f32 [n_layers][n_ctx][n_kv_embd] for K and V, plus the C descriptor."""
+
+    def __init__(self, cfg, n_ctx: int, device, fill: float = 0.0):
+        kv_embd = cfg.n_head_kv * cfg.head_dim
+        self.k = torch.full((cfg.n_layers, n_ctx, kv_embd), fill, dtype=torch.float32, device=device)
+        self.v = torch.full((cfg.n_layers, n_ctx, kv_embd), fill, dtype=torch.float32, device=device)
+        self._pk = (C.c_void_p * max(cfg.n_layers, 1))(*[self.k[i].data_ptr() for i in range(cfg.n_layers)])
+        self._pv = (C.c_void_p * max(cfg.n_layers, 1))(*[self.v[i].data_ptr() for i in range(cfg.n_layers)])
+        self.regions = B.KvRegions(self._pk, self._pv, cfg.n_layers, n_ctx, kv_embd)
