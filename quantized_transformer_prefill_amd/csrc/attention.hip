@@ -40,46 +40,64 @@ typedef double v4d __attribute__((ext_vector_type(4)));
 
 constexpr double LAZY_MAX = 16.0;  // natural-log units
 
+// The regions may come from a tile table in memory, where the compiler cannot tell that they are
+// global memory: loads through address-space-1 pointers are global loads, not flat ones.
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef const float __attribute__((address_space(1))) gfloat;
+typedef const f4v __attribute__((address_space(1))) gfloat4;
+
+// One key tile, in two halves with their own registers: the K half is consumed by the score
+// MFMAs and the V half by the PV MFMAs, so each half of the next tile is requested as soon as its
+// registers are free (one tile of registers, each load a phase ahead of its use).
 template <int HD>
-struct AttnTile {
-  float4 k[HD / 16];          // K row (key0 + l%16), dims slot*HD/4 .. +HD/4
-  float4 v[4][HD / 64];       // V rows key0 + 4c + slot, dims (l%16)*HD/16 .. +HD/16
+struct KHalf {
+  f4v k[HD / 16];             // K row (key0 + l%16), dims slot*HD/4 .. +HD/4
+};
+template <int HD>
+struct VHalf {
+  f4v v[4][HD / 64];          // V rows key0 + 4c + slot, dims (l%16)*HD/16 .. +HD/16
 };
 
-// Loads of one key tile.  Rows are clamped to max_pos (the largest position of the call, a row
-// this call wrote), so every load is in bounds; rows past a query's position are masked later:
-// their scores are replaced by -inf, and their V values (which may be anything) are zeroed on the
-// tile that straddles the largest position of the 16 queries (mask_tile_v).
+// Rows are clamped to max_pos (the largest position of the call or of the sequence, a row this
+// call wrote), so every load is in bounds; rows past a query's position are masked later: their
+// scores are replaced by -inf, and their V values (which may be anything) are zeroed on the tile
+// that straddles the largest position of the 16 queries (mask_v).
 template <int HD>
-__device__ __forceinline__ void load_tile(AttnTile<HD>& t, const float* kbase, const float* vbase, int kv_embd,
-                                          int key0, int max_pos, int qi, int slot) {
-  constexpr int Q4 = HD / 4, NB = HD / 16;
-  const float* kp = kbase + (int64_t)min(key0 + qi, max_pos) * kv_embd + slot * Q4;
+__device__ __forceinline__ void load_k(KHalf<HD>& t, gfloat* kbase, int kv_embd, int key0, int max_pos, int qi,
+                                       int slot) {
+  constexpr int Q4 = HD / 4;
+  gfloat* kp = kbase + (int64_t)min(key0 + qi, max_pos) * kv_embd + slot * Q4;
 #pragma unroll
-  for (int s = 0; s < Q4 / 4; ++s) t.k[s] = *reinterpret_cast<const float4*>(kp + 4 * s);
+  for (int s = 0; s < Q4 / 4; ++s) t.k[s] = *(gfloat4*)(kp + 4 * s);
+}
+
+template <int HD>
+__device__ __forceinline__ void load_v(VHalf<HD>& t, gfloat* vbase, int kv_embd, int key0, int max_pos, int qi,
+                                       int slot) {
+  constexpr int NB = HD / 16;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const float* vp = vbase + (int64_t)min(key0 + 4 * c + slot, max_pos) * kv_embd + qi * NB;
+    gfloat* vp = vbase + (int64_t)min(key0 + 4 * c + slot, max_pos) * kv_embd + qi * NB;
 #pragma unroll
-    for (int b = 0; b < NB / 4; ++b) t.v[c][b] = *reinterpret_cast<const float4*>(vp + 4 * b);
+    for (int b = 0; b < NB / 4; ++b) t.v[c][b] = *(gfloat4*)(vp + 4 * b);
   }
 }
 
 template <int HD>
-__device__ __forceinline__ void mask_tile_v(AttnTile<HD>& t, int key0, int pmax, int slot) {
+__device__ __forceinline__ void mask_v(VHalf<HD>& t, int key0, int pmax, int slot) {
 #pragma unroll
   for (int c = 0; c < 4; ++c)
     if (key0 + 4 * c + slot > pmax)
 #pragma unroll
-      for (int b = 0; b < HD / 64; ++b) t.v[c][b] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int b = 0; b < HD / 64; ++b) t.v[c][b] = f4v{0.f, 0.f, 0.f, 0.f};
 }
 
-__device__ __forceinline__ double f4get(const float4& v, int e) {
-  return e == 0 ? (double)v.x : e == 1 ? (double)v.y : e == 2 ? (double)v.z : (double)v.w;
-}
+__device__ __forceinline__ double f4get(const f4v& v, int e) { return (double)v[e]; }
 
+// head_dim 128: at least two waves per SIMD (two workgroups per CU), which keeps the working set in
+// 256 registers per lane, with no accumulator copies through AGPRs
 template <int HD, int NW, int NG>
-__global__ void __launch_bounds__(64 * NW * NG) k_attention(const float* __restrict__ q, int64_t ld_q,
+__global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(const float* __restrict__ q, int64_t ld_q,
                                                        const float* __restrict__ k_region,
                                                        const float* __restrict__ v_region,
                                                        const int32_t* __restrict__ pos, int n_tokens,
@@ -93,7 +111,9 @@ __global__ void __launch_bounds__(64 * NW * NG) k_attention(const float* __restr
   __shared__ double exp_tab[64];
   __shared__ double sh_m[NG][NW][64], sh_l[NG][NW][64];
   __shared__ double sh_o[NG][NW / 2][NB * 4][64];
-  const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) % NW, grp = (threadIdx.x >> 6) / NW;
+  // wave and group are uniform in a wave (scalar registers: the tile descriptor is a scalar load)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) % NW),
+            grp = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) / NW);
   const int qi = lane & 15, slot = lane >> 4;
   exp2_table_fill(exp_tab, threadIdx.x);
   const int h = blockIdx.y;
@@ -127,19 +147,14 @@ __global__ void __launch_bounds__(64 * NW * NG) k_attention(const float* __restr
     pmin = min(pmin, __shfl_xor(pmin, o));
   }
 
-  // query fragment: dims slot*Q4 + s, pre-scaled by 1/sqrt(hd) in f64
+  // query fragment: dims slot*Q4 + s, kept as f32 (exact; widened at each MFMA, which halves its
+  // registers); the scores are scaled by 1/sqrt(hd) in f64 after the dot products
   const double scale = 1.0 / sqrt((double)HD);
-  double qf[Q4];
+  f4v qf[Q4 / 4];
   {
     const float* qp = q + (int64_t)(valid ? t : 0) * ld_q + (int64_t)h * HD + slot * Q4;
 #pragma unroll
-    for (int s = 0; s < Q4; s += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(qp + s);
-      qf[s] = (double)v.x * scale;
-      qf[s + 1] = (double)v.y * scale;
-      qf[s + 2] = (double)v.z * scale;
-      qf[s + 3] = (double)v.w * scale;
-    }
+    for (int s = 0; s < Q4 / 4; ++s) qf[s] = *reinterpret_cast<const f4v*>(qp + 4 * s);
   }
 
   v4d acc[NB];
@@ -147,26 +162,39 @@ __global__ void __launch_bounds__(64 * NW * NG) k_attention(const float* __restr
   for (int b = 0; b < NB; ++b) acc[b] = v4d{0.0, 0.0, 0.0, 0.0};
   double m_run = -INFINITY, l_run = 0.0;   // l_run: this lane's keys only
 
-  const float* kbase = k_reg + (int64_t)g * HD;
-  const float* vbase = v_reg + (int64_t)g * HD;
+  gfloat* kbase = (gfloat*)k_reg + (int64_t)g * HD;
+  gfloat* vbase = (gfloat*)v_reg + (int64_t)g * HD;
   const int ntiles = gactive ? pmax / 16 + 1 : 0;
 
-  // one key tile: scores, online softmax, O += V^T P^T
-  auto tile_step = [&](AttnTile<HD>& cur, int key0) {
-    if (key0 + 15 > pmax) mask_tile_v<HD>(cur, key0, pmax, slot);
+  // Tiles wave, wave + NW, ... of the 16 queries' keys.  Per tile: scores from the K half; the
+  // next tile's K half requested; online softmax; O += V^T P^T from the V half; the next tile's
+  // V half requested.  The first tile is requested before the positions arrive.
+  KHalf<HD> kt;
+  VHalf<HD> vt;
+  load_k<HD>(kt, kbase, kv_embd, wave * 16, max_pos, qi, slot);
+  load_v<HD>(vt, vbase, kv_embd, wave * 16, max_pos, qi, slot);
+  __syncthreads();  // exp_tab
+  for (int tile = wave; tile < ntiles; tile += NW) {
+    const int key0 = tile * 16;
+    const bool more = tile + NW < ntiles;
+    // keep the f32 query in the loop: otherwise its f64 widening is hoisted and holds twice the registers
+#pragma unroll
+    for (int s = 0; s < Q4 / 4; ++s) asm volatile("" : "+v"(qf[s]));
     v4d sc0 = {0.0, 0.0, 0.0, 0.0}, sc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int s = 0; s < Q4; s += 2) {
-      sc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(cur.k[s / 4], s % 4), qf[s], sc0, 0, 0, 0);
-      sc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(cur.k[(s + 1) / 4], (s + 1) % 4), qf[s + 1], sc1, 0, 0, 0);
+      sc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(kt.k[s / 4], s % 4), f4get(qf[s / 4], s % 4), sc0, 0, 0, 0);
+      sc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(kt.k[(s + 1) / 4], (s + 1) % 4), f4get(qf[(s + 1) / 4], (s + 1) % 4),
+                                                 sc1, 0, 0, 0);
     }
+    if (more) load_k<HD>(kt, kbase, kv_embd, key0 + 16 * NW, max_pos, qi, slot);
     // ---- online softmax for query l%16 over keys key0 + 4i + slot
     const bool full = key0 + 15 <= pmin;  // every query of the 16 sees every key of the tile
     double sv[4];
     double tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sv[i] = sc0[i] + sc1[i];
+      sv[i] = (sc0[i] + sc1[i]) * scale;
       if (!full && key0 + 4 * i + slot > p) sv[i] = -INFINITY;
       tmax = fmax(tmax, sv[i]);
     }
@@ -188,25 +216,13 @@ __global__ void __launch_bounds__(64 * NW * NG) k_attention(const float* __restr
       pv[i] = (sv[i] == -INFINITY) ? 0.0 : exp_f64(sv[i] - m_run, exp_tab);
       l_run += pv[i];
     }
+    if (key0 + 15 > pmax) mask_v<HD>(vt, key0, pmax, slot);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(cur.v[c][b / 4], b % 4), pv[c], acc[b], 0, 0, 0);
-  };
-
-  // tiles wave, wave + NW, ...; two tile buffers alternate (the loop body handles two tiles), the
-  // next tile's loads in flight while the current one computes.  The first tile is requested
-  // before the positions arrive.
-  AttnTile<HD> ta, tb;
-  load_tile<HD>(ta, kbase, vbase, kv_embd, wave * 16, max_pos, qi, slot);
-  __syncthreads();  // exp_tab
-  for (int tile = wave; tile < ntiles; tile += 2 * NW) {
-    if (tile + NW < ntiles) load_tile<HD>(tb, kbase, vbase, kv_embd, (tile + NW) * 16, max_pos, qi, slot);
-    tile_step(ta, tile * 16);
-    if (tile + NW >= ntiles) break;
-    if (tile + 2 * NW < ntiles) load_tile<HD>(ta, kbase, vbase, kv_embd, (tile + 2 * NW) * 16, max_pos, qi, slot);
-    tile_step(tb, (tile + NW) * 16);
+        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(vt.v[c][b / 4], b % 4), pv[c], acc[b], 0, 0, 0);
+    if (more) load_v<HD>(vt, vbase, kv_embd, key0 + 16 * NW, max_pos, qi, slot);
   }
 
   // ---- merge: the query's sum over its 4 lanes, then the waves' partial states (f64, fixed order)
