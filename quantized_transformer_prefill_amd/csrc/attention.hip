@@ -14,9 +14,11 @@
 // fixed order (o = sum_w O_w e^(m_w - m) / sum_w l_w e^(m_w - m)).  The next tile's K and V are
 // loaded while the current tile computes.
 //
-// Softmax bookkeeping per tile, kept off the critical path:
+// Softmax in base 2: scores carry the factor log2(e)/sqrt(hd), so the weights are 2^(s - m) (the
+// same softmax; one f64 rounding of the factor).  Every VALU instruction here costs the SIMD as
+// much as it would alone (the f64 MFMA does not run beside it), so the bookkeeping is kept small:
 //  * the running max is raised lazily: a query's reference m moves only when a score exceeds it
-//    by more than LAZY_MAX (softmax is invariant to the reference, and e^(s - m) <= e^LAZY_MAX is
+//    by more than LAZY_MAX (softmax is invariant to the reference, and 2^(s - m) <= 2^LAZY_MAX is
 //    harmless in f64), so most tiles need neither the cross-lane max nor the rescale of O;
 //  * the running sum is kept per lane (each lane sums its own keys) and reduced once at the end;
 //  * the causal mask is applied only on tiles that some query of the 16 does not fully see.
@@ -38,7 +40,20 @@ namespace mi {
 
 typedef double v4d __attribute__((ext_vector_type(4)));
 
-constexpr double LAZY_MAX = 16.0;  // natural-log units
+constexpr double LAZY_MAX = 24.0;  // base-2 units
+
+// 2^y for y <= LAZY_MAX; -inf and NaN (a masked score against a reference still at -inf) give 0.
+// y = k/64 + r with |r| <= 1/128 (exact); 2^(k/64) from the table `tab` (2^(j/64), j < 64) and an
+// exponent shift; 2^r by its degree-5 Taylor polynomial in r ln2 (truncation below 4e-17).
+__device__ __forceinline__ double exp2_att(double y, const double* tab) {
+  y = fmax(y, -1100.0);
+  const double kf = rint(y * 64.0);
+  const double r = fma(kf, -1.0 / 64.0, y);
+  const double p = fma(fma(fma(fma(fma(0x1.5d87fe78a6731p-10, r, 0x1.3b2ab6fba4e77p-7), r, 0x1.c6b08d704a0c0p-5), r,
+                                   0x1.ebfbdff82c58fp-3), r, 0x1.62e42fefa39efp-1), r, 1.0);
+  const int k = (int)kf;
+  return ldexp(tab[k & 63] * p, k >> 6);
+}
 
 // The regions may come from a tile table in memory, where the compiler cannot tell that they are
 // global memory: loads through address-space-1 pointers are global loads, not flat ones.
@@ -59,14 +74,14 @@ struct VHalf {
 };
 
 // Rows are clamped to max_pos (the largest position of the call or of the sequence, a row this
-// call wrote), so every load is in bounds; rows past a query's position are masked later: their
+// call wrote), so every load is in bounds (row * kv_embd < 2^31, checked by the callers); rows past a query's position are masked later: their
 // scores are replaced by -inf, and their V values (which may be anything) are zeroed on the tile
 // that straddles the largest position of the 16 queries (mask_v).
 template <int HD>
 __device__ __forceinline__ void load_k(KHalf<HD>& t, gfloat* kbase, int kv_embd, int key0, int max_pos, int qi,
                                        int slot) {
   constexpr int Q4 = HD / 4;
-  gfloat* kp = kbase + (int64_t)min(key0 + qi, max_pos) * kv_embd + slot * Q4;
+  gfloat* kp = kbase + (uint32_t)(min(key0 + qi, max_pos) * kv_embd + slot * Q4);
 #pragma unroll
   for (int s = 0; s < Q4 / 4; ++s) t.k[s] = *(gfloat4*)(kp + 4 * s);
 }
@@ -77,7 +92,7 @@ __device__ __forceinline__ void load_v(VHalf<HD>& t, gfloat* vbase, int kv_embd,
   constexpr int NB = HD / 16;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    gfloat* vp = vbase + (int64_t)min(key0 + 4 * c + slot, max_pos) * kv_embd + qi * NB;
+    gfloat* vp = vbase + (uint32_t)(min(key0 + 4 * c + slot, max_pos) * kv_embd + qi * NB);
 #pragma unroll
     for (int b = 0; b < NB / 4; ++b) t.v[c][b] = *(gfloat4*)(vp + 4 * b);
   }
@@ -125,7 +140,8 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
   // With a tile table (several sequences in one call) a query tile is up to 16 rows of one
   // sequence, with that sequence's regions and largest position.
   const int nqt = tiles ? n_tiles : (n_tokens + 15) / 16;
-  const int qt = grp == 0 ? blockIdx.x : nqt - 1 - blockIdx.x;
+  // (one group: the tiles in decreasing order, the heaviest first, so the last workgroups are short)
+  const int qt = (NG == 1 || grp == 1) ? nqt - 1 - blockIdx.x : blockIdx.x;
   const bool gactive = grp == 0 || qt != (int)blockIdx.x;
   int t0 = qt * 16, tcount = min(16, n_tokens - qt * 16), max_pos = max_pos_p ? *max_pos_p : max_pos_v;
   const float* k_reg = k_region;
@@ -147,15 +163,26 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
     pmin = min(pmin, __shfl_xor(pmin, o));
   }
 
-  // query fragment: dims slot*Q4 + s, kept as f32 (exact; widened at each MFMA, which halves its
-  // registers); the scores are scaled by 1/sqrt(hd) in f64 after the dot products
-  const double scale = 1.0 / sqrt((double)HD);
+  // query fragment: dims slot*Q4 + s.  head_dim 64: f64, pre-multiplied by the score factor.
+  // head_dim 128: f32 (exact; widened at each MFMA, which halves its registers), the scores
+  // multiplied by the factor after the dot products.
+  constexpr bool QWIDE = HD <= 64;
+  const double scale = 0x1.71547652b82fep+0 / sqrt((double)HD);  // log2(e) / sqrt(hd)
   f4v qf[Q4 / 4];
+  double qd[QWIDE ? Q4 : 1];
   {
     const float* qp = q + (int64_t)(valid ? t : 0) * ld_q + (int64_t)h * HD + slot * Q4;
 #pragma unroll
     for (int s = 0; s < Q4 / 4; ++s) qf[s] = *reinterpret_cast<const f4v*>(qp + 4 * s);
+    if constexpr (QWIDE) {
+#pragma unroll
+      for (int s = 0; s < Q4; ++s) qd[s] = (double)qf[s / 4][s % 4] * scale;
+    }
   }
+  auto qop = [&](int s) -> double {
+    if constexpr (QWIDE) return qd[s];
+    else return f4get(qf[s / 4], s % 4);
+  };
 
   v4d acc[NB];
 #pragma unroll
@@ -177,15 +204,16 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
   for (int tile = wave; tile < ntiles; tile += NW) {
     const int key0 = tile * 16;
     const bool more = tile + NW < ntiles;
-    // keep the f32 query in the loop: otherwise its f64 widening is hoisted and holds twice the registers
+    if constexpr (!QWIDE) {
+      // keep the f32 query in the loop: otherwise its f64 widening is hoisted and holds twice the registers
 #pragma unroll
-    for (int s = 0; s < Q4 / 4; ++s) asm volatile("" : "+v"(qf[s]));
+      for (int s = 0; s < Q4 / 4; ++s) asm volatile("" : "+v"(qf[s]));
+    }
     v4d sc0 = {0.0, 0.0, 0.0, 0.0}, sc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int s = 0; s < Q4; s += 2) {
-      sc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(kt.k[s / 4], s % 4), f4get(qf[s / 4], s % 4), sc0, 0, 0, 0);
-      sc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(kt.k[(s + 1) / 4], (s + 1) % 4), f4get(qf[(s + 1) / 4], (s + 1) % 4),
-                                                 sc1, 0, 0, 0);
+      sc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(kt.k[s / 4], s % 4), qop(s), sc0, 0, 0, 0);
+      sc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(kt.k[(s + 1) / 4], (s + 1) % 4), qop(s + 1), sc1, 0, 0, 0);
     }
     if (more) load_k<HD>(kt, kbase, kv_embd, key0 + 16 * NW, max_pos, qi, slot);
     // ---- online softmax for query l%16 over keys key0 + 4i + slot
@@ -194,7 +222,7 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
     double tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sv[i] = (sc0[i] + sc1[i]) * scale;
+      sv[i] = QWIDE ? sc0[i] + sc1[i] : (sc0[i] + sc1[i]) * scale;
       if (!full && key0 + 4 * i + slot > p) sv[i] = -INFINITY;
       tmax = fmax(tmax, sv[i]);
     }
@@ -203,7 +231,7 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
       tmax = fmax(tmax, __shfl_xor(tmax, 32));
       if (tmax > m_run) {  // the same decision on the 4 lanes of a query
         // a query whose keys so far were all masked has m = -inf and nothing to rescale
-        const double corr = (m_run == -INFINITY) ? 0.0 : exp_f64(m_run - tmax, exp_tab);
+        const double corr = (m_run == -INFINITY) ? 0.0 : exp2_att(m_run - tmax, exp_tab);
         l_run *= corr;
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[b] *= corr;
@@ -213,7 +241,7 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
     double pv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pv[i] = (sv[i] == -INFINITY) ? 0.0 : exp_f64(sv[i] - m_run, exp_tab);
+      pv[i] = exp2_att(sv[i] - m_run, exp_tab);  // 0 for a masked key
       l_run += pv[i];
     }
     if (key0 + 15 > pmax) mask_v<HD>(vt, key0, pmax, slot);
@@ -235,7 +263,7 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
 #pragma unroll
   for (int w = 0; w < NW; ++w) m_all = fmax(m_all, sh_m[grp][w][lane]);
   {
-    const double f_self = (m_run == -INFINITY) ? 0.0 : exp_f64(m_run - m_all, exp_tab);
+    const double f_self = (m_run == -INFINITY) ? 0.0 : exp2_att(m_run - m_all, exp_tab);
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] *= f_self;
   }
@@ -261,7 +289,7 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const double mw = sh_m[grp][w][lane];
-      l_all += (mw == -INFINITY) ? 0.0 : sh_l[grp][w][lane] * exp_f64(mw - m_all, exp_tab);
+      l_all += (mw == -INFINITY) ? 0.0 : sh_l[grp][w][lane] * exp2_att(mw - m_all, exp_tab);
     }
     const double inv = recip_f64(l_all);
     // lane holds dims (4i + slot)*NB + b of query l%16 (i = 0..3, b = 0..NB-1)

@@ -218,6 +218,8 @@ extern "C" int mi_attention_gqa(const float* q, const float* k_region, const flo
       n_head % n_head_kv || n_ctx <= 0)
     return set_error(MI_ERR_INVALID_ARG, "mi_attention_gqa: bad arguments");
   if (max_pos < 0 || max_pos >= n_ctx) return set_error(MI_ERR_POSITION_RANGE, "max_pos %d outside [0, %d)", max_pos, n_ctx);
+  if ((int64_t)n_ctx * n_head_kv * head_dim > INT32_MAX)
+    return set_error(MI_ERR_INVALID_ARG, "mi_attention_gqa: n_ctx * n_head_kv * head_dim exceeds 2^31 elements");
   return launch_attention(q, (int64_t)n_head * head_dim, k_region, v_region, positions, n_tokens, nullptr, max_pos,
                           n_head, n_head_kv, head_dim, out, (int64_t)n_head * head_dim, as_stream(stream));
 }
@@ -282,6 +284,8 @@ static int validate_kv(const mi_hparams& hp, const mi_kv_regions* kv, int32_t n_
     return set_error(MI_ERR_KV_MISMATCH, "forward: kv descriptor does not match the model");
   for (int l = 0; l < hp.n_layers; ++l)
     if (!kv->k[l] || !kv->v[l]) return set_error(MI_ERR_KV_MISMATCH, "forward: kv region of layer %d is NULL", l);
+  if ((int64_t)n_ctx * kv->n_kv_embd > INT32_MAX)  // the kernels address a region with 32-bit element offsets
+    return set_error(MI_ERR_INVALID_ARG, "forward: n_ctx * n_kv_embd exceeds 2^31 elements");
   return MI_OK;
 }
 
