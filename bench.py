@@ -158,7 +158,8 @@ def main():
     tf = os.path.join(ROOT, "profiles", TRAFFIC_FILE)
     if os.path.exists(tf):
         rec = json.load(open(tf))
-        if rec.get("kernel_source_hash") == kernel_source_hash():
+        # counters taken on this kernel's current source and at this very shape only
+        if rec.get("kernel_source_hash") == kernel_source_hash() and rec.get("shape_mnk") == [M, N2, H]:
             traffic = rec.get("bytes_per_launch")
     roofline = {"bound": "mfma", "kernel": "k_gemm_q8<EPI_SWIGLU_Q8> (gate|up + SwiGLU + Q8_0)",
                 "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8)",
@@ -426,7 +427,7 @@ def _counter_rows(d, counter):
     return rows
 
 
-def write_traffic(fetch_dir, write_dir):
+def write_traffic(fetch_dir, write_dir, shape=(512, 9728, 896)):
     """HBM bytes per launch of the dominant kernel from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
     each scaled by the factor that maps the same counter onto the known bytes of the streaming kernel."""
     out = {}
@@ -441,7 +442,8 @@ def write_traffic(fetch_dir, write_dir):
         out[key] = {"counter": counter, "kernel_kib_median": float(np.median(gemm)), "dispatches": len(gemm),
                     "calibration_kib_median": copy_kib, "calibration_bytes": COPY_BYTES, "factor": factor,
                     "bytes_per_launch": float(np.median(gemm)) * 1024.0 * factor}
-    rec = {"kernel": "k_gemm_q8<EPI_SWIGLU_Q8> (gate|up + SwiGLU + Q8_0), 512 x 9728 x 896",
+    rec = {"kernel": "k_gemm_q8<EPI_SWIGLU_Q8> (gate|up + SwiGLU + Q8_0), %d x %d x %d" % tuple(shape),
+           "shape_mnk": list(shape),
            "kernel_source_hash": kernel_source_hash(),
            "bytes_per_launch": round(out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]),
            "fetch": out["fetch"], "write": out["write"],
