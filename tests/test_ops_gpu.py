@@ -264,7 +264,8 @@ def test_attention_invariants():
 
 def test_lm_head_row_matches_oracle():
     dev = need_gpu()
-    for vocab, hidden in [(8192, 896), (151936, 896), (4000, 4096), (3000, 3584)]:
+    # row counts that are and are not multiples of the kernel's 4 rows per wave iteration
+    for vocab, hidden in [(8192, 896), (151936, 896), (4000, 4096), (3000, 3584), (1001, 896), (4003, 4096)]:
         say(f"lm_head vocab={vocab} hidden={hidden}")
         w = synth.gen_normal(101, f"o{vocab}", (vocab, hidden), std=0.02, device=dev)
         x = synth.gen_normal(102, f"h{hidden}", (hidden,), std=1.5, device=dev)
