@@ -1,6 +1,7 @@
 """Prefill benchmark: one JSON line for the 24-layer 0.5B-shaped model on its 512-token prompt.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+    python bench.py --counter-run | --write-counters C F W OUT     (per-kernel counter summary)
 
 A step is one forward over the whole 512-token prompt (all layers, the KV stores, the last-token
 lm_head) on seeded synthetic Q8_0 weights resident in HBM, launched as a replay of the captured
@@ -43,6 +44,10 @@ def parse():
                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE pass")
     p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn the two counter passes of --traffic-run into profiles/" + TRAFFIC_FILE)
+    p.add_argument("--counter-run", action="store_true",
+                   help="launches for the per-kernel counters: two eager forwards, then the calibration kernel")
+    p.add_argument("--write-counters", nargs=4, metavar=("COMPUTE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT"),
+                   help="turn the three counter passes of --counter-run into a per-kernel summary (OUT)")
     p.add_argument("--decode", action="store_true",
                    help="time decode steps (one token per step, mi_decode_step via a captured graph) after "
                         "the workload's prompt instead of the prefill; prints its own JSON line")
@@ -82,6 +87,10 @@ def main():
     if args.write_traffic:
         write_traffic(*args.write_traffic)
         return
+    if args.write_counters:
+        import synth
+        write_counters(synth.MODEL_CONFIGS[args.workload] if args.workload else synth.HEADLINE, *args.write_counters)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -100,6 +109,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.traffic_run:
         traffic_run(cfg, dev)
+        return
+    if args.counter_run:
+        counter_run(cfg, dev)
         return
     t0 = time.time()
     model = PrefillModel(cfg, synth.iter_tensors(cfg, device=dev), cfg.prefix_tokens + cfg.n_tokens, cfg.n_ctx,
@@ -409,6 +421,159 @@ def traffic_run(cfg, dev):
         torch.mul(src, 2.0, out=dst)
     torch.cuda.synchronize()
     print(json.dumps({"traffic_run": cfg.name, "shape_mnk": list(shape), "copy_bytes": COPY_BYTES}), flush=True)
+
+
+COUNTERS_COMPUTE = ["SQ_INSTS_VALU_MFMA_MOPS_I8", "SQ_INSTS_VALU_MFMA_MOPS_F64", "SQ_VALU_MFMA_BUSY_CYCLES",
+                    "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_VALU_FMA_F64", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
+                    "SQ_LDS_BANK_CONFLICT"]
+
+
+def counter_run(cfg, dev):
+    """Launches for the per-kernel counters: the model is built, the prompt prefilled twice (eager
+    mi_prefill_forward), then the streaming calibration kernel of traffic_run."""
+    import torch
+
+    import synth
+    from quantized_transformer_prefill_amd.model import PrefillModel
+
+    model = PrefillModel(cfg, synth.iter_tensors(cfg, device=dev), cfg.prefix_tokens + cfg.n_tokens, cfg.n_ctx,
+                         device=dev)
+    pre_ids, ids = synth.gen_token_ids(cfg)
+    pre_pos, pos = synth.positions_for(cfg)
+    if cfg.prefix_tokens:
+        model.forward(pre_ids, pre_pos)
+    for _ in range(2):
+        model.forward(ids, pos)
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_run": cfg.name, "forwards": 2, "copy_bytes": COPY_BYTES}), flush=True)
+
+
+def _dispatch_table(d):
+    """{dispatch id: (kernel name, grid size, {counter: value summed over the dispatch's rows})} and
+    {dispatch id: duration ns} (from the kernel trace of the same run, when present)."""
+    import csv
+    import glob
+
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                did = int(r["Dispatch_Id"])
+                name, grid, vals = out.setdefault(did, (r["Kernel_Name"], r.get("Grid_Size", ""), {}))
+                vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    dur = {}
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                dur[int(r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return out, dur
+
+
+def _forward_kernels(cfg):
+    """(kernel-name prefix, label, algorithmic int8 ops per launch or 0, algorithmic HBM bytes or 0)
+    of the forward's kernels at the full prompt (tail layers run on fewer rows and are grouped apart)."""
+    M, H, F = cfg.n_tokens, cfg.hidden, cfg.ffn
+    nq, nkv = cfg.n_head * cfg.head_dim, cfg.n_head_kv * cfg.head_dim
+    q8 = lambda rows, cols: rows * cols * 34 // 32
+    return [
+        ("void mi::k_gemm_q8<1, 2, 1, false, 2>", f"gate|up + SwiGLU + Q8_0 ({M}x{2 * F}x{H})", 2 * M * 2 * F * H,
+         q8(2 * F, H) + q8(M, H) + q8(M, F)),
+        ("void mi::k_gemm_q8<1, 1, 0, true, 2>", f"down, split-K partials ({M}x{H}x{F})", 2 * M * H * F,
+         q8(H, F) + q8(M, F) + 2 * 8 * M * H),
+        ("void mi::k_gemm_q8<1, 1, 0, false, 2>", f"Wo + residual ({M}x{H}x{nq})", 2 * M * H * nq,
+         q8(H, nq) + q8(M, nq) + 8 * M * H),
+        ("void mi::k_gemm_q8<1, 1, 2, false, 2>", f"Q|K|V + bias + RoPE + KV store ({M}x{nq + 2 * nkv}x{H})",
+         2 * M * (nq + 2 * nkv) * H, q8(nq + 2 * nkv, H) + q8(M, H) + 4 * M * (nq + 2 * nkv)),
+        ("void mi::k_attention<", f"causal GQA attention + Q8_0 of the output ({M} tokens)", 0,
+         4 * M * nq + 8 * M * nkv + q8(M, nq)),
+        ("mi::k_rmsnorm_quant", f"RMSNorm + Q8_0 ({M}x{H}; half of them also reduce 2 split-K partials)", 0,
+         M * H * (4 + 4) + q8(M, H)),
+        ("mi::k_lm_head", f"last-row lm_head ({cfg.vocab}x{H})", 0, q8(cfg.vocab, H) + 4 * cfg.vocab),
+        ("mi::k_embed", f"embedding rows ({M}x{H})", 0, q8(M, H) + 4 * M * H),
+    ]
+
+
+def write_counters(cfg, cdir, fdir, wdir, out_path):
+    """Per-kernel counter summary of --counter-run: int8 and f64 MFMA work, f64 VALU FMAs, MFMA busy
+    share, LDS, and HBM bytes (FETCH_SIZE / WRITE_SIZE scaled on the streaming kernel as in
+    write_traffic).  Rates use the kernel-trace durations of the compute pass (kernels serialized
+    by the counter collection)."""
+    comp, dur = _dispatch_table(cdir)
+    fet, _ = _dispatch_table(fdir)
+    wri, _ = _dispatch_table(wdir)
+
+    def calib(tab, counter):
+        # the calibration multiplies are the run's last five elementwise-multiply launches (model
+        # loading launches smaller ones earlier)
+        v = [(did, vals[counter]) for did, (n, g, vals) in tab.items()
+             if ("MulFunctor" in n or "mul_kernel" in n) and counter in vals]
+        v = [x for _, x in sorted(v)[-5:]]
+        return COPY_BYTES / (float(np.median(v)) * 1024.0) if v else float("nan")
+
+    ff, fw = calib(fet, "FETCH_SIZE"), calib(wri, "WRITE_SIZE")
+
+    def by_name(tab, prefix):
+        groups = {}
+        for did, (n, g, vals) in tab.items():
+            if n.startswith(prefix):
+                groups.setdefault(g, []).append((did, vals))
+        return groups
+
+    lines = [f"# Per-kernel counters: {cfg.description} ({cfg.name})", "",
+             "Commands (repository root on the GPU host; run from /tmp with TMPDIR=/tmp):", "",
+             "    rocprofv3 --kernel-trace --pmc " + " ".join(COUNTERS_COMPUTE) +
+             " --output-format csv -d gpurun_out/cnt_compute -o p -- python3 bench.py --counter-run",
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/cnt_fetch -o p -- python3 bench.py --counter-run",
+             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/cnt_write -o p -- python3 bench.py --counter-run",
+             "    python3 bench.py --write-counters gpurun_out/cnt_compute gpurun_out/cnt_fetch gpurun_out/cnt_write "
+             "profiles/counters_" + cfg.name + ".md", "",
+             f"Byte counters scaled on a streaming kernel of {COPY_BYTES >> 20} MiB read + written: FETCH_SIZE x "
+             f"{ff:.3f}, WRITE_SIZE x {fw:.3f}.  Per kernel: the group of launches at the full prompt (the most "
+             "launches of that kernel), medians over its launches.  Durations are from the kernel trace of the "
+             "counter pass (kernels serialized), so rates are lower bounds of the bench's.  MFMA busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (duration x 2.4 GHz x 1024 SIMDs); co-exec = VALU issued while the MFMA "
+             "unit was busy, as a share of its busy cycles.  int8 ops count the MFMA's all 32 rows (the odd "
+             "rows carry the f64 conversion constant, no data), so they are 2x the algorithmic 2MNK.", "",
+             "| kernel | launches | us | int8 MFMA ops (vs 2MNK) | int8 TOP/s (% of 5000) | f64 MFMA TFLOP/s | "
+             "f64 VALU FMA TFLOP/s (% of 78.6) | MFMA busy | co-exec | LDS bank conflicts / LDS instr | "
+             "HBM MB (vs algorithmic) | HBM GB/s (% of 8000) |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    med = lambda xs: float(np.median(xs)) if xs else float("nan")
+    for prefix, label, ops_alg, bytes_alg in _forward_kernels(cfg):
+        label = label.replace("|", "\\|")
+        groups = by_name(comp, prefix)
+        if not groups:
+            continue
+        g, disp = max(groups.items(), key=lambda kv: len(kv[1]))
+        ids = [d for d, _ in disp]
+        dns = med([dur[d] for d in ids if d in dur])
+        cv = lambda c: med([v.get(c, float("nan")) for _, v in disp])
+        i8 = cv("SQ_INSTS_VALU_MFMA_MOPS_I8") * 512
+        f64m = cv("SQ_INSTS_VALU_MFMA_MOPS_F64") * 512
+        fma64 = cv("SQ_INSTS_VALU_FMA_F64") * 64 * 2
+        busy = cv("SQ_VALU_MFMA_BUSY_CYCLES")
+        coex = cv("SQ_VALU_MFMA_COEXEC_CYCLES")
+        ldsc = cv("SQ_LDS_BANK_CONFLICT") / max(cv("SQ_INSTS_LDS"), 1.0)
+        fg = by_name(fet, prefix).get(g, [])
+        wg = by_name(wri, prefix).get(g, [])
+        hbm = (med([v["FETCH_SIZE"] for _, v in fg]) * 1024 * ff if fg else float("nan")) + \
+              (med([v["WRITE_SIZE"] for _, v in wg]) * 1024 * fw if wg else float("nan"))
+        s_ = dns * 1e-9
+        r8 = i8 / s_ / 1e12
+        lines.append(
+            f"| {label} | {len(disp)} | {dns / 1e3:.1f} | {i8 / 1e9:.2f} G"
+            + (f" ({i8 / ops_alg:.2f}x)" if ops_alg else "") + f" | {r8:.0f} ({100 * r8 / INT8_PEAK_TOPS:.1f}%) | "
+            f"{f64m / s_ / 1e12:.1f} | {fma64 / s_ / 1e12:.1f} ({100 * fma64 / s_ / 1e12 / F64_VALU_PEAK_TFLOPS:.0f}%) | "
+            f"{100 * busy / (s_ * 2.4e9 * 1024):.0f}% | {100 * coex / busy if busy else 0:.0f}% | {ldsc:.3f} | "
+            f"{hbm / 1e6:.2f} ({hbm / bytes_alg:.2f}x) | {hbm / s_ / 1e9:.0f} ({100 * hbm / s_ / 1e9 / HBM_PEAK_GBS:.0f}%) |")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def _counter_rows(d, counter):
