@@ -272,3 +272,47 @@ def test_large_configs_match_oracle(name):
     say(f"  K regions rel-L2 {d:.3e}, identical {np.mean(gk[:, :used] == kk[:, :used]):.6f}")
     assert d <= 1e-3
     assert np.all(gk[:, used:] == SENTINEL)
+
+
+@pytest.mark.parametrize("name", ["qwen2p5_7b_pp2048", "qwen3_8b_chunk3072at1024"])
+def test_large_configs_full_size_properties(name):
+    """The 7B- and 8B-shaped configurations at full size, in the launch configuration the bench
+    times (eager call and captured-graph replay), checked by properties that hold at any size (the
+    oracle comparison of the same configurations needs minutes of host time: the slow test above):
+    a repeated call and the graph replay give bit-identical logits and KV regions; rows no call
+    wrote keep their sentinel; logits are finite; changing only the last token leaves every KV row
+    at an earlier position bit-identical in every layer, and changes the last position's K row."""
+    dev = need_gpu()
+    cfg = synth.MODEL_CONFIGS[name]
+    say(f"properties {cfg.name}: loading")
+    m = PrefillModel(cfg, synth.iter_tensors(cfg, device=dev), cfg.prefix_tokens + cfg.n_tokens, cfg.n_ctx,
+                     device=dev, kv_fill=SENTINEL)
+    pre_ids, ids = synth.gen_token_ids(cfg)
+    pre_pos, pos = synth.positions_for(cfg)
+    if cfg.prefix_tokens:
+        m.forward(pre_ids, pre_pos)
+    say(f"  eager call x2")
+    l1 = m.forward(ids, pos).clone()
+    k1, v1 = m.kv_k.clone(), m.kv_v.clone()
+    l2 = m.forward(ids, pos).clone()
+    assert torch.equal(l1, l2) and torch.equal(m.kv_k, k1) and torch.equal(m.kv_v, v1)
+    assert bool(torch.isfinite(l1).all())
+    used = int(pos.max()) + 1
+    assert bool((k1[:, used:] == SENTINEL).all()) and bool((v1[:, used:] == SENTINEL).all())
+    assert not bool((k1[:, :used] == SENTINEL).any())
+    say(f"  graph replay")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        g = m.graph(cfg.n_tokens)
+        l3 = g.launch(ids, pos).clone()
+        torch.cuda.synchronize()
+        g.close()
+    assert torch.equal(l1.reshape(-1), l3.reshape(-1)) and torch.equal(m.kv_k, k1) and torch.equal(m.kv_v, v1)
+    say(f"  last token changed")
+    ids2 = ids.copy()
+    ids2[-1] = (ids2[-1] + 1) % cfg.vocab
+    l4 = m.forward(ids2, pos)
+    last = int(pos[-1])
+    assert torch.equal(m.kv_k[:, :last], k1[:, :last]) and torch.equal(m.kv_v[:, :last], v1[:, :last])
+    assert not torch.equal(m.kv_k[0, last], k1[0, last])
+    assert not torch.equal(l4, l1)
