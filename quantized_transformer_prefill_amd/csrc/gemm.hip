@@ -84,6 +84,12 @@ __device__ __forceinline__ void lds_dma2(void* lds, const uint16_t* gbase, uint3
                : "s"(l), "v"(voff), "s"(gbase)
                : "memory", "m0");
 }
+// x, as a value the compiler cannot compute ahead of this point (keeps loop-invariant address
+// arithmetic inside the loop instead of in registers)
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 // s_waitcnt vmcnt(N), expcnt and lgkmcnt left at their maxima
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -189,24 +195,35 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
   // K position goes into the uniform base address.
   constexpr int A_DMA = BM / 32, B_DMA = BN / 32;   // instructions per wave per stage
   const int lchunk = (lane & 7) ^ (lane >> 3);
-  uint32_t a_off[A_DMA], b_off[B_DMA];
+  // The 4-row-group tile keeps one offset per operand: in a tile without row (column) tail the
+  // instructions differ by 32 rows, which go into the uniform base address; a tail tile computes
+  // its clamped offsets at each issue (from a value the compiler cannot hoist), so they hold no
+  // registers through the K loop.
+  constexpr bool LEAN = RG == 4;
+  constexpr int A_OFF = LEAN ? 1 : A_DMA, B_OFF = LEAN ? 1 : B_DMA;
+  const bool a_full = m0 + BM <= M, b_full = n0 + BN <= N;
+  const int a_r0 = m0 + 8 * wave + (lane >> 3), b_r0 = n0 + 8 * wave + (lane >> 3);
+  uint32_t a_off[A_OFF], b_off[B_OFF];
 #pragma unroll
-  for (int q = 0; q < A_DMA; ++q)
-    a_off[q] = (uint32_t)min(m0 + 8 * (4 * q + wave) + (lane >> 3), M - 1) * (uint32_t)K + lchunk * 16;
+  for (int q = 0; q < A_OFF; ++q) a_off[q] = (uint32_t)min(a_r0 + 32 * q, M - 1) * (uint32_t)K + lchunk * 16;
 #pragma unroll
-  for (int q = 0; q < B_DMA; ++q)
-    b_off[q] = (uint32_t)min(n0 + 8 * (4 * q + wave) + (lane >> 3), N - 1) * (uint32_t)K + lchunk * 16;
+  for (int q = 0; q < B_OFF; ++q) b_off[q] = (uint32_t)min(b_r0 + 32 * q, N - 1) * (uint32_t)K + lchunk * 16;
   // ---- scales: global -> LDS directly too, 2 bytes per lane.  Per stage, wave w moves the
-  // A-scale elements AS_L*w + l (l < AS_L; AS_L*w / BM = w is the block, l the row) and the
-  // B-scale elements 64(w + 4i) + l (block (64(w + 4i) + l) / BN, row (64(w + 4i) + l) % BN).
-  constexpr int AS_L = BM * G_KS / 4;       // 32 or 64
+  // A scales of block w (rows 64i + l, l < AS_L, one instruction per 64 rows) and the B-scale
+  // elements 64(w + 4i) + l (block (64(w + 4i) + l) / BN, row (64(w + 4i) + l) % BN).
+  static_assert(G_KS == 4, "one A-scale block per wave");
+  constexpr int AS_L = BM < 64 ? BM : 64;   // lanes per A-scale instruction
+  constexpr int AS_I = BM / AS_L;           // A-scale instructions per wave: 1 or 2
   constexpr int BS_I = BN * G_KS / 256;     // 1 or 2
-  static_assert(AS_L * 4 == BM * G_KS && BS_I * 256 == BN * G_KS, "scale transfer shape");
-  constexpr int L_OPS = A_DMA + B_DMA + 1 + BS_I;  // transfers per wave per stage
-  const uint32_t as_off = (uint32_t)min(m0 + lane, M - 1) * (uint32_t)(KB * 2);
-  uint32_t bs_off[BS_I];
+  static_assert(AS_L * AS_I == BM && BS_I * 256 == BN * G_KS, "scale transfer shape");
+  constexpr int L_OPS = A_DMA + B_DMA + AS_I + BS_I;  // transfers per wave per stage
+  constexpr int AS_OFF = LEAN ? 1 : AS_I;
+  uint32_t as_off[AS_OFF];
 #pragma unroll
-  for (int i = 0; i < BS_I; ++i) bs_off[i] = (uint32_t)min(n0 + (64 * (wave + 4 * i) + lane) % BN, N - 1) * (uint32_t)(KB * 2);
+  for (int i = 0; i < AS_OFF; ++i) as_off[i] = (uint32_t)min(m0 + 64 * i + lane, M - 1) * (uint32_t)(KB * 2);
+  // row (64(w + 4i) + l) % BN does not depend on i (256 is a multiple of BN)
+  static_assert(256 % BN == 0, "B-scale rows");
+  const uint32_t bs_off = (uint32_t)min(n0 + (64 * wave + lane) % BN, N - 1) * (uint32_t)(KB * 2);
   auto issue = [&](int kbs, int st) {
     // a stage past the end of the slice (K not a multiple of the stage) re-reads its last block
     // for the missing ones; compute() skips them
@@ -214,15 +231,47 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
     const uint32_t fix = nbk < G_KS ? (uint32_t)((min(lchunk, 2 * nbk - 1) - lchunk) * 16) : 0u;
     const int8_t* ga = a_codes + (int64_t)kbs * QK;
     const int8_t* gb = w_codes + (int64_t)kbs * QK;
+    const uint16_t* gas = a_scales + kbs + min(wave, nbk - 1);
+    if constexpr (LEAN) {
+      if (a_full) {
 #pragma unroll
-    for (int q = 0; q < A_DMA; ++q) lds_dma16(&sm.a[st][8 * (4 * q + wave)][0], ga, a_off[q] + fix);
+        for (int q = 0; q < A_DMA; ++q) lds_dma16(&sm.a[st][8 * (4 * q + wave)][0], ga + (int64_t)32 * q * K, a_off[0] + fix);
 #pragma unroll
-    for (int q = 0; q < B_DMA; ++q) lds_dma16(&sm.b[st][8 * (4 * q + wave)][0], gb, b_off[q] + fix);
-    if (lane < AS_L) lds_dma2(&sm.as[st][0][0] + AS_L * wave, a_scales + kbs + min(wave, nbk - 1), as_off);
+        for (int i = 0; i < AS_I; ++i)
+          if (lane < AS_L) lds_dma2(&sm.as[st][wave][64 * i], gas + (int64_t)64 * i * KB, as_off[0]);
+      } else {
+        const int r0 = (int)opaque_u32((uint32_t)a_r0), l0 = (int)opaque_u32((uint32_t)lane);
+#pragma unroll
+        for (int q = 0; q < A_DMA; ++q)
+          lds_dma16(&sm.a[st][8 * (4 * q + wave)][0], ga,
+                    (uint32_t)min(r0 + 32 * q, M - 1) * (uint32_t)K + lchunk * 16 + fix);
+#pragma unroll
+        for (int i = 0; i < AS_I; ++i)
+          if (lane < AS_L) lds_dma2(&sm.as[st][wave][64 * i], gas, (uint32_t)min(m0 + 64 * i + l0, M - 1) * (uint32_t)(KB * 2));
+      }
+      if (b_full) {
+#pragma unroll
+        for (int q = 0; q < B_DMA; ++q) lds_dma16(&sm.b[st][8 * (4 * q + wave)][0], gb + (int64_t)32 * q * K, b_off[0] + fix);
+      } else {
+        const int r0 = (int)opaque_u32((uint32_t)b_r0);
+#pragma unroll
+        for (int q = 0; q < B_DMA; ++q)
+          lds_dma16(&sm.b[st][8 * (4 * q + wave)][0], gb,
+                    (uint32_t)min(r0 + 32 * q, N - 1) * (uint32_t)K + lchunk * 16 + fix);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < A_DMA; ++q) lds_dma16(&sm.a[st][8 * (4 * q + wave)][0], ga, a_off[q] + fix);
+#pragma unroll
+      for (int q = 0; q < B_DMA; ++q) lds_dma16(&sm.b[st][8 * (4 * q + wave)][0], gb, b_off[q] + fix);
+#pragma unroll
+      for (int i = 0; i < AS_I; ++i)
+        if (lane < AS_L) lds_dma2(&sm.as[st][wave][64 * i], gas, as_off[i]);
+    }
 #pragma unroll
     for (int i = 0; i < BS_I; ++i)
       lds_dma2(&sm.bs[st][0][0] + 64 * (wave + 4 * i), w_scales + kbs + min(64 * (wave + 4 * i) / BN, nbk - 1),
-               bs_off[i]);
+               bs_off);
   };
 
   v16i cinit;
@@ -269,9 +318,12 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
 #pragma unroll
       for (int cg = 0; cg < CG; ++cg)
         fb[cg] = *reinterpret_cast<const v4i*>(&sm.b[st][b_rrow + cg * 32][swz(b_rrow, 2 * jb + khalf)]);
+      // 4-row-group tiles produce and consume the MFMA results one row group at a time (all of
+      // them at once would not fit in the registers of two waves per SIMD)
+      constexpr int RD = RG == 4 ? 1 : RG;
       v16i d[RG][CG];
 #pragma unroll
-      for (int rg = 0; rg < RG; ++rg)
+      for (int rg = 0; rg < RD; ++rg)
 #pragma unroll
         for (int cg = 0; cg < CG; ++cg) d[rg][cg] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[rg], fb[cg], cinit, 0, 0, 0);
       double dw[CG], cdw[CG];
@@ -284,6 +336,9 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
       for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
         for (int cg = 0; cg < CG; ++cg) {
+          if constexpr (RD < RG) {
+            if (rg > 0) d[rg][cg] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[rg], fb[cg], cinit, 0, 0, 0);
+          }
           // the 8 (even, odd) register pairs are the f64 values 1.5*2^52 + 2^31 + I
           v8d xv = __builtin_bit_cast(v8d, d[rg][cg]);
           double x[8];
@@ -522,7 +577,8 @@ __global__ void __launch_bounds__(256) k_splitk_swiglu(const double* __restrict_
 
 // Tile and split choice: aim for at least ~4 waves per CU of independent work; split K only when
 // the output tiles alone cannot fill the chip, keeping >= 2 stages (8 blocks) per split.
-// Tile shapes: 0 = 1x1 MFMA wave tile (workgroup 32 x 64), 1 = 2x2 (64 x 128), 2 = 1x2 (32 x 128).
+// Tile shapes: 0 = 1x1 MFMA wave tile (workgroup 32 x 64), 1 = 2x2 (64 x 128), 2 = 1x2 (32 x 128),
+// 3 = 4x2 (128 x 128).
 struct GemmPlan { int shape; int split; };
 
 static GemmPlan plan_gemm(int m, int n, int k, bool swiglu) {
@@ -542,7 +598,13 @@ static GemmPlan plan_gemm(int m, int n, int k, bool swiglu) {
   const int target = 512;
   const size_t max_partial = KB >= 256 ? ((size_t)64 << 20) : ((size_t)8 << 20);
   if (KB >= 256 && tiles_big >= 128 && !swiglu) p.shape = 1;  // long reductions: big tiles, split K
-  const int tiles2 = p.shape == 1 ? tiles_big : tiles;
+#ifndef MI_TILE42_MIN_M
+#define MI_TILE42_MIN_M 1024
+#endif
+  // many rows: 128 x 128 workgroups (fewer transfers and fragment reads per output)
+  const int tiles_huge = ((m + 127) / 128) * ((n + 127) / 128);
+  if (p.shape == 1 && m >= MI_TILE42_MIN_M) p.shape = 3;
+  const int tiles2 = p.shape == 1 ? tiles_big : p.shape == 3 ? tiles_huge : tiles;
   if (KB > 64)
     while (p.split < 16 && tiles2 * p.split < target && KB / (p.split * 2) >= 2 * G_KS &&
            (size_t)(p.split * 2) * m * n * sizeof(double) <= max_partial)
@@ -603,7 +665,8 @@ int launch_gemm_q8(const GemmArgs& g, hipStream_t s) {
   int kb_per = (KB + split - 1) / split;
   kb_per = ((kb_per + G_KS - 1) / G_KS) * G_KS;
   split = (KB + kb_per - 1) / kb_per;
-  if (p.shape == 1) launch_tiles<2, 2, G_NS_22>(g, split, kb_per, s);
+  if (p.shape == 3) launch_tiles<4, 2, G_NS_22>(g, split, kb_per, s);
+  else if (p.shape == 1) launch_tiles<2, 2, G_NS_22>(g, split, kb_per, s);
   else if (p.shape == 2) launch_tiles<1, 2, G_NS_12>(g, split, kb_per, s);
   else launch_tiles<1, 1, G_NS_11>(g, split, kb_per, s);
   MI_LAUNCH_CHECK("k_gemm_q8");

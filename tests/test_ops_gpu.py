@@ -73,6 +73,8 @@ GEMM_CASES = [  # m, k, n, bias, residual, split
     (45, 160, 224, False, False, 1),     # one 1-block stage after a full one; row and column tails
     (3, 96, 96, True, False, 1),         # K shorter than one 4-block stage
     (520, 160, 8224, False, True, 0),    # 2x2 tiles with row, column and K-stage tails
+    (1030, 160, 3936, True, True, 1),    # 4x2 wave tiles (128 x 128 workgroups): row, column, K-stage tails
+    (1024, 8192, 1024, False, False, 0), # 4x2 tiles, split K chosen by the library
 ]
 
 
@@ -133,8 +135,9 @@ def test_gemm_full_size_sampled(case):
 
 def test_gemm_swiglu_matches_oracle():
     dev = need_gpu()
-    # 1x2 wave tiles for the first three, 2x2 for the last (>= 1024 workgroup tiles)
-    for m, k, f in [(100, 896, 320), (16, 3584, 512), (1, 896, 4864), (512, 256, 8192)]:
+    # 1x2 wave tiles for the first three, 2x2 for the fourth (>= 1024 workgroup tiles), 4x2 for
+    # the last (>= 1024 rows as well)
+    for m, k, f in [(100, 896, 320), (16, 3584, 512), (1, 896, 4864), (512, 256, 8192), (1100, 256, 3680)]:
         say(f"gemm+swiglu m={m} k={k} ffn={f}")
         x = synth.gen_normal(31, f"x{m}", (m, k), device=dev)
         wg = synth.gen_normal(32, f"g{f}", (f, k), std=0.02, device=dev)
