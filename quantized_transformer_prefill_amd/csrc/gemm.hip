@@ -17,7 +17,8 @@
 //   MFMA: half-used MFMAs cost nothing extra.
 //
 // Tiling: 256 threads = 4 waves (2 x 2).  Wave tile RG x CG MFMAs of 16 real rows x 32 columns:
-// 2 x 2 (workgroup 64 x 128) for large problems, 1 x 1 (workgroup 32 x 64) for small ones.  A
+// 4 x 2 (workgroup 128 x 128) for large problems of >= 1024 rows, 2 x 2 (64 x 128) for other
+// large ones, 1 x 2 (32 x 128) and 1 x 1 (workgroup 32 x 64) for small ones.  A
 // stage of 4 blocks (128 K values) of codes and f64 scales goes through LDS, double-buffered,
 // with the next stage's global loads in flight while the current one computes.  Split-K writes f64 partials that a second kernel
 // reduces in a fixed order (deterministic).
