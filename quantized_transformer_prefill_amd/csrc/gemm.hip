@@ -581,6 +581,9 @@ __global__ void __launch_bounds__(256) k_splitk_swiglu(const double* __restrict_
 // Tile shapes: 0 = 1x1 MFMA wave tile (workgroup 32 x 64), 1 = 2x2 (64 x 128), 2 = 1x2 (32 x 128),
 // 3 = 4x2 (128 x 128).
 struct GemmPlan { int shape; int split; };
+#ifndef G_TILE42_REL
+#define G_TILE42_REL 0.89  // time of a 4x2-tile workgroup / two 2x2-tile workgroups (measured)
+#endif
 
 static GemmPlan plan_gemm(int m, int n, int k, bool swiglu) {
   const int KB = k / QK;
@@ -599,17 +602,26 @@ static GemmPlan plan_gemm(int m, int n, int k, bool swiglu) {
   const int target = 512;
   const size_t max_partial = KB >= 256 ? ((size_t)64 << 20) : ((size_t)8 << 20);
   if (KB >= 256 && tiles_big >= 128 && !swiglu) p.shape = 1;  // long reductions: big tiles, split K
-#ifndef MI_TILE42_MIN_M
-#define MI_TILE42_MIN_M 1024
-#endif
-  // many rows: 128 x 128 workgroups (fewer transfers and fragment reads per output)
+  auto split_for = [&](int t) {
+    int sp = 1;
+    if (KB > 64)
+      while (sp < 16 && t * sp < target && KB / (sp * 2) >= 2 * G_KS &&
+             (size_t)(sp * 2) * m * n * sizeof(double) <= max_partial)
+        sp *= 2;
+    return sp;
+  };
+  // 128 x 128 workgroups (4x2 wave tiles) do the same work in fewer transfers and fragment reads
+  // per output (measured: 0.89x the time of two 64 x 128 workgroups), but half as many
+  // workgroups fill the chip's 512 slots (two per CU) in coarser rounds.  Cost of a plan: rounds
+  // of workgroups x area of a workgroup / split.
   const int tiles_huge = ((m + 127) / 128) * ((n + 127) / 128);
-  if (p.shape == 1 && m >= MI_TILE42_MIN_M) p.shape = 3;
-  const int tiles2 = p.shape == 1 ? tiles_big : p.shape == 3 ? tiles_huge : tiles;
-  if (KB > 64)
-    while (p.split < 16 && tiles2 * p.split < target && KB / (p.split * 2) >= 2 * G_KS &&
-           (size_t)(p.split * 2) * m * n * sizeof(double) <= max_partial)
-      p.split *= 2;
+  if (p.shape == 1 && m >= 256) {
+    const int s22 = split_for(tiles_big), s42 = split_for(tiles_huge);
+    const double c22 = (double)((tiles_big * s22 + 511) / 512) / s22;
+    const double c42 = (double)((tiles_huge * s42 + 511) / 512) * (2.0 * G_TILE42_REL) / s42;
+    if (c42 < c22) p.shape = 3;
+  }
+  p.split = split_for(p.shape == 1 ? tiles_big : p.shape == 3 ? tiles_huge : tiles);
   return p;
 }
 

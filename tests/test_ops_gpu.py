@@ -72,9 +72,11 @@ GEMM_CASES = [  # m, k, n, bias, residual, split
     (256, 512, 16384, True, False, 0),   # 2x2 wave tiles (64 x 128 workgroups)
     (45, 160, 224, False, False, 1),     # one 1-block stage after a full one; row and column tails
     (3, 96, 96, True, False, 1),         # K shorter than one 4-block stage
-    (520, 160, 8224, False, True, 0),    # 2x2 tiles with row, column and K-stage tails
-    (1030, 160, 3936, True, True, 1),    # 4x2 wave tiles (128 x 128 workgroups): row, column, K-stage tails
+    (520, 160, 8224, False, True, 0),    # 4x2 wave tiles (128 x 128 workgroups): row, column, K-stage tails
+    (520, 160, 16608, True, False, 0),   # 2x2 tiles with row, column and K-stage tails
+    (1030, 160, 3936, True, True, 1),    # 4x2 tiles: row, column, K-stage tails
     (1024, 8192, 1024, False, False, 0), # 4x2 tiles, split K chosen by the library
+    (600, 8192, 1664, True, True, 0),    # 4x2 tiles for a long reduction over fewer rows, split K, row tail
 ]
 
 
@@ -135,8 +137,8 @@ def test_gemm_full_size_sampled(case):
 
 def test_gemm_swiglu_matches_oracle():
     dev = need_gpu()
-    # 1x2 wave tiles for the first three, 2x2 for the fourth (>= 1024 workgroup tiles), 4x2 for
-    # the last (>= 1024 rows as well)
+    # 1x2 wave tiles for the first three, then 4x2 (128 x 128 workgroups) and 2x2 (64 x 128): the
+    # library picks the one that fills the chip's workgroup slots in fewer rounds
     for m, k, f in [(100, 896, 320), (16, 3584, 512), (1, 896, 4864), (512, 256, 8192), (1100, 256, 3680)]:
         say(f"gemm+swiglu m={m} k={k} ffn={f}")
         x = synth.gen_normal(31, f"x{m}", (m, k), device=dev)
