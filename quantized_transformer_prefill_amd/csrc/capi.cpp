@@ -447,8 +447,14 @@ static int enqueue_forward(const mi_model* md, const Ws& w, int32_t n_tokens, in
     go.w_codes = L.wo.codes; go.w_scales = L.wo.scales; go.n = H; go.k = nq;
     go.residual = h_rows; go.out = h_rows; go.ld_out = H;
     go.workspace = w.gemm_ws; go.workspace_bytes = w.gemm_ws_bytes;
+    // split-K partials of the output projection (short reductions included), reduced with its
+    // residual add by the FFN RMSNorm
+    int pending_o = 1;
+    go.split_out = &pending_o;
     if ((rc = launch_gemm_q8(go, s))) return rc;
-    if ((rc = launch_rmsnorm_quant(h_rows, L.ffn_norm, rows, H, eps, w.xq, w.xs, nullptr, s))) return rc;
+    if ((rc = launch_rmsnorm_quant(h_rows, L.ffn_norm, rows, H, eps, w.xq, w.xs, nullptr, s, (const double*)w.gemm_ws,
+                                   pending_o)))
+      return rc;
     GemmArgs gg{};
     gg.a_codes = w.xq; gg.a_scales = w.xs; gg.m = rows;
     gg.w_codes = L.w_gate_up.codes; gg.w_scales = L.w_gate_up.scales; gg.n = 2 * F; gg.k = H;

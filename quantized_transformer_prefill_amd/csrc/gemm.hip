@@ -585,7 +585,9 @@ struct GemmPlan { int shape; int split; };
 #define G_TILE42_REL 0.89  // time of a 4x2-tile workgroup / two 2x2-tile workgroups (measured)
 #endif
 
-static GemmPlan plan_gemm(int m, int n, int k, bool swiglu) {
+// defer: the caller reduces f32-epilogue partials itself (no reduction kernel), which makes a
+// split worth it for short reductions too.
+static GemmPlan plan_gemm(int m, int n, int k, bool swiglu, bool defer = false) {
   const int KB = k / QK;
   GemmPlan p{1, 1};
   const int tiles_big = ((m + 63) / 64) * ((n + 127) / 128);
@@ -602,10 +604,12 @@ static GemmPlan plan_gemm(int m, int n, int k, bool swiglu) {
   const int target = 512;
   const size_t max_partial = KB >= 256 ? ((size_t)64 << 20) : ((size_t)8 << 20);
   if (KB >= 256 && tiles_big >= 128 && !swiglu) p.shape = 1;  // long reductions: big tiles, split K
+  // blocks per split at least 2 stages (1.5 for deferred partials)
+  const int min_kb = defer ? 3 * G_KS / 2 : 2 * G_KS;
   auto split_for = [&](int t) {
     int sp = 1;
-    if (KB > 64)
-      while (sp < 16 && t * sp < target && KB / (sp * 2) >= 2 * G_KS &&
+    if (KB > (defer ? 16 : 64))
+      while (sp < 16 && t * sp < target && KB / (sp * 2) >= min_kb &&
              (size_t)(sp * 2) * m * n * sizeof(double) <= max_partial)
         sp *= 2;
     return sp;
@@ -628,7 +632,8 @@ static GemmPlan plan_gemm(int m, int n, int k, bool swiglu) {
 size_t gemm_workspace_bytes(int m, int n, int k) {
   const GemmPlan p = plan_gemm(m, n, k, false);
   const GemmPlan q = plan_gemm(m, n, k, true);
-  const int s = std::max(p.split, q.split);
+  const GemmPlan d = plan_gemm(m, n, k, false, true);
+  int s = std::max(std::max(p.split, q.split), d.split);
   return s > 1 ? (size_t)s * m * n * sizeof(double) : 0;
 }
 
@@ -661,7 +666,8 @@ static void launch_tiles(const GemmArgs& g, int split, int kb_per, hipStream_t s
 int launch_gemm_q8(const GemmArgs& g, hipStream_t s) {
   if (g.m == 0) return MI_OK;
   const int KB = g.k / QK;
-  GemmPlan p = plan_gemm(g.m, g.n, g.k, g.q_codes != nullptr);
+  GemmPlan p = plan_gemm(g.m, g.n, g.k, g.q_codes != nullptr,
+                         g.split_out && !g.q_codes && !g.bias && !g.qkv.pos);
   if (g.split_k > 0) p.split = g.split_k;
   if (g.qkv.pos) {  // whole heads per tile, no split
     p.split = 1;
