@@ -122,6 +122,7 @@ def main():
     pre_pos, pos = synth.positions_for(cfg)
     if cfg.prefix_tokens:  # untimed: the KV rows of the earlier positions; each timed chunk call
         model.forward(pre_ids, pre_pos)  # rewrites the same chunk rows with the same values
+        torch.cuda.synchronize()  # the calls below run on another stream
     if args.decode:
         decode_bench(args, cfg, model, ids, pos, load_s)
         return
