@@ -710,7 +710,7 @@ int launch_gemm_q8(const GemmArgs& g, hipStream_t s) {
 
 // ---------------------------------------------------------------- last-row lm_head
 // logits[v] = f32( sum_kb dx[kb] * dw[v][kb] * sum_32 qx * qw ), one row of activations.
-// HBM-bound: every weight byte is read once.  One wave per weight row at a time; a lane
+// HBM-bound: every weight byte is read once.  One wave per two weight rows at a time; a lane
 // takes 16-byte chunks (half a block), sdot4 gives the integer half-block sums, lane pairs
 // combine to the block sum, and the exact f64 epilogue accumulates per lane.
 constexpr int LM_MAXC = 4;  // 16-byte activation chunks held per lane (K <= 4096)
@@ -732,28 +732,57 @@ __global__ void __launch_bounds__(256) k_lm_head(const int8_t* __restrict__ xq, 
     xc[c] = ch < nchunk ? *reinterpret_cast<const v4i*>(xq + ch * 16) : v4i{0, 0, 0, 0};
     xd[c] = ch < nchunk ? (double)f16_bits_to_f32(xs[ch / 2]) : 0.0;
   }
-  for (int64_t r = wave; r < rows; r += nwaves) {
+  // two rows per wave and iteration (r and r + nwaves), both rows' loads issued before either's
+  // arithmetic: twice the bytes in flight per wave
+  for (int64_t r = wave; r < rows; r += 2 * nwaves) {
+    const int64_t r2 = r + nwaves;
+    const bool two = r2 < rows;  // uniform in the wave
     const int8_t* wr = w_codes + r * K;
     const uint16_t* wsr = w_scales + r * KB;
-    double acc = 0.0;
+    const int8_t* wr2 = w_codes + (two ? r2 : r) * K;
+    const uint16_t* wsr2 = w_scales + (two ? r2 : r) * KB;
+    v4i wv[LM_MAXC], wv2[LM_MAXC];
+    uint16_t sb[LM_MAXC], sb2[LM_MAXC];
 #pragma unroll
     for (int c = 0; c < LM_MAXC; ++c) {
       const int ch = lane + 64 * c;
-      int isum = 0;
-      double dw = 0.0;
       if (ch < nchunk) {
-        const v4i wv = *reinterpret_cast<const v4i*>(wr + ch * 16);
-        isum = __builtin_amdgcn_sdot4(xc[c][0], wv[0], isum, false);
-        isum = __builtin_amdgcn_sdot4(xc[c][1], wv[1], isum, false);
-        isum = __builtin_amdgcn_sdot4(xc[c][2], wv[2], isum, false);
-        isum = __builtin_amdgcn_sdot4(xc[c][3], wv[3], isum, false);
-        dw = (double)f16_bits_to_f32(wsr[ch / 2]);
+        wv[c] = *reinterpret_cast<const v4i*>(wr + ch * 16);
+        wv2[c] = *reinterpret_cast<const v4i*>(wr2 + ch * 16);
+        sb[c] = wsr[ch / 2];
+        sb2[c] = wsr2[ch / 2];
+      }
+    }
+    double acc = 0.0, acc2 = 0.0;
+#pragma unroll
+    for (int c = 0; c < LM_MAXC; ++c) {
+      const int ch = lane + 64 * c;
+      int isum = 0, isum2 = 0;
+      double dw = 0.0, dw2 = 0.0;
+      if (ch < nchunk) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          isum = __builtin_amdgcn_sdot4(xc[c][e], wv[c][e], isum, false);
+          isum2 = __builtin_amdgcn_sdot4(xc[c][e], wv2[c][e], isum2, false);
+        }
+        dw = (double)f16_bits_to_f32(sb[c]);
+        dw2 = (double)f16_bits_to_f32(sb2[c]);
       }
       isum += __shfl_xor(isum, 1);  // both lanes of the pair now hold the block sum
-      if ((lane & 1) == 0 && ch < nchunk) acc = fma((double)isum * dw, xd[c], acc);
+      isum2 += __shfl_xor(isum2, 1);
+      if ((lane & 1) == 0 && ch < nchunk) {
+        acc = fma((double)isum * dw, xd[c], acc);
+        acc2 = fma((double)isum2 * dw2, xd[c], acc2);
+      }
     }
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-    if (lane == 0) logits[r] = (float)acc;
+    for (int o = 32; o > 0; o >>= 1) {
+      acc += __shfl_xor(acc, o);
+      acc2 += __shfl_xor(acc2, o);
+    }
+    if (lane == 0) {
+      logits[r] = (float)acc;
+      if (two) logits[r2] = (float)acc2;
+    }
   }
 }
 
