@@ -19,7 +19,7 @@ SENTINEL = -777.25
 MAX_ABS, REL_L2 = 2e-2, 1e-3
 
 
-def load_pair(cfg, dev, max_tokens=None):
+def load_pair(cfg, dev, max_tokens=None, kv_fill=SENTINEL):
     """GPU model and oracle weights from the same seeded draws (drawn once, on the device)."""
     host = {}
 
@@ -29,7 +29,7 @@ def load_pair(cfg, dev, max_tokens=None):
             yield name, kind, t
 
     m = PrefillModel(cfg, tensors(), max_tokens or cfg.prefix_tokens + cfg.n_tokens, cfg.n_ctx, device=dev,
-                     kv_fill=SENTINEL)
+                     kv_fill=kv_fill)
     q8 = [n for n, s, k in synth.tensor_specs(cfg) if k == "q8"]
     return m, oracle.weights_from_arrays(host, q8)
 
@@ -174,6 +174,37 @@ def test_prefill_equals_replay_and_chunks_on_gpu():
     m.forward(ids[:5], pos[:5])                         # prefix, then the rest at later positions
     two = m.forward(ids[5:], pos[5:]).cpu().numpy().copy()
     assert_f32_match(two, full, max_ulp=4, max_frac_inexact=0.01, what="chunked logits")
+
+
+TINY_PERM = synth.ModelConfig(name="tiny_qwen2_perm", n_layers=2, hidden=128, n_head=4, n_head_kv=1, head_dim=64,
+                              ffn=192, vocab=700, n_tokens=37, n_ctx=64, seed=9, qkv_bias=True)
+
+
+def test_forward_positions_out_of_order_match_oracle():
+    """Positions are data (a token at position p attends to region rows 0..p after this call's
+    stores): 37 tokens given out of order with gaps, the largest position n_ctx - 1 on a middle
+    token and not on the last one, whose logits are returned (row nt - 1).  Rows the call does not
+    write keep what the caller left there (zeros) and are read as such by later positions."""
+    dev = need_gpu()
+    cfg = TINY_PERM
+    m, w = load_pair(cfg, dev, kv_fill=0.0)
+    _, ids = synth.gen_token_ids(cfg)
+    rng = np.random.default_rng(11)
+    pos = rng.choice(cfg.n_ctx - 1, cfg.n_tokens, replace=False).astype(np.int32)
+    pos[cfg.n_tokens // 2] = cfg.n_ctx - 1
+    say(f"forward {cfg.name}: positions {pos.tolist()}")
+    kk, vv = oracle.new_kv_regions(cfg, cfg.n_ctx, fill=0.0)
+    got = m.forward(ids, pos).cpu().numpy()
+    want = oracle.prefill_forward(cfg, w, ids, pos, cfg.n_ctx, kk, vv)[0]
+    compare_logits(got, want, f"{cfg.name} logits")
+    written = np.zeros(cfg.n_ctx, dtype=bool)
+    written[pos] = True
+    gk, gv = m.kv_k.cpu().numpy(), m.kv_v.cpu().numpy()
+    assert np.all(gk[:, ~written] == 0) and np.all(gv[:, ~written] == 0)
+    for name, g, o in (("K", gk, kk), ("V", gv, vv)):
+        d = np.linalg.norm(g[:, written] - o[:, written]) / np.linalg.norm(o[:, written])
+        say(f"  {name} rows rel-L2 {d:.3e}")
+        assert d <= 1e-3
 
 
 def test_future_tokens_leave_earlier_kv_rows_bit_identical():
