@@ -581,9 +581,7 @@ __global__ void __launch_bounds__(256) k_splitk_swiglu(const double* __restrict_
 // Tile shapes: 0 = 1x1 MFMA wave tile (workgroup 32 x 64), 1 = 2x2 (64 x 128), 2 = 1x2 (32 x 128),
 // 3 = 4x2 (128 x 128).
 struct GemmPlan { int shape; int split; };
-#ifndef G_TILE42_REL
-#define G_TILE42_REL 0.89  // time of a 4x2-tile workgroup / two 2x2-tile workgroups (measured)
-#endif
+constexpr double G_TILE42_REL = 0.89;  // time of a 4x2-tile workgroup / two 2x2-tile workgroups (measured)
 
 // defer: the caller reduces f32-epilogue partials itself (no reduction kernel), which makes a
 // split worth it for short reductions too.
