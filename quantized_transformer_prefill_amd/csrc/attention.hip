@@ -163,10 +163,14 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
     pmin = min(pmin, __shfl_xor(pmin, o));
   }
 
-  // query fragment: dims slot*Q4 + s.  head_dim 64: f64, pre-multiplied by the score factor.
-  // head_dim 128: f32 (exact; widened at each MFMA, which halves its registers), the scores
-  // multiplied by the factor after the dot products.
+  // query fragment: dims slot*Q4 + s, f64, pre-multiplied by the score factor.  head_dim 64: in
+  // registers.  head_dim 128: in LDS (16 KB per group, laid out [slot][s/2][query][s%2] so that
+  // the 16 lanes of a slot read 256 contiguous bytes), read at each pair of score MFMAs: LDS
+  // reads do not stall the f64 MFMA the way VALU widening does, and the registers stay free.
   constexpr bool QWIDE = HD <= 64;
+  constexpr bool QLDS = !QWIDE;
+  static_assert(!QLDS || NG == 1, "one query group per workgroup with the query in LDS");
+  __shared__ double2 sh_q[QLDS ? 4 * (Q4 / 2) * 16 : 1];
   const double scale = 0x1.71547652b82fep+0 / sqrt((double)HD);  // log2(e) / sqrt(hd)
   f4v qf[Q4 / 4];
   double qd[QWIDE ? Q4 : 1];
@@ -177,12 +181,16 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
     if constexpr (QWIDE) {
 #pragma unroll
       for (int s = 0; s < Q4; ++s) qd[s] = (double)qf[s / 4][s % 4] * scale;
+    } else {
+      if (wave == 0) {
+#pragma unroll
+        for (int s = 0; s < Q4; s += 2)
+          sh_q[(slot * (Q4 / 2) + s / 2) * 16 + qi] =
+              double2{(double)qf[s / 4][s % 4] * scale, (double)qf[(s + 1) / 4][(s + 1) % 4] * scale};
+      }
     }
   }
-  auto qop = [&](int s) -> double {
-    if constexpr (QWIDE) return qd[s];
-    else return f4get(qf[s / 4], s % 4);
-  };
+  const double2* sq = sh_q + slot * (Q4 / 2) * 16 + qi;  // this lane's query pairs, stride 16
 
   v4d acc[NB];
 #pragma unroll
@@ -204,16 +212,22 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
   for (int tile = wave; tile < ntiles; tile += NW) {
     const int key0 = tile * 16;
     const bool more = tile + NW < ntiles;
-    if constexpr (!QWIDE) {
-      // keep the f32 query in the loop: otherwise its f64 widening is hoisted and holds twice the registers
-#pragma unroll
-      for (int s = 0; s < Q4 / 4; ++s) asm volatile("" : "+v"(qf[s]));
-    }
+    // the query pairs are read from LDS in the loop (not hoisted into registers)
+    if constexpr (QLDS) asm volatile("" ::: "memory");
     v4d sc0 = {0.0, 0.0, 0.0, 0.0}, sc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int s = 0; s < Q4; s += 2) {
-      sc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(kt.k[s / 4], s % 4), qop(s), sc0, 0, 0, 0);
-      sc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(kt.k[(s + 1) / 4], (s + 1) % 4), qop(s + 1), sc1, 0, 0, 0);
+      double q0, q1;
+      if constexpr (QLDS) {
+        const double2 qq = sq[(s / 2) * 16];
+        q0 = qq.x;
+        q1 = qq.y;
+      } else {
+        q0 = qd[s];
+        q1 = qd[s + 1];
+      }
+      sc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(kt.k[s / 4], s % 4), q0, sc0, 0, 0, 0);
+      sc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(kt.k[(s + 1) / 4], (s + 1) % 4), q1, sc1, 0, 0, 0);
     }
     if (more) load_k<HD>(kt, kbase, kv_embd, key0 + 16 * NW, max_pos, qi, slot);
     // ---- online softmax for query l%16 over keys key0 + 4i + slot
@@ -222,7 +236,7 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
     double tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sv[i] = QWIDE ? sc0[i] + sc1[i] : (sc0[i] + sc1[i]) * scale;
+      sv[i] = sc0[i] + sc1[i];
       if (!full && key0 + 4 * i + slot > p) sv[i] = -INFINITY;
       tmax = fmax(tmax, sv[i]);
     }
