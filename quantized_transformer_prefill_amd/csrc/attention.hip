@@ -27,8 +27,9 @@
 // l%16), D register i lane l -> (m = 4i + l/16, n = l%16).
 //  * scores S^T = K . Q^T  (m = key, n = query, k = head dims): the order of the dims in the
 //    contraction is free, so lane slot g = l/16 owns the contiguous dims [g*hd/4, (g+1)*hd/4) and
-//    MFMA s uses dim g*hd/4 + s: K and Q are read as float4s.  Two accumulators (even/odd s) keep
-//    the MFMA dependency chain short.
+//    MFMA s uses dim g*hd/4 + s: K is read from the region as float4s, Q (f64, stored in LDS
+//    once per workgroup) as pairs for MFMAs s, s+1.  Two accumulators (even/odd s) keep the MFMA
+//    dependency chain short.
 //  * lane l then holds the scores of query l%16 against keys 4i + l/16 (i = 0..3); the max over
 //    a query's keys reduces over the 4 registers and the lanes l^16, l^32.
 //  * O^T += V^T . P^T  (m = output dim, n = query, k = key): MFMA c takes key slot s = l/16 as key
@@ -163,34 +164,23 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
     pmin = min(pmin, __shfl_xor(pmin, o));
   }
 
-  // query fragment: dims slot*Q4 + s, f64, pre-multiplied by the score factor.  head_dim 64: in
-  // registers.  head_dim 128: in LDS (16 KB per group, laid out [slot][s/2][query][s%2] so that
-  // the 16 lanes of a slot read 256 contiguous bytes), read at each pair of score MFMAs: LDS
-  // reads do not stall the f64 MFMA the way VALU widening does, and the registers stay free.
-  constexpr bool QWIDE = HD <= 64;
-  constexpr bool QLDS = !QWIDE;
-  static_assert(!QLDS || NG == 1, "one query group per workgroup with the query in LDS");
-  __shared__ double2 sh_q[QLDS ? 4 * (Q4 / 2) * 16 : 1];
+  // query fragment: dims slot*Q4 + s, f64, pre-multiplied by the score factor, in LDS (per group
+  // 8 KB at head_dim 64, 16 KB at 128, laid out [slot][s/2][query][s%2] so that the 16 lanes of a
+  // slot read 256 contiguous bytes), read as a pair at each pair of score MFMAs.  LDS reads do not
+  // stall the f64 MFMA the way VALU instructions do, and the registers stay free for the tiles.
+  __shared__ double2 sh_q[NG * 4 * (Q4 / 2) * 16];
   const double scale = 0x1.71547652b82fep+0 / sqrt((double)HD);  // log2(e) / sqrt(hd)
-  f4v qf[Q4 / 4];
-  double qd[QWIDE ? Q4 : 1];
-  {
+  if (wave == 0) {  // one wave per group writes the group's 16 queries
     const float* qp = q + (int64_t)(valid ? t : 0) * ld_q + (int64_t)h * HD + slot * Q4;
+    f4v qf[Q4 / 4];
 #pragma unroll
     for (int s = 0; s < Q4 / 4; ++s) qf[s] = *reinterpret_cast<const f4v*>(qp + 4 * s);
-    if constexpr (QWIDE) {
 #pragma unroll
-      for (int s = 0; s < Q4; ++s) qd[s] = (double)qf[s / 4][s % 4] * scale;
-    } else {
-      if (wave == 0) {
-#pragma unroll
-        for (int s = 0; s < Q4; s += 2)
-          sh_q[(slot * (Q4 / 2) + s / 2) * 16 + qi] =
-              double2{(double)qf[s / 4][s % 4] * scale, (double)qf[(s + 1) / 4][(s + 1) % 4] * scale};
-      }
-    }
+    for (int s = 0; s < Q4; s += 2)
+      sh_q[((grp * 4 + slot) * (Q4 / 2) + s / 2) * 16 + qi] =
+          double2{(double)qf[s / 4][s % 4] * scale, (double)qf[(s + 1) / 4][(s + 1) % 4] * scale};
   }
-  const double2* sq = sh_q + slot * (Q4 / 2) * 16 + qi;  // this lane's query pairs, stride 16
+  const double2* sq = sh_q + (grp * 4 + slot) * (Q4 / 2) * 16 + qi;  // this lane's query pairs, stride 16
 
   v4d acc[NB];
 #pragma unroll
@@ -213,21 +203,13 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
     const int key0 = tile * 16;
     const bool more = tile + NW < ntiles;
     // the query pairs are read from LDS in the loop (not hoisted into registers)
-    if constexpr (QLDS) asm volatile("" ::: "memory");
+    asm volatile("" ::: "memory");
     v4d sc0 = {0.0, 0.0, 0.0, 0.0}, sc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int s = 0; s < Q4; s += 2) {
-      double q0, q1;
-      if constexpr (QLDS) {
-        const double2 qq = sq[(s / 2) * 16];
-        q0 = qq.x;
-        q1 = qq.y;
-      } else {
-        q0 = qd[s];
-        q1 = qd[s + 1];
-      }
-      sc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(kt.k[s / 4], s % 4), q0, sc0, 0, 0, 0);
-      sc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(kt.k[(s + 1) / 4], (s + 1) % 4), q1, sc1, 0, 0, 0);
+      const double2 qq = sq[(s / 2) * 16];
+      sc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(kt.k[s / 4], s % 4), qq.x, sc0, 0, 0, 0);
+      sc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(f4get(kt.k[(s + 1) / 4], (s + 1) % 4), qq.y, sc1, 0, 0, 0);
     }
     if (more) load_k<HD>(kt, kbase, kv_embd, key0 + 16 * NW, max_pos, qi, slot);
     // ---- online softmax for query l%16 over keys key0 + 4i + slot
