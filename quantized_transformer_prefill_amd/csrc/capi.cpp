@@ -48,7 +48,6 @@ struct Ws {
   float* attn;       // [T][nq]
   int8_t* sq;        // [T][ffn] SwiGLU output codes
   uint16_t* ss;      // [T][ffn/32]
-  int8_t* lm_q; uint16_t* lm_s;  // final row quantized
   double* attn_part; // decode: partial attention states [n_head][AD_MAX_RANGES][head_dim + 2]
   // several sequences: one staging area copied in one transfer per call, holding the attention
   // query tiles [n_layers][n_tiles], region pointers [2][n_layers][MI_MAX_SLOTS] (K, V), the slot
@@ -79,8 +78,6 @@ static Ws carve(const mi_hparams& hp, int T, char* base) {
   w.attn = (float*)take(sizeof(float) * (size_t)T * nq);
   w.sq = (int8_t*)take((size_t)T * hp.ffn);
   w.ss = (uint16_t*)take(sizeof(uint16_t) * (size_t)T * (hp.ffn / QK));
-  w.lm_q = (int8_t*)take((size_t)hp.hidden);
-  w.lm_s = (uint16_t*)take(sizeof(uint16_t) * (size_t)(hp.hidden / QK));
   w.attn_part = (double*)take(sizeof(double) * (size_t)hp.n_head * AD_MAX_RANGES * (hp.head_dim + 2));
   w.slot_tiles_max = T / 16 + MI_MAX_SLOTS;
   {
@@ -433,6 +430,40 @@ static int enqueue_forward(const mi_model* md, const Ws& w, int32_t n_tokens, in
     g.qkv.q_norm = hp.qk_norm ? L.q_norm : nullptr; g.qkv.k_norm = hp.qk_norm ? L.k_norm : nullptr; g.qkv.eps = eps;
     if ((rc = launch_gemm_q8(g, s))) return rc;
     float* q = w.qkv;
+    if (last && n_out == 1) {
+      // From here on only the last token continues, through the one-token kernels of the decode
+      // step: single-query attention over key ranges (reading the regions after the store above),
+      // then matrix-vector products whose prologues merge the ranges or apply the RMSNorm and whose
+      // epilogues add the residual or apply SwiGLU + Q8_0; the final RMSNorm is the lm_head's
+      // prologue.  The previous layer's deferred partials were reduced by this layer's RMSNorm.
+      const int32_t* pos1 = w.pos + (nt - 1);
+      if ((rc = launch_attn_decode(q + (size_t)(nt - 1) * nqkv, kv->k[l], kv->v[l], pos1, n_ctx, hp.n_head,
+                                   hp.n_head_kv, hp.head_dim, w.attn_part, s)))
+        return rc;
+      GemvArgs go{};
+      go.attn.part = w.attn_part; go.attn.pos = pos1; go.attn.n_head = hp.n_head; go.attn.head_dim = hp.head_dim;
+      go.attn.n_range = attn_decode_ranges(n_ctx, &go.attn.keys_per_range);
+      go.k = nq;
+      go.w_codes = L.wo.codes; go.w_scales = L.wo.scales; go.n = H;
+      go.residual = h_tail; go.out = h_tail; go.epi = GV_RES;
+      if ((rc = launch_gemv_q8(go, s))) return rc;
+      GemvArgs gg{};
+      gg.x = h_tail; gg.gamma = L.ffn_norm; gg.eps = eps; gg.k = H;
+      gg.w_codes = L.w_gate_up.codes; gg.w_scales = L.w_gate_up.scales; gg.n = 2 * F;
+      gg.q_codes = w.sq; gg.q_scales = w.ss; gg.epi = GV_SWIGLU;
+      if ((rc = launch_gemv_q8(gg, s))) return rc;
+      GemvArgs gd{};
+      gd.xq = w.sq; gd.xs = w.ss; gd.k = F;
+      gd.w_codes = L.w_down.codes; gd.w_scales = L.w_down.scales; gd.n = H;
+      gd.residual = h_tail; gd.out = h_tail; gd.epi = GV_RES;
+      if ((rc = launch_gemv_q8(gd, s))) return rc;
+      const mi_q8_matrix& head1 = hp.tied ? md->token_embd : md->output;
+      GemvArgs gl{};
+      gl.x = h_tail; gl.gamma = md->output_norm; gl.eps = eps; gl.k = H;
+      gl.w_codes = head1.codes; gl.w_scales = head1.scales; gl.n = head1.rows;
+      gl.out = logits_out; gl.epi = GV_F32;
+      return launch_gemv_q8(gl, s);
+    }
     // attention, its output rows quantized to Q8_0 in the same kernel.  In the last layer only the
     // last n_out tokens continue past the output projection, so only their rows are computed (the
     // KV store above covered every token).
@@ -471,24 +502,18 @@ static int enqueue_forward(const mi_model* md, const Ws& w, int32_t n_tokens, in
     gd.split_out = &pending;
     if ((rc = launch_gemm_q8(gd, s))) return rc;
   }
+  // several rows (n_out > 1; one row returned inside the last layer): the MFMA matmul, logits
+  // [n_out][vocab]
   const mi_q8_matrix& head = hp.tied ? md->token_embd : md->output;
-  if (n_out == 1) {  // one row: the HBM-bound row kernel
-    if ((rc = launch_rmsnorm_quant(h_tail, md->output_norm, 1, H, eps, w.lm_q, w.lm_s, nullptr, s,
-                                   (const double*)w.gemm_ws, pending)))
-      return rc;
-    if ((rc = launch_lm_head(w.lm_q, w.lm_s, H, head.codes, head.scales, head.rows, logits_out, s))) return rc;
-  } else {  // several rows: the MFMA matmul, logits [n_out][vocab]
-    if ((rc = launch_rmsnorm_quant(h_tail, md->output_norm, n_out, H, eps, w.xq, w.xs, nullptr, s,
-                                   (const double*)w.gemm_ws, pending)))
-      return rc;
-    GemmArgs gl{};
-    gl.a_codes = w.xq; gl.a_scales = w.xs; gl.m = n_out;
-    gl.w_codes = head.codes; gl.w_scales = head.scales; gl.n = head.rows; gl.k = H;
-    gl.out = logits_out; gl.ld_out = head.rows;
-    gl.split_k = 1;
-    if ((rc = launch_gemm_q8(gl, s))) return rc;
-  }
-  return MI_OK;
+  if ((rc = launch_rmsnorm_quant(h_tail, md->output_norm, n_out, H, eps, w.xq, w.xs, nullptr, s,
+                                 (const double*)w.gemm_ws, pending)))
+    return rc;
+  GemmArgs gl{};
+  gl.a_codes = w.xq; gl.a_scales = w.xs; gl.m = n_out;
+  gl.w_codes = head.codes; gl.w_scales = head.scales; gl.n = head.rows; gl.k = H;
+  gl.out = logits_out; gl.ld_out = head.rows;
+  gl.split_k = 1;
+  return launch_gemm_q8(gl, s);
 }
 
 extern "C" int mi_prefill_forward(const mi_model* md, const int32_t* token_ids, const int32_t* positions,
