@@ -476,8 +476,10 @@ def _dispatch_table(d):
 
 
 def _forward_kernels(cfg):
-    """(kernel-name prefix, label, algorithmic int8 ops per launch or 0, algorithmic HBM bytes or 0)
-    of the forward's kernels at the full prompt (tail layers run on fewer rows and are grouped apart)."""
+    """(kernel-name prefix, label, algorithmic int8 ops per launch or 0, algorithmic HBM bytes or 0,
+    name prefix of the kernel dispatched just before it or None) of the forward's kernels at the full
+    prompt (tail layers run on fewer rows and are grouped apart).  The output and down projections
+    are the same kernel at the same grid at this shape; the kernel before each tells them apart."""
     M, H, F = cfg.n_tokens, cfg.hidden, cfg.ffn
     nq, nkv = cfg.n_head * cfg.head_dim, cfg.n_head_kv * cfg.head_dim
     q8 = lambda rows, cols: rows * cols * 34 // 32
@@ -485,16 +487,17 @@ def _forward_kernels(cfg):
         ("void mi::k_gemm_q8<1, 2, 1, false, 2>", f"gate|up + SwiGLU + Q8_0 ({M}x{2 * F}x{H})", 2 * M * 2 * F * H,
          q8(2 * F, H) + q8(M, H) + q8(M, F)),
         ("void mi::k_gemm_q8<1, 1, 0, true, 2>", f"down, split-K partials ({M}x{H}x{F})", 2 * M * H * F,
-         q8(H, F) + q8(M, F) + 2 * 8 * M * H),
-        ("void mi::k_gemm_q8<1, 1, 0, false, 2>", f"Wo + residual ({M}x{H}x{nq})", 2 * M * H * nq,
-         q8(H, nq) + q8(M, nq) + 8 * M * H),
+         q8(H, F) + q8(M, F) + 2 * 8 * M * H, "void mi::k_gemm_q8<1, 2, 1"),
+        ("void mi::k_gemm_q8<1, 1, 0, true, 2>", f"Wo, split-K partials ({M}x{H}x{nq})", 2 * M * H * nq,
+         q8(H, nq) + q8(M, nq) + 2 * 8 * M * H, "void mi::k_attention<"),
         ("void mi::k_gemm_q8<1, 1, 2, false, 2>", f"Q|K|V + bias + RoPE + KV store ({M}x{nq + 2 * nkv}x{H})",
          2 * M * (nq + 2 * nkv) * H, q8(nq + 2 * nkv, H) + q8(M, H) + 4 * M * (nq + 2 * nkv)),
         ("void mi::k_attention<", f"causal GQA attention + Q8_0 of the output ({M} tokens)", 0,
          4 * M * nq + 8 * M * nkv + q8(M, nq)),
-        ("mi::k_rmsnorm_quant", f"RMSNorm + Q8_0 ({M}x{H}; half of them also reduce 2 split-K partials)", 0,
-         M * H * (4 + 4) + q8(M, H)),
-        ("mi::k_lm_head", f"last-row lm_head ({cfg.vocab}x{H})", 0, q8(cfg.vocab, H) + 4 * cfg.vocab),
+        ("mi::k_rmsnorm_quant", f"RMSNorm + Q8_0 ({M}x{H}), reducing the 2 split-K partials of the matmul before",
+         0, M * H * (4 + 4) + 2 * 8 * M * H + q8(M, H)),
+        ("void mi::k_gemv_q8<4, 1, 1>", f"last-row lm_head, final RMSNorm in its prologue ({cfg.vocab}x{H})", 0,
+         q8(cfg.vocab, H) + 4 * cfg.vocab),
         ("mi::k_embed", f"embedding rows ({M}x{H})", 0, q8(M, H) + 4 * M * H),
     ]
 
@@ -518,10 +521,10 @@ def write_counters(cfg, cdir, fdir, wdir, out_path):
 
     ff, fw = calib(fet, "FETCH_SIZE"), calib(wri, "WRITE_SIZE")
 
-    def by_name(tab, prefix):
+    def by_name(tab, prefix, prev=None):
         groups = {}
         for did, (n, g, vals) in tab.items():
-            if n.startswith(prefix):
+            if n.startswith(prefix) and (prev is None or (did - 1 in tab and tab[did - 1][0].startswith(prev))):
                 groups.setdefault(g, []).append((did, vals))
         return groups
 
@@ -545,9 +548,10 @@ def write_counters(cfg, cdir, fdir, wdir, out_path):
              "HBM MB (vs algorithmic) | HBM GB/s (% of 8000) |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     med = lambda xs: float(np.median(xs)) if xs else float("nan")
-    for prefix, label, ops_alg, bytes_alg in _forward_kernels(cfg):
+    for prefix, label, ops_alg, bytes_alg, *prev in _forward_kernels(cfg):
+        prev = prev[0] if prev else None
         label = label.replace("|", "\\|")
-        groups = by_name(comp, prefix)
+        groups = by_name(comp, prefix, prev)
         if not groups:
             continue
         g, disp = max(groups.items(), key=lambda kv: len(kv[1]))
@@ -560,8 +564,8 @@ def write_counters(cfg, cdir, fdir, wdir, out_path):
         busy = cv("SQ_VALU_MFMA_BUSY_CYCLES")
         coex = cv("SQ_VALU_MFMA_COEXEC_CYCLES")
         ldsc = cv("SQ_LDS_BANK_CONFLICT") / max(cv("SQ_INSTS_LDS"), 1.0)
-        fg = by_name(fet, prefix).get(g, [])
-        wg = by_name(wri, prefix).get(g, [])
+        fg = by_name(fet, prefix, prev).get(g, [])
+        wg = by_name(wri, prefix, prev).get(g, [])
         hbm = (med([v["FETCH_SIZE"] for _, v in fg]) * 1024 * ff if fg else float("nan")) + \
               (med([v["WRITE_SIZE"] for _, v in wg]) * 1024 * fw if wg else float("nan"))
         s_ = dns * 1e-9
