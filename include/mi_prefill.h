@@ -54,9 +54,10 @@ typedef enum {
   MI_ERR_UNSUPPORTED = 7      /* shape outside what the kernels implement              */
 } mi_status;
 
-/* Model shape.  n_head % n_head_kv == 0; head_dim even and <= 128; hidden, ffn,
- * n_head*head_dim multiples of 32.  rms_eps is used for every RMSNorm (and the
- * Qwen3 per-head QK norm); rope_theta is the NeoX RoPE base. */
+/* Model shape.  n_head % n_head_kv == 0; head_dim 64 or 128; hidden, ffn, n_head*head_dim
+ * multiples of 32; hidden and n_head*head_dim at most 4096 (MI_ERR_UNSUPPORTED otherwise).
+ * rms_eps is used for every RMSNorm (and the Qwen3 per-head QK norm); rope_theta is the NeoX
+ * RoPE base. */
 typedef struct {
   int32_t n_layers, hidden, n_head, n_head_kv, head_dim, ffn, vocab;
   float rms_eps, rope_theta;
@@ -92,6 +93,22 @@ typedef struct {
   const float *q_norm, *k_norm;
 } mi_layer_weights;
 
+/* Pinned host staging of the host arrays a forward call reads: its token ids and positions (and,
+ * for several sequences, the attention tile table and region pointers).  The prefill page takes
+ * token ids and positions as host slices that are only read during the call ("09", section 2.2,
+ * the forward signature), so the call copies them into pinned host memory before it returns and
+ * the transfer to the device runs asynchronously from there.  The stage is a ring of MI_STAGE_RING
+ * pinned buffers, each guarded by a HIP event: a buffer is rewritten only after the transfer that
+ * last read it has completed, so back-to-back calls never wait for the GPU unless they are
+ * MI_STAGE_RING calls ahead of it.  Created once per model (it allocates pinned host memory and
+ * events; nothing on the device); not thread-safe, like the mi_model that refers to it.
+ *   mi_stage_create   hp and max_tokens as for mi_prefill_workspace_bytes; *out NULL on error
+ *   mi_stage_destroy  waits for the transfers still reading the stage, then frees it (NULL: no-op) */
+#define MI_STAGE_RING 4
+typedef struct mi_stage mi_stage;
+int mi_stage_create(const mi_hparams* hp, int32_t max_tokens, mi_stage** out);
+void mi_stage_destroy(mi_stage* stage);
+
 /* A loaded model plus the per-model buffers one forward uses.  Not thread-safe:
  * calls that share one mi_model (its workspace) must be serialized. */
 typedef struct {
@@ -106,6 +123,7 @@ typedef struct {
   size_t workspace_bytes;           /* >= mi_prefill_workspace_bytes(...)    */
   int32_t max_tokens;               /* largest n_tokens the workspace serves */
   void* stream;                     /* hipStream_t                           */
+  mi_stage* stage;                  /* from mi_stage_create with >= max_tokens and these hparams */
 } mi_model;
 
 /* Persistent KV regions ("09", section 2.5): for each layer one K and one V
@@ -143,7 +161,11 @@ int mi_rope_table_init(const mi_hparams* hp, int32_t rows, double* table, void* 
  * Checks before enqueueing: every position in [0, n_ctx) (MI_ERR_POSITION_RANGE),
  * no position repeated (MI_ERR_DUP_POSITION), descriptor shapes
  * (MI_ERR_KV_MISMATCH), n_tokens <= model->max_tokens and workspace size
- * (MI_ERR_WORKSPACE), rope table rows >= n_ctx. */
+ * (MI_ERR_WORKSPACE), rope table rows >= n_ctx, the KV regions of all layers pairwise
+ * disjoint (MI_ERR_INVALID_ARG), model->stage present and sized for max_tokens
+ * (MI_ERR_INVALID_ARG / MI_ERR_WORKSPACE), and every activation offset of the kernels
+ * (max_tokens times the widest row) below 2^31 (MI_ERR_UNSUPPORTED).
+ * token_ids and positions are copied into model->stage before the call returns. */
 int mi_prefill_forward(const mi_model* model, const int32_t* token_ids, const int32_t* positions,
                        int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv, float* logits_out);
 
@@ -169,9 +191,9 @@ int mi_prefill_forward_n(const mi_model* model, const int32_t* token_ids, const 
  *   kv           host array [n_slots] of region descriptors (each as for mi_prefill_forward)
  *   logits_out   device f32 [n_slots][vocab]: the last token of each slot
  * 1 <= n_slots <= MI_MAX_SLOTS; the total token count <= model->max_tokens; positions must not
- * repeat within a slot.  The slots' region sets must be distinct (two slots writing one region
- * set race).  Errors as mi_prefill_forward (nothing written).  Returns after the call's work is
- * done (the per-call staging buffer is host memory). */
+ * repeat within a slot.  No two regions of any slots may overlap (two slots writing one region
+ * would race): MI_ERR_INVALID_ARG.  Errors as mi_prefill_forward (nothing written).  The host
+ * arrays are copied into model->stage before the call returns; the work is asynchronous. */
 #define MI_MAX_SLOTS 64
 int mi_prefill_forward_slots(const mi_model* model, const int32_t* token_ids, const int32_t* positions,
                              const int32_t* slot_tokens, int32_t n_slots, int32_t n_ctx, const mi_kv_regions* kv,
@@ -232,11 +254,12 @@ int mi_sample(const float* logits, int32_t vocab, const int32_t* window, int32_t
  * mi_prefill_graph_create validates the shapes like mi_prefill_forward_n, then captures the
  * forward's kernel sequence on model->stream (which must be a non-default stream) into a graph;
  * nothing runs and nothing is allocated on the device.  The graph keeps the pointers of `model`
- * (weights, workspace, RoPE table), of `kv` and of `logits_out` as they are now: the caller keeps
- * them alive and unchanged until mi_prefill_graph_destroy.
+ * (weights, workspace, RoPE table, stage), of `kv` and of `logits_out` as they are now: the caller
+ * keeps them alive and unchanged until mi_prefill_graph_destroy.
  * mi_prefill_graph_launch validates token ids and positions (as mi_prefill_forward_n: errors leave
- * everything untouched), stages them into the workspace and replays the graph on the captured
- * stream; it computes exactly what mi_prefill_forward_n computes for the same arguments.
+ * everything untouched), copies them into the model's pinned stage, enqueues their transfer to the
+ * workspace and replays the graph on the captured stream; it computes exactly what
+ * mi_prefill_forward_n computes for the same arguments.
  * Launches of one graph run in stream order; different graphs sharing a workspace must not
  * overlap.  *out is set to NULL on error. */
 typedef struct mi_prefill_graph mi_prefill_graph;
@@ -256,12 +279,23 @@ void mi_prefill_graph_destroy(mi_prefill_graph* graph);
 int mi_quantize_q8_0(const float* x, int64_t rows, int32_t cols, int8_t* codes, uint16_t* scales,
                      void* stream);
 
+/* Q8_0 blocks in their canonical byte layout -> the library's two planes (the walkthrough index,
+ * stage 10: quantized weights are fixed-layout C blocks).  A canonical block is 34 bytes: the fp16
+ * scale (little-endian bits) followed by the 32 int8 codes; a row of cols values is cols/32 blocks
+ * back to back, rows follow each other.  The planes receive exactly those bytes:
+ * scales[r][b] = bytes 0..1 of block (r, b), codes[r][32b + i] = byte 2 + i of it.
+ *   blocks  device, rows * (cols/32) * 34 bytes, 2-byte aligned
+ *   codes   device int8 [rows][cols], 16-byte aligned; scales device uint16 [rows][cols/32]
+ * cols % 32 == 0 and rows, cols > 0 (MI_ERR_INVALID_ARG otherwise). */
+int mi_pack_q8_0(const void* blocks, int64_t rows, int32_t cols, int8_t* codes, uint16_t* scales, void* stream);
+
 /* Q8_0 x Q8_0 matmul with inline bias and optional residual ("05", sections 2.5, 3.2):
  *   out[t][n] = residual[t][n] + f32( sum_kb da[t][kb] dw[n][kb] sum_32 qa qw + bias[n] )
  * a_codes/a_scales: device, the activations already in Q8_0 [m][k];
  * w: the weight [n][k]; bias device f32 [n] or NULL; residual device f32 [m][n] or
  * NULL (may alias out); out device f32 [m][n].  The block sums are exact (int8
- * MFMA, int32) and the scaled sum is accumulated in f64. */
+ * MFMA, int32) and the scaled sum is accumulated in f64.  The kernels address operands with
+ * 32-bit offsets: m*k, n*k and m*n must be below 2^31 (MI_ERR_UNSUPPORTED otherwise). */
 int mi_gemm_q8_0(const int8_t* a_codes, const uint16_t* a_scales, int32_t m, const mi_q8_matrix* w,
                  const float* bias, const float* residual, float* out, void* stream);
 
@@ -276,7 +310,8 @@ size_t mi_gemm_q8_0_workspace_bytes(int32_t m, int32_t n, int32_t k);
 /* gate|up matmul with SwiGLU and Q8_0 in the epilogue ("05", section 2.5 gate, up, SwiGLU):
  *   g = f32(x.Wgate), u = f32(x.Wup), s = f32(silu(g) * u), then s -> Q8_0.
  *   w_gate_up in the interleaved layout of mi_layer_weights ([2*ffn][k], rows % 64 == 0);
- *   s_codes device int8 [m][ffn], s_scales device uint16 [m][ffn/32]; workspace as above. */
+ *   s_codes device int8 [m][ffn], s_scales device uint16 [m][ffn/32]; workspace as above.
+ *   32-bit offsets as for mi_gemm_q8_0. */
 int mi_gemm_swiglu_q8_0(const int8_t* a_codes, const uint16_t* a_scales, int32_t m,
                         const mi_q8_matrix* w_gate_up, int8_t* s_codes, uint16_t* s_scales,
                         void* workspace, size_t workspace_bytes, void* stream);

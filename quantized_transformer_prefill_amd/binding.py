@@ -46,7 +46,8 @@ class Model(C.Structure):
     _fields_ = [("hp", Hparams), ("token_embd", Q8Matrix), ("output", Q8Matrix),
                 ("output_norm", C.c_void_p), ("layers", C.POINTER(LayerWeights)),
                 ("rope_table", C.c_void_p), ("rope_rows", C.c_int32), ("workspace", C.c_void_p),
-                ("workspace_bytes", C.c_size_t), ("max_tokens", C.c_int32), ("stream", C.c_void_p)]
+                ("workspace_bytes", C.c_size_t), ("max_tokens", C.c_int32), ("stream", C.c_void_p),
+                ("stage", C.c_void_p)]
 
 
 class KvRegions(C.Structure):
@@ -64,6 +65,8 @@ _P, _I32, _I64, _F, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_
 # name -> (restype, argtypes); mirrors include/mi_prefill.h
 SIGNATURES = {
     "mi_prefill_workspace_bytes": (_SZ, [C.POINTER(Hparams), _I32]),
+    "mi_stage_create": (C.c_int, [C.POINTER(Hparams), _I32, C.POINTER(C.c_void_p)]),
+    "mi_stage_destroy": (None, [_P]),
     "mi_rope_table_bytes": (_SZ, [C.POINTER(Hparams), _I32]),
     "mi_rope_table_init": (C.c_int, [C.POINTER(Hparams), _I32, _P, _P]),
     "mi_prefill_forward": (C.c_int, [C.POINTER(Model), _P, _P, _I32, _I32, C.POINTER(KvRegions), _P]),
@@ -75,6 +78,7 @@ SIGNATURES = {
     "mi_prefill_graph_launch": (C.c_int, [_P, _P, _P]),
     "mi_prefill_graph_destroy": (None, [_P]),
     "mi_quantize_q8_0": (C.c_int, [_P, _I64, _I32, _P, _P, _P]),
+    "mi_pack_q8_0": (C.c_int, [_P, _I64, _I32, _P, _P, _P]),
     "mi_gemm_q8_0": (C.c_int, [_P, _P, _I32, C.POINTER(Q8Matrix), _P, _P, _P, _P]),
     "mi_gemm_q8_0_ws": (C.c_int, [_P, _P, _I32, C.POINTER(Q8Matrix), _P, _P, _P, _P, _SZ, _I32, _P]),
     "mi_gemm_q8_0_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
@@ -142,6 +146,35 @@ def quantize_q8_0(x: torch.Tensor):
     scales = torch.empty((rows, cols // 32), dtype=torch.int16, device=x.device)
     check(lib().mi_quantize_q8_0(x.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(), stream_ptr()))
     return codes, scales
+
+
+def pack_q8_0(blocks: torch.Tensor, rows: int, cols: int):
+    """Canonical 34-byte Q8_0 blocks (a device uint8 tensor of rows*cols/32*34 bytes) -> (codes, scales)."""
+    _dev(blocks, torch.uint8)
+    codes = torch.empty((rows, cols), dtype=torch.int8, device=blocks.device)
+    scales = torch.empty((rows, cols // 32), dtype=torch.int16, device=blocks.device)
+    check(lib().mi_pack_q8_0(blocks.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(), stream_ptr()))
+    return codes, scales
+
+
+class Stage:
+    """mi_stage_create / mi_stage_destroy: the pinned host staging a model's forward calls go through."""
+
+    def __init__(self, hp: Hparams, max_tokens: int):
+        h = C.c_void_p()
+        check(lib().mi_stage_create(C.byref(hp), max_tokens, C.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            lib().mi_stage_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def gemm_q8_0(a_codes, a_scales, w_codes, w_scales, bias=None, residual=None, split_k: int = 1, out=None):

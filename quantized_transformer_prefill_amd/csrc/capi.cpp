@@ -39,6 +39,8 @@ static bool q8_ok(const mi_q8_matrix& w, int rows, int cols) {
 
 // ---------------------------------------------------------------- workspace layout
 struct Ws {
+  // the staged part, contiguous at the start: one host-to-device copy from the pinned stage
+  // (mi_stage) fills it with the same layout
   int32_t* ids; int32_t* pos;
   int32_t* maxpos;   // [1] largest position of the call
   float* h;          // [T][hidden]
@@ -54,6 +56,7 @@ struct Ws {
   // of each row [T] and the last row of each slot [MI_MAX_SLOTS]
   char* slot_stage;
   size_t slot_stage_bytes;
+  size_t staged_bytes;   // ids .. end of slot_stage
   int slot_tiles_max;    // per layer: T/16 + MI_MAX_SLOTS
   float* slot_h;         // several sequences: the slots' last rows gathered [MI_MAX_SLOTS][hidden]
   void* gemm_ws; size_t gemm_ws_bytes;
@@ -71,14 +74,6 @@ static Ws carve(const mi_hparams& hp, int T, char* base) {
   w.ids = (int32_t*)take(sizeof(int32_t) * T);
   w.pos = (int32_t*)take(sizeof(int32_t) * T);
   w.maxpos = (int32_t*)take(sizeof(int32_t));
-  w.h = (float*)take(sizeof(float) * T * (size_t)hp.hidden);
-  w.xq = (int8_t*)take((size_t)T * wide);
-  w.xs = (uint16_t*)take(sizeof(uint16_t) * (size_t)T * (wide / QK));
-  w.qkv = (float*)take(sizeof(float) * (size_t)T * (nq + 2 * nkv));
-  w.attn = (float*)take(sizeof(float) * (size_t)T * nq);
-  w.sq = (int8_t*)take((size_t)T * hp.ffn);
-  w.ss = (uint16_t*)take(sizeof(uint16_t) * (size_t)T * (hp.ffn / QK));
-  w.attn_part = (double*)take(sizeof(double) * (size_t)hp.n_head * AD_MAX_RANGES * (hp.head_dim + 2));
   w.slot_tiles_max = T / 16 + MI_MAX_SLOTS;
   {
     const size_t L = (size_t)std::max(hp.n_layers, 1);
@@ -87,6 +82,15 @@ static Ws carve(const mi_hparams& hp, int T, char* base) {
                          align_up(sizeof(int32_t) * MI_MAX_SLOTS);
     w.slot_stage = take(w.slot_stage_bytes);
   }
+  w.staged_bytes = off;
+  w.h = (float*)take(sizeof(float) * T * (size_t)hp.hidden);
+  w.xq = (int8_t*)take((size_t)T * wide);
+  w.xs = (uint16_t*)take(sizeof(uint16_t) * (size_t)T * (wide / QK));
+  w.qkv = (float*)take(sizeof(float) * (size_t)T * (nq + 2 * nkv));
+  w.attn = (float*)take(sizeof(float) * (size_t)T * nq);
+  w.sq = (int8_t*)take((size_t)T * hp.ffn);
+  w.ss = (uint16_t*)take(sizeof(uint16_t) * (size_t)T * (hp.ffn / QK));
+  w.attn_part = (double*)take(sizeof(double) * (size_t)hp.n_head * AD_MAX_RANGES * (hp.head_dim + 2));
   w.slot_h = (float*)take(sizeof(float) * MI_MAX_SLOTS * (size_t)hp.hidden);
   size_t g = 0;
   g = std::max(g, gemm_workspace_bytes(T, (int)(nq + 2 * nkv), hp.hidden));
@@ -113,13 +117,98 @@ static int check_hparams(const mi_hparams* hp) {
   if (hp->head_dim != 64 && hp->head_dim != 128)
     return set_error(MI_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", hp->head_dim);
   if (hp->hidden > 4096) return set_error(MI_ERR_UNSUPPORTED, "hidden %d > 4096", hp->hidden);
+  // the one-row matrix-vector kernels (the last layer's tail row, decode) hold a whole input row of
+  // at most 4096 values, the attention output (n_head * head_dim values) included
+  if ((int64_t)hp->n_head * hp->head_dim > 4096)
+    return set_error(MI_ERR_UNSUPPORTED, "n_head * head_dim %d > 4096", hp->n_head * hp->head_dim);
   if (hp->ffn % 32) return set_error(MI_ERR_INVALID_ARG, "ffn %% 32 != 0");
   return MI_OK;
 }
 
 }  // namespace mi
 
+// ---------------------------------------------------------------- pinned host staging
+// A ring of pinned host buffers, each a mirror of the workspace's staged part (ids, positions,
+// largest position, the several-sequence tables) with the same offsets, so one call fills a buffer
+// and sends it with a single asynchronous host-to-device copy.  The event recorded after that copy
+// tells when the buffer may be written again.
+struct mi_stage {
+  mi_hparams hp{};
+  int32_t max_tokens = 0;
+  size_t bytes = 0;  // per buffer
+  char* host[MI_STAGE_RING] = {};
+  hipEvent_t ev[MI_STAGE_RING] = {};
+  bool pending[MI_STAGE_RING] = {};
+  int next = 0;
+};
+
+namespace mi {
+
+static void stage_free(mi_stage* st) {
+  for (int i = 0; i < MI_STAGE_RING; ++i) {
+    if (st->ev[i]) {
+      if (st->pending[i]) (void)hipEventSynchronize(st->ev[i]);
+      (void)hipEventDestroy(st->ev[i]);
+    }
+    if (st->host[i]) (void)hipHostFree(st->host[i]);
+  }
+  delete st;
+}
+
+// The staged part of workspace `w` (the carve of the model's max_tokens) must fit one buffer.
+static int check_stage(const mi_model* md, const Ws& w) {
+  if (!md->stage) return set_error(MI_ERR_INVALID_ARG, "forward: model->stage is NULL (mi_stage_create)");
+  if (md->stage->bytes < w.staged_bytes)
+    return set_error(MI_ERR_WORKSPACE, "forward: stage made for fewer tokens or layers than the model's max_tokens");
+  return MI_OK;
+}
+
+// Take the next ring buffer (waiting for the copy that last read it), let fill() write it, and send
+// its first n bytes to dev (the workspace's staged part) on stream s.
+template <class F>
+static int stage_send(mi_stage* st, void* dev, size_t n, hipStream_t s, F fill) {
+  const int i = st->next;
+  if (st->pending[i]) {
+    MI_HIP(hipEventSynchronize(st->ev[i]));
+    st->pending[i] = false;
+  }
+  st->next = (i + 1) % MI_STAGE_RING;
+  fill(st->host[i]);
+  MI_HIP(hipMemcpyAsync(dev, st->host[i], n, hipMemcpyHostToDevice, s));
+  MI_HIP(hipEventRecord(st->ev[i], s));
+  st->pending[i] = true;
+  return MI_OK;
+}
+
+}  // namespace mi
+
 using namespace mi;
+
+extern "C" int mi_stage_create(const mi_hparams* hp, int32_t max_tokens, mi_stage** out) {
+  if (!out) return set_error(MI_ERR_INVALID_ARG, "mi_stage_create: NULL output handle");
+  *out = nullptr;
+  int rc = check_hparams(hp);
+  if (rc) return rc;
+  if (max_tokens < 1) return set_error(MI_ERR_INVALID_ARG, "mi_stage_create: max_tokens must be >= 1");
+  mi_stage* st = new mi_stage();
+  st->hp = *hp;
+  st->max_tokens = max_tokens;
+  st->bytes = carve(*hp, max_tokens, nullptr).staged_bytes;
+  for (int i = 0; i < MI_STAGE_RING; ++i) {
+    hipError_t e = hipHostMalloc((void**)&st->host[i], st->bytes, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&st->ev[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      stage_free(st);
+      return hip_check(e, "mi_stage_create");
+    }
+  }
+  *out = st;
+  return MI_OK;
+}
+
+extern "C" void mi_stage_destroy(mi_stage* st) {
+  if (st) stage_free(st);
+}
 
 extern "C" const char* mi_last_error(void) { return g_err; }
 extern "C" const char* mi_version(void) { return "mi_prefill 0.1 gfx950"; }
@@ -137,11 +226,29 @@ extern "C" int mi_quantize_q8_0(const float* x, int64_t rows, int32_t cols, int8
   return launch_quantize(x, rows, cols, cols, codes, scales, as_stream(stream));
 }
 
+extern "C" int mi_pack_q8_0(const void* blocks, int64_t rows, int32_t cols, int8_t* codes, uint16_t* scales,
+                            void* stream) {
+  if (!blocks || !codes || !scales || rows <= 0 || cols <= 0 || cols % QK || ((uintptr_t)blocks & 1) ||
+      ((uintptr_t)codes & 15) || ((uintptr_t)scales & 1))
+    return set_error(MI_ERR_INVALID_ARG, "mi_pack_q8_0: bad arguments (cols a positive multiple of 32, blocks and "
+                     "scales 2-byte aligned, codes 16-byte aligned)");
+  return launch_pack_q8_0(blocks, rows, cols, codes, scales, as_stream(stream));
+}
+
+// The matmul kernels address their operands with 32-bit offsets (row * K and row * N)
+static int check_gemm_offsets(const char* who, int64_t m, int64_t n, int64_t k) {
+  if (m * k >= ((int64_t)1 << 31) || n * k >= ((int64_t)1 << 31) || m * n >= ((int64_t)1 << 31))
+    return set_error(MI_ERR_UNSUPPORTED, "%s: m*k, n*k and m*n must be below 2^31 (m %lld, n %lld, k %lld)", who,
+                     (long long)m, (long long)n, (long long)k);
+  return MI_OK;
+}
+
 extern "C" int mi_gemm_q8_0(const int8_t* a_codes, const uint16_t* a_scales, int32_t m, const mi_q8_matrix* w,
                             const float* bias, const float* residual, float* out, void* stream) {
   if (!a_codes || !a_scales || !w || !w->codes || !w->scales || !out || m < 0 || w->rows <= 0 || w->cols <= 0 ||
       w->cols % QK || w->rows % QK)
     return set_error(MI_ERR_INVALID_ARG, "mi_gemm_q8_0: bad arguments (k and n multiples of 32)");
+  if (int rc = check_gemm_offsets("mi_gemm_q8_0", m, w->rows, w->cols)) return rc;
   GemmArgs g{};
   g.a_codes = a_codes; g.a_scales = a_scales; g.m = m;
   g.w_codes = w->codes; g.w_scales = w->scales; g.n = w->rows; g.k = w->cols;
@@ -156,6 +263,7 @@ extern "C" int mi_gemm_q8_0_ws(const int8_t* a_codes, const uint16_t* a_scales, 
   if (!a_codes || !a_scales || !w || !w->codes || !w->scales || !out || m < 0 || w->rows <= 0 || w->cols <= 0 ||
       w->cols % QK || w->rows % QK || split_k < 0)
     return set_error(MI_ERR_INVALID_ARG, "mi_gemm_q8_0_ws: bad arguments");
+  if (int rc = check_gemm_offsets("mi_gemm_q8_0_ws", m, w->rows, w->cols)) return rc;
   GemmArgs g{};
   g.a_codes = a_codes; g.a_scales = a_scales; g.m = m;
   g.w_codes = w->codes; g.w_scales = w->scales; g.n = w->rows; g.k = w->cols;
@@ -175,6 +283,7 @@ extern "C" int mi_gemm_swiglu_q8_0(const int8_t* a_codes, const uint16_t* a_scal
   if (!a_codes || !a_scales || !w_gate_up || !w_gate_up->codes || !w_gate_up->scales || !s_codes || !s_scales ||
       m < 0 || w_gate_up->rows <= 0 || w_gate_up->rows % 64 || w_gate_up->cols % QK)
     return set_error(MI_ERR_INVALID_ARG, "mi_gemm_swiglu_q8_0: bad arguments (rows a multiple of 64)");
+  if (int rc = check_gemm_offsets("mi_gemm_swiglu_q8_0", m, w_gate_up->rows, w_gate_up->cols)) return rc;
   GemmArgs g{};
   g.a_codes = a_codes; g.a_scales = a_scales; g.m = m;
   g.w_codes = w_gate_up->codes; g.w_scales = w_gate_up->scales; g.n = w_gate_up->rows; g.k = w_gate_up->cols;
@@ -286,6 +395,25 @@ static int validate_kv(const mi_hparams& hp, const mi_kv_regions* kv, int32_t n_
   return MI_OK;
 }
 
+// No two KV regions of the descriptors overlap (two regions sharing memory would make the stores of
+// one call race, or one sequence overwrite another's rows).
+static int validate_kv_disjoint(const mi_kv_regions* kv, int n_sets) {
+  std::vector<std::pair<uintptr_t, uintptr_t>> iv;
+  for (int sl = 0; sl < n_sets; ++sl) {
+    const size_t bytes = sizeof(float) * (size_t)kv[sl].n_ctx * kv[sl].n_kv_embd;
+    for (int l = 0; l < kv[sl].n_layers; ++l) {
+      iv.emplace_back((uintptr_t)kv[sl].k[l], (uintptr_t)kv[sl].k[l] + bytes);
+      iv.emplace_back((uintptr_t)kv[sl].v[l], (uintptr_t)kv[sl].v[l] + bytes);
+    }
+  }
+  std::sort(iv.begin(), iv.end());
+  for (size_t i = 1; i < iv.size(); ++i)
+    if (iv[i].first < iv[i - 1].second)
+      return set_error(MI_ERR_INVALID_ARG, "forward: two KV regions overlap (each layer's K and V region, and each "
+                       "sequence's, must be distinct memory)");
+  return MI_OK;
+}
+
 static int validate_static(const mi_model* md, int32_t nt, int32_t n_ctx, const mi_kv_regions* kv,
                            const float* logits, int32_t n_out) {
   if (!md || !kv || !logits) return set_error(MI_ERR_INVALID_ARG, "forward: NULL argument");
@@ -296,6 +424,7 @@ static int validate_static(const mi_model* md, int32_t nt, int32_t n_ctx, const 
   if (n_out < 1 || n_out > nt) return set_error(MI_ERR_INVALID_ARG, "forward: n_out %d outside [1, n_tokens = %d]", n_out, nt);
   if (n_ctx < 1) return set_error(MI_ERR_INVALID_ARG, "forward: n_ctx must be >= 1");
   if ((rc = validate_kv(hp, kv, n_ctx))) return rc;
+  if ((rc = validate_kv_disjoint(kv, 1))) return rc;
   if (nt > md->max_tokens) return set_error(MI_ERR_WORKSPACE, "forward: n_tokens %d > max_tokens %d", nt, md->max_tokens);
   if (!md->workspace || md->workspace_bytes < carve(hp, md->max_tokens, nullptr).total)
     return set_error(MI_ERR_WORKSPACE, "forward: workspace smaller than mi_prefill_workspace_bytes(max_tokens)");
@@ -312,6 +441,13 @@ static int validate_static(const mi_model* md, int32_t nt, int32_t n_ctx, const 
       return set_error(MI_ERR_INVALID_ARG, "forward: layer %d tensors missing or mis-shaped", l);
   }
   if (hp.ffn % 32) return set_error(MI_ERR_INVALID_ARG, "forward: ffn %% 32");
+  // 32-bit offsets of the kernels: activation rows (max_tokens of them) and weight rows
+  const int64_t wide = std::max({(int64_t)hp.hidden, (int64_t)nq + 2 * nkv, (int64_t)2 * hp.ffn});
+  const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)md->max_tokens * wide >= lim || ((int64_t)nq + 2 * nkv) * hp.hidden >= lim ||
+      (int64_t)2 * hp.ffn * hp.hidden >= lim || (int64_t)hp.vocab * hp.hidden >= lim)
+    return set_error(MI_ERR_UNSUPPORTED, "forward: max_tokens %d x row width %lld (or a weight matrix) reaches 2^31 "
+                     "elements, beyond the kernels' 32-bit offsets", md->max_tokens, (long long)wide);
   return MI_OK;
 }
 
@@ -335,13 +471,17 @@ static int validate_tokens(const mi_hparams& hp, const int32_t* ids, const int32
   return MI_OK;
 }
 
-// boundary staging: token ids, positions and the largest position to the device
-static int stage_tokens(const Ws& w, const int32_t* ids, const int32_t* pos, int32_t nt, const int32_t* max_pos,
+// boundary staging: token ids, positions and the largest position copied into the next pinned
+// buffer of the stage (before the call returns), then one asynchronous copy to the workspace
+static int stage_tokens(mi_stage* st, const Ws& w, const int32_t* ids, const int32_t* pos, int32_t nt, int32_t max_pos,
                         hipStream_t s) {
-  MI_HIP(hipMemcpyAsync(w.ids, ids, sizeof(int32_t) * nt, hipMemcpyHostToDevice, s));
-  MI_HIP(hipMemcpyAsync(w.pos, pos, sizeof(int32_t) * nt, hipMemcpyHostToDevice, s));
-  MI_HIP(hipMemcpyAsync(w.maxpos, max_pos, sizeof(int32_t), hipMemcpyHostToDevice, s));
-  return MI_OK;
+  char* base = reinterpret_cast<char*>(w.ids);
+  const size_t o_pos = (char*)w.pos - base, o_max = (char*)w.maxpos - base;
+  return stage_send(st, base, o_max + sizeof(int32_t), s, [&](char* h) {
+    std::memcpy(h, ids, sizeof(int32_t) * nt);
+    std::memcpy(h + o_pos, pos, sizeof(int32_t) * nt);
+    std::memcpy(h + o_max, &max_pos, sizeof(int32_t));
+  });
 }
 
 // The decode step: one token through the same layers and regions, with the one-row kernels
@@ -535,7 +675,8 @@ extern "C" int mi_prefill_forward_n(const mi_model* md, const int32_t* token_ids
   if ((rc = validate_tokens(md->hp, token_ids, positions, n_tokens, n_ctx, &max_pos))) return rc;
   hipStream_t s = as_stream(md->stream);
   const Ws w = carve(md->hp, md->max_tokens, (char*)md->workspace);
-  if ((rc = stage_tokens(w, token_ids, positions, n_tokens, &max_pos, s))) return rc;
+  if ((rc = check_stage(md, w))) return rc;
+  if ((rc = stage_tokens(md->stage, w, token_ids, positions, n_tokens, max_pos, s))) return rc;
   return enqueue_forward(md, w, n_tokens, n_ctx, kv, n_out, logits_out, s);
 }
 
@@ -637,11 +778,13 @@ extern "C" int mi_prefill_forward_slots(const mi_model* md, const int32_t* token
   if (rc) return rc;
   for (int sl = 1; sl < n_slots; ++sl)
     if ((rc = validate_kv(md->hp, &kv[sl], n_ctx))) return rc;
+  if ((rc = validate_kv_disjoint(kv, n_slots))) return rc;
   for (int sl = 0; sl < n_slots; ++sl)  // positions: ranges; no repeat within a slot
     if ((rc = validate_tokens(md->hp, token_ids + off[sl], positions + off[sl], slot_tokens[sl], n_ctx, &maxpos[sl])))
       return rc;
   hipStream_t s = as_stream(md->stream);
   const Ws w = carve(md->hp, md->max_tokens, (char*)md->workspace);
+  if ((rc = check_stage(md, w))) return rc;
   const int L = std::max(md->hp.n_layers, 1);
   // attention query tiles: up to 16 rows of one slot each
   int n_tiles = 0;
@@ -653,37 +796,43 @@ extern "C" int mi_prefill_forward_slots(const mi_model* md, const int32_t* token
                o_last = o_rows + align_up(sizeof(int32_t) * (size_t)nt),
                bytes = o_last + sizeof(int32_t) * MI_MAX_SLOTS;
   if (bytes > w.slot_stage_bytes) return set_error(MI_ERR_WORKSPACE, "forward_slots: staging area too small");
-  std::vector<char> blob(bytes, 0);
-  AttnSlotTile* tiles = reinterpret_cast<AttnSlotTile*>(blob.data() + o_tiles);
-  float** regions = reinterpret_cast<float**>(blob.data() + o_regions);
-  int32_t* slot_of_row = reinterpret_cast<int32_t*>(blob.data() + o_rows);
-  int32_t* last = reinterpret_cast<int32_t*>(blob.data() + o_last);
-  for (int l = 0; l < md->hp.n_layers; ++l) {
-    int i = 0;
-    for (int sl = 0; sl < n_slots; ++sl) {
-      regions[(size_t)l * MI_MAX_SLOTS + sl] = kv[sl].k[l];
-      regions[((size_t)L + l) * MI_MAX_SLOTS + sl] = kv[sl].v[l];
-      for (int t = 0; t < slot_tokens[sl]; t += 16)
-        tiles[(size_t)l * n_tiles + i++] =
-            AttnSlotTile{kv[sl].k[l], kv[sl].v[l], off[sl] + t, std::min(16, slot_tokens[sl] - t), maxpos[sl], 0};
-    }
-  }
-  for (int sl = 0; sl < n_slots; ++sl) {
-    for (int t = 0; t < slot_tokens[sl]; ++t) slot_of_row[off[sl] + t] = sl;
-    last[sl] = off[sl] + slot_tokens[sl] - 1;
-  }
   int32_t mp_all = 0;
   for (int sl = 0; sl < n_slots; ++sl) mp_all = std::max(mp_all, maxpos[sl]);
-  if ((rc = stage_tokens(w, token_ids, positions, nt, &mp_all, s))) return rc;
-  MI_HIP(hipMemcpyAsync(w.slot_stage, blob.data(), bytes, hipMemcpyHostToDevice, s));
+  // ids, positions, the largest position and the tables, written into the next pinned buffer of the
+  // stage in the workspace's layout and sent in one copy
+  char* base = reinterpret_cast<char*>(w.ids);
+  const size_t o_pos = (char*)w.pos - base, o_max = (char*)w.maxpos - base, o_blob = w.slot_stage - base;
+  rc = stage_send(md->stage, base, o_blob + bytes, s, [&](char* h) {
+    std::memcpy(h, token_ids, sizeof(int32_t) * nt);
+    std::memcpy(h + o_pos, positions, sizeof(int32_t) * nt);
+    std::memcpy(h + o_max, &mp_all, sizeof(int32_t));
+    char* blob = h + o_blob;
+    std::memset(blob, 0, bytes);
+    AttnSlotTile* tiles = reinterpret_cast<AttnSlotTile*>(blob + o_tiles);
+    float** regions = reinterpret_cast<float**>(blob + o_regions);
+    int32_t* slot_of_row = reinterpret_cast<int32_t*>(blob + o_rows);
+    int32_t* last = reinterpret_cast<int32_t*>(blob + o_last);
+    for (int l = 0; l < md->hp.n_layers; ++l) {
+      int i = 0;
+      for (int sl = 0; sl < n_slots; ++sl) {
+        regions[(size_t)l * MI_MAX_SLOTS + sl] = kv[sl].k[l];
+        regions[((size_t)L + l) * MI_MAX_SLOTS + sl] = kv[sl].v[l];
+        for (int t = 0; t < slot_tokens[sl]; t += 16)
+          tiles[(size_t)l * n_tiles + i++] =
+              AttnSlotTile{kv[sl].k[l], kv[sl].v[l], off[sl] + t, std::min(16, slot_tokens[sl] - t), maxpos[sl], 0};
+      }
+    }
+    for (int sl = 0; sl < n_slots; ++sl) {
+      for (int t = 0; t < slot_tokens[sl]; ++t) slot_of_row[off[sl] + t] = sl;
+      last[sl] = off[sl] + slot_tokens[sl] - 1;
+    }
+  });
+  if (rc) return rc;
   const SlotStage st{reinterpret_cast<const AttnSlotTile*>(w.slot_stage + o_tiles),
                      reinterpret_cast<float* const*>(w.slot_stage + o_regions),
                      reinterpret_cast<const int32_t*>(w.slot_stage + o_rows),
                      reinterpret_cast<const int32_t*>(w.slot_stage + o_last), n_tiles};
-  rc = enqueue_slots(md, w, st, nt, n_slots, kv, logits_out, s);
-  // the staging buffer above is host heap memory: wait for the copy before returning
-  MI_HIP(hipStreamSynchronize(s));
-  return rc;
+  return enqueue_slots(md, w, st, nt, n_slots, kv, logits_out, s);
 }
 
 // ---------------------------------------------------------------- graph replay
@@ -691,6 +840,7 @@ struct mi_prefill_graph {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   hipStream_t stream = nullptr;
+  mi_stage* stage = nullptr;  // the model's stage: ids and positions of each launch go through it
   mi_hparams hp{};
   Ws w{};
   int32_t n_tokens = 0, n_ctx = 0;
@@ -709,6 +859,11 @@ extern "C" int mi_prefill_graph_create(const mi_model* md, int32_t n_tokens, int
   g->stream = s;
   g->hp = md->hp;
   g->w = carve(md->hp, md->max_tokens, (char*)md->workspace);
+  if ((rc = check_stage(md, g->w))) {
+    delete g;
+    return rc;
+  }
+  g->stage = md->stage;
   g->n_tokens = n_tokens;
   g->n_ctx = n_ctx;
   hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
@@ -739,7 +894,7 @@ extern "C" int mi_prefill_graph_launch(mi_prefill_graph* g, const int32_t* token
   if (!g || !g->exec) return set_error(MI_ERR_INVALID_ARG, "graph: NULL handle");
   int rc = validate_tokens(g->hp, token_ids, positions, g->n_tokens, g->n_ctx, &g->max_pos);
   if (rc) return rc;
-  if ((rc = stage_tokens(g->w, token_ids, positions, g->n_tokens, &g->max_pos, g->stream))) return rc;
+  if ((rc = stage_tokens(g->stage, g->w, token_ids, positions, g->n_tokens, g->max_pos, g->stream))) return rc;
   MI_HIP(hipGraphLaunch(g->exec, g->stream));
   return MI_OK;
 }

@@ -158,6 +158,8 @@ __device__ __forceinline__ float swiglu_f32(float g, float u, const double* tab)
 // All take device pointers, assume validated shapes, launch on `s`.
 int launch_quantize(const float* x, int64_t rows, int cols, int64_t ld_x, int8_t* codes,
                     uint16_t* scales, hipStream_t s);
+// canonical 34-byte Q8_0 blocks (fp16 scale bits, 32 codes) -> the two planes; codes 16-byte aligned
+int launch_pack_q8_0(const void* blocks, int64_t rows, int cols, int8_t* codes, uint16_t* scales, hipStream_t s);
 // x [rows][cols]; with n_split > 1, x += f32(sum of the split-K partials [n_split][rows][cols]) first
 // (written back), as the deferred reduction of the matmul that produced them.
 int launch_rmsnorm_quant(float* x, const float* gamma, int64_t rows, int cols, float eps,

@@ -29,6 +29,32 @@ __global__ void __launch_bounds__(256) k_quantize(const float* __restrict__ x, i
   }
 }
 
+// ---------------------------------------------------------------- canonical blocks -> planes
+// One thread per 34-byte block (fp16 scale bits, then 32 codes; 2-byte aligned): 17 two-byte
+// loads, the scale to its plane, the codes as two 16-byte stores (code rows are 32-byte multiples).
+__global__ void __launch_bounds__(256) k_pack_q8_0(const uint16_t* __restrict__ blocks, int64_t n_blocks,
+                                                   int8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+  for (int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; b < n_blocks; b += (int64_t)gridDim.x * blockDim.x) {
+    const uint16_t* src = blocks + b * 17;
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = (uint32_t)src[1 + 2 * i] | ((uint32_t)src[2 + 2 * i] << 16);
+    scales[b] = src[0];
+    uint4* dst = reinterpret_cast<uint4*>(codes + b * QK);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+int launch_pack_q8_0(const void* blocks, int64_t rows, int cols, int8_t* codes, uint16_t* scales, hipStream_t s) {
+  const int64_t n_blocks = rows * (cols / QK);
+  const int64_t wg = std::min<int64_t>((n_blocks + 255) / 256, 65536);
+  hipLaunchKernelGGL(k_pack_q8_0, dim3((unsigned)wg), dim3(256), 0, s, reinterpret_cast<const uint16_t*>(blocks),
+                     n_blocks, codes, scales);
+  MI_LAUNCH_CHECK("k_pack_q8_0");
+  return MI_OK;
+}
+
 // The shuffle inside q8_block_quant4 needs all 8 lanes of a block active, so grid-stride
 // loops must keep whole lane groups together: total % 8 == 0 always holds (cols % 32 == 0)
 // and the stride is a multiple of 64, so a group is either fully in range or fully out.

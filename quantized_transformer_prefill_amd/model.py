@@ -80,9 +80,10 @@ class PrefillModel:
         if ws_bytes == 0:
             B.check(B.MI_ERR_INVALID_ARG)
         self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
+        self.stage = B.Stage(hp, max_tokens)  # pinned host staging of ids and positions
         self.model = B.Model(hp, B.q8(*emb), B.q8(*out), f32["output_norm.weight"].data_ptr(),
                              C.cast(layers, C.POINTER(B.LayerWeights)), self.rope.data_ptr(), n_ctx,
-                             self.workspace.data_ptr(), ws_bytes, max_tokens, None)
+                             self.workspace.data_ptr(), ws_bytes, max_tokens, None, self.stage.handle)
         kv_embd = cfg.n_head_kv * cfg.head_dim
         self.kv_k = torch.full((cfg.n_layers, n_ctx, kv_embd), kv_fill, dtype=torch.float32, device=self.device)
         self.kv_v = torch.full((cfg.n_layers, n_ctx, kv_embd), kv_fill, dtype=torch.float32, device=self.device)

@@ -49,9 +49,11 @@ def make_model(n_layers=2, hidden=64, nh=4, nkv=2, hd=64, ffn=96, vocab=50, max_
     model = B.Model(hp, _fake_q8(vocab, hidden), _fake_q8(vocab, hidden), FAKE,
                     C.cast(layers, C.POINTER(B.LayerWeights)), FAKE, n_ctx, FAKE,
                     need if ws_bytes is None else ws_bytes, max_tokens, None)
-    kk = (C.c_void_p * n_layers)(*([FAKE] * n_layers))
-    kv = B.KvRegions(kk, kk, n_layers, n_ctx, nkv * hd)
-    return model, kv, (layers, kk)
+    region = 4 * n_ctx * nkv * hd  # distinct, non-overlapping fake regions (never dereferenced)
+    kk = (C.c_void_p * n_layers)(*[FAKE + (2 * i) * region for i in range(n_layers)])
+    vv = (C.c_void_p * n_layers)(*[FAKE + (2 * i + 1) * region for i in range(n_layers)])
+    kv = B.KvRegions(kk, vv, n_layers, n_ctx, nkv * hd)
+    return model, kv, (layers, kk, vv)
 
 
 def call_forward(model, kv, ids, pos, n_ctx=16):
@@ -135,3 +137,77 @@ def test_workspace_grows_with_tokens():
     b = B.lib().mi_prefill_workspace_bytes(C.byref(hp), 512)
     assert 0 < a < b
     assert B.lib().mi_rope_table_bytes(C.byref(hp), 4096) == 4096 * 32 * 2 * 8
+
+
+def test_forward_rejects_wide_attention_rows():
+    """n_head * head_dim above 4096 (the one-row kernels of the last layer hold a whole attention
+    output row) is refused up front, before any layer is enqueued."""
+    hp = B.Hparams(1, 4096, 40, 8, 128, 4096, 50, 1e-6, 1e6, 0, 1, 0)
+    assert B.lib().mi_prefill_workspace_bytes(C.byref(hp), 8) == 0
+    assert b"n_head * head_dim" in B.lib().mi_last_error()
+    model, kv, keep = make_model(hidden=4096, nh=40, nkv=8, hd=128, ffn=4096)
+    assert call_forward(model, kv, [1], [0]) == B.MI_ERR_UNSUPPORTED
+
+
+def test_forward_rejects_overlapping_regions():
+    model, kv, keep = make_model()
+    layers, kk, vv = keep
+    vv[1] = kk[0]                       # V of layer 1 is K of layer 0
+    assert call_forward(model, kv, [1, 2], [0, 1]) == B.MI_ERR_INVALID_ARG
+    assert b"overlap" in B.lib().mi_last_error()
+    model, kv, keep = make_model()
+    layers, kk, vv = keep
+    vv[0] = kk[0] + 4 * 64              # partly overlapping: shifted by one row
+    assert call_forward(model, kv, [1, 2], [0, 1]) == B.MI_ERR_INVALID_ARG
+
+
+def test_forward_needs_a_stage():
+    model, kv, keep = make_model()
+    assert call_forward(model, kv, [1, 2], [0, 1]) == B.MI_ERR_INVALID_ARG
+    assert b"stage" in B.lib().mi_last_error()
+
+
+def test_forward_rejects_shapes_past_32bit_offsets():
+    """max_tokens x the widest activation row reaching 2^31 elements is refused on the host: the
+    kernels address rows with 32-bit offsets."""
+    hp = B.Hparams(2, 64, 4, 2, 64, 96, 50, 1e-6, 1e6, 1, 0, 0)
+    max_tokens = (1 << 31) // 512 + 1   # the widest row here is Q|K|V: 4*64 + 2*2*64 = 512 values
+    need = B.lib().mi_prefill_workspace_bytes(C.byref(hp), max_tokens)
+    model, kv, keep = make_model(max_tokens=max_tokens, ws_bytes=need)
+    assert call_forward(model, kv, [1, 2], [0, 1]) == B.MI_ERR_UNSUPPORTED
+    assert b"2^31" in B.lib().mi_last_error()
+    L = B.lib()
+    w = _fake_q8(4096, 4096)
+    assert L.mi_gemm_q8_0(FAKE, FAKE, 1 << 19, C.byref(w), None, None, FAKE, None) == B.MI_ERR_UNSUPPORTED
+    assert L.mi_gemm_q8_0_ws(FAKE, FAKE, 1 << 19, C.byref(w), None, None, FAKE, None, 0, 0, None) == \
+        B.MI_ERR_UNSUPPORTED
+    gu = _fake_q8(1 << 17, 1 << 14)    # n * k = 2^31
+    assert L.mi_gemm_swiglu_q8_0(FAKE, FAKE, 2, C.byref(gu), FAKE, FAKE, None, 0, None) == B.MI_ERR_UNSUPPORTED
+
+
+def test_slots_reject_shared_regions():
+    """Two sequences of one call must not share KV regions (their stores would race)."""
+    model, kv, keep = make_model()
+    ids = np.array([1, 2, 3], dtype=np.int32)
+    pos = np.array([0, 1, 0], dtype=np.int32)
+    counts = np.array([2, 1], dtype=np.int32)
+    kvs = (B.KvRegions * 2)(kv, kv)     # the same region set twice
+    rc = B.lib().mi_prefill_forward_slots(C.byref(model), ids.ctypes.data, pos.ctypes.data, counts.ctypes.data, 2,
+                                          16, kvs, FAKE)
+    assert rc == B.MI_ERR_INVALID_ARG and b"overlap" in B.lib().mi_last_error()
+
+
+def test_pack_and_stage_argument_checks():
+    L = B.lib()
+    assert L.mi_pack_q8_0(FAKE, 4, 48, FAKE, FAKE, None) == B.MI_ERR_INVALID_ARG       # cols % 32
+    assert L.mi_pack_q8_0(FAKE + 1, 4, 64, FAKE, FAKE, None) == B.MI_ERR_INVALID_ARG   # blocks odd address
+    assert L.mi_pack_q8_0(FAKE, 4, 64, FAKE + 8, FAKE, None) == B.MI_ERR_INVALID_ARG   # codes not 16-aligned
+    assert L.mi_pack_q8_0(FAKE, 0, 64, FAKE, FAKE, None) == B.MI_ERR_INVALID_ARG       # no rows
+    hp = B.Hparams(2, 64, 4, 2, 64, 96, 50, 1e-6, 1e6, 1, 0, 0)
+    assert L.mi_stage_create(C.byref(hp), 8, None) == B.MI_ERR_INVALID_ARG
+    h = C.c_void_p(FAKE)
+    assert L.mi_stage_create(C.byref(hp), 0, C.byref(h)) == B.MI_ERR_INVALID_ARG
+    assert h.value is None
+    bad = B.Hparams(2, 64, 4, 3, 64, 96, 50, 1e-6, 1e6, 1, 0, 0)
+    assert L.mi_stage_create(C.byref(bad), 8, C.byref(h)) == B.MI_ERR_INVALID_ARG
+    L.mi_stage_destroy(None)  # a no-op

@@ -130,3 +130,41 @@ def test_headline_config_decode_matches_oracle():
     d = np.linalg.norm(gk[:, :end] - kk[:, :end]) / np.linalg.norm(kk[:, :end])
     say(f"  K regions rel-L2 {d:.3e}, identical {np.mean(gk[:, :end] == kk[:, :end]):.6f}")
     assert d <= 1e-3 and np.all(gk[:, end:] == SENTINEL)
+
+
+# head_dim 128 with keys spread over several of the one-token attention's key ranges (256 keys each
+# for n_ctx 800): the last prompt token sits at position 599, so its attention merges three ranges
+TINY_Q3_LONG = synth.ModelConfig(name="tiny_qwen3_long", n_layers=2, hidden=256, n_head=4, n_head_kv=2,
+                                 head_dim=128, ffn=384, vocab=1000, n_tokens=40, n_ctx=800, seed=17,
+                                 qkv_bias=False, qk_norm=True, tied=True, prefix_tokens=560)
+
+
+def test_one_token_tail_merges_key_ranges_head_dim_128():
+    """The last prompt token of a prefill (n_out = 1) and the decode steps after it run the
+    one-token attention, whose key ranges are merged in the output projection's prologue: with
+    head_dim 128 and positions past 512 several ranges carry keys.  Logits and regions against the
+    oracle, for the prefill and for 3 decode steps at 600..602."""
+    dev = need_gpu()
+    cfg = TINY_Q3_LONG
+    m, w = load_pair(cfg, dev)
+    pre_ids, ids = synth.gen_token_ids(cfg)
+    pre_pos, pos = synth.positions_for(cfg)
+    kk, vv = oracle.new_kv_regions(cfg, cfg.n_ctx, fill=SENTINEL)
+    m.forward(pre_ids, pre_pos)
+    oracle.prefill_forward(cfg, w, pre_ids, pre_pos, cfg.n_ctx, kk, vv)
+    got = m.forward(ids, pos).cpu().numpy()
+    want = oracle.prefill_forward(cfg, w, ids, pos, cfg.n_ctx, kk, vv)[0]
+    compare_logits(got, want, f"{cfg.name} prefill logits (last position {int(pos[-1])})")
+    assert_f32_match(got, want, max_ulp=64, max_frac_inexact=0.05, what="prefill logits ulp")
+    for i, tok in enumerate(decode_tokens(cfg, 3)):
+        p = int(pos[-1]) + 1 + i
+        say(f"decode {cfg.name} step {i} position {p}")
+        got = m.decode(int(tok), p).cpu().numpy().copy()
+        want = oracle.prefill_forward(cfg, w, np.array([tok], np.int32), np.array([p], np.int32), cfg.n_ctx, kk, vv)[0]
+        compare_logits(got, want, f"{cfg.name} step {i} logits")
+        assert_f32_match(got, want, max_ulp=64, max_frac_inexact=0.05, what=f"step {i} logits ulp")
+    end = int(pos[-1]) + 4
+    gk, gv = m.kv_k.cpu().numpy(), m.kv_v.cpu().numpy()
+    assert np.all(gk[:, end:] == SENTINEL) and np.all(gv[:, end:] == SENTINEL), "stray KV writes"
+    assert_f32_match(gk[:, :end], kk[:, :end], max_ulp=64, max_frac_inexact=0.05, what="K regions")
+    assert_f32_match(gv[:, :end], vv[:, :end], max_ulp=64, max_frac_inexact=0.05, what="V regions")

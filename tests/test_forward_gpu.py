@@ -1,6 +1,4 @@
 """End-to-end parity of mi_prefill_forward with the oracle, plus the forward's invariants on GPU."""
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -239,70 +237,24 @@ def test_forward_errors_leave_state_untouched():
 
 
 def test_headline_config_matches_oracle():
-    """The 24-layer 0.5B-shaped model on its 512-token prompt, logits and all KV rows."""
+    """The 24-layer 0.5B-shaped model on its 512-token prompt: logits, and the K and V rows of every
+    layer, against the oracle."""
     dev = need_gpu()
     cfg = synth.QWEN2_0P5B
     say(f"forward {cfg.name}")
     m, logits, want, kk, vv = run_pair(cfg, dev)
     compare_logits(logits, want, f"{cfg.name} logits")
-    gk = m.kv_k.cpu().numpy()
-    n = cfg.n_tokens
-    assert np.all(gk[:, n:] == SENTINEL)
-    d = np.linalg.norm(gk[:, :n] - kk[:, :n]) / np.linalg.norm(kk[:, :n])
-    say(f"  K regions rel-L2 {d:.3e}, identical {np.mean(gk[:, :n] == kk[:, :n]):.6f}")
-    assert d <= 1e-3
+    compare_regions(m.kv_k.cpu().numpy(), m.kv_v.cpu().numpy(), kk, vv, cfg.n_tokens, cfg.name)
 
 
-@pytest.mark.slow
-@pytest.mark.parametrize("name", ["qwen2p5_7b_pp2048", "qwen3_8b_chunk3072at1024"])
-def test_large_configs_match_oracle(name):
-    """The 7B- and 8B-shaped configurations at full size: last-token logits and the KV rows of
-    every layer against the oracle.  The oracle needs tens of TFLOP of f64 work on the host, so
-    the test runs only with MI_RUN_SLOW=1; weights are regenerated on the device for the oracle
-    (the same seeded draws) instead of being held as f32 host copies."""
-    if not os.environ.get("MI_RUN_SLOW"):
-        pytest.skip("set MI_RUN_SLOW=1 (the oracle needs tens of TFLOP on the host)")
-    import time
-    dev = need_gpu()
-    cfg = synth.MODEL_CONFIGS[name]
-    specs = {n: (shape, kind) for n, shape, kind in synth.tensor_specs(cfg)}
-    say(f"forward {cfg.name}: loading")
-    m = PrefillModel(cfg, synth.iter_tensors(cfg, device=dev), cfg.prefix_tokens + cfg.n_tokens, cfg.n_ctx,
-                     device=dev, kv_fill=SENTINEL)
-    pre_ids, ids = synth.gen_token_ids(cfg)
-    pre_pos, pos = synth.positions_for(cfg)
-    torch.cuda.synchronize()
-    t0 = time.time()
-    if cfg.prefix_tokens:
-        m.forward(pre_ids, pre_pos)
-    torch.cuda.synchronize()
-    t1 = time.time()
-    logits = m.forward(ids, pos).cpu().numpy()
-    t2 = time.time()
-    say(f"  GPU: prefix {t1 - t0:.3f} s, chunk {t2 - t1:.3f} s ({cfg.n_tokens / (t2 - t1):.0f} tok/s, first call)")
-    gk = m.kv_k.cpu().numpy()
-    del m
-    torch.cuda.empty_cache()
-
-    def source(n):
-        shape, kind = specs[n]
-        return synth.gen_tensor(cfg.seed, n, shape, kind, device=dev).cpu().numpy()
-
-    q8 = [n for n, (shape, kind) in specs.items() if kind == "q8"]
-    w = oracle.QuantizedWeights(source, q8, cache=True)
-    kk, vv = oracle.new_kv_regions(cfg, cfg.n_ctx, fill=SENTINEL)
-    t3 = time.time()
-    tick = lambda il: say(f"  oracle layer {il} done at {time.time() - t3:.0f} s")
-    if cfg.prefix_tokens:
-        oracle.prefill_forward(cfg, w, pre_ids, pre_pos, cfg.n_ctx, kk, vv, progress=tick)
-    want = oracle.prefill_forward(cfg, w, ids, pos, cfg.n_ctx, kk, vv, progress=tick)[0]
-    say(f"  oracle: {time.time() - t3:.0f} s")
-    compare_logits(logits, want, f"{cfg.name} logits")
-    used = cfg.prefix_tokens + cfg.n_tokens
-    d = np.linalg.norm(gk[:, :used] - kk[:, :used]) / np.linalg.norm(kk[:, :used])
-    say(f"  K regions rel-L2 {d:.3e}, identical {np.mean(gk[:, :used] == kk[:, :used]):.6f}")
-    assert d <= 1e-3
-    assert np.all(gk[:, used:] == SENTINEL)
+def compare_regions(gk, gv, kk, vv, used, what):
+    """K and V regions of every layer (host copies): rows 0..used-1 against the oracle's (f32 values
+    rounded from f64 node results: identical but for rare one-ulp f64 ties), rows past them untouched."""
+    for name, g, o in (("K", gk, kk), ("V", gv, vv)):
+        assert np.all(g[:, used:] == SENTINEL), f"{what}: stray {name} writes"
+        d = np.linalg.norm(g[:, :used] - o[:, :used]) / np.linalg.norm(o[:, :used])
+        say(f"  {what} {name} regions rel-L2 {d:.3e}")
+        assert_f32_match(g[:, :used], o[:, :used], max_ulp=64, max_frac_inexact=1e-3, what=f"{what} {name} regions")
 
 
 @pytest.mark.parametrize("name", ["qwen2p5_7b_pp2048", "qwen3_8b_chunk3072at1024"])

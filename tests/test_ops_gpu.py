@@ -113,9 +113,10 @@ def test_gemm_in_place_residual():
 
 
 @pytest.mark.parametrize("case", synth.GEMM_SWEEP, ids=lambda c: c.name)
-def test_gemm_full_size_sampled(case):
-    """The GEMM sweep at full size, in the launch configuration the benchmark uses (library's own
-    split choice); the oracle computes 512 sampled outputs one by one."""
+def test_gemm_full_size_matches_oracle(case):
+    """The GEMM sweep at full size, in the launch configuration the benchmark uses (the library's own
+    tile and split choice): every output element against the oracle's f64 matmul of the same Q8_0
+    operands (the activations with 1% x20 outliers are quantized by both sides, bit-identically)."""
     dev = need_gpu()
     say(f"gemm full size {case.name}")
     x, w = synth.gen_gemm_inputs(case, device=dev)
@@ -123,16 +124,35 @@ def test_gemm_full_size_sampled(case):
     wc, ws = B.quantize_q8_0(w)
     out = B.gemm_q8_0(xc, xs, wc, ws, split_k=0)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(case.m + case.n)
-    rows = rng.integers(0, case.m, 512)
-    cols = rng.integers(0, case.n, 512)
-    rows[:2], cols[:2] = [0, case.m - 1], [0, case.n - 1]
-    xr = x[torch.as_tensor(rows, device=dev)].cpu().numpy()
-    wr = w[torch.as_tensor(cols, device=dev)].cpu().numpy()
-    oq, od = quantize_q8_0(wr)
-    want = np.array([ops.matmul_q8_0(xr[i:i + 1], oq[i:i + 1], od[i:i + 1])[0, 0] for i in range(512)], dtype=f32)
-    got = out.cpu().numpy()[rows, cols]
-    assert_f32_match(got, want, what=f"{case.name} sampled")
+    got = out.cpu().numpy()
+    del out, xc, xs, wc, ws
+    oq, od = quantize_q8_0(w.cpu().numpy())
+    want = ops.matmul_q8_0(x.cpu().numpy(), oq, od)
+    d = got.astype(np.float64) - want
+    say(f"  {case.name}: max-abs {np.abs(d).max():.3e} rel-L2 {np.linalg.norm(d) / np.linalg.norm(want):.3e}")
+    assert_f32_match(got, want, what=f"{case.name} all outputs")
+
+
+def test_pack_canonical_blocks():
+    """mi_pack_q8_0: canonical 34-byte blocks (fp16 scale, 32 codes), built on the host from the
+    oracle's quantization, land in the two planes byte for byte -- the oracle's codes and scales,
+    and the library's own quantization of the same f32 values."""
+    dev = need_gpu()
+    for rows, cols in [(3, 32), (7, 896), (129, 4864)]:
+        w = synth.gen_normal(111, f"p{rows}x{cols}", (rows, cols), std=0.02, device=dev)
+        w[0, :32] = 0.0                                   # an all-zero block
+        oc, os_ = quantize_q8_0(w.cpu().numpy())
+        blk = np.zeros(rows * (cols // 32), dtype=np.dtype([("d", "<u2"), ("qs", "i1", 32)], align=False))
+        assert blk.dtype.itemsize == 34
+        blk["d"] = os_.view(np.uint16).reshape(-1)
+        blk["qs"] = oc.reshape(-1, 32)
+        raw = torch.as_tensor(np.frombuffer(blk.tobytes(), dtype=np.uint8).copy(), device=dev)
+        pc, ps = B.pack_q8_0(raw, rows, cols)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(pc.cpu().numpy(), oc)
+        np.testing.assert_array_equal(ps.cpu().numpy().view(np.uint16), os_.view(np.uint16))
+        gc, gs = B.quantize_q8_0(w)
+        assert torch.equal(gc, pc) and torch.equal(gs, ps)
 
 
 def test_gemm_swiglu_matches_oracle():
