@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--slots", type=int, default=0,
                    help="time one call of N independent sequences (mi_prefill_forward_slots) that split the "
                         "workload's prompt evenly, each with its own KV regions; prints its own JSON line")
+    p.add_argument("--probes", action="store_true",
+                   help="run the rate probes (libmi_probes.so: f64 FMA, int8 MFMA, the matmul's block loop with "
+                        "the exact f64 and with an f32 epilogue) and print their rates as one JSON line")
     p.add_argument("--workload", default=None,
                    help="model workload name (default: the 512-token 0.5B-shaped headline); the others "
                         "are reported for context: " + ", ".join(["layer1_896", "qwen2_0p5b_pp512",
@@ -107,6 +110,9 @@ def main():
     B.lib()  # fail loudly if the HIP library is not built
     cfg = synth.MODEL_CONFIGS[args.workload] if args.workload else synth.HEADLINE
     dev = torch.device("cuda:0")
+    if args.probes:
+        print(json.dumps({"probes": probe_rates(dev)}), flush=True)
+        return
     if args.traffic_run:
         traffic_run(cfg, dev)
         return
@@ -174,11 +180,18 @@ def main():
         # counters taken on this kernel's current source and at this very shape only
         if rec.get("kernel_source_hash") == kernel_source_hash() and rec.get("shape_mnk") == [M, N2, H]:
             traffic = rec.get("bytes_per_launch")
+    # the ceiling of this kernel's instruction mix: its block loop (1 x 2 wave tile, exact f64
+    # epilogue) with operands in registers, measured now on this GPU
+    rates = probe_rates(dev, only=("loop_exact_1x2",))
+    ceiling = {"what": "the matmul's block loop alone (1 x 2 wave tile, int8 MFMA + exact f64 epilogue, "
+                       "operands in registers, no memory traffic)",
+               "achieved": rates["loop_exact_1x2"]["rate"], "unit": "TOP/s (int8)",
+               "frac": round(rates["loop_exact_1x2"]["rate"] / INT8_PEAK_TOPS, 4)}
     roofline = {"bound": "mfma", "kernel": "k_gemm_q8<EPI_SWIGLU_Q8> (gate|up + SwiGLU + Q8_0)",
                 "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8)",
                 "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
                 "algorithmic_ops_per_launch": ops, "avg_launch_ms": round(k_ms, 5), "shape_mnk": [M, N2, H],
-                "launches_timed": reps,
+                "launches_timed": reps, "ceiling": ceiling,
                 "f64_epilogue": {"bound": "alu", "achieved": round(f64_achieved, 2), "peak": F64_VALU_PEAK_TFLOPS,
                                  "unit": "TFLOP/s (f64 vector)", "frac": round(f64_achieved / F64_VALU_PEAK_TFLOPS, 4),
                                  "flops_per_launch": f64_flops}}
@@ -383,6 +396,49 @@ def cpu_baseline_decode(cfg, min_seconds: float = 10.0, max_reps: int = 64):
                       f"{cfg.n_tokens}-token prompt ({t:.1f} s of CPU time; prompt prefill and weight "
                       f"quantization untimed)",
             "host_cpus": os.cpu_count()}
+
+
+PROBES = {  # name: (probe id of mi_probes.h, workgroups, iterations, unit of the work)
+    "f64_fma": (0, 2048, 20000, "T FMA/s"),
+    "mfma_i8": (1, 2048, 5000, "TOP/s (int8)"),
+    "loop_exact_1x2": (2, 3072, 500, "TOP/s (int8)"),
+    "loop_exact_4x2": (3, 2048, 200, "TOP/s (int8)"),
+    "loop_f32_2x2": (4, 2048, 2000, "TOP/s (int8)"),
+}
+
+
+def probe_rates(dev, only=None):
+    """Rates of the probe kernels (libmi_probes.so), each timed over 5 launches with HIP events on
+    the stream they run on, after one untimed launch."""
+    import ctypes as C
+
+    import torch
+
+    from quantized_transformer_prefill_amd import binding as B
+
+    lib = C.CDLL(os.path.join(ROOT, "quantized_transformer_prefill_amd", "libmi_probes.so"))
+    lib.mi_probe_run.restype = C.c_int
+    lib.mi_probe_run.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.POINTER(C.c_double), C.c_void_p]
+    out = {}
+    for name, (pid, wg, iters, unit) in PROBES.items():
+        if only and name not in only:
+            continue
+        buf = torch.empty(wg * 256, dtype=torch.float64, device=dev)
+        work = C.c_double()
+
+        def run():
+            rc = lib.mi_probe_run(pid, wg, iters, buf.data_ptr(), C.byref(work), B.stream_ptr())
+            if rc:
+                raise RuntimeError(f"mi_probe_run({name}) failed: {rc}")
+        ms = timed_loop(run, 5, torch)
+        rate = work.value / (ms / 1e3) / 1e12
+        rec = {"rate": round(rate, 2), "unit": unit, "ms_per_launch": round(ms, 4)}
+        if unit.startswith("TOP"):
+            rec["int8_peak_frac"] = round(rate / INT8_PEAK_TOPS, 4)
+        else:
+            rec["f64_peak_frac"] = round(2 * rate / F64_VALU_PEAK_TFLOPS, 4)
+        out[name] = rec
+    return out
 
 
 def dominant_kernel(cfg, dev, w_gate_up=None):

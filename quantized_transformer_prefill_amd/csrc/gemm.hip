@@ -23,6 +23,7 @@
 // with the next stage's global loads in flight while the current one computes.  Split-K writes f64 partials that a second kernel
 // reduces in a fixed order (deterministic).
 #include "common.h"
+#include "q8_epilogue.h"
 
 namespace mi {
 
@@ -32,7 +33,6 @@ typedef double v8d __attribute__((ext_vector_type(8)));
 
 constexpr int G_THREADS = 256;
 constexpr int G_KS = 4;     // Q8_0 blocks per LDS stage (128 K values)
-constexpr double G_MAGIC = 0x1.8p+52 + 0x1p+31;  // 1.5*2^52 + 2^31, exact
 
 // Wave tile = RG x CG MFMAs (16 real rows x 32 columns each); workgroup = 2 x 2 waves.
 // LDS rows hold the 4 blocks of a stage back to back (128 bytes = 8 chunks of 16).  Chunk c of
@@ -96,39 +96,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
-}
-
-// acc[j] += bcast(da, lane 8*HALF + j of each 16-lane row) * x[j] for j = 0..7: v_fmac_f64 with a
-// DPP row_newbcast source (the one DPP form of the f64 ALU).  da comes from an LDS load; the
-// leading s_nop gives the two wait states a DPP source needs after any VALU write of it.
-template <int HALF>
-__device__ __forceinline__ void fmac8_bcast(double (&acc)[8], const double (&x)[8], double da) {
-  if constexpr (HALF == 0)
-    asm("s_nop 1\n\t"
-        "v_fmac_f64_dpp %0, %8, %9 row_newbcast:0\n\t"
-        "v_fmac_f64_dpp %1, %8, %10 row_newbcast:1\n\t"
-        "v_fmac_f64_dpp %2, %8, %11 row_newbcast:2\n\t"
-        "v_fmac_f64_dpp %3, %8, %12 row_newbcast:3\n\t"
-        "v_fmac_f64_dpp %4, %8, %13 row_newbcast:4\n\t"
-        "v_fmac_f64_dpp %5, %8, %14 row_newbcast:5\n\t"
-        "v_fmac_f64_dpp %6, %8, %15 row_newbcast:6\n\t"
-        "v_fmac_f64_dpp %7, %8, %16 row_newbcast:7"
-        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6]),
-          "+v"(acc[7])
-        : "v"(da), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
-  else
-    asm("s_nop 1\n\t"
-        "v_fmac_f64_dpp %0, %8, %9 row_newbcast:8\n\t"
-        "v_fmac_f64_dpp %1, %8, %10 row_newbcast:9\n\t"
-        "v_fmac_f64_dpp %2, %8, %11 row_newbcast:10\n\t"
-        "v_fmac_f64_dpp %3, %8, %12 row_newbcast:11\n\t"
-        "v_fmac_f64_dpp %4, %8, %13 row_newbcast:12\n\t"
-        "v_fmac_f64_dpp %5, %8, %14 row_newbcast:13\n\t"
-        "v_fmac_f64_dpp %6, %8, %15 row_newbcast:14\n\t"
-        "v_fmac_f64_dpp %7, %8, %16 row_newbcast:15"
-        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6]),
-          "+v"(acc[7])
-        : "v"(da), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
 }
 
 template <int RG, int CG, int EPI, bool SPLIT, int NS>

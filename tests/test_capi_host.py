@@ -9,11 +9,14 @@ import pytest
 
 from quantized_transformer_prefill_amd import binding as B
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mi_prefill.h")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi_prefill.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "mi_probes.h")
+PROBE_LIB = os.path.join(ROOT, "quantized_transformer_prefill_amd", "libmi_probes.so")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(mi_\w+)\s*\(", text, flags=re.M)))
 
@@ -26,6 +29,20 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), f"{n} declared in mi_prefill.h but not exported"
         assert n in B.SIGNATURES, f"{n} has no binding signature"
     assert lib.mi_version().startswith(b"mi_prefill")
+
+
+def test_probe_library_exports_its_header():
+    """libmi_probes.so (the rate probes behind the matmul's ceilings) loads and exports what
+    mi_probes.h declares; bad arguments are refused before any launch."""
+    names = declared_functions(PROBE_HEADER)
+    assert names == ["mi_probe_run"], names
+    lib = C.CDLL(PROBE_LIB)
+    lib.mi_probe_run.restype = C.c_int
+    lib.mi_probe_run.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.POINTER(C.c_double), C.c_void_p]
+    w = C.c_double()
+    assert lib.mi_probe_run(0, 0, 10, FAKE, C.byref(w), None) == B.MI_ERR_INVALID_ARG
+    assert lib.mi_probe_run(0, 4, 10, None, C.byref(w), None) == B.MI_ERR_INVALID_ARG
+    assert lib.mi_probe_run(99, 4, 10, FAKE, C.byref(w), None) == B.MI_ERR_INVALID_ARG
 
 
 FAKE = 0x10000  # a non-null pointer value that is never dereferenced on these paths
