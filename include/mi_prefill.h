@@ -307,6 +307,18 @@ int mi_gemm_q8_0_ws(const int8_t* a_codes, const uint16_t* a_scales, int32_t m, 
                     size_t workspace_bytes, int32_t split_k, void* stream);
 size_t mi_gemm_q8_0_workspace_bytes(int32_t m, int32_t n, int32_t k);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): mi_gemm_q8_0_ws with the split-K partials in a static device
+ * array of the library, MI_STATIC_SCRATCH_BYTES per GPU, held from the library's first use on that
+ * GPU until the process ends.  Calls allocate nothing.  split_k = 0 lets the library choose and
+ * lowers the split to what the array holds; an explicit split_k > 1 whose partials
+ * (split_k * m * n * 8 bytes) exceed the array fails with MI_ERR_WORKSPACE.  All calls on one GPU
+ * share the array: calls that may overlap on one GPU (other streams, other threads) race, so the
+ * caller serializes them.  Results are those of mi_gemm_q8_0_ws with the same split. */
+#define MI_STATIC_SCRATCH_BYTES (64u << 20)
+int mi_gemm_q8_0_static(const int8_t* a_codes, const uint16_t* a_scales, int32_t m, const mi_q8_matrix* w,
+                        const float* bias, const float* residual, float* out, int32_t split_k, void* stream);
+
 /* gate|up matmul with SwiGLU and Q8_0 in the epilogue ("05", section 2.5 gate, up, SwiGLU):
  *   g = f32(x.Wgate), u = f32(x.Wup), s = f32(silu(g) * u), then s -> Q8_0.
  *   w_gate_up in the interleaved layout of mi_layer_weights ([2*ffn][k], rows % 64 == 0);

@@ -82,6 +82,7 @@ SIGNATURES = {
     "mi_gemm_q8_0": (C.c_int, [_P, _P, _I32, C.POINTER(Q8Matrix), _P, _P, _P, _P]),
     "mi_gemm_q8_0_ws": (C.c_int, [_P, _P, _I32, C.POINTER(Q8Matrix), _P, _P, _P, _P, _SZ, _I32, _P]),
     "mi_gemm_q8_0_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "mi_gemm_q8_0_static": (C.c_int, [_P, _P, _I32, C.POINTER(Q8Matrix), _P, _P, _P, _I32, _P]),
     "mi_sampler_workspace_bytes": (_SZ, []),
     "mi_sample": (C.c_int, [_P, _I32, _P, _I32, C.POINTER(SamplerParams), C.c_uint64, C.c_uint64, _P, _SZ, _P, _P]),
     "mi_gemm_swiglu_q8_0": (C.c_int, [_P, _P, _I32, C.POINTER(Q8Matrix), _P, _P, _P, _SZ, _P]),

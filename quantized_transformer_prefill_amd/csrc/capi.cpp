@@ -272,6 +272,26 @@ extern "C" int mi_gemm_q8_0_ws(const int8_t* a_codes, const uint16_t* a_scales, 
   return launch_gemm_q8(g, as_stream(stream));
 }
 
+extern "C" int mi_gemm_q8_0_static(const int8_t* a_codes, const uint16_t* a_scales, int32_t m,
+                                   const mi_q8_matrix* w, const float* bias, const float* residual, float* out,
+                                   int32_t split_k, void* stream) {
+  if (!a_codes || !a_scales || !w || !w->codes || !w->scales || !out || m < 0 || w->rows <= 0 || w->cols <= 0 ||
+      w->cols % QK || w->rows % QK || split_k < 0)
+    return set_error(MI_ERR_INVALID_ARG, "mi_gemm_q8_0_static: bad arguments");
+  if (int rc = check_gemm_offsets("mi_gemm_q8_0_static", m, w->rows, w->cols)) return rc;
+  if (split_k > 1 && (uint64_t)split_k * (uint64_t)m * (uint64_t)w->rows * sizeof(double) > MI_STATIC_SCRATCH_BYTES)
+    return set_error(MI_ERR_WORKSPACE, "mi_gemm_q8_0_static: split %d x %d x %d f64 partials exceed the %u-byte "
+                     "static scratch", split_k, m, w->rows, (unsigned)MI_STATIC_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  if (int rc = static_scratch(&scratch)) return rc;
+  GemmArgs g{};
+  g.a_codes = a_codes; g.a_scales = a_scales; g.m = m;
+  g.w_codes = w->codes; g.w_scales = w->scales; g.n = w->rows; g.k = w->cols;
+  g.bias = bias; g.residual = residual; g.out = out; g.ld_out = w->rows;
+  g.workspace = scratch; g.workspace_bytes = MI_STATIC_SCRATCH_BYTES; g.split_k = split_k;
+  return launch_gemm_q8(g, as_stream(stream));
+}
+
 extern "C" size_t mi_gemm_q8_0_workspace_bytes(int32_t m, int32_t n, int32_t k) {
   if (m <= 0 || n <= 0 || k <= 0) return 0;
   return gemm_workspace_bytes(m, n, k);

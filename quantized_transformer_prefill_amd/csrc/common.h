@@ -231,6 +231,8 @@ struct GemmArgs {
 };
 int launch_gemm_q8(const GemmArgs& a, hipStream_t s);
 size_t gemm_workspace_bytes(int m, int n, int k);
+// the current device's address of the library's static scratch array (MI_STATIC_SCRATCH_BYTES)
+int static_scratch(void** ptr);
 int launch_lm_head(const int8_t* xq, const uint16_t* xs, int cols, const int8_t* w_codes,
                    const uint16_t* w_scales, int rows, float* logits, hipStream_t s);
 

@@ -22,6 +22,8 @@
 // stage of 4 blocks (128 K values) of codes and f64 scales goes through LDS, double-buffered,
 // with the next stage's global loads in flight while the current one computes.  Split-K writes f64 partials that a second kernel
 // reduces in a fixed order (deterministic).
+#include <mutex>
+
 #include "common.h"
 #include "q8_epilogue.h"
 
@@ -670,6 +672,30 @@ int launch_gemm_q8(const GemmArgs& g, hipStream_t s) {
                        g.residual, g.out, g.ld_out);
   }
   MI_LAUNCH_CHECK("k_splitk_reduce");
+  return MI_OK;
+}
+
+// ---------------------------------------------------------------- static scratch
+// Split-K partials of the matmul variant that allocates nothing (mi_gemm_q8_0_static): one array per
+// GPU for the life of the process.  Host code never passes `scratch` itself to a kernel (on the host
+// that name is only a stand-in); it looks up the device address once per device and uses that.
+__device__ __align__(256) char scratch[MI_STATIC_SCRATCH_BYTES];
+
+int static_scratch(void** ptr) {
+  constexpr int MAX_DEV = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEV] = {};
+  int dev = 0;
+  MI_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEV) return set_error(MI_ERR_UNSUPPORTED, "static scratch: device %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    MI_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return set_error(MI_ERR_HIP, "static scratch: no device address");
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
   return MI_OK;
 }
 
