@@ -76,34 +76,20 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-template <int NT>
-__device__ double block_sum_f64(double v, double* sh) {
-  v = wave_sum_f64(v);
-  const int w = threadIdx.x / 64, l = threadIdx.x % 64;
-  if (l == 0) sh[w] = v;
-  __syncthreads();
-  double t = 0;
-  if (threadIdx.x < NT / 64) t = sh[threadIdx.x];
-  if (threadIdx.x < 64) {
-    t = wave_sum_f64(t);
-    if (threadIdx.x == 0) sh[NT / 64] = t;
-  }
-  __syncthreads();
-  return sh[NT / 64];
-}
-
 // ---------------------------------------------------------------- RMSNorm + quantize
 // One workgroup per row.  y = f32(x / sqrt(mean(x^2) + eps) * gamma) with the mean, sqrt,
-// reciprocal and gain in f64; then Q8_0 per 32-block.  Rows of up to RN_MAXV float4 per thread
-// stay in registers, longer rows are re-read.
+// reciprocal and gain in f64; then Q8_0 per 32-block.  A row of up to NV float4 per thread is held
+// in registers between the two passes, indexed only by unrolled (compile-time) loop counters so it
+// stays in VGPRs; the gains are requested together with the row.  Longer rows take the NV = 0
+// variant, which reads the row again in the second pass.
 //
 // Pending split-K partials (partial != null): the row first becomes
 // x + f32(sum_z partial[z][r]) (the residual add of the matmul that produced the partials, summed
 // in the fixed order z = 0..n_split-1 exactly as the split-K reduction would), which is written
 // back to x before the norm.
 constexpr int RN_THREADS = 256;
-constexpr int RN_MAXV = 8;  // float4 per thread kept in registers
 
+template <int NV>
 __global__ void __launch_bounds__(RN_THREADS) k_rmsnorm_quant(float* __restrict__ x,
                                                              const float* __restrict__ gamma, int cols,
                                                              float eps, int8_t* __restrict__ codes,
@@ -111,7 +97,7 @@ __global__ void __launch_bounds__(RN_THREADS) k_rmsnorm_quant(float* __restrict_
                                                              float* __restrict__ y_out,
                                                              const double* __restrict__ partial, int n_split,
                                                              int64_t rows) {
-  __shared__ double sh[RN_THREADS / 64 + 1];
+  __shared__ double sh[RN_THREADS / 64];
   const int64_t r = blockIdx.x;
   float* xr = x + r * cols;
   const int nvec = cols / 4;
@@ -130,29 +116,13 @@ __global__ void __launch_bounds__(RN_THREADS) k_rmsnorm_quant(float* __restrict_
     }
     return v;
   };
-  float4 keep[RN_MAXV];
-  double ss = 0.0;
-#pragma unroll
-  for (int j = 0; j < RN_MAXV; ++j) {
-    const int c4 = threadIdx.x + j * RN_THREADS;
-    if (c4 < nvec) {
-      keep[j] = load(c4);
-      const double a = keep[j].x, b = keep[j].y, c = keep[j].z, d = keep[j].w;
-      ss += a * a + b * b + c * c + d * d;
-    }
-  }
-  for (int c4 = threadIdx.x + RN_MAXV * RN_THREADS; c4 < nvec; c4 += RN_THREADS) {
-    const float4 v = load(c4);
+  auto sq = [](float4 v) {
     const double a = v.x, b = v.y, c = v.z, d = v.w;
-    ss += a * a + b * b + c * c + d * d;
-  }
-  const double total = block_sum_f64<RN_THREADS>(ss, sh);
-  const double inv_rms = recip_f64(sqrt(total / (double)cols + (double)eps));
-  // rows are a multiple of 32 values; lane groups of 8 cover one block, and all 8 lanes of
-  // a group share the same loop trip count, so the cross-lane maxima see a full group.
-  for (int c4 = threadIdx.x, j = 0; c4 < nvec; c4 += RN_THREADS, ++j) {
-    const float4 v = (j < RN_MAXV) ? keep[j] : reinterpret_cast<const float4*>(xr)[c4];
-    const float4 g = reinterpret_cast<const float4*>(gamma)[c4];
+    return a * a + b * b + c * c + d * d;
+  };
+  // rows are a multiple of 32 values; lane groups of 8 cover one block, and all 8 lanes of a group
+  // are in or out of range together, so the cross-lane maxima see a full group
+  auto emit = [&](int c4, float4 v, float4 g, double inv_rms) {
     float4 o;
     o.x = (float)((double)v.x * inv_rms * (double)g.x);
     o.y = (float)((double)v.y * inv_rms * (double)g.y);
@@ -163,6 +133,42 @@ __global__ void __launch_bounds__(RN_THREADS) k_rmsnorm_quant(float* __restrict_
     const uint32_t q = q8_block_quant4(o, d);
     reinterpret_cast<uint32_t*>(codes + r * cols)[c4] = q;
     if ((c4 & 7) == 0) scales[r * (cols / QK) + c4 / 8] = f32_to_f16_bits(d);
+  };
+  const float4* g4 = reinterpret_cast<const float4*>(gamma);
+  double ss = 0.0;
+  float4 keep[NV > 0 ? NV : 1], gk[NV > 0 ? NV : 1];
+  if constexpr (NV > 0) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int c4 = threadIdx.x + j * RN_THREADS;
+      if (c4 < nvec) {
+        keep[j] = load(c4);
+        gk[j] = g4[c4];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if (threadIdx.x + j * RN_THREADS < nvec) ss += sq(keep[j]);
+  } else {
+    for (int c4 = threadIdx.x; c4 < nvec; c4 += RN_THREADS) ss += sq(load(c4));
+  }
+  // the row's sum: wave sums, then every thread adds the 4 wave sums in a fixed order
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  double total = 0.0;
+#pragma unroll
+  for (int w = 0; w < RN_THREADS / 64; ++w) total += sh[w];
+  const double inv_rms = recip_f64(sqrt(total / (double)cols + (double)eps));
+  if constexpr (NV > 0) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int c4 = threadIdx.x + j * RN_THREADS;
+      if (c4 < nvec) emit(c4, keep[j], gk[j], inv_rms);
+    }
+  } else {
+    for (int c4 = threadIdx.x; c4 < nvec; c4 += RN_THREADS)
+      emit(c4, reinterpret_cast<const float4*>(xr)[c4], g4[c4], inv_rms);
   }
 }
 
@@ -170,8 +176,17 @@ int launch_rmsnorm_quant(float* x, const float* gamma, int64_t rows, int cols, f
                          int8_t* codes, uint16_t* scales, float* y, hipStream_t s, const double* partial,
                          int n_split) {
   if (rows == 0) return MI_OK;
-  hipLaunchKernelGGL(k_rmsnorm_quant, dim3((unsigned)rows), dim3(RN_THREADS), 0, s, x, gamma, cols, eps,
-                     codes, scales, y, n_split > 1 ? partial : nullptr, n_split, rows);
+  const double* pp = n_split > 1 ? partial : nullptr;
+  const int per_thread = (cols / 4 + RN_THREADS - 1) / RN_THREADS;  // float4 per thread
+#define MI_RN(NV)                                                                                        \
+  hipLaunchKernelGGL(k_rmsnorm_quant<NV>, dim3((unsigned)rows), dim3(RN_THREADS), 0, s, x, gamma, cols, eps, \
+                     codes, scales, y, pp, n_split, rows)
+  if (per_thread <= 1) MI_RN(1);
+  else if (per_thread <= 2) MI_RN(2);
+  else if (per_thread <= 4) MI_RN(4);
+  else if (per_thread <= 8) MI_RN(8);
+  else MI_RN(0);
+#undef MI_RN
   MI_LAUNCH_CHECK("k_rmsnorm_quant");
   return MI_OK;
 }
