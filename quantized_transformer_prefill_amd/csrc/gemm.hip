@@ -45,17 +45,25 @@ constexpr int G_ROWB = G_KS * QK;  // bytes per LDS row
 // Ring depth (stages in LDS) per tile shape.  Two: deeper rings cost more in workgroups per CU (LDS)
 // than they gain in latency hiding at the model's shapes (measured for 3 and 4 stages).
 constexpr int G_NS_11 = 2, G_NS_12 = 2, G_NS_22 = 2;
+#ifndef G_SP_42
+#define G_SP_42 0
+#endif
 __device__ __forceinline__ int swz(int row, int chunk) { return ((chunk ^ (row & 7)) << 4); }
 
 // NS stages live in a ring; every load into it is a global->LDS transfer.
-template <int RG, int CG, int NS>
+// Scales of a stage, two layouts:
+//  * SP (scale pairs; the row length in blocks is even): word [row][p] holds the fp16 scales of
+//    blocks 2p (low half) and 2p+1 (high half) of the stage, moved 4 bytes per lane -- one
+//    transfer instruction covers 32 rows x 4 blocks;
+//  * otherwise word [block][row] holds one fp16 scale in its low half, moved 2 bytes per lane.
+template <int RG, int CG, int NS, bool SP>
 struct GemmTile {
   static constexpr int BM = 2 * 16 * RG;   // real activation rows per workgroup
   static constexpr int BN = 2 * 32 * CG;   // weight rows (output columns) per workgroup
   int8_t a[NS][BM + 1][G_ROWB];   // row BM is all zeros
   int8_t b[NS][BN][G_ROWB];
-  uint32_t as[NS][G_KS][BM];      // fp16 scale bits in the low half of each word
-  uint32_t bs[NS][G_KS][BN];
+  uint32_t as[NS][SP ? 2 * BM : G_KS * BM];
+  uint32_t bs[NS][SP ? 2 * BN : G_KS * BN];
 };
 
 // 16 bytes per lane from gbase + voff into LDS at lds + 16 * lane (global_load_lds_dwordx4: M0
@@ -87,6 +95,15 @@ __device__ __forceinline__ void lds_dma2(void* lds, const uint16_t* gbase, uint3
                : "s"(l), "v"(voff), "s"(gbase)
                : "memory", "m0");
 }
+// The same for 4 bytes per lane (global_load_lds_dword): lane l's word lands at lds + 4 * lane.
+__device__ __forceinline__ void lds_dma4(void* lds, const uint16_t* gbase, uint32_t voff) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  gbase = sgpr_ptr(gbase);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(l), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
 // x, as a value the compiler cannot compute ahead of this point (keeps loop-invariant address
 // arithmetic inside the loop instead of in registers)
 __device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
@@ -100,15 +117,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
 }
 
-template <int RG, int CG, int EPI, bool SPLIT, int NS>
+template <int RG, int CG, int EPI, bool SPLIT, int NS, bool SP>
 __global__ void __launch_bounds__(G_THREADS, RG == 1 ? 3 : 2)
 k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales, int M,
           const int8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales, int N, int K,
           const float* __restrict__ bias, const float* residual, float* out, int64_t ld_out,
           int8_t* __restrict__ q_codes, uint16_t* __restrict__ q_scales,
           double* __restrict__ partial, int kb_per_split, int xcd_order, QkvEpi qe) {
-  using T = GemmTile<RG, CG, NS>;
+  using T = GemmTile<RG, CG, NS, SP>;
   constexpr int BM = T::BM, BN = T::BN;
+  static_assert(!SP || NS == 2, "scale pairs: one wait for all of a stage's transfers");
   __shared__ __align__(16) T sm;
   __shared__ double exp_tab[EPI == EPI_SWIGLU_Q8 ? 64 : 1];  // 2^(j/64) for the SiLU
   const int tid = threadIdx.x;
@@ -178,22 +196,32 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
   for (int q = 0; q < A_OFF; ++q) a_off[q] = (uint32_t)min(a_r0 + 32 * q, M - 1) * (uint32_t)K + lchunk * 16;
 #pragma unroll
   for (int q = 0; q < B_OFF; ++q) b_off[q] = (uint32_t)min(b_r0 + 32 * q, N - 1) * (uint32_t)K + lchunk * 16;
-  // ---- scales: global -> LDS directly too, 2 bytes per lane.  Per stage, wave w moves the
-  // A scales of block w (rows 64i + l, l < AS_L, one instruction per 64 rows) and the B-scale
-  // elements 64(w + 4i) + l (block (64(w + 4i) + l) / BN, row (64(w + 4i) + l) % BN).
+  // ---- scales: global -> LDS directly too.
+  // SP: 4 bytes per lane; wave w moves the pairs of rows 32w..32w+31 (lane l: row l/2, pair l%2)
+  // of A (w < BM/32) and of B (w < BN/32).
+  // Otherwise 2 bytes per lane; per stage, wave w moves the A scales of block w (rows 64i + l,
+  // l < AS_L, one instruction per 64 rows) and the B-scale elements 64(w + 4i) + l (block
+  // (64(w + 4i) + l) / BN, row (64(w + 4i) + l) % BN).
   static_assert(G_KS == 4, "one A-scale block per wave");
   constexpr int AS_L = BM < 64 ? BM : 64;   // lanes per A-scale instruction
-  constexpr int AS_I = BM / AS_L;           // A-scale instructions per wave: 1 or 2
-  constexpr int BS_I = BN * G_KS / 256;     // 1 or 2
-  static_assert(AS_L * AS_I == BM && BS_I * 256 == BN * G_KS, "scale transfer shape");
-  constexpr int L_OPS = A_DMA + B_DMA + AS_I + BS_I;  // transfers per wave per stage
-  constexpr int AS_OFF = LEAN ? 1 : AS_I;
+  constexpr int AS_I = SP ? 0 : BM / AS_L;  // A-scale instructions per wave: 1 or 2
+  constexpr int BS_I = SP ? 0 : BN * G_KS / 256;  // 1 or 2
+  constexpr int AP_I = SP ? BM / 32 : 0, BP_I = SP ? BN / 32 : 0;  // waves moving pairs
+  static_assert(SP || (AS_L * AS_I == BM && BS_I * 256 == BN * G_KS), "scale transfer shape");
+  static_assert(AP_I <= 4 && BP_I <= 4, "one pair instruction per wave and operand");
+  constexpr int L_OPS = A_DMA + B_DMA + AS_I + BS_I + (SP ? 2 : 0);  // transfers per wave per stage (at most)
+  constexpr int AS_OFF = SP ? 1 : (LEAN ? 1 : AS_I);
   uint32_t as_off[AS_OFF];
+  if constexpr (SP) {
+    as_off[0] = (uint32_t)min(m0 + 32 * wave + (lane >> 1), M - 1) * (uint32_t)(KB * 2) + 4 * (lane & 1);
+  } else {
 #pragma unroll
-  for (int i = 0; i < AS_OFF; ++i) as_off[i] = (uint32_t)min(m0 + 64 * i + lane, M - 1) * (uint32_t)(KB * 2);
+    for (int i = 0; i < AS_OFF; ++i) as_off[i] = (uint32_t)min(m0 + 64 * i + lane, M - 1) * (uint32_t)(KB * 2);
+  }
   // row (64(w + 4i) + l) % BN does not depend on i (256 is a multiple of BN)
   static_assert(256 % BN == 0, "B-scale rows");
-  const uint32_t bs_off = (uint32_t)min(n0 + (64 * wave + lane) % BN, N - 1) * (uint32_t)(KB * 2);
+  const uint32_t bs_off = SP ? (uint32_t)min(n0 + 32 * wave + (lane >> 1), N - 1) * (uint32_t)(KB * 2) + 4 * (lane & 1)
+                             : (uint32_t)min(n0 + (64 * wave + lane) % BN, N - 1) * (uint32_t)(KB * 2);
   auto issue = [&](int kbs, int st) {
     // a stage past the end of the slice (K not a multiple of the stage) re-reads its last block
     // for the missing ones; compute() skips them
@@ -208,7 +236,7 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
         for (int q = 0; q < A_DMA; ++q) lds_dma16(&sm.a[st][8 * (4 * q + wave)][0], ga + (int64_t)32 * q * K, a_off[0] + fix);
 #pragma unroll
         for (int i = 0; i < AS_I; ++i)
-          if (lane < AS_L) lds_dma2(&sm.as[st][wave][64 * i], gas + (int64_t)64 * i * KB, as_off[0]);
+          if (lane < AS_L) lds_dma2(&sm.as[st][wave * BM + 64 * i], gas + (int64_t)64 * i * KB, as_off[0]);
       } else {
         const int r0 = (int)opaque_u32((uint32_t)a_r0), l0 = (int)opaque_u32((uint32_t)lane);
 #pragma unroll
@@ -217,7 +245,8 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
                     (uint32_t)min(r0 + 32 * q, M - 1) * (uint32_t)K + lchunk * 16 + fix);
 #pragma unroll
         for (int i = 0; i < AS_I; ++i)
-          if (lane < AS_L) lds_dma2(&sm.as[st][wave][64 * i], gas, (uint32_t)min(m0 + 64 * i + l0, M - 1) * (uint32_t)(KB * 2));
+          if (lane < AS_L)
+            lds_dma2(&sm.as[st][wave * BM + 64 * i], gas, (uint32_t)min(m0 + 64 * i + l0, M - 1) * (uint32_t)(KB * 2));
       }
       if (b_full) {
 #pragma unroll
@@ -236,12 +265,19 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
       for (int q = 0; q < B_DMA; ++q) lds_dma16(&sm.b[st][8 * (4 * q + wave)][0], gb, b_off[q] + fix);
 #pragma unroll
       for (int i = 0; i < AS_I; ++i)
-        if (lane < AS_L) lds_dma2(&sm.as[st][wave][64 * i], gas, as_off[i]);
+        if (lane < AS_L) lds_dma2(&sm.as[st][wave * BM + 64 * i], gas, as_off[i]);
     }
+    if constexpr (SP) {
+      // a stage shorter than G_KS blocks has 2 (rows hold an even number of blocks, and stages
+      // start at multiples of 4): its second pair re-reads the first, which compute() skips
+      const uint32_t pfix = (nbk < G_KS && (lane & 1)) ? 4u : 0u;
+      if (wave < AP_I) lds_dma4(&sm.as[st][64 * wave], a_scales + kbs, as_off[0] - pfix);
+      if (wave < BP_I) lds_dma4(&sm.bs[st][64 * wave], w_scales + kbs, bs_off - pfix);
+    } else {
 #pragma unroll
-    for (int i = 0; i < BS_I; ++i)
-      lds_dma2(&sm.bs[st][0][0] + 64 * (wave + 4 * i), w_scales + kbs + min(64 * (wave + 4 * i) / BN, nbk - 1),
-               bs_off);
+      for (int i = 0; i < BS_I; ++i)
+        lds_dma2(&sm.bs[st][64 * (wave + 4 * i)], w_scales + kbs + min(64 * (wave + 4 * i) / BN, nbk - 1), bs_off);
+    }
   };
 
   v16i cinit;
@@ -275,7 +311,8 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
       for (int p = 0; p < 2; ++p)
-        dav[rg][p] = (double)f16_bits_to_f32((uint16_t)sm.as[st][2 * p + da_lblk][da_lrow + rg * 16]);
+        dav[rg][p] = SP ? (double)f16_bits_to_f32((uint16_t)(sm.as[st][2 * (da_lrow + rg * 16) + p] >> (16 * da_lblk)))
+                        : (double)f16_bits_to_f32((uint16_t)sm.as[st][(2 * p + da_lblk) * BM + da_lrow + rg * 16]);
 #pragma unroll
     for (int jb = 0; jb < G_KS; ++jb) {
       if (jb >= nbk) break;  // past the end of the slice
@@ -299,7 +336,8 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
       double dw[CG], cdw[CG];
 #pragma unroll
       for (int cg = 0; cg < CG; ++cg) {
-        dw[cg] = (double)f16_bits_to_f32((uint16_t)sm.bs[st][jb][b_rrow + cg * 32]);
+        dw[cg] = SP ? (double)f16_bits_to_f32((uint16_t)(sm.bs[st][2 * (b_rrow + cg * 32) + (jb >> 1)] >> (16 * (jb & 1))))
+                    : (double)f16_bits_to_f32((uint16_t)sm.bs[st][jb * BN + b_rrow + cg * 32]);
         cdw[cg] = -G_MAGIC * dw[cg];
       }
 #pragma unroll
@@ -604,28 +642,28 @@ size_t gemm_workspace_bytes(int m, int n, int k) {
   return s > 1 ? (size_t)s * m * n * sizeof(double) : 0;
 }
 
-template <int RG, int CG, int NS>
+template <int RG, int CG, int NS, bool SP>
 static void launch_tiles(const GemmArgs& g, int split, int kb_per, hipStream_t s) {
-  using T = GemmTile<RG, CG, NS>;
+  using T = GemmTile<RG, CG, NS, SP>;
   dim3 grid((g.n + T::BN - 1) / T::BN, (g.m + T::BM - 1) / T::BM, split);
   // XCD-aware order once the weights outgrow one XCD's 4 MB L2 several times over
   const int xcd = (int64_t)g.n * g.k > ((int64_t)16 << 20) ? 1 : 0;
   double* partial = reinterpret_cast<double*>(g.workspace);
   if (split > 1)
-    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, true, NS>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
+    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, true, NS, SP>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
                        g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
                        partial, kb_per, xcd, g.qkv);
   else if (g.qkv.pos)
-    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_QKV, false, NS>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
+    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_QKV, false, NS, SP>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
                        g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
                        nullptr, kb_per, xcd, g.qkv);
   else if (g.q_codes) {
     if constexpr (CG >= 2)
-      hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_SWIGLU_Q8, false, NS>), grid, dim3(G_THREADS), 0, s, g.a_codes,
+      hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_SWIGLU_Q8, false, NS, SP>), grid, dim3(G_THREADS), 0, s, g.a_codes,
                          g.a_scales, g.m, g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out,
                          g.q_codes, g.q_scales, nullptr, kb_per, xcd, g.qkv);
   } else
-    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, false, NS>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
+    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, false, NS, SP>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
                        g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
                        nullptr, kb_per, xcd, g.qkv);
 }
@@ -651,10 +689,19 @@ int launch_gemm_q8(const GemmArgs& g, hipStream_t s) {
   int kb_per = (KB + split - 1) / split;
   kb_per = ((kb_per + G_KS - 1) / G_KS) * G_KS;
   split = (KB + kb_per - 1) / kb_per;
-  if (p.shape == 3) launch_tiles<4, 2, G_NS_22>(g, split, kb_per, s);
-  else if (p.shape == 1) launch_tiles<2, 2, G_NS_22>(g, split, kb_per, s);
-  else if (p.shape == 2) launch_tiles<1, 2, G_NS_12>(g, split, kb_per, s);
-  else launch_tiles<1, 1, G_NS_11>(g, split, kb_per, s);
+  // scale pairs: rows of an even number of blocks, scale planes 4-byte aligned
+  const bool sp = KB % 2 == 0 && ((uintptr_t)g.a_scales & 3) == 0 && ((uintptr_t)g.w_scales & 3) == 0;
+  if (sp && (G_SP_42 || p.shape != 3)) {
+    if (p.shape == 3) launch_tiles<4, 2, G_NS_22, true>(g, split, kb_per, s);
+    else if (p.shape == 1) launch_tiles<2, 2, G_NS_22, true>(g, split, kb_per, s);
+    else if (p.shape == 2) launch_tiles<1, 2, G_NS_12, true>(g, split, kb_per, s);
+    else launch_tiles<1, 1, G_NS_11, true>(g, split, kb_per, s);
+  } else {
+    if (p.shape == 3) launch_tiles<4, 2, G_NS_22, false>(g, split, kb_per, s);
+    else if (p.shape == 1) launch_tiles<2, 2, G_NS_22, false>(g, split, kb_per, s);
+    else if (p.shape == 2) launch_tiles<1, 2, G_NS_12, false>(g, split, kb_per, s);
+    else launch_tiles<1, 1, G_NS_11, false>(g, split, kb_per, s);
+  }
   MI_LAUNCH_CHECK("k_gemm_q8");
   const bool defer = g.split_out && !g.q_codes && !g.bias && split > 1;  // the consumer reduces the partials
   if (g.split_out) *g.split_out = defer ? split : 1;
