@@ -45,7 +45,6 @@ constexpr int G_ROWB = G_KS * QK;  // bytes per LDS row
 // Ring depth (stages in LDS) per tile shape.  Two: deeper rings cost more in workgroups per CU (LDS)
 // than they gain in latency hiding at the model's shapes (measured for 3 and 4 stages).
 constexpr int G_NS_11 = 2, G_NS_12 = 2, G_NS_22 = 2;
-
 __device__ __forceinline__ int swz(int row, int chunk) { return ((chunk ^ (row & 7)) << 4); }
 
 // NS stages live in a ring; every load into it is a global->LDS transfer.
@@ -689,9 +688,8 @@ int launch_gemm_q8(const GemmArgs& g, hipStream_t s) {
   split = (KB + kb_per - 1) / kb_per;
   // scale pairs: rows of an even number of blocks, scale planes 4-byte aligned
   const bool sp = KB % 2 == 0 && ((uintptr_t)g.a_scales & 3) == 0 && ((uintptr_t)g.w_scales & 3) == 0;
-  if (sp && p.shape != 3) {  // (the 4x2 tile: more spills with pairs, no faster)
-    if (p.shape == 3) launch_tiles<4, 2, G_NS_22, true>(g, split, kb_per, s);
-    else if (p.shape == 1) launch_tiles<2, 2, G_NS_22, true>(g, split, kb_per, s);
+  if (sp && p.shape != 3) {  // (the 4x2 tile: more spills with pairs, measured no faster)
+    if (p.shape == 1) launch_tiles<2, 2, G_NS_22, true>(g, split, kb_per, s);
     else if (p.shape == 2) launch_tiles<1, 2, G_NS_12, true>(g, split, kb_per, s);
     else launch_tiles<1, 1, G_NS_11, true>(g, split, kb_per, s);
   } else {
