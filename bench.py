@@ -48,6 +48,11 @@ def parse():
                    help="launches for the per-kernel counters: two eager forwards, then the calibration kernel")
     p.add_argument("--write-counters", nargs=4, metavar=("COMPUTE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT"),
                    help="turn the three counter passes of --counter-run into a per-kernel summary (OUT)")
+    p.add_argument("--write-kernel-summary", nargs=2, metavar=("TRACE_DIR", "OUT"),
+                   help="turn a rocprofv3 --kernel-trace run of this benchmark into a per-forward kernel table "
+                        "(OUT); --skip-forwards leaves out the first forwards, --trace-command records the command")
+    p.add_argument("--skip-forwards", type=int, default=1)
+    p.add_argument("--trace-command", default="")
     p.add_argument("--decode", action="store_true",
                    help="time decode steps (one token per step, mi_decode_step via a captured graph) after "
                         "the workload's prompt instead of the prefill; prints its own JSON line")
@@ -93,6 +98,11 @@ def main():
     if args.write_counters:
         import synth
         write_counters(synth.MODEL_CONFIGS[args.workload] if args.workload else synth.HEADLINE, *args.write_counters)
+        return
+    if args.write_kernel_summary:
+        import synth
+        write_kernel_summary(synth.MODEL_CONFIGS[args.workload] if args.workload else synth.HEADLINE,
+                             *args.write_kernel_summary, args.skip_forwards, args.trace_command)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -152,6 +162,7 @@ def main():
         stream.synchronize()
         eager_ms = e0.elapsed_time(e1) / args.steps
         graph = model.graph(cfg.n_tokens)
+        kernels_per_forward = graph.nodes()
         for _ in range(args.warmup):
             graph.launch(ids, pos)
         torch.cuda.synchronize()
@@ -233,6 +244,7 @@ def main():
         "config": {"workload": cfg.name, "description": cfg.description, "n_tokens": cfg.n_tokens,
                    "n_ctx": cfg.n_ctx, "parallelism": "single GPU"},
         "eager_ms_per_step": round(eager_ms, 4),
+        "kernels_per_forward": kernels_per_forward,
         "roofline": roofline,
         "gemm_sweep": sweep,
         "cpu_baseline": cpu,
@@ -531,31 +543,142 @@ def _dispatch_table(d):
     return out, dur
 
 
+def _short(name):
+    """mi::kernel<template args> of a trace's kernel name."""
+    import re
+
+    m = re.search(r"mi::(\w+)(<[^(]*>)?", name)
+    return (m.group(1) + (m.group(2) or "")) if m else name
+
+
+def _gemm_args(short):
+    """(RG, CG, EPI, split) of a k_gemm_q8 instance name, or None."""
+    import re
+
+    m = re.match(r"k_gemm_q8<(\d+), (\d+), (\d+), (true|false)", short or "")
+    return (int(m.group(1)), int(m.group(2)), int(m.group(3)), m.group(4) == "true") if m else None
+
+
+def _classify(short, prev):
+    """The forward node a kernel launch is, from its name and the launch before it."""
+    ga = _gemm_args(short)
+    if ga:
+        epi, split = ga[2], ga[3]
+        if epi == 2:
+            return "qkv"
+        if epi == 1:
+            return "gate_up"
+        pa = _gemm_args(prev)
+        if prev and prev.startswith("k_attention"):
+            return "wo_split" if split else "wo"
+        if pa and pa[2] == 1:
+            return "down_split" if split else "down"
+        return "gemm_other"
+    if short.startswith("k_rmsnorm_quant"):
+        pa = _gemm_args(prev)
+        return "norm_partials" if pa and pa[3] else "norm"
+    if short.startswith("k_attention"):
+        return "attention"
+    if short.startswith("k_gemv_q8<4, 1, 1>"):
+        return "lm_head"
+    if short.startswith("k_embed"):
+        return "embed"
+    return None
+
+
 def _forward_kernels(cfg):
-    """(kernel-name prefix, label, algorithmic int8 ops per launch or 0, algorithmic HBM bytes or 0,
-    name prefix of the kernel dispatched just before it or None) of the forward's kernels at the full
-    prompt (tail layers run on fewer rows and are grouped apart).  The output and down projections
-    are the same kernel at the same grid at this shape; the kernel before each tells them apart."""
+    """{node: (label, algorithmic int8 ops per launch or 0, algorithmic HBM bytes per launch)} of
+    the forward's nodes at the full prompt (the split-K variants write, and the RMSNorm after them
+    reads, two f64 partials per output: the library's split at these shapes)."""
     M, H, F = cfg.n_tokens, cfg.hidden, cfg.ffn
     nq, nkv = cfg.n_head * cfg.head_dim, cfg.n_head_kv * cfg.head_dim
+    kv_rows = cfg.prefix_tokens + cfg.n_tokens
     q8 = lambda rows, cols: rows * cols * 34 // 32
-    return [
-        ("void mi::k_gemm_q8<1, 2, 1, false, 2>", f"gate|up + SwiGLU + Q8_0 ({M}x{2 * F}x{H})", 2 * M * 2 * F * H,
-         q8(2 * F, H) + q8(M, H) + q8(M, F)),
-        ("void mi::k_gemm_q8<1, 1, 0, true, 2>", f"down, split-K partials ({M}x{H}x{F})", 2 * M * H * F,
-         q8(H, F) + q8(M, F) + 2 * 8 * M * H, "void mi::k_gemm_q8<1, 2, 1"),
-        ("void mi::k_gemm_q8<1, 1, 0, true, 2>", f"Wo, split-K partials ({M}x{H}x{nq})", 2 * M * H * nq,
-         q8(H, nq) + q8(M, nq) + 2 * 8 * M * H, "void mi::k_attention<"),
-        ("void mi::k_gemm_q8<1, 1, 2, false, 2>", f"Q|K|V + bias + RoPE + KV store ({M}x{nq + 2 * nkv}x{H})",
-         2 * M * (nq + 2 * nkv) * H, q8(nq + 2 * nkv, H) + q8(M, H) + 4 * M * (nq + 2 * nkv)),
-        ("void mi::k_attention<", f"causal GQA attention + Q8_0 of the output ({M} tokens)", 0,
-         4 * M * nq + 8 * M * nkv + q8(M, nq)),
-        ("mi::k_rmsnorm_quant", f"RMSNorm + Q8_0 ({M}x{H}), reducing the 2 split-K partials of the matmul before",
-         0, M * H * (4 + 4) + 2 * 8 * M * H + q8(M, H)),
-        ("void mi::k_gemv_q8<4, 1, 1>", f"last-row lm_head, final RMSNorm in its prologue ({cfg.vocab}x{H})", 0,
-         q8(cfg.vocab, H) + 4 * cfg.vocab),
-        ("mi::k_embed", f"embedding rows ({M}x{H})", 0, q8(M, H) + 4 * M * H),
-    ]
+    return {
+        "gate_up": (f"gate|up + SwiGLU + Q8_0 ({M}x{2 * F}x{H})", 2 * M * 2 * F * H, q8(2 * F, H) + q8(M, H) + q8(M, F)),
+        "down_split": (f"down, split-K partials ({M}x{H}x{F})", 2 * M * H * F, q8(H, F) + q8(M, F) + 2 * 8 * M * H),
+        "down": (f"down + residual ({M}x{H}x{F})", 2 * M * H * F, q8(H, F) + q8(M, F) + 8 * M * H),
+        "wo_split": (f"Wo, split-K partials ({M}x{H}x{nq})", 2 * M * H * nq, q8(H, nq) + q8(M, nq) + 2 * 8 * M * H),
+        "wo": (f"Wo + residual ({M}x{H}x{nq})", 2 * M * H * nq, q8(H, nq) + q8(M, nq) + 8 * M * H),
+        "qkv": (f"Q|K|V (+bias) + [QK norm] + RoPE + KV store ({M}x{nq + 2 * nkv}x{H})", 2 * M * (nq + 2 * nkv) * H,
+                q8(nq + 2 * nkv, H) + q8(M, H) + 4 * M * (nq + 2 * nkv)),
+        "attention": (f"causal GQA attention + Q8_0 of the output ({M} queries, keys up to {kv_rows})", 0,
+                      4 * M * nq + 8 * kv_rows * nkv + q8(M, nq)),
+        "norm_partials": (f"RMSNorm + Q8_0 ({M}x{H}) reducing 2 split-K partials", 0,
+                          M * H * (4 + 4) + 2 * 8 * M * H + q8(M, H)),
+        "norm": (f"RMSNorm + Q8_0 ({M}x{H})", 0, M * H * 4 + q8(M, H)),
+        "lm_head": (f"last-row lm_head, final RMSNorm in its prologue ({cfg.vocab}x{H})", 0,
+                    q8(cfg.vocab, H) + 4 * cfg.vocab),
+        "embed": (f"embedding rows ({M}x{H})", 0, q8(M, H) + 4 * M * H),
+    }
+
+
+def write_kernel_summary(cfg, trace_dir, out_path, skip, command):
+    """Per-forward kernel table of a kernel trace of this benchmark: a forward runs from an embedding
+    launch to the last-row lm_head; the first `skip` forwards are left out (first call, and the
+    untimed prefix of a chunked workload)."""
+    import collections
+    import csv
+    import glob
+
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            rows += [r for r in csv.DictReader(fh) if "mi::" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    fwds, cur, after = [], None, []
+    for r in rows:
+        k = _short(r["Kernel_Name"])
+        if k == "k_embed":
+            cur = []
+            fwds.append(cur)
+        if cur is not None:
+            cur.append((k, int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r))
+            if k.startswith("k_gemv_q8<4, 1, 1>"):
+                cur = None
+        else:
+            after.append((k, int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r))
+    use = fwds[skip:]
+    spans = [(f[-1][2] - f[0][1]) / 1e3 for f in fwds]
+    agg = collections.defaultdict(lambda: [0, 0.0])
+    info = {}
+    for f in use:
+        for k, a, b, r in f:
+            agg[k][0] += 1
+            agg[k][1] += (b - a) / 1e3
+            info.setdefault(k, f"{r.get('Grid_Size_X', '?')}x{r.get('Grid_Size_Y', '?')}x{r.get('Grid_Size_Z', '?')} "
+                               f"x {r.get('Workgroup_Size_X', '?')}, {r.get('VGPR_Count', '?')}, "
+                               f"{r.get('LDS_Block_Size', '?')}")
+    n = max(len(use), 1)
+    lines = [f"# rocprofv3 kernel summary: {cfg.description} ({cfg.name})", "#",
+             "# commands (repository root on the GPU host; rocprofv3 run from /tmp with TMPDIR=/tmp):",
+             f"#   {command}" if command else "#   (trace command not recorded)",
+             f"#   python3 bench.py --workload {cfg.name} --write-kernel-summary <trace dir> <this file> "
+             f"--skip-forwards {skip}",
+             "# Durations in microseconds, from the kernel trace (End - Start).  A forward runs from the embedding",
+             "# launch to the last-row lm_head.  Grid: the trace's grid size in threads (x, y, z) x workgroup size;",
+             "# then VGPRs and LDS bytes as the trace reports them.", "#",
+             "# forward span (first kernel start -> lm_head end), us: " + ", ".join(f"{x:.0f}" for x in spans),
+             f"# per forward = total over forwards {skip + 1}..{len(fwds)} / {len(use)}", "#",
+             f"# {'kernel':58s} {'calls/fwd':>9s} {'us/fwd':>9s} {'avg_us':>8s}  grid x block, VGPRs, LDS bytes"]
+    tot = 0.0
+    for k, (c, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        lines.append(f"{k:60s} {c / n:9.1f} {t / n:9.1f} {t / c:8.2f}  {info[k]}")
+        tot += t / n
+    lines.append(f"# sum of kernel time per forward: {tot:.1f} us")
+    end = fwds[-1][-1][2] if fwds else 0
+    after = [x for x in after if x[1] >= end]  # launches after the last forward (the roofline loop)
+    if after:
+        la = collections.defaultdict(list)
+        for k, a, b, r in after:
+            la[k].append((b - a) / 1e3)
+        for k, v in la.items():
+            if len(v) >= 20:
+                lines.append(f"# standalone loop after the forwards: {k}, {len(v)} launches, mean {np.mean(v):.2f} us, "
+                             f"median {np.median(v):.2f} us")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def write_counters(cfg, cdir, fdir, wdir, out_path):
@@ -577,10 +700,12 @@ def write_counters(cfg, cdir, fdir, wdir, out_path):
 
     ff, fw = calib(fet, "FETCH_SIZE"), calib(wri, "WRITE_SIZE")
 
-    def by_name(tab, prefix, prev=None):
+    def by_node(tab, node):
+        """{grid: [(dispatch, counters)]} of the launches of one forward node (by name and predecessor)."""
         groups = {}
         for did, (n, g, vals) in tab.items():
-            if n.startswith(prefix) and (prev is None or (did - 1 in tab and tab[did - 1][0].startswith(prev))):
+            prev = _short(tab[did - 1][0]) if did - 1 in tab else None
+            if _classify(_short(n), prev) == node:
                 groups.setdefault(g, []).append((did, vals))
         return groups
 
@@ -604,10 +729,9 @@ def write_counters(cfg, cdir, fdir, wdir, out_path):
              "HBM MB (vs algorithmic) | HBM GB/s (% of 8000) |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     med = lambda xs: float(np.median(xs)) if xs else float("nan")
-    for prefix, label, ops_alg, bytes_alg, *prev in _forward_kernels(cfg):
-        prev = prev[0] if prev else None
+    for node, (label, ops_alg, bytes_alg) in _forward_kernels(cfg).items():
         label = label.replace("|", "\\|")
-        groups = by_name(comp, prefix, prev)
+        groups = by_node(comp, node)
         if not groups:
             continue
         g, disp = max(groups.items(), key=lambda kv: len(kv[1]))
@@ -620,8 +744,8 @@ def write_counters(cfg, cdir, fdir, wdir, out_path):
         busy = cv("SQ_VALU_MFMA_BUSY_CYCLES")
         coex = cv("SQ_VALU_MFMA_COEXEC_CYCLES")
         ldsc = cv("SQ_LDS_BANK_CONFLICT") / max(cv("SQ_INSTS_LDS"), 1.0)
-        fg = by_name(fet, prefix, prev).get(g, [])
-        wg = by_name(wri, prefix, prev).get(g, [])
+        fg = by_node(fet, node).get(g, [])
+        wg = by_node(wri, node).get(g, [])
         hbm = (med([v["FETCH_SIZE"] for _, v in fg]) * 1024 * ff if fg else float("nan")) + \
               (med([v["WRITE_SIZE"] for _, v in wg]) * 1024 * fw if wg else float("nan"))
         s_ = dns * 1e-9

@@ -266,6 +266,8 @@ typedef struct mi_prefill_graph mi_prefill_graph;
 int mi_prefill_graph_create(const mi_model* model, int32_t n_tokens, int32_t n_ctx, const mi_kv_regions* kv,
                             int32_t n_out, float* logits_out, mi_prefill_graph** out);
 int mi_prefill_graph_launch(mi_prefill_graph* graph, const int32_t* token_ids, const int32_t* positions);
+/* The number of nodes (kernel launches) in the captured forward, into *n_nodes. */
+int mi_prefill_graph_nodes(const mi_prefill_graph* graph, int32_t* n_nodes);
 void mi_prefill_graph_destroy(mi_prefill_graph* graph);
 
 /* ------------------------------------------------------------------ per-op calls */

@@ -76,6 +76,7 @@ SIGNATURES = {
     "mi_prefill_graph_create": (C.c_int, [C.POINTER(Model), _I32, _I32, C.POINTER(KvRegions), _I32, _P,
                                           C.POINTER(C.c_void_p)]),
     "mi_prefill_graph_launch": (C.c_int, [_P, _P, _P]),
+    "mi_prefill_graph_nodes": (C.c_int, [_P, C.POINTER(C.c_int32)]),
     "mi_prefill_graph_destroy": (None, [_P]),
     "mi_quantize_q8_0": (C.c_int, [_P, _I64, _I32, _P, _P, _P]),
     "mi_pack_q8_0": (C.c_int, [_P, _I64, _I32, _P, _P, _P]),

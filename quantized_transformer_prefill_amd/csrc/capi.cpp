@@ -919,6 +919,14 @@ extern "C" int mi_prefill_graph_launch(mi_prefill_graph* g, const int32_t* token
   return MI_OK;
 }
 
+extern "C" int mi_prefill_graph_nodes(const mi_prefill_graph* g, int32_t* n_nodes) {
+  if (!g || !g->graph || !n_nodes) return set_error(MI_ERR_INVALID_ARG, "graph: NULL handle or output");
+  size_t n = 0;
+  MI_HIP(hipGraphGetNodes(g->graph, nullptr, &n));
+  *n_nodes = (int32_t)n;
+  return MI_OK;
+}
+
 extern "C" void mi_prefill_graph_destroy(mi_prefill_graph* g) {
   if (!g) return;
   if (g->exec) (void)hipGraphExecDestroy(g->exec);

@@ -179,6 +179,12 @@ class PrefillGraph:
         B.check(B.lib().mi_prefill_graph_launch(self.handle, ids.ctypes.data, pos.ctypes.data))
         return self.logits
 
+    def nodes(self) -> int:
+        """Kernel launches in the captured forward."""
+        n = C.c_int32()
+        B.check(B.lib().mi_prefill_graph_nodes(self.handle, C.byref(n)))
+        return n.value
+
     def close(self):
         if self.handle:
             B.lib().mi_prefill_graph_destroy(self.handle)

@@ -133,6 +133,8 @@ def test_forward_n_and_graph_argument_checks():
     assert L.mi_prefill_graph_create(C.byref(model), 3, 16, C.byref(kv), 1, FAKE, C.byref(h)) == B.MI_ERR_INVALID_ARG
     assert b"non-default stream" in L.mi_last_error()
     assert L.mi_prefill_graph_launch(None, ids.ctypes.data, pos.ctypes.data) == B.MI_ERR_INVALID_ARG
+    n = C.c_int32(-1)
+    assert L.mi_prefill_graph_nodes(None, C.byref(n)) == B.MI_ERR_INVALID_ARG and n.value == -1
     L.mi_prefill_graph_destroy(None)  # a no-op
 
 

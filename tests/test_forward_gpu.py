@@ -130,6 +130,7 @@ def test_graph_replay_equals_eager(cfg, n_out):
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         g = m.graph(nt, n_out)
+        assert g.nodes() >= 2 + 5 * cfg.n_layers   # embedding, >= 5 kernels per layer, the head
         shifts = [0, 3, 0] if cfg.prefix_tokens == 0 else [0, 0]
         for r, shift in enumerate(shifts):
             say(f"graph {cfg.name} replay {r} shift {shift}")
