@@ -33,16 +33,42 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int GV_THREADS = 1024;  // 16 waves
 constexpr int GV_WAVES = GV_THREADS / 64;
 
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// f64 cross-lane reduction over a wave, every lane receiving the result: DPP row permutations for
+// the 16-lane rows (each 32-bit half moved separately), a bit-mode swizzle across the two rows of a
+// 32-lane half, then the two halves through scalar registers.  Each step combines a lane with its
+// partner symmetrically, so every lane ends with the same value.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
-__device__ __forceinline__ double wave_max_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
-  return v;
+__device__ __forceinline__ double swz16_f64(double v) {  // lane ^ 16 inside each 32-lane half
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)b, 0x401F);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(b >> 32), 0x401F);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
+__device__ __forceinline__ double lane_f64(double v, int l) {  // lane l's value, in every lane
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <bool MAX>
+__device__ __forceinline__ double wave_reduce_f64(double v) {
+  auto op = [](double a, double b) { return MAX ? fmax(a, b) : a + b; };
+  v = op(v, dpp_f64<DPP_XOR1>(v));
+  v = op(v, dpp_f64<DPP_XOR2>(v));
+  v = op(v, dpp_f64<DPP_HALF_MIRROR>(v));
+  v = op(v, dpp_f64<DPP_ROW_MIRROR>(v));
+  v = op(v, swz16_f64(v));
+  return op(lane_f64(v, 0), lane_f64(v, 32));
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) { return wave_reduce_f64<false>(v); }
+__device__ __forceinline__ double wave_max_d(double v) { return wave_reduce_f64<true>(v); }
 
 // Prologue modes: the activation row comes as Q8_0 (GV_IN_Q8), is built from the f32 residual
 // stream by RMSNorm + Q8_0 (GV_IN_NORM), or is the attention output merged from the per-range
@@ -184,7 +210,7 @@ __global__ void __launch_bounds__(GV_THREADS) k_gemv_q8(const float* __restrict_
             isum = __builtin_amdgcn_sdot4(xa[3], wv[b][i][3], isum, false);
             dw = (double)f16_bits_to_f32(sv[b][i]);
           }
-          isum += __shfl_xor(isum, 1);  // both lanes of the pair hold the block sum
+          isum += __builtin_amdgcn_update_dpp(0, isum, DPP_XOR1, 0xF, 0xF, false);  // both lanes of the pair: the block sum
           if (on && (lane & 1) == 0) acc[ib + i] = fma((double)isum * dw, da, acc[ib + i]);  // I*dw exact
         }
       }
@@ -342,6 +368,11 @@ constexpr int AD_THREADS = 256;  // 4 waves; a wave takes 64 keys of its range p
 // and writes its partial state to part[(h * n_range + r) * (HD + 2)] = m, l, o[HD] (f64): m the
 // range's largest score, l = sum e^(s - m), o = sum e^(s - m) v, with s = (q * 1/sqrt(hd)) . k as
 // in the prefill kernel.  Ranges past pos write nothing.  The output projection merges the ranges.
+//
+// A wave takes 64-key tiles.  Scores: lane <-> key, the dot product in four independent f64 chains.
+// Weighted sum: each V load instruction brings KG keys x all HD dims as float4s (lane <-> key group
+// kg, dim quad), so a lane accumulates 4 dims over the keys kg, kg + KG, ... of the tile in four
+// chains; the key groups and the waves are summed in the final merge through LDS (fixed order).
 template <int HD>
 __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restrict__ q,
                                                             const float* __restrict__ k_region,
@@ -349,12 +380,18 @@ __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restr
                                                             const int32_t* __restrict__ pos_dev, int n_head,
                                                             int n_head_kv, int keys_per_range,
                                                             double* __restrict__ part) {
-  constexpr int DPL = HD / 64;   // output dims per lane
-  constexpr bool V_EARLY = HD == 64;  // V values requested with the K rows (registers allow it)
-  __shared__ double qs[HD];
-  __shared__ double pw[AD_THREADS / 64][64];
-  __shared__ double wst[AD_THREADS / 64][HD + 2];
-  __shared__ double exp_tab[64];
+  constexpr int NW = AD_THREADS / 64;
+  constexpr int DQ = HD / 4;        // dim quads
+  constexpr int KG = 64 / DQ;       // keys per V load instruction: 4 (HD 64), 2 (HD 128)
+  constexpr int VI = 64 / KG;       // V load instructions per 64-key tile
+  constexpr bool V_EARLY = HD == 64;  // V requested together with K (registers allow it)
+  // wave-private LDS: the query (f64, scaled), the e^x table and the tile's weights, so no wave
+  // waits for another before the final merge (a wave's own LDS accesses complete in order)
+  __shared__ double qs[NW][HD];
+  __shared__ double etab[NW][64];
+  __shared__ double pw[NW][64];
+  __shared__ double wst[NW][KG][HD];
+  __shared__ double wml[NW][2];
   const int h = blockIdx.x, r = blockIdx.y, n_range = gridDim.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = h / (n_head / n_head_kv);
@@ -362,97 +399,84 @@ __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restr
   const int n_keys = *pos_dev + 1;
   const int j0 = r * keys_per_range, j1 = min(j0 + keys_per_range, n_keys);
   if (j0 >= j1) return;  // uniform for the workgroup
-  exp2_table_fill(exp_tab, tid);
-  const double scale = 1.0 / sqrt((double)HD);
-  double m_w = -1e300, l_w = 0.0, o_w[DPL];
+  const int kg = lane / DQ, dq = lane % DQ;
+  const float* kbase = k_region + g * HD;
+  const float* vbase = v_region + g * HD + 4 * dq;
+  double* qw = qs[wave];
+  const double* tab = etab[wave];
+  exp2_table_fill(etab[wave], lane);
+  double m_w = -1e300, l_w = 0.0, o[4] = {0.0, 0.0, 0.0, 0.0};
+  const int t_first = j0 + 64 * wave;
+  for (int t0 = t_first; t0 < j1; t0 += 64 * NW) {
+    const int nk = min(64, j1 - t0);
+    // rows past the tile's keys re-read its last key (their weights are 0; the row is one this call
+    // or an earlier one wrote)
+    float4 kreg[DQ];
+    {
+      const float4* kr = reinterpret_cast<const float4*>(kbase + (int64_t)(t0 + min(lane, nk - 1)) * n_kv);
 #pragma unroll
-  for (int k = 0; k < DPL; ++k) o_w[k] = 0.0;
-  bool staged = false;
-  // wave w takes the 64-key tiles w, w + 4, ... of the range (one tile each for ranges of 256)
-  for (int t0 = j0 + 64 * wave; t0 < j1 || !staged; t0 += 64 * (AD_THREADS / 64)) {
-    const int nk = t0 < j1 ? min(64, j1 - t0) : 0;
-    // this tile's K row (lane <-> key) and, for HD 64, V values (lane <-> dim) go out together
-    float4 kreg[HD / 4];
-    float vreg[V_EARLY ? 64 : 1];
-    if (lane < nk) {
-      const float4* kr = reinterpret_cast<const float4*>(k_region + (int64_t)(t0 + lane) * n_kv + g * HD);
-#pragma unroll
-      for (int d4 = 0; d4 < HD / 4; ++d4) kreg[d4] = kr[d4];
+      for (int d4 = 0; d4 < DQ; ++d4) kreg[d4] = kr[d4];
     }
-    if constexpr (V_EARLY) {
+    float4 vreg[VI];
+    auto load_v = [&]() {
 #pragma unroll
-      for (int kk = 0; kk < 64; ++kk)
-        if (kk < nk) vreg[kk] = v_region[(int64_t)(t0 + kk) * n_kv + g * HD + lane];
+      for (int i = 0; i < VI; ++i)
+        vreg[i] = *reinterpret_cast<const float4*>(vbase + (int64_t)(t0 + min(KG * i + kg, nk - 1)) * n_kv);
+    };
+    if constexpr (V_EARLY) load_v();
+    if (t0 == t_first) {  // the query, scaled by 1/sqrt(hd) in f64, while the loads are in flight
+      const double scale = 1.0 / sqrt((double)HD);
+      for (int i = lane; i < HD; i += 64) qw[i] = (double)q[h * HD + i] * scale;
     }
-    if (!staged) {  // the query, scaled by 1/sqrt(hd) in f64, while the first loads are in flight
-      for (int i = tid; i < HD; i += AD_THREADS) qs[i] = (double)q[h * HD + i] * scale;
-      __syncthreads();
-      staged = true;
-    }
-    if (nk == 0) continue;
-    double s = -1e300;
-    if (lane < nk) {
-      double a = 0.0;
+    double a[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int d4 = 0; d4 < HD / 4; ++d4) {
-        a = fma(qs[4 * d4], (double)kreg[d4].x, a);
-        a = fma(qs[4 * d4 + 1], (double)kreg[d4].y, a);
-        a = fma(qs[4 * d4 + 2], (double)kreg[d4].z, a);
-        a = fma(qs[4 * d4 + 3], (double)kreg[d4].w, a);
-      }
-      s = a;
+    for (int d4 = 0; d4 < DQ; ++d4) {
+      const double2 q01 = *reinterpret_cast<const double2*>(&qw[4 * d4]);
+      const double2 q23 = *reinterpret_cast<const double2*>(&qw[4 * d4 + 2]);
+      a[0] = fma(q01.x, (double)kreg[d4].x, a[0]);
+      a[1] = fma(q01.y, (double)kreg[d4].y, a[1]);
+      a[2] = fma(q23.x, (double)kreg[d4].z, a[2]);
+      a[3] = fma(q23.y, (double)kreg[d4].w, a[3]);
     }
-    const double mt = wave_max_d(s);
-    const double m_new = fmax(m_w, mt);
-    const double p = lane < nk ? exp_f64(s - m_new, exp_tab) : 0.0;
-    const double resc = exp_f64(m_w - m_new, exp_tab);  // 0 for the first tile (m_w = -1e300)
-    l_w = l_w * resc + wave_sum_d(p);
+    if constexpr (!V_EARLY) {
+      asm volatile("" ::: "memory");  // the V loads reuse the K registers: issued after the scores
+      load_v();
+    }
+    const double s = lane < nk ? (a[0] + a[1]) + (a[2] + a[3]) : -1e300;
+    const double m_new = fmax(m_w, wave_reduce_f64<true>(s));
+    const double p = lane < nk ? exp_f64(s - m_new, tab) : 0.0;
+    const double resc = exp_f64(m_w - m_new, tab);  // 0 for the first tile (m_w = -1e300)
+    l_w = l_w * resc + wave_reduce_f64<false>(p);
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) o_w[k] *= resc;
+    for (int c = 0; c < 4; ++c) o[c] *= resc;
     m_w = m_new;
-    pw[wave][lane] = p;  // the wave's own LDS row: its accesses complete in order
-    if constexpr (V_EARLY) {
+    pw[wave][lane] = p;
 #pragma unroll
-      for (int kk = 0; kk < 64; ++kk)
-        if (kk < nk) o_w[0] = fma(pw[wave][kk], (double)vreg[kk], o_w[0]);
-    } else {
-      for (int kb = 0; kb < nk; kb += 32) {
-        float vb[32][DPL];
-#pragma unroll
-        for (int kk = 0; kk < 32; ++kk)
-          if (kb + kk < nk) {
-#pragma unroll
-            for (int k = 0; k < DPL; ++k) vb[kk][k] = v_region[(int64_t)(t0 + kb + kk) * n_kv + g * HD + lane + 64 * k];
-          }
-#pragma unroll
-        for (int kk = 0; kk < 32; ++kk)
-          if (kb + kk < nk) {
-            const double pk = pw[wave][kb + kk];
-#pragma unroll
-            for (int k = 0; k < DPL; ++k) o_w[k] = fma(pk, (double)vb[kk][k], o_w[k]);
-          }
-      }
+    for (int i = 0; i < VI; ++i) {
+      const double pk = pw[wave][KG * i + kg];
+      o[0] = fma(pk, (double)vreg[i].x, o[0]);
+      o[1] = fma(pk, (double)vreg[i].y, o[1]);
+      o[2] = fma(pk, (double)vreg[i].z, o[2]);
+      o[3] = fma(pk, (double)vreg[i].w, o[3]);
     }
   }
-  // merge the waves (fixed order)
-  if (lane == 0) {
-    wst[wave][0] = m_w;
-    wst[wave][1] = l_w;
-  }
+  // merge the waves and key groups (fixed order)
 #pragma unroll
-  for (int k = 0; k < DPL; ++k) wst[wave][2 + lane + 64 * k] = o_w[k];
+  for (int c = 0; c < 4; ++c) wst[wave][kg][4 * dq + c] = o[c];
+  if (lane == 0) {
+    wml[wave][0] = m_w;
+    wml[wave][1] = l_w;
+  }
   __syncthreads();
   if (wave == 0) {
     double m = -1e300;
-    for (int w = 0; w < AD_THREADS / 64; ++w) m = fmax(m, wst[w][0]);
-    double l = 0.0, o[DPL];
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) o[k] = 0.0;
-    for (int w = 0; w < AD_THREADS / 64; ++w) {
-      const double f = exp_f64(wst[w][0] - m, exp_tab);
-      l = fma(wst[w][1], f, l);
+    for (int w = 0; w < NW; ++w) m = fmax(m, wml[w][0]);
+    double f[NW], l = 0.0;
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) o[k] = fma(wst[w][2 + lane + 64 * k], f, o[k]);
+    for (int w = 0; w < NW; ++w) {
+      f[w] = exp_f64(wml[w][0] - m, tab);
+      l = fma(wml[w][1], f[w], l);
     }
     double* out = part + ((int64_t)h * n_range + r) * (HD + 2);
     if (lane == 0) {
@@ -460,7 +484,18 @@ __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restr
       out[1] = l;
     }
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) out[2 + lane + 64 * k] = o[k];
+    for (int k = 0; k < HD / 64; ++k) {
+      const int d = lane + 64 * k;
+      double od = 0.0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        double ow = 0.0;
+#pragma unroll
+        for (int gg = 0; gg < KG; ++gg) ow += wst[w][gg][d];
+        od = fma(ow, f[w], od);
+      }
+      out[2 + d] = od;
+    }
   }
 }
 
@@ -480,7 +515,7 @@ __device__ __forceinline__ void attn_merge_head(const double* __restrict__ part,
   const double l = wave_sum_d(lr * f_own);
   double o[4] = {0.0, 0.0, 0.0, 0.0};
   for (int rr = 0; rr < n_ne; ++rr) {
-    const double f = __shfl(f_own, rr);
+    const double f = lane_f64(f_own, rr);
     if (lane < HD / 4) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) o[k] = fma(ph[rr * (HD + 2) + 2 + 4 * lane + k], f, o[k]);
