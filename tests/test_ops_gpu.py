@@ -182,7 +182,7 @@ def test_gemm_swiglu_matches_oracle():
 # ---------------------------------------------------------------- row / elementwise ops
 def test_rmsnorm_quant_matches_oracle():
     dev = need_gpu()
-    # the last two: enough rows for the row-walking kernel (each workgroup takes several rows)
+    # the last two: full-size row counts of the 7B- and 8B-shaped prompts
     for rows, cols in [(37, 896), (5, 4096), (3, 3584), (2, 18944), (1, 64), (2100, 3584), (2600, 2048)]:
         x = synth.gen_normal(41, f"x{rows}", (rows, cols), std=0.7, device=dev)
         gam = (1 + synth.gen_normal(42, f"g{cols}", (cols,), std=0.02, device=dev)).contiguous()
