@@ -709,14 +709,15 @@ def write_counters(cfg, cdir, fdir, wdir, out_path):
                 groups.setdefault(g, []).append((did, vals))
         return groups
 
+    run = f"python3 bench.py --workload {cfg.name} --counter-run"
     lines = [f"# Per-kernel counters: {cfg.description} ({cfg.name})", "",
              "Commands (repository root on the GPU host; run from /tmp with TMPDIR=/tmp):", "",
              "    rocprofv3 --kernel-trace --pmc " + " ".join(COUNTERS_COMPUTE) +
-             " --output-format csv -d gpurun_out/cnt_compute -o p -- python3 bench.py --counter-run",
-             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/cnt_fetch -o p -- python3 bench.py --counter-run",
-             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/cnt_write -o p -- python3 bench.py --counter-run",
-             "    python3 bench.py --write-counters gpurun_out/cnt_compute gpurun_out/cnt_fetch gpurun_out/cnt_write "
-             "profiles/counters_" + cfg.name + ".md", "",
+             " --output-format csv -d gpurun_out/cnt_compute -o p -- " + run,
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/cnt_fetch -o p -- " + run,
+             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/cnt_write -o p -- " + run,
+             f"    python3 bench.py --workload {cfg.name} --write-counters gpurun_out/cnt_compute gpurun_out/cnt_fetch "
+             "gpurun_out/cnt_write profiles/counters_" + cfg.name + ".md", "",
              f"Byte counters scaled on a streaming kernel of {COPY_BYTES >> 20} MiB read + written: FETCH_SIZE x "
              f"{ff:.3f}, WRITE_SIZE x {fw:.3f}.  Per kernel: the group of launches at the full prompt (the most "
              "launches of that kernel), medians over its launches.  Durations are from the kernel trace of the "
