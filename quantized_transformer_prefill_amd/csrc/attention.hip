@@ -10,9 +10,9 @@
 // from row 0 to the largest position among the 16 queries) are dealt round-robin to the waves,
 // so every wave sees early and late tiles alike.  For head_dim 64 a workgroup holds two groups,
 // for query tiles x and (last - x), which balances the causal work across workgroups and SIMDs.  Each wave keeps its own running max,
-// sum and output; at the end the partial states are merged in f64 through LDS, pairwise in a
-// fixed order (o = sum_w O_w e^(m_w - m) / sum_w l_w e^(m_w - m)).  The next tile's K and V are
-// loaded while the current tile computes.
+// sum and output; at the end wave 0 merges the partial states in f64 through LDS in a fixed order
+// (o = sum_w O_w 2^(m_w - m) / sum_w l_w 2^(m_w - m)), after two barriers.  The next tile's K and
+// V are loaded while the current tile computes.
 //
 // Softmax in base 2: scores carry the factor log2(e)/sqrt(hd), so the weights are 2^(s - m) (the
 // same softmax; one f64 rounding of the factor).  Every VALU instruction here costs the SIMD as
@@ -126,7 +126,13 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
   constexpr int NB = HD / 16;   // output dim blocks
   __shared__ double exp_tab[64];
   __shared__ double sh_m[NG][NW][64], sh_l[NG][NW][64];
-  __shared__ double sh_o[NG][NW / 2][NB * 4][64];
+  // one buffer for the query pairs (during the key loop) and then, after a barrier, the partial
+  // outputs of waves 1..NW-1 for the merge
+  constexpr int Q_BYTES = NG * 4 * (Q4 / 2) * 16 * (int)sizeof(double2);
+  constexpr int O_BYTES = NG * (NW - 1) * NB * 4 * 64 * (int)sizeof(double);
+  __shared__ __attribute__((aligned(16))) char sh_u[Q_BYTES > O_BYTES ? Q_BYTES : O_BYTES];
+  double2* const sh_q = reinterpret_cast<double2*>(sh_u);
+  double* const sh_o = reinterpret_cast<double*>(sh_u);
   // wave and group are uniform in a wave (scalar registers: the tile descriptor is a scalar load)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) % NW),
             grp = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) / NW);
@@ -168,7 +174,6 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
   // 8 KB at head_dim 64, 16 KB at 128, laid out [slot][s/2][query][s%2] so that the 16 lanes of a
   // slot read 256 contiguous bytes), read as a pair at each pair of score MFMAs.  LDS reads do not
   // stall the f64 MFMA the way VALU instructions do, and the registers stay free for the tiles.
-  __shared__ double2 sh_q[NG * 4 * (Q4 / 2) * 16];
   const double scale = 0x1.71547652b82fep+0 / sqrt((double)HD);  // log2(e) / sqrt(hd)
   if (wave == 0) {  // one wave per group writes the group's 16 queries
     const float* qp = q + (int64_t)(valid ? t : 0) * ld_q + (int64_t)h * HD + slot * Q4;
@@ -198,7 +203,7 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
   VHalf<HD> vt;
   load_k<HD>(kt, kbase, kv_embd, wave * 16, max_pos, qi, slot);
   load_v<HD>(vt, vbase, kv_embd, wave * 16, max_pos, qi, slot);
-  __syncthreads();  // exp_tab
+  __syncthreads();  // exp_tab, query pairs
   for (int tile = wave; tile < ntiles; tile += NW) {
     const int key0 = tile * 16;
     const bool more = tile + NW < ntiles;
@@ -249,43 +254,43 @@ __global__ void __launch_bounds__(64 * NW * NG, (HD > 64 ? 2 : 1)) k_attention(c
     if (more) load_v<HD>(vt, vbase, kv_embd, key0 + 16 * NW, max_pos, qi, slot);
   }
 
-  // ---- merge: the query's sum over its 4 lanes, then the waves' partial states (f64, fixed order)
+  // ---- merge: the query's sum over its 4 lanes; then wave 0 adds the waves' partial states,
+  // each scaled to the common reference max (f64, waves in order 0..NW-1)
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   sh_m[grp][wave][lane] = m_run;
   sh_l[grp][wave][lane] = l_run;
+  __syncthreads();  // every key loop is done: the query pairs are dead, their LDS takes the outputs
+  if (wave > 0) {
+    double* dst = sh_o + (grp * (NW - 1) + wave - 1) * (NB * 4 * 64) + lane;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(b * 4 + i) * 64] = acc[b][i];
+  }
   __syncthreads();
-  double m_all = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) m_all = fmax(m_all, sh_m[grp][w][lane]);
-  {
-    const double f_self = (m_run == -INFINITY) ? 0.0 : exp2_att(m_run - m_all, exp_tab);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] *= f_self;
-  }
-#pragma unroll
-  for (int half = NW / 2; half >= 1; half /= 2) {
-    if (wave >= half && wave < 2 * half) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sh_o[grp][wave - half][b * 4 + i][lane] = acc[b][i];
-    }
-    __syncthreads();
-    if (wave < half) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[b][i] += sh_o[grp][wave][b * 4 + i][lane];
-    }
-    if (half > 1) __syncthreads();
-  }
   if (wave == 0) {
+    double m_all = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m_all = fmax(m_all, sh_m[grp][w][lane]);
+    double f[NW];
     double l_all = 0.0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const double mw = sh_m[grp][w][lane];
-      l_all += (mw == -INFINITY) ? 0.0 : sh_l[grp][w][lane] * exp2_att(mw - m_all, exp_tab);
+      f[w] = (mw == -INFINITY) ? 0.0 : exp2_att(mw - m_all, exp_tab);
+      l_all += sh_l[grp][w][lane] * f[w];
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      asm volatile("" ::: "memory");  // one dim block's partials in flight at a time (registers)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        double o = acc[b][i] * f[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) o = fma(sh_o[(grp * (NW - 1) + w - 1) * (NB * 4 * 64) + (b * 4 + i) * 64 + lane], f[w], o);
+        acc[b][i] = o;
+      }
     }
     const double inv = recip_f64(l_all);
     // lane holds dims (4i + slot)*NB + b of query l%16 (i = 0..3, b = 0..NB-1)
