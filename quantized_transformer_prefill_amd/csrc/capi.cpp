@@ -506,8 +506,8 @@ static int stage_tokens(mi_stage* st, const Ws& w, const int32_t* ids, const int
 
 // The decode step: one token through the same layers and regions, with the one-row kernels
 // (decode.hip).  Per layer: Q|K|V matrix-vector product with the attention RMSNorm in its prologue
-// and bias, QK norm, RoPE and the K/V store in its epilogue; single-query attention over ranges of
-// keys 0..pos; output projection (the ranges merged into a Q8_0 row in its prologue) + residual;
+// and the bias in its epilogue; QK norm, RoPE and the K/V store per head; single-query attention
+// over ranges of keys 0..pos; the ranges merged into a Q8_0 row; output projection + residual;
 // gate|up with the ffn RMSNorm in its prologue and SwiGLU + Q8_0 in its epilogue; down projection
 // + residual.  Then the lm_head with the final RMSNorm in its prologue.
 static int enqueue_decode(const mi_model* md, const Ws& w, int32_t n_ctx, const mi_kv_regions* kv, float* logits_out,
@@ -523,18 +523,18 @@ static int enqueue_decode(const mi_model* md, const Ws& w, int32_t n_ctx, const 
     GemvArgs g{};
     g.x = w.h; g.gamma = L.attn_norm; g.eps = eps; g.k = H;
     g.w_codes = L.wqkv.codes; g.w_scales = L.wqkv.scales; g.n = nqkv;
-    g.bias = hp.qkv_bias ? L.bqkv : nullptr; g.epi = GV_QKV;
-    g.qkv.pos = w.pos; g.qkv.rope = md->rope_table; g.qkv.n_q = nq; g.qkv.n_kv = nkv; g.qkv.head_dim = hp.head_dim;
-    g.qkv.q_out = w.qkv; g.qkv.k_region = kv->k[l]; g.qkv.v_region = kv->v[l];
-    g.qkv.q_norm = hp.qk_norm ? L.q_norm : nullptr; g.qkv.k_norm = hp.qk_norm ? L.k_norm : nullptr; g.qkv.eps = eps;
+    g.bias = hp.qkv_bias ? L.bqkv : nullptr; g.out = w.qkv; g.epi = GV_F32;
     if ((rc = launch_gemv_q8(g, s))) return rc;
+    if ((rc = launch_qkv_finish(w.qkv, w.pos, md->rope_table, hp.n_head, hp.n_head_kv, hp.head_dim,
+                                hp.qk_norm ? L.q_norm : nullptr, hp.qk_norm ? L.k_norm : nullptr, eps, kv->k[l],
+                                kv->v[l], s)))
+      return rc;
     if ((rc = launch_attn_decode(w.qkv, kv->k[l], kv->v[l], w.pos, n_ctx, hp.n_head, hp.n_head_kv, hp.head_dim,
                                  w.attn_part, s)))
       return rc;
-    GemvArgs go{};  // input: the attention ranges merged in the prologue
-    go.attn.part = w.attn_part; go.attn.pos = w.pos; go.attn.n_head = hp.n_head; go.attn.head_dim = hp.head_dim;
-    go.attn.n_range = attn_decode_ranges(n_ctx, &go.attn.keys_per_range);
-    go.k = nq;
+    if ((rc = launch_attn_merge(w.attn_part, n_ctx, w.pos, hp.n_head, hp.head_dim, w.xq, w.xs, s))) return rc;
+    GemvArgs go{};  // input: the merged attention row
+    go.xq = w.xq; go.xs = w.xs; go.k = nq;
     go.w_codes = L.wo.codes; go.w_scales = L.wo.scales; go.n = H;
     go.residual = w.h; go.out = w.h; go.epi = GV_RES;
     if ((rc = launch_gemv_q8(go, s))) return rc;
@@ -593,17 +593,17 @@ static int enqueue_forward(const mi_model* md, const Ws& w, int32_t n_tokens, in
     if (last && n_out == 1) {
       // From here on only the last token continues, through the one-token kernels of the decode
       // step: single-query attention over key ranges (reading the regions after the store above),
-      // then matrix-vector products whose prologues merge the ranges or apply the RMSNorm and whose
-      // epilogues add the residual or apply SwiGLU + Q8_0; the final RMSNorm is the lm_head's
-      // prologue.  The previous layer's deferred partials were reduced by this layer's RMSNorm.
+      // the ranges merged into a Q8_0 row, then matrix-vector products whose prologues apply the
+      // RMSNorm and whose epilogues add the residual or apply SwiGLU + Q8_0; the final RMSNorm is
+      // the lm_head's prologue.  The previous layer's deferred partials were reduced by this
+      // layer's RMSNorm.
       const int32_t* pos1 = w.pos + (nt - 1);
       if ((rc = launch_attn_decode(q + (size_t)(nt - 1) * nqkv, kv->k[l], kv->v[l], pos1, n_ctx, hp.n_head,
                                    hp.n_head_kv, hp.head_dim, w.attn_part, s)))
         return rc;
+      if ((rc = launch_attn_merge(w.attn_part, n_ctx, pos1, hp.n_head, hp.head_dim, w.xq, w.xs, s))) return rc;
       GemvArgs go{};
-      go.attn.part = w.attn_part; go.attn.pos = pos1; go.attn.n_head = hp.n_head; go.attn.head_dim = hp.head_dim;
-      go.attn.n_range = attn_decode_ranges(n_ctx, &go.attn.keys_per_range);
-      go.k = nq;
+      go.xq = w.xq; go.xs = w.xs; go.k = nq;
       go.w_codes = L.wo.codes; go.w_scales = L.wo.scales; go.n = H;
       go.residual = h_tail; go.out = h_tail; go.epi = GV_RES;
       if ((rc = launch_gemv_q8(go, s))) return rc;

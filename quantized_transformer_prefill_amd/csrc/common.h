@@ -237,46 +237,32 @@ int launch_lm_head(const int8_t* xq, const uint16_t* xs, int cols, const int8_t*
                    const uint16_t* w_scales, int rows, float* logits, hipStream_t s);
 
 // ---- decode step (one activation row): exact Q8_0 matrix-vector products and single-query attention
-enum GemvEpi { GV_RES = 0, GV_F32 = 1, GV_QKV = 2, GV_SWIGLU = 3 };
-// GV_QKV: the workgroup's rows are one head of Q, K or V of the stacked Q|K|V weight: bias in f64,
-// [per-head QK RMSNorm], NeoX RoPE at *pos, Q -> q_out, K and V rows -> the regions at *pos.
-struct GemvQkv {
-  const int32_t* pos;      // device [1]
-  const double* rope;      // [n_ctx][head_dim/2] of (cos, sin)
-  int n_q, n_kv, head_dim;
-  float* q_out;            // [n_q]
-  float* k_region;         // [n_ctx][n_kv]
-  float* v_region;
-  const float* q_norm;     // [head_dim] or null
-  const float* k_norm;
-  float eps;
-};
-// the output projection's input: the per-range attention partial states of k_attn_decode
-struct GemvAttnIn {
-  const double* part;      // [n_head][n_range][head_dim + 2], or null
-  const int32_t* pos;      // device [1]: keys 0..*pos
-  int n_head, head_dim, n_range, keys_per_range;
-};
+enum GemvEpi { GV_RES = 0, GV_F32 = 1, GV_SWIGLU = 3 };
 struct GemvArgs {
   // input row: with x non-null, RMSNorm(x; gamma, eps) + Q8_0 inside the kernel; else xq/xs
   const float* x; const float* gamma; float eps;
   const int8_t* xq; const uint16_t* xs;
   int k;
   const int8_t* w_codes; const uint16_t* w_scales; int n;   // weights [n][k]
-  const float* bias;                                         // GV_QKV: [n] or null
+  const float* bias;                                         // GV_F32: [n] or null
   const float* residual; float* out;                         // GV_RES: out = residual + y; GV_F32: out = y
   int8_t* q_codes; uint16_t* q_scales;                       // GV_SWIGLU: Q8_0 [n/2]
   int epi;
-  GemvQkv qkv;
-  GemvAttnIn attn;         // GV_RES only: with attn.part non-null the input row is the merged attention output
 };
 int launch_gemv_q8(const GemvArgs& g, hipStream_t s);
 // attention of one query per head over keys 0..*pos_dev: partial states per key range in `part`
-// (n_head * n_range * (head_dim + 2) f64, n_range <= AD_MAX_RANGES), merged by the output projection
+// (n_head * n_range * (head_dim + 2) f64, n_range <= AD_MAX_RANGES), merged by launch_attn_merge
 constexpr int AD_MAX_RANGES = 16;
 int attn_decode_ranges(int n_ctx, int* keys_per_range);
 int launch_attn_decode(const float* q, const float* k_region, const float* v_region, const int32_t* pos_dev,
                        int n_ctx, int n_head, int n_head_kv, int head_dim, double* part, hipStream_t s);
+// the ranges of `part` merged per head, normalized and quantized: the Q8_0 row [n_head * head_dim]
+int launch_attn_merge(const double* part, int n_ctx, const int32_t* pos_dev, int n_head, int head_dim, int8_t* codes,
+                      uint16_t* scales, hipStream_t s);
+// one token's Q|K|V row (bias added) -> [QK norm], RoPE at *pos_dev; Q in place, K and V rows stored
+int launch_qkv_finish(float* qkv, const int32_t* pos_dev, const double* rope, int n_head, int n_head_kv,
+                      int head_dim, const float* q_norm, const float* k_norm, float eps, float* k_region,
+                      float* v_region, hipStream_t s);
 
 // ---- sampler (sampler.hip)
 size_t sampler_workspace_bytes();

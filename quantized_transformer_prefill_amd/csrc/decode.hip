@@ -3,25 +3,30 @@
 // matmul is a matrix-vector product bound by HBM, and the attention has one query per head.
 //
 // k_gemv_q8: y[n] = sum_kb dx[kb] * dw[n][kb] * sum_32 qx * qw, one activation row.
-//  * 16 waves per workgroup, RPW weight rows per wave in flight at once; a lane takes 16-byte
-//    chunks (half a block) of every row, sdot4 gives the integer half-block sums, lane pairs
-//    combine them to the block sum, and the exact f64 epilogue (block sum times dw, times dx,
-//    one rounding per block) accumulates per lane; the lanes' partial sums then reduce in f64.
+//  * 16 waves per workgroup, RPW weight rows per wave (up to 4 in flight at once); a lane takes
+//    16-byte chunks (half a block) of every row, sdot4 gives the integer half-block sums, lane
+//    pairs combine them to the block sum, and the exact f64 epilogue (block sum times dw, times
+//    dx, one rounding per block) accumulates per lane; the lanes' partial sums then reduce in f64.
+//    The weight loads are double buffered: the next step's requests go out before this step's
+//    math, and are unconditional (clamped addresses) so that the wait for one buffer never
+//    includes the other's requests.
 //  * The activation row is staged in LDS as codes + f64 scales.  The workgroup can build it
-//    itself: from the f32 residual stream (RMSNorm in f64, one rounding to f32, Q8_0 -- the same
-//    arithmetic as the prefill's k_rmsnorm_quant), or, for the output projection, by merging the
-//    attention's per-range partial states -- so the decode step has no normalization or merge
+//    itself from the f32 residual stream (RMSNorm in f64, one rounding to f32, Q8_0 -- the same
+//    arithmetic as the prefill's k_rmsnorm_quant), so the decode step has no normalization
 //    kernels.  The weight loads of the first rows go out before this prologue.
-//  * Epilogues: residual add (output projection, down projection), plain f32 (lm_head), the
-//    attention inputs (bias, per-head QK RMSNorm, NeoX RoPE, K/V rows stored at the position; a
-//    workgroup holds one head), SwiGLU + Q8_0 (a workgroup holds one interleaved group of 32
-//    gate and 32 up rows, i.e. one Q8_0 block of the SwiGLU output).
+//  * Epilogues: residual add (output projection, down projection), plain f32 with an optional
+//    bias (lm_head; the Q|K|V rows), SwiGLU + Q8_0 (a workgroup holds one interleaved group of 32
+//    gate and 32 up rows, i.e. one Q8_0 block of the SwiGLU output).  Every epilogue is per row,
+//    so a workgroup takes 16 or 64 rows and even the small matrices spread over the chip.
+//
+// k_qkv_finish: the per-head steps after the Q|K|V rows (per-head QK RMSNorm, NeoX RoPE at the
+// position, the K and V rows stored in the regions), one workgroup per head.
 //
 // k_attn_decode: the query's keys 0..pos are split into fixed ranges (the grid depends only on
 // n_ctx, so the launch can be captured once and replayed for any position); each workgroup
 // computes the partial softmax state (max, sum, unnormalized output) of one head over one range in
-// f64.  The output projection's prologue combines the ranges in order, normalizes, and quantizes
-// each head's output row to Q8_0.
+// f64.  k_attn_merge combines a head's ranges in order, normalizes, and quantizes the head's
+// output row to Q8_0, the output projection's input.
 #include <algorithm>
 
 #include "common.h"
@@ -32,6 +37,10 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int GV_THREADS = 1024;  // 16 waves
 constexpr int GV_WAVES = GV_THREADS / 64;
+constexpr int GV_NORM_K = 4096;                                  // widest row the norm prologue takes
+constexpr int GV_NV = (GV_NORM_K / 4 + GV_THREADS - 1) / GV_THREADS;  // float4s of the row per thread
+constexpr int GV_RPW_SWIGLU = 64 / GV_WAVES;                       // a SwiGLU group is 64 rows
+constexpr int GV_MAX_WG = (2048 / GV_THREADS) * 256;               // workgroups resident on the chip
 
 // f64 cross-lane reduction over a wave, every lane receiving the result: DPP row permutations for
 // the 16-lane rows (each 32-bit half moved separately), a bit-mode swizzle across the two rows of a
@@ -70,14 +79,9 @@ __device__ __forceinline__ double wave_reduce_f64(double v) {
 __device__ __forceinline__ double wave_sum_d(double v) { return wave_reduce_f64<false>(v); }
 __device__ __forceinline__ double wave_max_d(double v) { return wave_reduce_f64<true>(v); }
 
-// Prologue modes: the activation row comes as Q8_0 (GV_IN_Q8), is built from the f32 residual
-// stream by RMSNorm + Q8_0 (GV_IN_NORM), or is the attention output merged from the per-range
-// partial states of k_attn_decode, normalized and quantized per head (GV_IN_ATTN).
-enum { GV_IN_Q8 = 0, GV_IN_NORM = 1, GV_IN_ATTN = 2 };
-
-template <int HD>
-__device__ __forceinline__ void attn_merge_head(const double* __restrict__ part, int n_range, int n_ne, int h, int lane,
-                                                const double* exp_tab, int8_t* a_codes, double* a_d);
+// Prologue modes: the activation row comes as Q8_0 (GV_IN_Q8) or is built from the f32 residual
+// stream by RMSNorm + Q8_0 (GV_IN_NORM).
+enum { GV_IN_Q8 = 0, GV_IN_NORM = 1 };
 
 template <int RPW, int EPI, int PRO>
 __global__ void __launch_bounds__(GV_THREADS) k_gemv_q8(const float* __restrict__ x, const float* __restrict__ gamma,
@@ -87,69 +91,67 @@ __global__ void __launch_bounds__(GV_THREADS) k_gemv_q8(const float* __restrict_
                                                        const uint16_t* __restrict__ w_scales, int N,
                                                        const float* __restrict__ bias, const float* residual,
                                                        float* out, int8_t* __restrict__ q_codes,
-                                                       uint16_t* __restrict__ q_scales, GemvQkv qe, GemvAttnIn ai) {
+                                                       uint16_t* __restrict__ q_scales) {
   constexpr int RWG = RPW * GV_WAVES;  // weight rows per group
-  constexpr int B = (RPW >= 8 || EPI == GV_QKV || EPI == GV_SWIGLU) ? 1 : (RPW >= 4 ? 2 : 4);  // 64-chunk steps of K in flight together
+  // 64-chunk steps of K per load batch; two batches are in flight (double buffered)
+  constexpr int B = (EPI == GV_SWIGLU || RPW >= 4) ? 1 : 2;
   extern __shared__ __align__(16) unsigned char gv_lds[];
   const int KB = K / QK;
   int8_t* a_codes = reinterpret_cast<int8_t*>(gv_lds);                           // [K]
   double* a_d = reinterpret_cast<double*>(gv_lds + ((K + 15) & ~15));             // [KB]
   float* y = reinterpret_cast<float*>(a_d + KB);                                   // [RWG]
   double* red = reinterpret_cast<double*>(y + RWG + (RWG & 1));                    // [GV_WAVES + 1]
-  __shared__ double exp_tab[(EPI == GV_SWIGLU || PRO == GV_IN_ATTN) ? 64 : 1];
+  __shared__ double exp_tab[EPI == GV_SWIGLU ? 64 : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nchunk = K / 16;
   const int n_groups = (N + RWG - 1) / RWG;
 
   // ---- requests that do not depend on the activation row go out first
-  int64_t qpos = 0;
-  if constexpr (EPI == GV_QKV) qpos = *qe.pos;
   constexpr int RS = RPW < 4 ? RPW : 4;  // rows of a wave whose loads are in flight together
-  v4i wv[B][RS];
-  uint16_t sv[B][RS];
-  float bias_r[RPW];
+  struct Buf {
+    v4i wv[B][RS];
+    uint16_t sv[B][RS];
+  };
+  Buf buf0, buf1;  // two steps of K in flight: the next step's loads go out before this step's math
   // 32-bit offsets from the uniform matrix bases (rows * K < 2^31 is checked by the launcher);
   // rows ib..ib+RS-1 of the wave's RPW
-  auto load_batch = [&](int grp, int c0, int ib) {
+  auto load_batch = [&](Buf& bf, int grp, int c0, int ib) {
     const int r0 = grp * RWG + wave * RPW + ib;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       const int ch = c0 + 64 * b + lane;
 #pragma unroll
       for (int i = 0; i < RS; ++i) {
-        const uint32_t r = (uint32_t)min(r0 + i, N - 1);  // rows past N re-read the last row; never stored
-        if (ch < nchunk) {
-          wv[b][i] = *reinterpret_cast<const v4i*>(w_codes + (r * (uint32_t)K + (uint32_t)ch * 16u));
-          sv[b][i] = w_scales[r * (uint32_t)KB + (uint32_t)(ch >> 1)];
-        }
+        // rows past N re-read the last row and chunks past the row its last chunk (never used):
+        // the loads are unconditional, so the waits for one buffer never cover the other's
+        const uint32_t r = (uint32_t)min(r0 + i, N - 1);
+        const uint32_t c = (uint32_t)min(ch, nchunk - 1);
+        bf.wv[b][i] = *reinterpret_cast<const v4i*>(w_codes + (r * (uint32_t)K + c * 16u));
+        bf.sv[b][i] = w_scales[r * (uint32_t)KB + (c >> 1)];
       }
     }
   };
-  load_batch(blockIdx.x, 0, 0);
-  if constexpr (EPI == GV_QKV) {
-    const int r0 = blockIdx.x * RWG + wave * RPW;
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) bias_r[i] = bias ? bias[min(r0 + i, N - 1)] : 0.0f;
-  }
-  if constexpr (EPI == GV_SWIGLU || PRO == GV_IN_ATTN) exp2_table_fill(exp_tab, tid);
+  load_batch(buf0, blockIdx.x, 0, 0);
+  if constexpr (EPI == GV_SWIGLU) exp2_table_fill(exp_tab, tid);
 
   // ---- the activation row -> LDS (codes, f64 scales)
   const int nvec = K / 4;
-  if constexpr (PRO == GV_IN_ATTN) {  // wave w merges heads w, w + 16, ...
-    __syncthreads();  // exp_tab
-    const int n_ne = (*ai.pos + 1 + ai.keys_per_range - 1) / ai.keys_per_range;
-    for (int h = wave; h < ai.n_head; h += GV_WAVES) {
-      if (ai.head_dim == 64) attn_merge_head<64>(ai.part, ai.n_range, n_ne, h, lane, exp_tab, a_codes, a_d);
-      else attn_merge_head<128>(ai.part, ai.n_range, n_ne, h, lane, exp_tab, a_codes, a_d);
+  if constexpr (PRO == GV_IN_NORM) {  // K <= GV_NORM_K: NV float4s of x per thread, kept across both passes
+    float4 v[GV_NV], g[GV_NV];
+    double sq = 0.0;
+#pragma unroll
+    for (int j = 0; j < GV_NV; ++j) {
+      const int c4 = tid + j * GV_THREADS;
+      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      g[j] = v[j];
+      if (c4 < nvec) {
+        v[j] = reinterpret_cast<const float4*>(x)[c4];
+        g[j] = reinterpret_cast<const float4*>(gamma)[c4];
+      }
+      const double a = v[j].x, b = v[j].y, c = v[j].z, d = v[j].w;
+      sq += a * a + b * b + c * c + d * d;
     }
-  } else if constexpr (PRO == GV_IN_NORM) {  // K <= GV_THREADS * 4: one float4 of x per thread, kept across both passes
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f), g = v;
-    if (tid < nvec) {
-      v = reinterpret_cast<const float4*>(x)[tid];
-      g = reinterpret_cast<const float4*>(gamma)[tid];
-    }
-    const double a = v.x, b = v.y, c = v.z, d = v.w;
-    double ss = wave_sum_d(a * a + b * b + c * c + d * d);
+    double ss = wave_sum_d(sq);
     if (lane == 0) red[wave] = ss;
     __syncthreads();
     if (wave == 0) {
@@ -160,16 +162,20 @@ __global__ void __launch_bounds__(GV_THREADS) k_gemv_q8(const float* __restrict_
     __syncthreads();
     const double inv_rms = recip_f64(sqrt(red[GV_WAVES] / (double)K + (double)eps));
     // groups of 8 lanes cover one block; a group is entirely inside or outside [0, nvec)
-    if (tid < nvec) {
-      float4 o;
-      o.x = (float)((double)v.x * inv_rms * (double)g.x);
-      o.y = (float)((double)v.y * inv_rms * (double)g.y);
-      o.z = (float)((double)v.z * inv_rms * (double)g.z);
-      o.w = (float)((double)v.w * inv_rms * (double)g.w);
-      float dq;
-      const uint32_t qv = q8_block_quant4(o, dq);
-      reinterpret_cast<uint32_t*>(a_codes)[tid] = qv;
-      if ((tid & 7) == 0) a_d[tid / 8] = (double)f16_bits_to_f32(f32_to_f16_bits(dq));
+#pragma unroll
+    for (int j = 0; j < GV_NV; ++j) {
+      const int c4 = tid + j * GV_THREADS;
+      if (c4 < nvec) {
+        float4 o;
+        o.x = (float)((double)v[j].x * inv_rms * (double)g[j].x);
+        o.y = (float)((double)v[j].y * inv_rms * (double)g[j].y);
+        o.z = (float)((double)v[j].z * inv_rms * (double)g[j].z);
+        o.w = (float)((double)v[j].w * inv_rms * (double)g[j].w);
+        float dq;
+        const uint32_t qv = q8_block_quant4(o, dq);
+        reinterpret_cast<uint32_t*>(a_codes)[c4] = qv;
+        if ((c4 & 7) == 0) a_d[c4 / 8] = (double)f16_bits_to_f32(f32_to_f16_bits(dq));
+      }
     }
   } else {
     for (int c4 = tid; c4 < nvec; c4 += GV_THREADS)
@@ -183,12 +189,8 @@ __global__ void __launch_bounds__(GV_THREADS) k_gemv_q8(const float* __restrict_
     double acc[RPW];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) acc[i] = 0.0;
-#pragma unroll
-    for (int ib = 0; ib < RPW; ib += RS) {
-    if (ib || grp != (int)blockIdx.x) load_batch(grp, 0, ib);
-#pragma unroll 1
-    for (int c0 = 0; c0 < nchunk; c0 += 64 * B) {
-      if (c0) load_batch(grp, c0, ib);
+    // one step: B chunks of 16 bytes per lane of RS rows, the block sums in the exact f64 epilogue
+    auto step = [&](const Buf& bf, int c0, double* a) {
 #pragma unroll
       for (int b = 0; b < B; ++b) {
         const int ch = c0 + 64 * b + lane;
@@ -204,17 +206,32 @@ __global__ void __launch_bounds__(GV_THREADS) k_gemv_q8(const float* __restrict_
           int isum = 0;
           double dw = 0.0;
           if (on) {
-            isum = __builtin_amdgcn_sdot4(xa[0], wv[b][i][0], 0, false);
-            isum = __builtin_amdgcn_sdot4(xa[1], wv[b][i][1], isum, false);
-            isum = __builtin_amdgcn_sdot4(xa[2], wv[b][i][2], isum, false);
-            isum = __builtin_amdgcn_sdot4(xa[3], wv[b][i][3], isum, false);
-            dw = (double)f16_bits_to_f32(sv[b][i]);
+            isum = __builtin_amdgcn_sdot4(xa[0], bf.wv[b][i][0], 0, false);
+            isum = __builtin_amdgcn_sdot4(xa[1], bf.wv[b][i][1], isum, false);
+            isum = __builtin_amdgcn_sdot4(xa[2], bf.wv[b][i][2], isum, false);
+            isum = __builtin_amdgcn_sdot4(xa[3], bf.wv[b][i][3], isum, false);
+            dw = (double)f16_bits_to_f32(bf.sv[b][i]);
           }
           isum += __builtin_amdgcn_update_dpp(0, isum, DPP_XOR1, 0xF, 0xF, false);  // both lanes of the pair: the block sum
-          if (on && (lane & 1) == 0) acc[ib + i] = fma((double)isum * dw, da, acc[ib + i]);  // I*dw exact
+          if (on && (lane & 1) == 0) a[i] = fma((double)isum * dw, da, a[i]);  // I*dw exact
         }
       }
-    }
+    };
+    constexpr int STEP = 64 * B;
+#pragma unroll
+    for (int ib = 0; ib < RPW; ib += RS) {
+      if (ib || grp != (int)blockIdx.x) load_batch(buf0, grp, 0, ib);
+#pragma unroll 1
+      for (int c0 = 0;; c0 += 2 * STEP) {
+        load_batch(buf1, grp, c0 + STEP, ib);
+        step(buf0, c0, acc + ib);
+        if (c0 + 2 * STEP >= nchunk) {  // uniform
+          step(buf1, c0 + STEP, acc + ib);
+          break;
+        }
+        load_batch(buf0, grp, c0 + 2 * STEP, ib);
+        step(buf1, c0 + STEP, acc + ib);
+      }
     }
 #pragma unroll
     for (int i = 0; i < RPW; ++i) acc[i] = wave_sum_d(acc[i]);
@@ -225,73 +242,30 @@ __global__ void __launch_bounds__(GV_THREADS) k_gemv_q8(const float* __restrict_
         for (int i = 0; i < RPW; ++i) {
           const int r = r0 + i;
           if (r < N) {
-            float v = (float)acc[i];
-            if (EPI == GV_RES) v = residual[r] + v;
+            float v;
+            if (EPI == GV_RES) v = residual[r] + (float)acc[i];
+            else v = (float)(bias ? acc[i] + (double)bias[r] : acc[i]);  // one rounding
             out[r] = v;
           }
         }
       }
-    } else {
+    } else {  // GV_SWIGLU
       if (lane == 0) {
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-          double v = acc[i];
-          if (EPI == GV_QKV) v += (double)bias_r[i];
-          y[wave * RPW + i] = (float)v;
-        }
+        for (int i = 0; i < RPW; ++i) y[wave * RPW + i] = (float)acc[i];
       }
       __syncthreads();
-      if constexpr (EPI == GV_SWIGLU) {
-        // rows 64p..64p+31 are gate rows 32p.., rows 64p+32..64p+63 up rows 32p..: one Q8_0 block
-        if (tid < 8) {
-          float4 sw;
-          sw.x = swiglu_f32(y[4 * tid + 0], y[32 + 4 * tid + 0], exp_tab);
-          sw.y = swiglu_f32(y[4 * tid + 1], y[32 + 4 * tid + 1], exp_tab);
-          sw.z = swiglu_f32(y[4 * tid + 2], y[32 + 4 * tid + 2], exp_tab);
-          sw.w = swiglu_f32(y[4 * tid + 3], y[32 + 4 * tid + 3], exp_tab);
-          float d;
-          const uint32_t q = q8_block_quant4(sw, d);
-          reinterpret_cast<uint32_t*>(q_codes + (int64_t)grp * QK)[tid] = q;
-          if (tid == 0) q_scales[grp] = f32_to_f16_bits(d);
-        }
-      } else {  // GV_QKV: this group's rows are one head of Q, K or V (one group per workgroup)
-        const int hd = qe.head_dim, half = hd / 2;
-        const int c0 = grp * RWG;
-        if (c0 >= qe.n_q + qe.n_kv) {  // V head: stored as is
-          for (int i = tid; i < hd; i += GV_THREADS) qe.v_region[qpos * qe.n_kv + (c0 - qe.n_q - qe.n_kv) + i] = y[i];
-        } else {
-          const bool isq = c0 < qe.n_q;
-          const float* gam = isq ? qe.q_norm : qe.k_norm;
-          if (gam) {  // per-head RMSNorm in f64, one rounding (wave 0)
-            if (wave == 0) {
-              double ss = 0.0;
-              for (int i = lane; i < hd; i += 64) ss += (double)y[i] * (double)y[i];
-              ss = wave_sum_d(ss);
-              const double ir = recip_f64(sqrt(ss / (double)hd + (double)qe.eps));
-              float t[2];
-#pragma unroll
-              for (int k = 0; k < 2; ++k) {
-                const int i = lane + 64 * k;
-                if (i < hd) t[k] = (float)((double)y[i] * ir * (double)gam[i]);
-              }
-#pragma unroll
-              for (int k = 0; k < 2; ++k) {
-                const int i = lane + 64 * k;
-                if (i < hd) y[i] = t[k];
-              }
-            }
-            __syncthreads();
-          }
-          for (int i = tid; i < half; i += GV_THREADS) {
-            const float a = y[i], b = y[i + half];
-            const double2 cs = reinterpret_cast<const double2*>(qe.rope)[qpos * half + i];
-            const float o0 = (float)((double)a * cs.x - (double)b * cs.y);
-            const float o1 = (float)((double)a * cs.y + (double)b * cs.x);
-            float* dst = isq ? qe.q_out + c0 : qe.k_region + qpos * qe.n_kv + (c0 - qe.n_q);
-            dst[i] = o0;
-            dst[i + half] = o1;
-          }
-        }
+      // rows 64p..64p+31 are gate rows 32p.., rows 64p+32..64p+63 up rows 32p..: one Q8_0 block
+      if (tid < 8) {
+        float4 sw;
+        sw.x = swiglu_f32(y[4 * tid + 0], y[32 + 4 * tid + 0], exp_tab);
+        sw.y = swiglu_f32(y[4 * tid + 1], y[32 + 4 * tid + 1], exp_tab);
+        sw.z = swiglu_f32(y[4 * tid + 2], y[32 + 4 * tid + 2], exp_tab);
+        sw.w = swiglu_f32(y[4 * tid + 3], y[32 + 4 * tid + 3], exp_tab);
+        float d;
+        const uint32_t q = q8_block_quant4(sw, d);
+        reinterpret_cast<uint32_t*>(q_codes + (int64_t)grp * QK)[tid] = q;
+        if (tid == 0) q_scales[grp] = f32_to_f16_bits(d);
       }
       __syncthreads();  // y is rewritten by the next group
     }
@@ -300,34 +274,28 @@ __global__ void __launch_bounds__(GV_THREADS) k_gemv_q8(const float* __restrict_
 
 int launch_gemv_q8(const GemvArgs& g, hipStream_t s) {
   const bool norm = g.x != nullptr;
-  if (g.attn.part) {  // the output projection: its input is the merged attention row
-    if (g.epi != GV_RES || norm || g.k != g.attn.n_head * g.attn.head_dim)
-      return set_error(MI_ERR_INVALID_ARG, "gemv: attention-merge input needs the residual epilogue");
-  }
   const int KB = g.k / QK;
   const size_t lds = (size_t)((g.k + 15) & ~15) + sizeof(double) * KB + sizeof(float) * 130 +
                      sizeof(double) * (GV_WAVES + 1);
-  if (g.k % QK || g.k <= 0 || lds > 64 * 1024 || ((norm || g.attn.part) && g.k > GV_THREADS * 4) ||
+  if (g.k % QK || g.k <= 0 || lds > 64 * 1024 || (norm && g.k > GV_NORM_K) ||
       (int64_t)g.n * g.k >= ((int64_t)1 << 31))
     return set_error(MI_ERR_UNSUPPORTED, "gemv: K %d (multiple of 32, LDS %zu bytes, <= %d with the norm)", g.k, lds,
-                     GV_THREADS * 4);
-  GemvQkv qe = g.qkv;
+                     GV_NORM_K);
+  if (g.bias && g.epi != GV_F32) return set_error(MI_ERR_INVALID_ARG, "gemv: a bias needs the plain f32 epilogue");
   // enough workgroups to keep every CU busy, looping over row groups beyond that
-  const int max_wg = 2 * 256;
+  const int max_wg = GV_MAX_WG;
   auto grid = [&](int rwg) { return dim3((unsigned)std::min((g.n + rwg - 1) / rwg, max_wg)); };
 #define GV_LAUNCH(RPW, EPI, NORM)                                                                          \
   hipLaunchKernelGGL((k_gemv_q8<RPW, EPI, NORM>), grid(RPW * GV_WAVES), dim3(GV_THREADS), lds, s, g.x, g.gamma, \
                      g.eps, g.xq, g.xs, g.k, g.w_codes, g.w_scales, g.n, g.bias, g.residual, g.out, g.q_codes,     \
-                     g.q_scales, qe, g.attn)
+                     g.q_scales)
   switch (g.epi) {
     case GV_RES:
     case GV_F32: {
       // one row per wave while that gives fewer groups than CUs x 2, else four
-      const bool small = g.n <= 16 * max_wg;
+      const bool small = g.n <= GV_WAVES * max_wg;
       if (g.epi == GV_RES) {
-        if (g.attn.part) {
-          if (small) GV_LAUNCH(1, GV_RES, GV_IN_ATTN); else GV_LAUNCH(4, GV_RES, GV_IN_ATTN);
-        } else if (small) {
+        if (small) {
           if (norm) GV_LAUNCH(1, GV_RES, GV_IN_NORM); else GV_LAUNCH(1, GV_RES, GV_IN_Q8);
         } else {
           if (norm) GV_LAUNCH(4, GV_RES, GV_IN_NORM); else GV_LAUNCH(4, GV_RES, GV_IN_Q8);
@@ -340,24 +308,72 @@ int launch_gemv_q8(const GemvArgs& g, hipStream_t s) {
     }
     case GV_SWIGLU:
       if (g.n % 64) return set_error(MI_ERR_UNSUPPORTED, "gemv: SwiGLU rows %d not a multiple of 64", g.n);
-      if (norm) GV_LAUNCH(4, GV_SWIGLU, GV_IN_NORM); else GV_LAUNCH(4, GV_SWIGLU, GV_IN_Q8);
-      break;
-    case GV_QKV:
-      if (g.n / (qe.head_dim > 0 ? qe.head_dim : 1) > max_wg)
-        return set_error(MI_ERR_UNSUPPORTED, "gemv: more than %d heads", max_wg);
-      if (qe.head_dim == 64 && g.n % 64 == 0) {
-        if (norm) GV_LAUNCH(4, GV_QKV, GV_IN_NORM); else GV_LAUNCH(4, GV_QKV, GV_IN_Q8);
-      } else if (qe.head_dim == 128 && g.n % 128 == 0) {
-        if (norm) GV_LAUNCH(8, GV_QKV, GV_IN_NORM); else GV_LAUNCH(8, GV_QKV, GV_IN_Q8);
-      } else {
-        return set_error(MI_ERR_UNSUPPORTED, "gemv: attention inputs need head_dim 64 or 128 (got %d)", qe.head_dim);
-      }
+      if (norm) GV_LAUNCH(GV_RPW_SWIGLU, GV_SWIGLU, GV_IN_NORM); else GV_LAUNCH(GV_RPW_SWIGLU, GV_SWIGLU, GV_IN_Q8);
       break;
     default:
       return set_error(MI_ERR_INVALID_ARG, "gemv: epilogue %d", g.epi);
   }
 #undef GV_LAUNCH
   MI_LAUNCH_CHECK("k_gemv_q8");
+  return MI_OK;
+}
+
+// The steps after the Q|K|V rows of one token (bias already added, one rounding): workgroup b < n_head
+// takes Q head b, then the K heads, then the V heads.  Q and K: [per-head RMSNorm in f64, one
+// rounding to f32], NeoX RoPE of the pair (i, i + hd/2) in f64 at the position, one rounding; Q in
+// place, K to its region row.  V: copied to its region row.  One wave; lane i < hd/2 takes pair i.
+template <int HD>
+__global__ void __launch_bounds__(64) k_qkv_finish(float* __restrict__ qkv, const int32_t* __restrict__ pos_dev,
+                                                   const double2* __restrict__ rope, int n_head, int n_head_kv,
+                                                   const float* __restrict__ q_norm, const float* __restrict__ k_norm,
+                                                   float eps, float* __restrict__ k_region,
+                                                   float* __restrict__ v_region) {
+  constexpr int HALF = HD / 2;
+  static_assert(HALF <= 64, "one pair per lane");
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int64_t p = *pos_dev;
+  const int n_kv = n_head_kv * HD;
+  const int nq = n_head * HD;
+  if (b >= n_head + n_head_kv) {  // V head
+    const int c = (b - n_head - n_head_kv) * HD;
+    for (int i = lane; i < HD; i += 64) v_region[p * n_kv + c + i] = qkv[nq + n_kv + c + i];
+    return;
+  }
+  const bool isq = b < n_head;
+  const int c = isq ? b * HD : nq + (b - n_head) * HD;  // the head's offset in the Q|K|V row
+  const float* gam = isq ? q_norm : k_norm;
+  const bool on = lane < HALF;
+  float a = on ? qkv[c + lane] : 0.0f, bb = on ? qkv[c + lane + HALF] : 0.0f;
+  if (gam) {  // per-head RMSNorm in f64, one rounding
+    const double ss = wave_sum_d((double)a * (double)a + (double)bb * (double)bb);
+    const double ir = recip_f64(sqrt(ss / (double)HD + (double)eps));
+    if (on) {
+      a = (float)((double)a * ir * (double)gam[lane]);
+      bb = (float)((double)bb * ir * (double)gam[lane + HALF]);
+    }
+  }
+  if (on) {
+    float* dst = isq ? qkv + c : k_region + p * n_kv + (b - n_head) * HD;
+    const double2 cs = rope[p * HALF + lane];
+    dst[lane] = (float)((double)a * cs.x - (double)bb * cs.y);
+    dst[lane + HALF] = (float)((double)a * cs.y + (double)bb * cs.x);
+  }
+}
+
+int launch_qkv_finish(float* qkv, const int32_t* pos_dev, const double* rope, int n_head, int n_head_kv,
+                      int head_dim, const float* q_norm, const float* k_norm, float eps, float* k_region,
+                      float* v_region, hipStream_t s) {
+  const dim3 grid(n_head + 2 * n_head_kv);
+  const double2* r = reinterpret_cast<const double2*>(rope);
+  if (head_dim == 64)
+    hipLaunchKernelGGL(k_qkv_finish<64>, grid, dim3(64), 0, s, qkv, pos_dev, r, n_head, n_head_kv, q_norm, k_norm,
+                       eps, k_region, v_region);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL(k_qkv_finish<128>, grid, dim3(64), 0, s, qkv, pos_dev, r, n_head, n_head_kv, q_norm, k_norm,
+                       eps, k_region, v_region);
+  else
+    return set_error(MI_ERR_UNSUPPORTED, "attention inputs: head_dim %d (supported: 64, 128)", head_dim);
+  MI_LAUNCH_CHECK("k_qkv_finish");
   return MI_OK;
 }
 
@@ -499,11 +515,11 @@ __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restr
   }
 }
 
-// Merge head h's n_ne ranges in order, normalize, round to f32 and Q8_0 into the LDS row (one
-// wave; lane holds dims 4*lane..4*lane+3, HD/4 lanes = whole groups of 8 per block).
+// Merge head h's n_ne ranges in order, normalize, round to f32 and Q8_0 (one wave; lane holds dims
+// 4*lane..4*lane+3, HD/4 lanes = whole groups of 8 per block).
 template <int HD>
 __device__ __forceinline__ void attn_merge_head(const double* __restrict__ part, int n_range, int n_ne, int h, int lane,
-                                                const double* exp_tab, int8_t* a_codes, double* a_d) {
+                                                const double* exp_tab, int8_t* a_codes, uint16_t* a_scales) {
   const double* ph = part + (int64_t)h * n_range * (HD + 2);
   double mr = -1e300, lr = 0.0;
   if (lane < n_ne) {  // one range per lane (n_ne <= AD_MAX_RANGES <= 64)
@@ -531,8 +547,36 @@ __device__ __forceinline__ void attn_merge_head(const double* __restrict__ part,
     float d;
     const uint32_t qv = q8_block_quant4(v, d);
     reinterpret_cast<uint32_t*>(a_codes + h * HD)[lane] = qv;
-    if ((lane & 7) == 0) a_d[h * (HD / QK) + lane / 8] = (double)f16_bits_to_f32(f32_to_f16_bits(d));
+    if ((lane & 7) == 0) a_scales[h * (HD / QK) + lane / 8] = f32_to_f16_bits(d);
   }
+}
+
+// The output projection's input row: wave w of workgroup b merges head 4b + w.
+template <int HD>
+__global__ void __launch_bounds__(256) k_attn_merge(const double* __restrict__ part, int n_range, int keys_per_range,
+                                                    const int32_t* __restrict__ pos_dev, int n_head,
+                                                    int8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+  __shared__ double exp_tab[64];
+  exp2_table_fill(exp_tab, threadIdx.x);
+  __syncthreads();
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int n_ne = (*pos_dev + keys_per_range) / keys_per_range;  // ranges holding keys 0..pos
+  if (h < n_head) attn_merge_head<HD>(part, n_range, n_ne, h, threadIdx.x & 63, exp_tab, codes, scales);
+}
+
+int launch_attn_merge(const double* part, int n_ctx, const int32_t* pos_dev, int n_head, int head_dim, int8_t* codes,
+                      uint16_t* scales, hipStream_t s) {
+  int kpr = 0;
+  const int n_range = attn_decode_ranges(n_ctx, &kpr);
+  const dim3 grid((n_head + 3) / 4);
+  if (head_dim == 64)
+    hipLaunchKernelGGL(k_attn_merge<64>, grid, dim3(256), 0, s, part, n_range, kpr, pos_dev, n_head, codes, scales);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL(k_attn_merge<128>, grid, dim3(256), 0, s, part, n_range, kpr, pos_dev, n_head, codes, scales);
+  else
+    return set_error(MI_ERR_UNSUPPORTED, "attention merge: head_dim %d", head_dim);
+  MI_LAUNCH_CHECK("k_attn_merge");
+  return MI_OK;
 }
 
 int attn_decode_ranges(int n_ctx, int* keys_per_range) {
