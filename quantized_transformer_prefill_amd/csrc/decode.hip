@@ -529,12 +529,25 @@ __device__ __forceinline__ void attn_merge_head(const double* __restrict__ part,
   const double m = wave_max_d(mr);
   const double f_own = lane < n_ne ? exp_f64(mr - m, exp_tab) : 0.0;
   const double l = wave_sum_d(lr * f_own);
-  double o[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int rr = 0; rr < n_ne; ++rr) {
-    const double f = lane_f64(f_own, rr);
-    if (lane < HD / 4) {
+  // every range's partial output requested at once (they do not depend on the max), then summed
+  // in range order
+  double2 po[AD_MAX_RANGES][2];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) o[k] = fma(ph[rr * (HD + 2) + 2 + 4 * lane + k], f, o[k]);
+  for (int rr = 0; rr < AD_MAX_RANGES; ++rr) {
+    const int r = rr < n_ne ? rr : 0;  // ranges past n_ne re-read range 0 (unused)
+    const double2* src = reinterpret_cast<const double2*>(ph + r * (HD + 2) + 2) + 2 * (lane & (HD / 4 - 1));
+    po[rr][0] = src[0];
+    po[rr][1] = src[1];
+  }
+  double o[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int rr = 0; rr < AD_MAX_RANGES; ++rr) {
+    if (rr < n_ne) {  // uniform
+      const double f = lane_f64(f_own, rr);
+      o[0] = fma(po[rr][0].x, f, o[0]);
+      o[1] = fma(po[rr][0].y, f, o[1]);
+      o[2] = fma(po[rr][1].x, f, o[2]);
+      o[3] = fma(po[rr][1].y, f, o[3]);
     }
   }
   const double inv = recip_f64(l);
