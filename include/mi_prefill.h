@@ -55,7 +55,8 @@ typedef enum {
 } mi_status;
 
 /* Model shape.  n_head % n_head_kv == 0; head_dim 64 or 128; hidden, ffn, n_head*head_dim
- * multiples of 32; hidden and n_head*head_dim at most 4096 (MI_ERR_UNSUPPORTED otherwise).
+ * multiples of 32; hidden at most 4096, n_head*head_dim and ffn at most 49152 (MI_ERR_UNSUPPORTED
+ * otherwise).
  * rms_eps is used for every RMSNorm (and the Qwen3 per-head QK norm); rope_theta is the NeoX
  * RoPE base. */
 typedef struct {

@@ -117,10 +117,11 @@ static int check_hparams(const mi_hparams* hp) {
   if (hp->head_dim != 64 && hp->head_dim != 128)
     return set_error(MI_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", hp->head_dim);
   if (hp->hidden > 4096) return set_error(MI_ERR_UNSUPPORTED, "hidden %d > 4096", hp->hidden);
-  // the one-row matrix-vector kernels (the last layer's tail row, decode) hold a whole input row of
-  // at most 4096 values, the attention output (n_head * head_dim values) included
-  if ((int64_t)hp->n_head * hp->head_dim > 4096)
-    return set_error(MI_ERR_UNSUPPORTED, "n_head * head_dim %d > 4096", hp->n_head * hp->head_dim);
+  // the one-row matrix-vector kernels (the last layer's tail row, decode) stage a whole Q8_0 input
+  // row in LDS: the attention output (n_head * head_dim values) and the SwiGLU row (ffn values)
+  if ((int64_t)hp->n_head * hp->head_dim > GV_MAX_K || hp->ffn > GV_MAX_K)
+    return set_error(MI_ERR_UNSUPPORTED, "n_head * head_dim %d or ffn %d above %d", hp->n_head * hp->head_dim,
+                     hp->ffn, GV_MAX_K);
   if (hp->ffn % 32) return set_error(MI_ERR_INVALID_ARG, "ffn %% 32 != 0");
   return MI_OK;
 }

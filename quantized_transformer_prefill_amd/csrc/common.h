@@ -238,6 +238,8 @@ int launch_lm_head(const int8_t* xq, const uint16_t* xs, int cols, const int8_t*
 
 // ---- decode step (one activation row): exact Q8_0 matrix-vector products and single-query attention
 enum GemvEpi { GV_RES = 0, GV_F32 = 1, GV_SWIGLU = 3 };
+// the one-row kernels stage their Q8_0 input row in LDS (K codes + K/32 f64 scales, 64 KB at most)
+constexpr int GV_MAX_K = 49152;
 struct GemvArgs {
   // input row: with x non-null, RMSNorm(x; gamma, eps) + Q8_0 inside the kernel; else xq/xs
   const float* x; const float* gamma; float eps;

@@ -158,13 +158,18 @@ def test_workspace_grows_with_tokens():
     assert B.lib().mi_rope_table_bytes(C.byref(hp), 4096) == 4096 * 32 * 2 * 8
 
 
-def test_forward_rejects_wide_attention_rows():
-    """n_head * head_dim above 4096 (the one-row kernels of the last layer hold a whole attention
-    output row) is refused up front, before any layer is enqueued."""
+def test_forward_rejects_rows_wider_than_the_one_row_kernels():
+    """The one-row kernels of the last layer stage a whole Q8_0 input row in LDS: an attention
+    output row (n_head * head_dim) or a SwiGLU row (ffn) above 49152 values is refused up front,
+    before any layer is enqueued; 40 heads of 128 (5120 values) are accepted."""
     hp = B.Hparams(1, 4096, 40, 8, 128, 4096, 50, 1e-6, 1e6, 0, 1, 0)
+    assert B.lib().mi_prefill_workspace_bytes(C.byref(hp), 8) > 0
+    hp = B.Hparams(1, 4096, 32, 8, 128, 65536, 50, 1e-6, 1e6, 0, 1, 0)
     assert B.lib().mi_prefill_workspace_bytes(C.byref(hp), 8) == 0
-    assert b"n_head * head_dim" in B.lib().mi_last_error()
-    model, kv, keep = make_model(hidden=4096, nh=40, nkv=8, hd=128, ffn=4096)
+    assert b"ffn" in B.lib().mi_last_error()
+    hp = B.Hparams(1, 4096, 512, 8, 128, 4096, 50, 1e-6, 1e6, 0, 1, 0)
+    assert B.lib().mi_prefill_workspace_bytes(C.byref(hp), 8) == 0
+    model, kv, keep = make_model(hidden=4096, nh=32, nkv=8, hd=128, ffn=65536)
     assert call_forward(model, kv, [1], [0]) == B.MI_ERR_UNSUPPORTED
 
 

@@ -60,10 +60,16 @@ def prefill_then_decode(cfg, dev, n_steps, graph=False):
     return m, steps, kk, vv, p0 + n_steps
 
 
-@pytest.mark.parametrize("cfg", [synth.LAYER1, TINY_Q3, TINY_Q2], ids=lambda c: c.name)
+# 40 query heads of 128: an attention output row of 5120 values, wider than the hidden size
+TINY_WIDE = synth.ModelConfig(name="tiny_wide_heads", n_layers=2, hidden=256, n_head=40, n_head_kv=8, head_dim=128,
+                              ffn=384, vocab=1000, n_tokens=24, n_ctx=64, seed=19, qkv_bias=True, tied=False)
+
+
+@pytest.mark.parametrize("cfg", [synth.LAYER1, TINY_Q3, TINY_Q2, TINY_WIDE], ids=lambda c: c.name)
 def test_decode_matches_oracle(cfg):
     """Head dims 64 and 128, QKV bias, per-head QK norm, tied and separate lm_heads, GQA 7:1, 4:1
-    and 4:1 with one KV head; several steps, each attending to the prompt and the earlier steps."""
+    and 4:1 with one KV head, an attention row wider than the hidden size (40 x 128 over 256);
+    several steps, each attending to the prompt and the earlier steps."""
     dev = need_gpu()
     m, steps, kk, vv, end = prefill_then_decode(cfg, dev, 4)
     for i, (got, want) in enumerate(steps):
