@@ -166,12 +166,16 @@ def main():
         for _ in range(args.warmup):
             graph.launch(ids, pos)
         torch.cuda.synchronize()
+        step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         e0.record(stream)
-        for _ in range(args.steps):
+        for i in range(args.steps):
             graph.launch(ids, pos)
+            step_ev[i].record(stream)  # per-step spread (the mean below spans e0..e1)
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
+        per_step = [e0.elapsed_time(step_ev[0])] + [step_ev[i - 1].elapsed_time(step_ev[i])
+                                                     for i in range(1, args.steps)]
         graph.close()
     tok_s = cfg.n_tokens / (ms / 1e3)
 
@@ -214,7 +218,7 @@ def main():
             xw, ww = synth.gen_gemm_inputs(case, device=dev)
             ac, as_ = B.quantize_q8_0(xw)
             wc, wsc = B.quantize_q8_0(ww)
-            del xw, ww
+            del ww
             need = B.lib().mi_gemm_q8_0_workspace_bytes(case.m, case.n, case.k)
             gws = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
             out = torch.empty(case.m, case.n, dtype=torch.float32, device=dev)
@@ -224,11 +228,18 @@ def main():
             def run():
                 B.check(B.lib().mi_gemm_q8_0_ws(ac.data_ptr(), as_.data_ptr(), case.m, C.byref(wmat), None, None,
                                                 out.data_ptr(), gws.data_ptr(), gws.numel(), 0, B.stream_ptr()))
+
+            def run_pair():  # the f32 activations quantized on the fly, then the matmul
+                B.check(B.lib().mi_quantize_q8_0(xw.data_ptr(), case.m, case.k, ac.data_ptr(), as_.data_ptr(),
+                                                 B.stream_ptr()))
+                run()
             g_ms = timed_loop(run, 50, torch)
+            p_ms = timed_loop(run_pair, 50, torch)
             tops = 2.0 * case.m * case.n * case.k / (g_ms / 1e3) / 1e12
             sweep.append({"mnk": [case.m, case.k, case.n], "ms": round(g_ms, 4), "tops": round(tops, 1),
-                          "int8_peak_frac": round(tops / INT8_PEAK_TOPS, 4)})
-            del ac, as_, wc, wsc, gws, out
+                          "int8_peak_frac": round(tops / INT8_PEAK_TOPS, 4),
+                          "quantize_plus_gemm_ms": round(p_ms, 4)})
+            del xw, ac, as_, wc, wsc, gws, out
 
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     cpu = None
@@ -243,6 +254,8 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights quantized to Q8_0, uniform token ids)",
         "config": {"workload": cfg.name, "description": cfg.description, "n_tokens": cfg.n_tokens,
                    "n_ctx": cfg.n_ctx, "parallelism": "single GPU"},
+        "ms_per_step_median": round(float(np.median(per_step)), 4),
+        "ms_per_step_stdev": round(float(np.std(per_step)), 4),
         "eager_ms_per_step": round(eager_ms, 4),
         "kernels_per_forward": kernels_per_forward,
         "roofline": roofline,
@@ -407,7 +420,7 @@ def cpu_baseline_decode(cfg, min_seconds: float = 10.0, max_reps: int = 64):
             "sample": f"{reps} decode steps (one token each, all {cfg.n_layers} layers and the lm_head) after the "
                       f"{cfg.n_tokens}-token prompt ({t:.1f} s of CPU time; prompt prefill and weight "
                       f"quantization untimed)",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), **host_info()}
 
 
 PROBES = {  # name: (probe id of mi_probes.h, workgroups, iterations, unit of the work)
@@ -845,7 +858,24 @@ def cpu_baseline(cfg, min_seconds: float = 10.0, max_reps: int = 8):
             "kind": "oracle",
             "sample": f"{reps} whole prefill call(s) of the {cfg.n_tokens}-token prompt through all {cfg.n_layers} "
                       f"layers and the lm_head ({t:.1f} s of CPU time; weights quantized beforehand)",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), **host_info()}
+
+
+def host_info():
+    """The host CPU model and numpy's BLAS, recorded beside the oracle's timing."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    blas = None
+    try:
+        info = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{info.get('name')} {info.get('version')}"
+    except Exception:  # numpy builds without the dict form
+        pass
+    return {"cpu_model": model, "blas": blas}
 
 
 if __name__ == "__main__":
