@@ -83,8 +83,10 @@ __device__ __forceinline__ double wave_max_d(double v) { return wave_reduce_f64<
 // stream by RMSNorm + Q8_0 (GV_IN_NORM).
 enum { GV_IN_Q8 = 0, GV_IN_NORM = 1 };
 
+// The plain-epilogue one-row-per-wave instance (the Q|K|V rows: 288 workgroups at the 7B shape) is
+// held to 64 registers, so that two workgroups fit a CU and the whole grid is resident at once.
 template <int RPW, int EPI, int PRO>
-__global__ void __launch_bounds__(GV_THREADS) k_gemv_q8(const float* __restrict__ x, const float* __restrict__ gamma,
+__global__ void __launch_bounds__(GV_THREADS, (RPW == 1 && EPI == GV_F32) ? 8 : 1) k_gemv_q8(const float* __restrict__ x, const float* __restrict__ gamma,
                                                        float eps, const int8_t* __restrict__ xq,
                                                        const uint16_t* __restrict__ xs, int K,
                                                        const int8_t* __restrict__ w_codes,
