@@ -174,3 +174,33 @@ def test_one_token_tail_merges_key_ranges_head_dim_128():
     assert np.all(gk[:, end:] == SENTINEL) and np.all(gv[:, end:] == SENTINEL), "stray KV writes"
     assert_f32_match(gk[:, :end], kk[:, :end], max_ulp=64, max_frac_inexact=0.05, what="K regions")
     assert_f32_match(gv[:, :end], vv[:, :end], max_ulp=64, max_frac_inexact=0.05, what="V regions")
+
+
+# n_ctx above 4096: the one-token attention's key ranges grow to 512 keys (10 ranges for 5120)
+TINY_FAR = synth.ModelConfig(name="tiny_far_positions", n_layers=2, hidden=128, n_head=4, n_head_kv=2, head_dim=64,
+                             ffn=192, vocab=700, n_tokens=20, n_ctx=5120, seed=23, qkv_bias=True)
+
+
+def test_far_positions_over_long_context():
+    """A prompt at positions 5000..5019 of a 5120-row context (the rows below it hold the regions'
+    fill, read by both sides), then 3 decode steps: every key range of 512 keys carries keys, and
+    the merge combines 10 ranges.  Logits and regions against the oracle."""
+    dev = need_gpu()
+    cfg = TINY_FAR
+    m, w = load_pair(cfg, dev, max_tokens=cfg.n_tokens)
+    _, ids = synth.gen_token_ids(cfg)
+    pos = np.arange(5000, 5000 + cfg.n_tokens, dtype=np.int32)
+    kk, vv = oracle.new_kv_regions(cfg, cfg.n_ctx, fill=SENTINEL)
+    got = m.forward(ids, pos).cpu().numpy().copy()
+    want = oracle.prefill_forward(cfg, w, ids, pos, cfg.n_ctx, kk, vv)[0]
+    compare_logits(got, want, f"{cfg.name} prefill logits")
+    for i, tok in enumerate(decode_tokens(cfg, 3)):
+        p = int(pos[-1]) + 1 + i
+        say(f"decode {cfg.name} step {i} position {p}")
+        got = m.decode(int(tok), p).cpu().numpy().copy()
+        want = oracle.prefill_forward(cfg, w, np.array([tok], np.int32), np.array([p], np.int32), cfg.n_ctx, kk, vv)[0]
+        compare_logits(got, want, f"{cfg.name} step {i} logits")
+        assert_f32_match(got, want, max_ulp=64, max_frac_inexact=0.05, what=f"step {i} logits ulp")
+    gk, gv = m.kv_k.cpu().numpy(), m.kv_v.cpu().numpy()
+    assert_f32_match(gk, kk, max_ulp=64, max_frac_inexact=0.05, what="K regions")
+    assert_f32_match(gv, vv, max_ulp=64, max_frac_inexact=0.05, what="V regions")
