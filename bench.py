@@ -726,11 +726,11 @@ def write_counters(cfg, cdir, fdir, wdir, out_path):
     lines = [f"# Per-kernel counters: {cfg.description} ({cfg.name})", "",
              "Commands (repository root on the GPU host; run from /tmp with TMPDIR=/tmp):", "",
              "    rocprofv3 --kernel-trace --pmc " + " ".join(COUNTERS_COMPUTE) +
-             " --output-format csv -d gpurun_out/cnt_compute -o p -- " + run,
-             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/cnt_fetch -o p -- " + run,
-             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/cnt_write -o p -- " + run,
-             f"    python3 bench.py --workload {cfg.name} --write-counters gpurun_out/cnt_compute gpurun_out/cnt_fetch "
-             "gpurun_out/cnt_write profiles/counters_" + cfg.name + ".md", "",
+             " --output-format csv -d out/cnt_compute -o p -- " + run,
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d out/cnt_fetch -o p -- " + run,
+             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d out/cnt_write -o p -- " + run,
+             f"    python3 bench.py --workload {cfg.name} --write-counters out/cnt_compute out/cnt_fetch "
+             "out/cnt_write profiles/counters_" + cfg.name + ".md", "",
              f"Byte counters scaled on a streaming kernel of {COPY_BYTES >> 20} MiB read + written: FETCH_SIZE x "
              f"{ff:.3f}, WRITE_SIZE x {fw:.3f}.  Per kernel: the group of launches at the full prompt (the most "
              "launches of that kernel), medians over its launches.  Durations are from the kernel trace of the "
@@ -811,11 +811,11 @@ def write_traffic(fetch_dir, write_dir, shape=(512, 9728, 896)):
            "kernel_source_hash": kernel_source_hash(),
            "bytes_per_launch": round(out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]),
            "fetch": out["fetch"], "write": out["write"],
-           "commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o p -- "
+           "commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d out/pmc_fetch -o p -- "
                         "python3 bench.py --traffic-run",
-                        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o p -- "
+                        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d out/pmc_write -o p -- "
                         "python3 bench.py --traffic-run",
-                        "python3 bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write"]}
+                        "python3 bench.py --write-traffic out/pmc_fetch out/pmc_write"]}
     path = os.path.join(ROOT, "profiles", TRAFFIC_FILE)
     with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 SENTINEL = -777.25
 
-# spec bar for last-token logits
+# the bar for last-token logits (max-abs and rel-L2 against the oracle)
 MAX_ABS, REL_L2 = 2e-2, 1e-3
 
 
