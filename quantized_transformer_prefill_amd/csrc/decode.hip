@@ -20,7 +20,7 @@
 //    so a workgroup takes 16 or 64 rows and even the small matrices spread over the chip.
 //
 // k_qkv_finish: the per-head steps after the Q|K|V rows (per-head QK RMSNorm, NeoX RoPE at the
-// position, the K and V rows stored in the regions), one workgroup per head.
+// position, the K and V rows stored in the regions), one single-wave workgroup per head.
 //
 // k_attn_decode: the query's keys 0..pos are split into fixed ranges (the grid depends only on
 // n_ctx, so the launch can be captured once and replayed for any position); each workgroup
@@ -40,7 +40,7 @@ constexpr int GV_WAVES = GV_THREADS / 64;
 constexpr int GV_NORM_K = 4096;                                  // widest row the norm prologue takes
 constexpr int GV_NV = (GV_NORM_K / 4 + GV_THREADS - 1) / GV_THREADS;  // float4s of the row per thread
 constexpr int GV_RPW_SWIGLU = 64 / GV_WAVES;                       // a SwiGLU group is 64 rows
-constexpr int GV_MAX_WG = (2048 / GV_THREADS) * 256;               // workgroups resident on the chip
+constexpr int GV_MAX_WG = (2048 / GV_THREADS) * 256;               // grid cap: two workgroups per CU
 
 // f64 cross-lane reduction over a wave, every lane receiving the result: DPP row permutations for
 // the 16-lane rows (each 32-bit half moved separately), a bit-mode swizzle across the two rows of a
