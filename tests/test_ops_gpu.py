@@ -257,8 +257,10 @@ def test_rope_kvstore_rows_and_values(nh, nkv, hd):
     np.testing.assert_array_equal(k.cpu().numpy(), k0)  # k itself is not modified
 
 
+# head_dim 128 takes the KV-head-shared kernel for 4..8 query heads per KV head (7 and 4 here) and
+# the per-head kernel otherwise (2 and 16)
 @pytest.mark.parametrize("nh,nkv,hd,n,n_ctx", [(14, 2, 64, 37, 300), (28, 4, 128, 21, 200), (32, 8, 128, 50, 700),
-                                               (4, 4, 64, 1, 5)])
+                                               (4, 4, 64, 1, 5), (4, 2, 128, 30, 100), (16, 1, 128, 20, 64)])
 def test_attention_matches_oracle(nh, nkv, hd, n, n_ctx):
     dev = need_gpu()
     say(f"attention nh={nh} nkv={nkv} hd={hd} n={n} n_ctx={n_ctx}")
