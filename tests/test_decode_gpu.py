@@ -204,3 +204,21 @@ def test_far_positions_over_long_context():
     gk, gv = m.kv_k.cpu().numpy(), m.kv_v.cpu().numpy()
     assert_f32_match(gk, kk, max_ulp=64, max_frac_inexact=0.05, what="K regions")
     assert_f32_match(gv, vv, max_ulp=64, max_frac_inexact=0.05, what="V regions")
+
+
+def test_decode_at_first_and_last_rows():
+    """A decode step as the very first token (position 0: one key, one range) and at the last row
+    of the context (position n_ctx - 1), each against the oracle's one-token forward."""
+    dev = need_gpu()
+    cfg = TINY_Q3
+    m, w = load_pair(cfg, dev)
+    kk, vv = oracle.new_kv_regions(cfg, cfg.n_ctx, fill=SENTINEL)
+    for tok, p in zip(decode_tokens(cfg, 2), [0, cfg.n_ctx - 1]):
+        say(f"decode {cfg.name} token {int(tok)} at position {p}")
+        got = m.decode(int(tok), p).cpu().numpy().copy()
+        want = oracle.prefill_forward(cfg, w, np.array([tok], np.int32), np.array([p], np.int32), cfg.n_ctx, kk, vv)[0]
+        compare_logits(got, want, f"position {p} logits")
+        assert_f32_match(got, want, max_ulp=64, max_frac_inexact=0.05, what=f"position {p} logits ulp")
+    gk, gv = m.kv_k.cpu().numpy(), m.kv_v.cpu().numpy()
+    assert_f32_match(gk, kk, max_ulp=64, max_frac_inexact=0.05, what="K regions")
+    assert_f32_match(gv, vv, max_ulp=64, max_frac_inexact=0.05, what="V regions")
