@@ -254,7 +254,7 @@ struct GemvArgs {
 int launch_gemv_q8(const GemvArgs& g, hipStream_t s);
 // attention of one query per head over keys 0..*pos_dev: partial states per key range in `part`
 // (n_head * n_range * (head_dim + 2) f64, n_range <= AD_MAX_RANGES), merged by launch_attn_merge
-constexpr int AD_MAX_RANGES = 16;
+constexpr int AD_MAX_RANGES = 64;
 int attn_decode_ranges(int n_ctx, int* keys_per_range);
 int launch_attn_decode(const float* q, const float* k_region, const float* v_region, const int32_t* pos_dev,
                        int n_ctx, int n_head, int n_head_kv, int head_dim, double* part, hipStream_t s);

@@ -24,8 +24,9 @@
 //
 // k_attn_decode: the query's keys 0..pos are split into fixed ranges (the grid depends only on
 // n_ctx, so the launch can be captured once and replayed for any position); each workgroup
-// computes the partial softmax state (max, sum, unnormalized output) of one head over one range in
-// f64.  k_attn_merge combines a head's ranges in order, normalizes, and quantizes the head's
+// computes the partial softmax states (max, sum, unnormalized output) of the query heads of one KV
+// head (up to 8 of them) over one range in f64, reading each K and V row once for all of them.
+// k_attn_merge combines a head's ranges (in a fixed order), normalizes, and quantizes the head's
 // output row to Q8_0, the output projection's input.
 #include <algorithm>
 
@@ -83,10 +84,10 @@ __device__ __forceinline__ double wave_max_d(double v) { return wave_reduce_f64<
 // stream by RMSNorm + Q8_0 (GV_IN_NORM).
 enum { GV_IN_Q8 = 0, GV_IN_NORM = 1 };
 
-// The plain-epilogue one-row-per-wave instance (the Q|K|V rows: 288 workgroups at the 7B shape) is
-// held to 64 registers, so that two workgroups fit a CU and the whole grid is resident at once.
-template <int RPW, int EPI, int PRO>
-__global__ void __launch_bounds__(GV_THREADS, (RPW == 1 && EPI == GV_F32) ? 8 : 1) k_gemv_q8(const float* __restrict__ x, const float* __restrict__ gamma,
+// The one-row-per-wave instances (the Q|K|V rows: 288 workgroups at the 7B shape; the output and
+// down projections) are held to 64 registers, so that two workgroups fit a CU.
+template <int RPW, int EPI, int PRO, int TH>
+__global__ void __launch_bounds__(TH, (RPW == 1 && EPI != GV_SWIGLU) ? 8 : 1) k_gemv_q8(const float* __restrict__ x, const float* __restrict__ gamma,
                                                        float eps, const int8_t* __restrict__ xq,
                                                        const uint16_t* __restrict__ xs, int K,
                                                        const int8_t* __restrict__ w_codes,
@@ -94,7 +95,9 @@ __global__ void __launch_bounds__(GV_THREADS, (RPW == 1 && EPI == GV_F32) ? 8 : 
                                                        const float* __restrict__ bias, const float* residual,
                                                        float* out, int8_t* __restrict__ q_codes,
                                                        uint16_t* __restrict__ q_scales) {
-  constexpr int RWG = RPW * GV_WAVES;  // weight rows per group
+  constexpr int WAVES = TH / 64;
+  constexpr int NV = (GV_NORM_K / 4 + TH - 1) / TH;  // float4s of the row per thread (norm prologue)
+  constexpr int RWG = RPW * WAVES;  // weight rows per group
   // 64-chunk steps of K per load batch; two batches are in flight (double buffered)
   constexpr int B = (EPI == GV_SWIGLU || RPW >= 4) ? 1 : 2;
   extern __shared__ __align__(16) unsigned char gv_lds[];
@@ -102,13 +105,41 @@ __global__ void __launch_bounds__(GV_THREADS, (RPW == 1 && EPI == GV_F32) ? 8 : 
   int8_t* a_codes = reinterpret_cast<int8_t*>(gv_lds);                           // [K]
   double* a_d = reinterpret_cast<double*>(gv_lds + ((K + 15) & ~15));             // [KB]
   float* y = reinterpret_cast<float*>(a_d + KB);                                   // [RWG]
-  double* red = reinterpret_cast<double*>(y + RWG + (RWG & 1));                    // [GV_WAVES + 1]
+  double* red = reinterpret_cast<double*>(y + RWG + (RWG & 1));                    // [WAVES + 1]
   __shared__ double exp_tab[EPI == GV_SWIGLU ? 64 : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nchunk = K / 16;
   const int n_groups = (N + RWG - 1) / RWG;
 
-  // ---- requests that do not depend on the activation row go out first
+  // ---- every request that depends on nothing goes out first: the activation row (the prologue's
+  // input; K <= GV_NORM_K with the norm, K <= GV_MAX_K without), then the first load batches of
+  // weights, so the prologue's waits never cover the weights and its latency overlaps them
+  const int nvec = K / 4;
+  constexpr int QW = (GV_MAX_K / 4 + TH - 1) / TH;   // code words of the Q8_0 row per thread
+  constexpr int QS = (GV_MAX_K / 32 + TH - 1) / TH;  // scales of the Q8_0 row per thread
+  float4 v[PRO == GV_IN_NORM ? NV : 1], gm[PRO == GV_IN_NORM ? NV : 1];
+  uint32_t xw[PRO == GV_IN_NORM ? 1 : QW];
+  uint16_t xsw[PRO == GV_IN_NORM ? 1 : QS];
+  if constexpr (PRO == GV_IN_NORM) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int c4 = tid + j * TH;
+      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      gm[j] = v[j];
+      if (c4 < nvec) {
+        v[j] = reinterpret_cast<const float4*>(x)[c4];
+        gm[j] = reinterpret_cast<const float4*>(gamma)[c4];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < QW; ++j)
+      if (tid + j * TH < nvec) xw[j] = reinterpret_cast<const uint32_t*>(xq)[tid + j * TH];
+#pragma unroll
+    for (int j = 0; j < QS; ++j)
+      if (tid + j * TH < KB) xsw[j] = xs[tid + j * TH];
+  }
+
   constexpr int RS = RPW < 4 ? RPW : 4;  // rows of a wave whose loads are in flight together
   struct Buf {
     v4i wv[B][RS];
@@ -133,23 +164,19 @@ __global__ void __launch_bounds__(GV_THREADS, (RPW == 1 && EPI == GV_F32) ? 8 : 
       }
     }
   };
+  constexpr int STEP = 64 * B;  // chunks per load batch
+  // one row per wave: both batches before the prologue (with more rows per wave the second batch
+  // waits for the loop, which keeps the registers live across the prologue to 64)
+  constexpr bool PRE2 = RPW == 1;
   load_batch(buf0, blockIdx.x, 0, 0);
+  if constexpr (PRE2) load_batch(buf1, blockIdx.x, STEP, 0);
   if constexpr (EPI == GV_SWIGLU) exp2_table_fill(exp_tab, tid);
 
   // ---- the activation row -> LDS (codes, f64 scales)
-  const int nvec = K / 4;
-  if constexpr (PRO == GV_IN_NORM) {  // K <= GV_NORM_K: NV float4s of x per thread, kept across both passes
-    float4 v[GV_NV], g[GV_NV];
+  if constexpr (PRO == GV_IN_NORM) {
     double sq = 0.0;
 #pragma unroll
-    for (int j = 0; j < GV_NV; ++j) {
-      const int c4 = tid + j * GV_THREADS;
-      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      g[j] = v[j];
-      if (c4 < nvec) {
-        v[j] = reinterpret_cast<const float4*>(x)[c4];
-        g[j] = reinterpret_cast<const float4*>(gamma)[c4];
-      }
+    for (int j = 0; j < NV; ++j) {
       const double a = v[j].x, b = v[j].y, c = v[j].z, d = v[j].w;
       sq += a * a + b * b + c * c + d * d;
     }
@@ -157,22 +184,22 @@ __global__ void __launch_bounds__(GV_THREADS, (RPW == 1 && EPI == GV_F32) ? 8 : 
     if (lane == 0) red[wave] = ss;
     __syncthreads();
     if (wave == 0) {
-      double t = lane < GV_WAVES ? red[lane] : 0.0;
+      double t = lane < WAVES ? red[lane] : 0.0;
       t = wave_sum_d(t);
-      if (lane == 0) red[GV_WAVES] = t;
+      if (lane == 0) red[WAVES] = t;
     }
     __syncthreads();
-    const double inv_rms = recip_f64(sqrt(red[GV_WAVES] / (double)K + (double)eps));
+    const double inv_rms = recip_f64(sqrt(red[WAVES] / (double)K + (double)eps));
     // groups of 8 lanes cover one block; a group is entirely inside or outside [0, nvec)
 #pragma unroll
-    for (int j = 0; j < GV_NV; ++j) {
-      const int c4 = tid + j * GV_THREADS;
+    for (int j = 0; j < NV; ++j) {
+      const int c4 = tid + j * TH;
       if (c4 < nvec) {
         float4 o;
-        o.x = (float)((double)v[j].x * inv_rms * (double)g[j].x);
-        o.y = (float)((double)v[j].y * inv_rms * (double)g[j].y);
-        o.z = (float)((double)v[j].z * inv_rms * (double)g[j].z);
-        o.w = (float)((double)v[j].w * inv_rms * (double)g[j].w);
+        o.x = (float)((double)v[j].x * inv_rms * (double)gm[j].x);
+        o.y = (float)((double)v[j].y * inv_rms * (double)gm[j].y);
+        o.z = (float)((double)v[j].z * inv_rms * (double)gm[j].z);
+        o.w = (float)((double)v[j].w * inv_rms * (double)gm[j].w);
         float dq;
         const uint32_t qv = q8_block_quant4(o, dq);
         reinterpret_cast<uint32_t*>(a_codes)[c4] = qv;
@@ -180,9 +207,12 @@ __global__ void __launch_bounds__(GV_THREADS, (RPW == 1 && EPI == GV_F32) ? 8 : 
       }
     }
   } else {
-    for (int c4 = tid; c4 < nvec; c4 += GV_THREADS)
-      reinterpret_cast<uint32_t*>(a_codes)[c4] = reinterpret_cast<const uint32_t*>(xq)[c4];
-    for (int b = tid; b < KB; b += GV_THREADS) a_d[b] = (double)f16_bits_to_f32(xs[b]);
+#pragma unroll
+    for (int j = 0; j < QW; ++j)
+      if (tid + j * TH < nvec) reinterpret_cast<uint32_t*>(a_codes)[tid + j * TH] = xw[j];
+#pragma unroll
+    for (int j = 0; j < QS; ++j)
+      if (tid + j * TH < KB) a_d[tid + j * TH] = (double)f16_bits_to_f32(xsw[j]);
   }
   __syncthreads();
 
@@ -219,20 +249,21 @@ __global__ void __launch_bounds__(GV_THREADS, (RPW == 1 && EPI == GV_F32) ? 8 : 
         }
       }
     };
-    constexpr int STEP = 64 * B;
 #pragma unroll
     for (int ib = 0; ib < RPW; ib += RS) {
-      if (ib || grp != (int)blockIdx.x) load_batch(buf0, grp, 0, ib);
+      if (ib || grp != (int)blockIdx.x) {  // uniform; the first pass's batches went out before the prologue
+        load_batch(buf0, grp, 0, ib);
+        if constexpr (PRE2) load_batch(buf1, grp, STEP, ib);
+      }
+      if constexpr (!PRE2) load_batch(buf1, grp, STEP, ib);
 #pragma unroll 1
       for (int c0 = 0;; c0 += 2 * STEP) {
-        load_batch(buf1, grp, c0 + STEP, ib);
         step(buf0, c0, acc + ib);
-        if (c0 + 2 * STEP >= nchunk) {  // uniform
-          step(buf1, c0 + STEP, acc + ib);
-          break;
-        }
+        if (c0 + STEP >= nchunk) break;  // uniform
         load_batch(buf0, grp, c0 + 2 * STEP, ib);
         step(buf1, c0 + STEP, acc + ib);
+        if (c0 + 2 * STEP >= nchunk) break;
+        load_batch(buf1, grp, c0 + 3 * STEP, ib);
       }
     }
 #pragma unroll
@@ -279,18 +310,21 @@ int launch_gemv_q8(const GemvArgs& g, hipStream_t s) {
   const int KB = g.k / QK;
   const size_t lds = (size_t)((g.k + 15) & ~15) + sizeof(double) * KB + sizeof(float) * 130 +
                      sizeof(double) * (GV_WAVES + 1);
-  if (g.k % QK || g.k <= 0 || lds > 64 * 1024 || (norm && g.k > GV_NORM_K) ||
+  if (g.k % QK || g.k <= 0 || lds > 64 * 1024 || (norm && g.k > GV_NORM_K) || g.k > GV_MAX_K ||
       (int64_t)g.n * g.k >= ((int64_t)1 << 31))
-    return set_error(MI_ERR_UNSUPPORTED, "gemv: K %d (multiple of 32, LDS %zu bytes, <= %d with the norm)", g.k, lds,
-                     GV_NORM_K);
+    return set_error(MI_ERR_UNSUPPORTED, "gemv: K %d (multiple of 32, LDS %zu bytes, <= %d, <= %d with the norm)", g.k,
+                     lds, GV_MAX_K, GV_NORM_K);
   if (g.bias && g.epi != GV_F32) return set_error(MI_ERR_INVALID_ARG, "gemv: a bias needs the plain f32 epilogue");
   // enough workgroups to keep every CU busy, looping over row groups beyond that
   const int max_wg = GV_MAX_WG;
-  auto grid = [&](int rwg) { return dim3((unsigned)std::min((g.n + rwg - 1) / rwg, max_wg)); };
-#define GV_LAUNCH(RPW, EPI, NORM)                                                                          \
-  hipLaunchKernelGGL((k_gemv_q8<RPW, EPI, NORM>), grid(RPW * GV_WAVES), dim3(GV_THREADS), lds, s, g.x, g.gamma, \
-                     g.eps, g.xq, g.xs, g.k, g.w_codes, g.w_scales, g.n, g.bias, g.residual, g.out, g.q_codes,     \
+  auto grid = [&](int rwg, int th) {
+    return dim3((unsigned)std::min((g.n + rwg - 1) / rwg, (2048 / th) * 256));
+  };
+#define GV_LAUNCH_T(RPW, EPI, NORM, TH)                                                                           \
+  hipLaunchKernelGGL((k_gemv_q8<RPW, EPI, NORM, TH>), grid(RPW * (TH / 64), TH), dim3(TH), lds, s, g.x, g.gamma, \
+                     g.eps, g.xq, g.xs, g.k, g.w_codes, g.w_scales, g.n, g.bias, g.residual, g.out, g.q_codes,      \
                      g.q_scales)
+#define GV_LAUNCH(RPW, EPI, NORM) GV_LAUNCH_T(RPW, EPI, NORM, GV_THREADS)
   switch (g.epi) {
     case GV_RES:
     case GV_F32: {
@@ -316,6 +350,7 @@ int launch_gemv_q8(const GemvArgs& g, hipStream_t s) {
       return set_error(MI_ERR_INVALID_ARG, "gemv: epilogue %d", g.epi);
   }
 #undef GV_LAUNCH
+#undef GV_LAUNCH_T
   MI_LAUNCH_CHECK("k_gemv_q8");
   return MI_OK;
 }
@@ -380,214 +415,286 @@ int launch_qkv_finish(float* qkv, const int32_t* pos_dev, const double* rope, in
 }
 
 // ---------------------------------------------------------------- single-query attention
-constexpr int AD_THREADS = 256;  // 4 waves; a wave takes 64 keys of its range per step
+constexpr int AD_THREADS = 512;  // 8 waves
+constexpr int AD_KEYS = 64;      // keys of a sub-chunk: 8 lanes per key in the score step
+constexpr int AD_HB = 4;         // query heads of a head block
 
-// Keys 0..pos of head h are split into ranges of keys_per_range; workgroup (h, r) takes range r
-// and writes its partial state to part[(h * n_range + r) * (HD + 2)] = m, l, o[HD] (f64): m the
-// range's largest score, l = sum e^(s - m), o = sum e^(s - m) v, with s = (q * 1/sqrt(hd)) . k as
-// in the prefill kernel.  Ranges past pos write nothing.  The output projection merges the ranges.
-//
-// A wave takes 64-key tiles.  Scores: lane <-> key, the dot product in four independent f64 chains.
-// Weighted sum: each V load instruction brings KG keys x all HD dims as float4s (lane <-> key group
-// kg, dim quad), so a lane accumulates 4 dims over the keys kg, kg + KG, ... of the tile in four
-// chains; the key groups and the waves are summed in the final merge through LDS (fixed order).
-template <int HD>
+// The query heads of KV head g share every K and V row they read, so a workgroup takes one KV head's
+// block of up to AD_HB query heads (GP, the block size rounded up to a power of two; heads past the
+// group get a zero query and are never written) over one range of keys, in sub-chunks of 64 keys:
+//   scores   lanes 8 * kk + pp share key kk, lane pp reading 16 bytes at offset 128 * i + 16 * pp of
+//            the row (every K load instruction reads 8 whole 128-byte lines); each lane converts its
+//            slice of the key once and forms the partial dot products of the GP heads (queries,
+//            scaled by 1/sqrt(hd) in f64, from LDS); exchange-and-add steps over the 8 lanes, each
+//            halving the heads a lane carries while GP allows, leave the full scores in LDS;
+//   softmax  wave w keeps head w's running max and sum (f64), lane <-> key;
+//   weights  thread (d, kp) accumulates dim d of every head over key part kp, V read as dwords
+//            (64 consecutive dims of a row per instruction); the parts are summed in order at the end.
+// K and V of a sub-chunk are requested together, before any of its arithmetic.  Workgroup (g, hb, r)
+// writes part[(h * n_range + r) * (HD + 2)] = m, l, o[HD] (f64) for its heads h: m the range's
+// largest score, l = sum e^(s - m), o = sum e^(s - m) v.  Ranges past pos write nothing.
+template <int HD, int GP>
 __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restrict__ q,
                                                             const float* __restrict__ k_region,
                                                             const float* __restrict__ v_region,
                                                             const int32_t* __restrict__ pos_dev, int n_head,
                                                             int n_head_kv, int keys_per_range,
                                                             double* __restrict__ part) {
-  constexpr int NW = AD_THREADS / 64;
-  constexpr int DQ = HD / 4;        // dim quads
-  constexpr int KG = 64 / DQ;       // keys per V load instruction: 4 (HD 64), 2 (HD 128)
-  constexpr int VI = 64 / KG;       // V load instructions per 64-key tile
-  constexpr bool V_EARLY = HD == 64;  // V requested together with K (registers allow it)
-  // wave-private LDS: the query (f64, scaled), the e^x table and the tile's weights, so no wave
-  // waits for another before the final merge (a wave's own LDS accesses complete in order)
-  __shared__ double qs[NW][HD];
-  __shared__ double etab[NW][64];
-  __shared__ double pw[NW][64];
-  __shared__ double wst[NW][KG][HD];
-  __shared__ double wml[NW][2];
-  const int h = blockIdx.x, r = blockIdx.y, n_range = gridDim.y;
+  constexpr int NI = HD / 32;              // K float4s per lane and key (8 lanes x NI x 16 B = one row)
+  constexpr int KP = AD_THREADS / HD;      // key parts of the weighted sum: 4 (HD 128), 8 (HD 64)
+  constexpr int KPP = AD_KEYS / KP;        // keys per part: 16 (HD 128), 8 (HD 64)
+  constexpr int LG = GP == 8 ? 3 : GP == 4 ? 2 : GP == 2 ? 1 : 0;  // halving steps
+  __shared__ double qs[GP][HD];
+  __shared__ double sc[GP][AD_KEYS];  // scores, then weights, of the sub-chunk
+  __shared__ double rs[GP];           // each head's rescale factor for the sub-chunk
+  __shared__ double etab[64];
+  __shared__ double red[KP - 1][GP][HD];
+  const int G = n_head / n_head_kv, n_hb = (G + AD_HB - 1) / AD_HB;
+  const int g = blockIdx.x / n_hb, hb = blockIdx.x % n_hb, r = blockIdx.y, n_range = gridDim.y;
+  const int h0 = g * G + hb * AD_HB, nh = min(GP, G - hb * AD_HB);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = h / (n_head / n_head_kv);
   const int n_kv = n_head_kv * HD;
   const int n_keys = *pos_dev + 1;
   const int j0 = r * keys_per_range, j1 = min(j0 + keys_per_range, n_keys);
   if (j0 >= j1) return;  // uniform for the workgroup
-  const int kg = lane / DQ, dq = lane % DQ;
-  const float* kbase = k_region + g * HD;
-  const float* vbase = v_region + g * HD + 4 * dq;
-  double* qw = qs[wave];
-  const double* tab = etab[wave];
-  exp2_table_fill(etab[wave], lane);
-  double m_w = -1e300, l_w = 0.0, o[4] = {0.0, 0.0, 0.0, 0.0};
-  const int t_first = j0 + 64 * wave;
-  for (int t0 = t_first; t0 < j1; t0 += 64 * NW) {
-    const int nk = min(64, j1 - t0);
-    // rows past the tile's keys re-read its last key (their weights are 0; the row is one this call
-    // or an earlier one wrote)
-    float4 kreg[DQ];
-    {
-      const float4* kr = reinterpret_cast<const float4*>(kbase + (int64_t)(t0 + min(lane, nk - 1)) * n_kv);
+  const int kk = tid >> 3, pp = tid & 7;  // scores: key kk of the sub-chunk, dim slice pp
+  const int d = tid % HD, kp = tid / HD;  // weighted sum: dim d over the keys of part kp
+  // 32-bit element offsets from the uniform region bases (n_ctx * n_kv < 2^31 is checked by the host)
+  const uint32_t k_off = (uint32_t)(g * HD + 4 * pp), v_off = (uint32_t)(g * HD + d);
+  float4 kv4[NI];
+  float vv[KPP];
+  auto load = [&](int t0, int nk) {
+    const uint32_t kr = (uint32_t)(t0 + min(kk, nk - 1)) * (uint32_t)n_kv + k_off;
 #pragma unroll
-      for (int d4 = 0; d4 < DQ; ++d4) kreg[d4] = kr[d4];
-    }
-    float4 vreg[VI];
-    auto load_v = [&]() {
+    for (int i = 0; i < NI; ++i) kv4[i] = *reinterpret_cast<const float4*>(k_region + kr + 32 * i);
+    // keys past the sub-chunk's end re-read its last key (their weights are 0)
 #pragma unroll
-      for (int i = 0; i < VI; ++i)
-        vreg[i] = *reinterpret_cast<const float4*>(vbase + (int64_t)(t0 + min(KG * i + kg, nk - 1)) * n_kv);
-    };
-    if constexpr (V_EARLY) load_v();
-    if (t0 == t_first) {  // the query, scaled by 1/sqrt(hd) in f64, while the loads are in flight
+    for (int j = 0; j < KPP; ++j) vv[j] = v_region[(uint32_t)(t0 + min(kp * KPP + j, nk - 1)) * (uint32_t)n_kv + v_off];
+  };
+  double m_w = -1e300, l_w = 0.0;  // wave w: head w's running max and sum
+  double o[GP];
+#pragma unroll
+  for (int hh = 0; hh < GP; ++hh) o[hh] = 0.0;
+  for (int t0 = j0; t0 < j1; t0 += AD_KEYS) {
+    const int nk = min(AD_KEYS, j1 - t0);
+    load(t0, nk);
+    if (t0 == j0) {  // while the first sub-chunk's loads are in flight
+      if (tid < 64) exp2_table_fill(etab, tid);
       const double scale = 1.0 / sqrt((double)HD);
-      for (int i = lane; i < HD; i += 64) qw[i] = (double)q[h * HD + i] * scale;
+      for (int i = tid; i < GP * HD; i += AD_THREADS) {
+        const int hh = i / HD;
+        qs[hh][i % HD] = hh < nh ? (double)q[(int64_t)(h0 + hh) * HD + i % HD] * scale : 0.0;
+      }
     }
-    double a[4] = {0.0, 0.0, 0.0, 0.0};
+    __syncthreads();  // the queries; after the first sub-chunk, sc and rs consumed
+    // ---- scores
+    double kd[4 * NI];
 #pragma unroll
-    for (int d4 = 0; d4 < DQ; ++d4) {
-      const double2 q01 = *reinterpret_cast<const double2*>(&qw[4 * d4]);
-      const double2 q23 = *reinterpret_cast<const double2*>(&qw[4 * d4 + 2]);
-      a[0] = fma(q01.x, (double)kreg[d4].x, a[0]);
-      a[1] = fma(q01.y, (double)kreg[d4].y, a[1]);
-      a[2] = fma(q23.x, (double)kreg[d4].z, a[2]);
-      a[3] = fma(q23.y, (double)kreg[d4].w, a[3]);
+    for (int i = 0; i < NI; ++i) {
+      kd[4 * i] = kv4[i].x;
+      kd[4 * i + 1] = kv4[i].y;
+      kd[4 * i + 2] = kv4[i].z;
+      kd[4 * i + 3] = kv4[i].w;
     }
-    if constexpr (!V_EARLY) {
-      asm volatile("" ::: "memory");  // the V loads reuse the K registers: issued after the scores
-      load_v();
+    // two heads at a time: their query slices are read from LDS just before use (the compiler
+    // barrier keeps it from hoisting every head's reads, which would need 4 * NI * GP registers)
+    constexpr int HS = GP < 2 ? GP : 2;
+    double ps[GP];
+#pragma unroll
+    for (int h2 = 0; h2 < GP; h2 += HS) {
+      asm volatile("" ::: "memory");
+      double a0[HS], a1[HS];
+#pragma unroll
+      for (int e = 0; e < HS; ++e) a0[e] = a1[e] = 0.0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+#pragma unroll
+        for (int e = 0; e < HS; ++e) {
+          const double2 q01 = *reinterpret_cast<const double2*>(&qs[h2 + e][32 * i + 4 * pp]);
+          const double2 q23 = *reinterpret_cast<const double2*>(&qs[h2 + e][32 * i + 4 * pp + 2]);
+          a0[e] = fma(q01.x, kd[4 * i], a0[e]);
+          a1[e] = fma(q01.y, kd[4 * i + 1], a1[e]);
+          a0[e] = fma(q23.x, kd[4 * i + 2], a0[e]);
+          a1[e] = fma(q23.y, kd[4 * i + 3], a1[e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < HS; ++e) ps[h2 + e] = a0[e] + a1[e];
     }
-    const double s = lane < nk ? (a[0] + a[1]) + (a[2] + a[3]) : -1e300;
-    const double m_new = fmax(m_w, wave_reduce_f64<true>(s));
-    const double p = lane < nk ? exp_f64(s - m_new, tab) : 0.0;
-    const double resc = exp_f64(m_w - m_new, tab);  // 0 for the first tile (m_w = -1e300)
-    l_w = l_w * resc + wave_reduce_f64<false>(p);
+    // over the 8 lanes of the key, partners lane 7 - pp (bit 2 of pp flips), pp ^ 2 (bit 1), pp ^ 1
+    // (bit 0): while a lane carries more than one head, each step keeps half of them (the half the
+    // partner does not keep) and adds the partner's sums of that half; then the steps just add
+    if constexpr (GP >= 2) {
+      const bool hi = pp & 4;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) o[c] *= resc;
-    m_w = m_new;
-    pw[wave][lane] = p;
+      for (int j = 0; j < GP / 2; ++j)
+        ps[j] = (hi ? ps[j + GP / 2] : ps[j]) + dpp_f64<DPP_HALF_MIRROR>(hi ? ps[j] : ps[j + GP / 2]);
+    } else {
+      ps[0] += dpp_f64<DPP_HALF_MIRROR>(ps[0]);
+    }
+    if constexpr (GP >= 4) {
+      const bool hi = pp & 2;
 #pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const double pk = pw[wave][KG * i + kg];
-      o[0] = fma(pk, (double)vreg[i].x, o[0]);
-      o[1] = fma(pk, (double)vreg[i].y, o[1]);
-      o[2] = fma(pk, (double)vreg[i].z, o[2]);
-      o[3] = fma(pk, (double)vreg[i].w, o[3]);
+      for (int j = 0; j < GP / 4; ++j)
+        ps[j] = (hi ? ps[j + GP / 4] : ps[j]) + dpp_f64<DPP_XOR2>(hi ? ps[j] : ps[j + GP / 4]);
+    } else {
+      ps[0] += dpp_f64<DPP_XOR2>(ps[0]);
+    }
+    if constexpr (GP >= 8) {
+      const bool hi = pp & 1;
+      ps[0] = (hi ? ps[1] : ps[0]) + dpp_f64<DPP_XOR1>(hi ? ps[0] : ps[1]);
+    } else {
+      ps[0] += dpp_f64<DPP_XOR1>(ps[0]);
+    }
+    // lane pp now holds the score of head pp >> (3 - LG); one lane of each head writes it
+    if ((pp & ((8 >> LG) - 1)) == 0) sc[pp >> (3 - LG)][kk] = kk < nk ? ps[0] : -1e300;
+    __syncthreads();
+    // ---- softmax: wave w, head w
+    if (wave < GP) {
+      const double s = sc[wave][lane];
+      const double m_new = fmax(m_w, wave_reduce_f64<true>(s));
+      const double p = lane < nk ? exp_f64(s - m_new, etab) : 0.0;
+      const double resc = exp_f64(m_w - m_new, etab);  // 0 for the first sub-chunk (m_w = -1e300)
+      l_w = l_w * resc + wave_reduce_f64<false>(p);
+      m_w = m_new;
+      sc[wave][lane] = p;
+      if (lane == 0) rs[wave] = resc;
+    }
+    __syncthreads();
+    // ---- weighted sum
+#pragma unroll
+    for (int hh = 0; hh < GP; ++hh) o[hh] *= rs[hh];
+#pragma unroll
+    for (int j = 0; j < KPP; j += 2) {
+      if (j % 4 == 0) asm volatile("" ::: "memory");  // weights read 4 keys at a time (registers)
+      const double v0 = vv[j], v1 = vv[j + 1];
+#pragma unroll
+      for (int hh = 0; hh < GP; ++hh) {
+        const double2 pk = *reinterpret_cast<const double2*>(&sc[hh][kp * KPP + j]);
+        o[hh] = fma(pk.x, v0, o[hh]);
+        o[hh] = fma(pk.y, v1, o[hh]);
+      }
     }
   }
-  // merge the waves and key groups (fixed order)
+  // ---- the key parts, summed in order; m and l from the head's wave
+  if (kp > 0) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) wst[wave][kg][4 * dq + c] = o[c];
-  if (lane == 0) {
-    wml[wave][0] = m_w;
-    wml[wave][1] = l_w;
+    for (int hh = 0; hh < GP; ++hh) red[kp - 1][hh][d] = o[hh];
+  }
+  if (wave < nh && lane == 0) {
+    double* out = part + ((int64_t)(h0 + wave) * n_range + r) * (HD + 2);
+    out[0] = m_w;
+    out[1] = l_w;
   }
   __syncthreads();
-  if (wave == 0) {
-    double m = -1e300;
+  if (kp == 0) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) m = fmax(m, wml[w][0]);
-    double f[NW], l = 0.0;
+    for (int hh = 0; hh < GP; ++hh) {
+      if (hh < nh) {
+        double od = o[hh];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      f[w] = exp_f64(wml[w][0] - m, tab);
-      l = fma(wml[w][1], f[w], l);
-    }
-    double* out = part + ((int64_t)h * n_range + r) * (HD + 2);
-    if (lane == 0) {
-      out[0] = m;
-      out[1] = l;
-    }
-#pragma unroll
-    for (int k = 0; k < HD / 64; ++k) {
-      const int d = lane + 64 * k;
-      double od = 0.0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        double ow = 0.0;
-#pragma unroll
-        for (int gg = 0; gg < KG; ++gg) ow += wst[w][gg][d];
-        od = fma(ow, f[w], od);
+        for (int k = 0; k < KP - 1; ++k) od += red[k][hh][d];
+        part[((int64_t)(h0 + hh) * n_range + r) * (HD + 2) + 2 + d] = od;
       }
-      out[2 + d] = od;
     }
   }
 }
 
-// Merge head h's n_ne ranges in order, normalize, round to f32 and Q8_0 (one wave; lane holds dims
-// 4*lane..4*lane+3, HD/4 lanes = whole groups of 8 per block).
+// Merge head h's n_ne ranges, normalize, round to f32 and Q8_0: workgroup h, thread t takes dims
+// 4 * dq .. 4 * dq + 3 (dq = t % (HD / 4)) over the ranges rs, rs + RSETS, ... (rs = t / (HD / 4)),
+// every one of its partial rows requested at once; wave 0 meanwhile forms the weights e^(m_r - m)
+// (one range per lane).  The range sets are then added in order through LDS, and the first HD / 4
+// lanes quantize the row (8 lanes per Q8_0 block).
+constexpr int AM_THREADS = 256;
+
 template <int HD>
-__device__ __forceinline__ void attn_merge_head(const double* __restrict__ part, int n_range, int n_ne, int h, int lane,
-                                                const double* exp_tab, int8_t* a_codes, uint16_t* a_scales) {
+__global__ void __launch_bounds__(AM_THREADS) k_attn_merge(const double* __restrict__ part, int n_range,
+                                                           int keys_per_range, const int32_t* __restrict__ pos_dev,
+                                                           int8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+  constexpr int DQN = HD / 4;                   // dim quads
+  constexpr int RSETS = AM_THREADS / DQN;       // range sets: 8 (HD 128), 16 (HD 64)
+  constexpr int RPS = AD_MAX_RANGES / RSETS;    // ranges per set at most
+  __shared__ double exp_tab[64];
+  __shared__ double fw[AD_MAX_RANGES];          // e^(m_r - m)
+  __shared__ double l_sh;
+  __shared__ double4 red[RSETS - 1][DQN];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int dq = tid % DQN, rs = tid / DQN;
+  const int n_ne = (*pos_dev + keys_per_range) / keys_per_range;  // ranges holding keys 0..pos
   const double* ph = part + (int64_t)h * n_range * (HD + 2);
-  double mr = -1e300, lr = 0.0;
-  if (lane < n_ne) {  // one range per lane (n_ne <= AD_MAX_RANGES <= 64)
-    mr = ph[lane * (HD + 2)];
-    lr = ph[lane * (HD + 2) + 1];
-  }
-  const double m = wave_max_d(mr);
-  const double f_own = lane < n_ne ? exp_f64(mr - m, exp_tab) : 0.0;
-  const double l = wave_sum_d(lr * f_own);
-  // every range's partial output requested at once (they do not depend on the max), then summed
-  // in range order
-  double2 po[AD_MAX_RANGES][2];
+  double2 po[RPS][2];
 #pragma unroll
-  for (int rr = 0; rr < AD_MAX_RANGES; ++rr) {
-    const int r = rr < n_ne ? rr : 0;  // ranges past n_ne re-read range 0 (unused)
-    const double2* src = reinterpret_cast<const double2*>(ph + r * (HD + 2) + 2) + 2 * (lane & (HD / 4 - 1));
-    po[rr][0] = src[0];
-    po[rr][1] = src[1];
+  for (int i = 0; i < RPS; ++i) {
+    const int r = min(rs + RSETS * i, n_ne - 1);  // ranges past n_ne re-read the last one (unused)
+    const double2* src = reinterpret_cast<const double2*>(ph + r * (HD + 2) + 2) + 2 * dq;
+    po[i][0] = src[0];
+    po[i][1] = src[1];
   }
+  exp2_table_fill(exp_tab, tid);
+  __syncthreads();
+  if (tid < 64) {
+    double mr = -1e300, lr = 0.0;
+    if (lane < n_ne) {  // one range per lane (n_ne <= AD_MAX_RANGES <= 64)
+      mr = ph[lane * (HD + 2)];
+      lr = ph[lane * (HD + 2) + 1];
+    }
+    const double m = wave_max_d(mr);
+    const double f = lane < n_ne ? exp_f64(mr - m, exp_tab) : 0.0;
+    fw[lane] = f;
+    const double l = wave_sum_d(lr * f);
+    if (lane == 0) l_sh = l;
+  }
+  __syncthreads();
   double o[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int rr = 0; rr < AD_MAX_RANGES; ++rr) {
-    if (rr < n_ne) {  // uniform
-      const double f = lane_f64(f_own, rr);
-      o[0] = fma(po[rr][0].x, f, o[0]);
-      o[1] = fma(po[rr][0].y, f, o[1]);
-      o[2] = fma(po[rr][1].x, f, o[2]);
-      o[3] = fma(po[rr][1].y, f, o[3]);
+  for (int i = 0; i < RPS; ++i) {
+    const int r = rs + RSETS * i;
+    if (r < n_ne) {
+      const double f = fw[r];
+      o[0] = fma(po[i][0].x, f, o[0]);
+      o[1] = fma(po[i][0].y, f, o[1]);
+      o[2] = fma(po[i][1].x, f, o[2]);
+      o[3] = fma(po[i][1].y, f, o[3]);
     }
   }
-  const double inv = recip_f64(l);
-  if (lane < HD / 4) {
-    float4 v;
-    v.x = (float)(o[0] * inv);
-    v.y = (float)(o[1] * inv);
-    v.z = (float)(o[2] * inv);
-    v.w = (float)(o[3] * inv);
-    float d;
-    const uint32_t qv = q8_block_quant4(v, d);
-    reinterpret_cast<uint32_t*>(a_codes + h * HD)[lane] = qv;
-    if ((lane & 7) == 0) a_scales[h * (HD / QK) + lane / 8] = f32_to_f16_bits(d);
-  }
-}
-
-// The output projection's input row: wave w of workgroup b merges head 4b + w.
-template <int HD>
-__global__ void __launch_bounds__(256) k_attn_merge(const double* __restrict__ part, int n_range, int keys_per_range,
-                                                    const int32_t* __restrict__ pos_dev, int n_head,
-                                                    int8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
-  __shared__ double exp_tab[64];
-  exp2_table_fill(exp_tab, threadIdx.x);
+  if (rs > 0) red[rs - 1][dq] = make_double4(o[0], o[1], o[2], o[3]);
   __syncthreads();
-  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int n_ne = (*pos_dev + keys_per_range) / keys_per_range;  // ranges holding keys 0..pos
-  if (h < n_head) attn_merge_head<HD>(part, n_range, n_ne, h, threadIdx.x & 63, exp_tab, codes, scales);
+  if (tid < 64) {  // wave 0: lanes 0..DQN-1 hold the row (whole groups of 8 lanes per block)
+    if (rs == 0) {
+#pragma unroll
+      for (int k = 0; k < RSETS - 1; ++k) {
+        const double4 v = red[k][dq];
+        o[0] += v.x;
+        o[1] += v.y;
+        o[2] += v.z;
+        o[3] += v.w;
+      }
+    }
+    const double inv = recip_f64(l_sh);
+    if (lane < DQN) {
+      float4 v;
+      v.x = (float)(o[0] * inv);
+      v.y = (float)(o[1] * inv);
+      v.z = (float)(o[2] * inv);
+      v.w = (float)(o[3] * inv);
+      float d;
+      const uint32_t qv = q8_block_quant4(v, d);
+      reinterpret_cast<uint32_t*>(codes + h * HD)[lane] = qv;
+      if ((lane & 7) == 0) scales[h * (HD / QK) + lane / 8] = f32_to_f16_bits(d);
+    }
+  }
 }
 
 int launch_attn_merge(const double* part, int n_ctx, const int32_t* pos_dev, int n_head, int head_dim, int8_t* codes,
                       uint16_t* scales, hipStream_t s) {
   int kpr = 0;
   const int n_range = attn_decode_ranges(n_ctx, &kpr);
-  const dim3 grid((n_head + 3) / 4);
   if (head_dim == 64)
-    hipLaunchKernelGGL(k_attn_merge<64>, grid, dim3(256), 0, s, part, n_range, kpr, pos_dev, n_head, codes, scales);
+    hipLaunchKernelGGL(k_attn_merge<64>, dim3(n_head), dim3(AM_THREADS), 0, s, part, n_range, kpr, pos_dev, codes,
+                       scales);
   else if (head_dim == 128)
-    hipLaunchKernelGGL(k_attn_merge<128>, grid, dim3(256), 0, s, part, n_range, kpr, pos_dev, n_head, codes, scales);
+    hipLaunchKernelGGL(k_attn_merge<128>, dim3(n_head), dim3(AM_THREADS), 0, s, part, n_range, kpr, pos_dev, codes,
+                       scales);
   else
     return set_error(MI_ERR_UNSUPPORTED, "attention merge: head_dim %d", head_dim);
   MI_LAUNCH_CHECK("k_attn_merge");
@@ -595,22 +702,33 @@ int launch_attn_merge(const double* part, int n_ctx, const int32_t* pos_dev, int
 }
 
 int attn_decode_ranges(int n_ctx, int* keys_per_range) {
-  int kpr = 256;  // one 64-key tile per wave
+  int kpr = AD_KEYS;  // one sub-chunk per workgroup up to 64 ranges, then longer ranges
   while ((n_ctx + kpr - 1) / kpr > AD_MAX_RANGES) kpr *= 2;
   *keys_per_range = kpr;
   return (n_ctx + kpr - 1) / kpr;
+}
+
+template <int HD>
+static void launch_attn_decode_hd(int gp, dim3 grid, hipStream_t s, const float* q, const float* k_region,
+                                  const float* v_region, const int32_t* pos_dev, int n_head, int n_head_kv, int kpr,
+                                  double* part) {
+  auto k = gp == 8 ? k_attn_decode<HD, 8> : gp == 4 ? k_attn_decode<HD, 4> : gp == 2 ? k_attn_decode<HD, 2>
+                                                                                     : k_attn_decode<HD, 1>;
+  hipLaunchKernelGGL(k, grid, dim3(AD_THREADS), 0, s, q, k_region, v_region, pos_dev, n_head, n_head_kv, kpr, part);
 }
 
 int launch_attn_decode(const float* q, const float* k_region, const float* v_region, const int32_t* pos_dev,
                        int n_ctx, int n_head, int n_head_kv, int head_dim, double* part, hipStream_t s) {
   int kpr = 0;
   const int n_range = attn_decode_ranges(n_ctx, &kpr);
+  const int G = n_head / n_head_kv, n_hb = (G + AD_HB - 1) / AD_HB;
+  int gp = 1;  // the head block, rounded up to a power of two
+  while (gp < G && gp < AD_HB) gp *= 2;
+  const dim3 grid(n_head_kv * n_hb, n_range);
   if (head_dim == 64)
-    hipLaunchKernelGGL(k_attn_decode<64>, dim3(n_head, n_range), dim3(AD_THREADS), 0, s, q, k_region, v_region,
-                       pos_dev, n_head, n_head_kv, kpr, part);
+    launch_attn_decode_hd<64>(gp, grid, s, q, k_region, v_region, pos_dev, n_head, n_head_kv, kpr, part);
   else if (head_dim == 128)
-    hipLaunchKernelGGL(k_attn_decode<128>, dim3(n_head, n_range), dim3(AD_THREADS), 0, s, q, k_region, v_region,
-                       pos_dev, n_head, n_head_kv, kpr, part);
+    launch_attn_decode_hd<128>(gp, grid, s, q, k_region, v_region, pos_dev, n_head, n_head_kv, kpr, part);
   else
     return set_error(MI_ERR_UNSUPPORTED, "attention decode: head_dim %d", head_dim);
   MI_LAUNCH_CHECK("k_attn_decode");

@@ -65,11 +65,20 @@ TINY_WIDE = synth.ModelConfig(name="tiny_wide_heads", n_layers=2, hidden=256, n_
                               ffn=384, vocab=1000, n_tokens=24, n_ctx=64, seed=19, qkv_bias=True, tied=False)
 
 
-@pytest.mark.parametrize("cfg", [synth.LAYER1, TINY_Q3, TINY_Q2, TINY_WIDE], ids=lambda c: c.name)
+# one query head per KV head, and 12 per KV head (two head blocks, the second one partly filled)
+TINY_MHA = synth.ModelConfig(name="tiny_mha", n_layers=2, hidden=128, n_head=4, n_head_kv=4, head_dim=64,
+                             ffn=256, vocab=1000, n_tokens=20, n_ctx=80, seed=23, qkv_bias=True, tied=True)
+TINY_G12 = synth.ModelConfig(name="tiny_gqa12", n_layers=2, hidden=256, n_head=24, n_head_kv=2, head_dim=128,
+                             ffn=384, vocab=1000, n_tokens=20, n_ctx=80, seed=29, qkv_bias=False, qk_norm=True,
+                             tied=False)
+
+
+@pytest.mark.parametrize("cfg", [synth.LAYER1, TINY_Q3, TINY_Q2, TINY_WIDE, TINY_MHA, TINY_G12],
+                         ids=lambda c: c.name)
 def test_decode_matches_oracle(cfg):
-    """Head dims 64 and 128, QKV bias, per-head QK norm, tied and separate lm_heads, GQA 7:1, 4:1
-    and 4:1 with one KV head, an attention row wider than the hidden size (40 x 128 over 256);
-    several steps, each attending to the prompt and the earlier steps."""
+    """Head dims 64 and 128, QKV bias, per-head QK norm, tied and separate lm_heads, GQA 7:1, 4:1,
+    4:1 with one KV head, 5:1, 1:1 and 12:1, an attention row wider than the hidden size (40 x 128
+    over 256); several steps, each attending to the prompt and the earlier steps."""
     dev = need_gpu()
     m, steps, kk, vv, end = prefill_then_decode(cfg, dev, 4)
     for i, (got, want) in enumerate(steps):
