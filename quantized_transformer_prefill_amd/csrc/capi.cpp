@@ -507,8 +507,8 @@ static int stage_tokens(mi_stage* st, const Ws& w, const int32_t* ids, const int
 
 // The decode step: one token through the same layers and regions, with the one-row kernels
 // (decode.hip).  Per layer: Q|K|V matrix-vector product with the attention RMSNorm in its prologue
-// and the bias in its epilogue; QK norm, RoPE and the K/V store per head; single-query attention
-// over ranges of keys 0..pos; the ranges merged into a Q8_0 row; output projection + residual;
+// and the bias in its epilogue; single-query attention over ranges of keys 0..pos, which also applies
+// the QK norm and RoPE and stores the new K/V rows; the ranges merged into a Q8_0 row; output projection + residual;
 // gate|up with the ffn RMSNorm in its prologue and SwiGLU + Q8_0 in its epilogue; down projection
 // + residual.  Then the lm_head with the final RMSNorm in its prologue.
 static int enqueue_decode(const mi_model* md, const Ws& w, int32_t n_ctx, const mi_kv_regions* kv, float* logits_out,
@@ -526,12 +526,9 @@ static int enqueue_decode(const mi_model* md, const Ws& w, int32_t n_ctx, const 
     g.w_codes = L.wqkv.codes; g.w_scales = L.wqkv.scales; g.n = nqkv;
     g.bias = hp.qkv_bias ? L.bqkv : nullptr; g.out = w.qkv; g.epi = GV_F32;
     if ((rc = launch_gemv_q8(g, s))) return rc;
-    if ((rc = launch_qkv_finish(w.qkv, w.pos, md->rope_table, hp.n_head, hp.n_head_kv, hp.head_dim,
-                                hp.qk_norm ? L.q_norm : nullptr, hp.qk_norm ? L.k_norm : nullptr, eps, kv->k[l],
-                                kv->v[l], s)))
-      return rc;
+    const AttnFinish fin{md->rope_table, hp.qk_norm ? L.q_norm : nullptr, hp.qk_norm ? L.k_norm : nullptr, eps};
     if ((rc = launch_attn_decode(w.qkv, kv->k[l], kv->v[l], w.pos, n_ctx, hp.n_head, hp.n_head_kv, hp.head_dim,
-                                 w.attn_part, s)))
+                                 w.attn_part, &fin, s)))
       return rc;
     if ((rc = launch_attn_merge(w.attn_part, n_ctx, w.pos, hp.n_head, hp.head_dim, w.xq, w.xs, s))) return rc;
     GemvArgs go{};  // input: the merged attention row
@@ -600,7 +597,7 @@ static int enqueue_forward(const mi_model* md, const Ws& w, int32_t n_tokens, in
       // layer's RMSNorm.
       const int32_t* pos1 = w.pos + (nt - 1);
       if ((rc = launch_attn_decode(q + (size_t)(nt - 1) * nqkv, kv->k[l], kv->v[l], pos1, n_ctx, hp.n_head,
-                                   hp.n_head_kv, hp.head_dim, w.attn_part, s)))
+                                   hp.n_head_kv, hp.head_dim, w.attn_part, nullptr, s)))
         return rc;
       if ((rc = launch_attn_merge(w.attn_part, n_ctx, pos1, hp.n_head, hp.head_dim, w.xq, w.xs, s))) return rc;
       GemvArgs go{};

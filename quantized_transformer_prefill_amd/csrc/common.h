@@ -256,15 +256,19 @@ int launch_gemv_q8(const GemvArgs& g, hipStream_t s);
 // (n_head * n_range * (head_dim + 2) f64, n_range <= AD_MAX_RANGES), merged by launch_attn_merge
 constexpr int AD_MAX_RANGES = 64;
 int attn_decode_ranges(int n_ctx, int* keys_per_range);
-int launch_attn_decode(const float* q, const float* k_region, const float* v_region, const int32_t* pos_dev,
-                       int n_ctx, int n_head, int n_head_kv, int head_dim, double* part, hipStream_t s);
+// With `fin` (the decode step), q is the raw Q|K|V row: the per-head QK norm and RoPE at *pos_dev are
+// applied in the kernel, and the new K and V rows are stored at row *pos_dev of the regions.
+// Without it, q holds finished queries and the regions hold row *pos_dev already.
+struct AttnFinish {
+  const double* rope;  // [rows][head_dim / 2] (cos, sin)
+  const float* q_norm; const float* k_norm;  // per-head RMSNorm weights, or null
+  float eps;
+};
+int launch_attn_decode(const float* q, float* k_region, float* v_region, const int32_t* pos_dev, int n_ctx,
+                       int n_head, int n_head_kv, int head_dim, double* part, const AttnFinish* fin, hipStream_t s);
 // the ranges of `part` merged per head, normalized and quantized: the Q8_0 row [n_head * head_dim]
 int launch_attn_merge(const double* part, int n_ctx, const int32_t* pos_dev, int n_head, int head_dim, int8_t* codes,
                       uint16_t* scales, hipStream_t s);
-// one token's Q|K|V row (bias added) -> [QK norm], RoPE at *pos_dev; Q in place, K and V rows stored
-int launch_qkv_finish(float* qkv, const int32_t* pos_dev, const double* rope, int n_head, int n_head_kv,
-                      int head_dim, const float* q_norm, const float* k_norm, float eps, float* k_region,
-                      float* v_region, hipStream_t s);
 
 // ---- sampler (sampler.hip)
 size_t sampler_workspace_bytes();

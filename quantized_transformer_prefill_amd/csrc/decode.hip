@@ -19,13 +19,13 @@
 //    gate and 32 up rows, i.e. one Q8_0 block of the SwiGLU output).  Every epilogue is per row,
 //    so a workgroup takes 16 or 64 rows and even the small matrices spread over the chip.
 //
-// k_qkv_finish: the per-head steps after the Q|K|V rows (per-head QK RMSNorm, NeoX RoPE at the
-// position, the K and V rows stored in the regions), one single-wave workgroup per head.
-//
 // k_attn_decode: the query's keys 0..pos are split into fixed ranges (the grid depends only on
 // n_ctx, so the launch can be captured once and replayed for any position); each workgroup
 // computes the partial softmax states (max, sum, unnormalized output) of the query heads of one KV
-// head (up to 8 of them) over one range in f64, reading each K and V row once for all of them.
+// head (up to 4 of them) over one range in f64, reading each K and V row once for all of them.  In
+// the decode step it also applies the per-head steps after the Q|K|V row (per-head QK RMSNorm, NeoX
+// RoPE at the position) to its queries and, in the range holding the position, to the new K row,
+// and stores the new K and V rows in the regions.
 // k_attn_merge combines a head's ranges (in a fixed order), normalizes, and quantizes the head's
 // output row to Q8_0, the output projection's input.
 #include <algorithm>
@@ -355,65 +355,6 @@ int launch_gemv_q8(const GemvArgs& g, hipStream_t s) {
   return MI_OK;
 }
 
-// The steps after the Q|K|V rows of one token (bias already added, one rounding): workgroup b < n_head
-// takes Q head b, then the K heads, then the V heads.  Q and K: [per-head RMSNorm in f64, one
-// rounding to f32], NeoX RoPE of the pair (i, i + hd/2) in f64 at the position, one rounding; Q in
-// place, K to its region row.  V: copied to its region row.  One wave; lane i < hd/2 takes pair i.
-template <int HD>
-__global__ void __launch_bounds__(64) k_qkv_finish(float* __restrict__ qkv, const int32_t* __restrict__ pos_dev,
-                                                   const double2* __restrict__ rope, int n_head, int n_head_kv,
-                                                   const float* __restrict__ q_norm, const float* __restrict__ k_norm,
-                                                   float eps, float* __restrict__ k_region,
-                                                   float* __restrict__ v_region) {
-  constexpr int HALF = HD / 2;
-  static_assert(HALF <= 64, "one pair per lane");
-  const int b = blockIdx.x, lane = threadIdx.x;
-  const int64_t p = *pos_dev;
-  const int n_kv = n_head_kv * HD;
-  const int nq = n_head * HD;
-  if (b >= n_head + n_head_kv) {  // V head
-    const int c = (b - n_head - n_head_kv) * HD;
-    for (int i = lane; i < HD; i += 64) v_region[p * n_kv + c + i] = qkv[nq + n_kv + c + i];
-    return;
-  }
-  const bool isq = b < n_head;
-  const int c = isq ? b * HD : nq + (b - n_head) * HD;  // the head's offset in the Q|K|V row
-  const float* gam = isq ? q_norm : k_norm;
-  const bool on = lane < HALF;
-  float a = on ? qkv[c + lane] : 0.0f, bb = on ? qkv[c + lane + HALF] : 0.0f;
-  if (gam) {  // per-head RMSNorm in f64, one rounding
-    const double ss = wave_sum_d((double)a * (double)a + (double)bb * (double)bb);
-    const double ir = recip_f64(sqrt(ss / (double)HD + (double)eps));
-    if (on) {
-      a = (float)((double)a * ir * (double)gam[lane]);
-      bb = (float)((double)bb * ir * (double)gam[lane + HALF]);
-    }
-  }
-  if (on) {
-    float* dst = isq ? qkv + c : k_region + p * n_kv + (b - n_head) * HD;
-    const double2 cs = rope[p * HALF + lane];
-    dst[lane] = (float)((double)a * cs.x - (double)bb * cs.y);
-    dst[lane + HALF] = (float)((double)a * cs.y + (double)bb * cs.x);
-  }
-}
-
-int launch_qkv_finish(float* qkv, const int32_t* pos_dev, const double* rope, int n_head, int n_head_kv,
-                      int head_dim, const float* q_norm, const float* k_norm, float eps, float* k_region,
-                      float* v_region, hipStream_t s) {
-  const dim3 grid(n_head + 2 * n_head_kv);
-  const double2* r = reinterpret_cast<const double2*>(rope);
-  if (head_dim == 64)
-    hipLaunchKernelGGL(k_qkv_finish<64>, grid, dim3(64), 0, s, qkv, pos_dev, r, n_head, n_head_kv, q_norm, k_norm,
-                       eps, k_region, v_region);
-  else if (head_dim == 128)
-    hipLaunchKernelGGL(k_qkv_finish<128>, grid, dim3(64), 0, s, qkv, pos_dev, r, n_head, n_head_kv, q_norm, k_norm,
-                       eps, k_region, v_region);
-  else
-    return set_error(MI_ERR_UNSUPPORTED, "attention inputs: head_dim %d (supported: 64, 128)", head_dim);
-  MI_LAUNCH_CHECK("k_qkv_finish");
-  return MI_OK;
-}
-
 // ---------------------------------------------------------------- single-query attention
 constexpr int AD_THREADS = 512;  // 8 waves
 constexpr int AD_KEYS = 64;      // keys of a sub-chunk: 8 lanes per key in the score step
@@ -433,13 +374,24 @@ constexpr int AD_HB = 4;         // query heads of a head block
 // K and V of a sub-chunk are requested together, before any of its arithmetic.  Workgroup (g, hb, r)
 // writes part[(h * n_range + r) * (HD + 2)] = m, l, o[HD] (f64) for its heads h: m the range's
 // largest score, l = sum e^(s - m), o = sum e^(s - m) v.  Ranges past pos write nothing.
+//
+// With `fin` (the decode step), q is the token's Q|K|V row (bias added, one rounding) and the
+// per-head steps run here, with the arithmetic of the prefill's Q|K|V epilogue: per-head RMSNorm in
+// f64 (when q_norm / k_norm are given), one rounding to f32; NeoX RoPE of the pair (i, i + hd/2) in
+// f64 at pos, one rounding.  Waves 0..GP-1 prepare the queries; in the range holding pos, wave 4
+// prepares the new K row and wave 5 takes the V row, both kept in LDS and used in place of what the
+// region held at row pos, and the head block 0 workgroup stores them there.  Without `fin`, q holds
+// finished queries and the regions already hold row pos.
 template <int HD, int GP>
 __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restrict__ q,
-                                                            const float* __restrict__ k_region,
-                                                            const float* __restrict__ v_region,
+                                                            float* __restrict__ k_region,
+                                                            float* __restrict__ v_region,
                                                             const int32_t* __restrict__ pos_dev, int n_head,
                                                             int n_head_kv, int keys_per_range,
-                                                            double* __restrict__ part) {
+                                                            double* __restrict__ part, int fin,
+                                                            const double2* __restrict__ rope,
+                                                            const float* __restrict__ q_norm,
+                                                            const float* __restrict__ k_norm, float eps) {
   constexpr int NI = HD / 32;              // K float4s per lane and key (8 lanes x NI x 16 B = one row)
   constexpr int KP = AD_THREADS / HD;      // key parts of the weighted sum: 4 (HD 128), 8 (HD 64)
   constexpr int KPP = AD_KEYS / KP;        // keys per part: 16 (HD 128), 8 (HD 64)
@@ -449,14 +401,18 @@ __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restr
   __shared__ double rs[GP];           // each head's rescale factor for the sub-chunk
   __shared__ double etab[64];
   __shared__ double red[KP - 1][GP][HD];
+  __shared__ float knew[HD], vnew[HD];  // the new K and V rows (fin, range holding pos)
+  constexpr int HALF = HD / 2;
+  static_assert(HALF <= 64, "one RoPE pair per lane");
   const int G = n_head / n_head_kv, n_hb = (G + AD_HB - 1) / AD_HB;
   const int g = blockIdx.x / n_hb, hb = blockIdx.x % n_hb, r = blockIdx.y, n_range = gridDim.y;
   const int h0 = g * G + hb * AD_HB, nh = min(GP, G - hb * AD_HB);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_kv = n_head_kv * HD;
-  const int n_keys = *pos_dev + 1;
+  const int pos = *pos_dev, n_keys = pos + 1;
   const int j0 = r * keys_per_range, j1 = min(j0 + keys_per_range, n_keys);
   if (j0 >= j1) return;  // uniform for the workgroup
+  const bool has_pos = fin && j1 == n_keys;  // this range holds key pos, the new row
   const int kk = tid >> 3, pp = tid & 7;  // scores: key kk of the sub-chunk, dim slice pp
   const int d = tid % HD, kp = tid / HD;  // weighted sum: dim d over the keys of part kp
   // 32-bit element offsets from the uniform region bases (n_ctx * n_kv < 2^31 is checked by the host)
@@ -475,18 +431,57 @@ __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restr
   double o[GP];
 #pragma unroll
   for (int hh = 0; hh < GP; ++hh) o[hh] = 0.0;
-  for (int t0 = j0; t0 < j1; t0 += AD_KEYS) {
-    const int nk = min(AD_KEYS, j1 - t0);
-    load(t0, nk);
-    if (t0 == j0) {  // while the first sub-chunk's loads are in flight
-      if (tid < 64) exp2_table_fill(etab, tid);
-      const double scale = 1.0 / sqrt((double)HD);
+  // the queries (and, with fin, the new K and V rows), while the first sub-chunk's loads are in flight
+  auto prep = [&]() {
+    if (tid < 64) exp2_table_fill(etab, tid);
+    const double scale = 1.0 / sqrt((double)HD);
+    if (!fin) {
       for (int i = tid; i < GP * HD; i += AD_THREADS) {
         const int hh = i / HD;
         qs[hh][i % HD] = hh < nh ? (double)q[(int64_t)(h0 + hh) * HD + i % HD] * scale : 0.0;
       }
+    } else if (wave < GP || (has_pos && wave == 4)) {  // a query head, or the new K row
+      const bool isq = wave < GP;
+      const bool live = isq ? wave < nh : true;  // uniform
+      const bool on = lane < HALF;
+      const float* src = isq ? q + (int64_t)(h0 + wave) * HD : q + n_head * HD + g * HD;
+      const float* gam = isq ? q_norm : k_norm;
+      float a = on && live ? src[lane] : 0.0f, bb = on && live ? src[lane + HALF] : 0.0f;
+      if (gam) {  // per-head RMSNorm in f64, one rounding
+        const double ss = wave_sum_d((double)a * (double)a + (double)bb * (double)bb);
+        const double ir = recip_f64(sqrt(ss / (double)HD + (double)eps));
+        if (on) {
+          a = (float)((double)a * ir * (double)gam[lane]);
+          bb = (float)((double)bb * ir * (double)gam[lane + HALF]);
+        }
+      }
+      if (on) {
+        const double2 cs = rope[(int64_t)pos * HALF + lane];
+        const float ra = (float)((double)a * cs.x - (double)bb * cs.y);
+        const float rb = (float)((double)a * cs.y + (double)bb * cs.x);
+        if (isq) {
+          qs[wave][lane] = live ? (double)ra * scale : 0.0;
+          qs[wave][lane + HALF] = live ? (double)rb * scale : 0.0;
+        } else {
+          knew[lane] = ra;
+          knew[lane + HALF] = rb;
+          if (hb == 0) {
+            float* dst = k_region + (int64_t)pos * n_kv + g * HD;
+            dst[lane] = ra;
+            dst[lane + HALF] = rb;
+          }
+        }
+      }
+    } else if (has_pos && wave == 5) {  // the new V row
+      for (int i = lane; i < HD; i += 64) {
+        const float vr = q[(int64_t)(n_head + n_head_kv) * HD + g * HD + i];
+        vnew[i] = vr;
+        if (hb == 0) v_region[(int64_t)pos * n_kv + g * HD + i] = vr;
+      }
     }
-    __syncthreads();  // the queries; after the first sub-chunk, sc and rs consumed
+  };
+  // one sub-chunk of 64 keys, its K and V in kv4 / vv
+  auto sub_chunk = [&](int t0, int nk) {
     // ---- scores
     double kd[4 * NI];
 #pragma unroll
@@ -495,6 +490,19 @@ __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restr
       kd[4 * i + 1] = kv4[i].y;
       kd[4 * i + 2] = kv4[i].z;
       kd[4 * i + 3] = kv4[i].w;
+    }
+    const int kpos = pos - t0;  // row pos within the sub-chunk (when 0 <= kpos < nk)
+    // the new K row, from LDS, for row pos and the rows past the sub-chunk's end (which re-read row
+    // pos and are masked below)
+    if (has_pos && kk >= kpos) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const float4 kn = *reinterpret_cast<const float4*>(&knew[32 * i + 4 * pp]);
+        kd[4 * i] = kn.x;
+        kd[4 * i + 1] = kn.y;
+        kd[4 * i + 2] = kn.z;
+        kd[4 * i + 3] = kn.w;
+      }
     }
     // two heads at a time: their query slices are read from LDS just before use (the compiler
     // barrier keeps it from hoisting every head's reads, which would need 4 * NI * GP registers)
@@ -562,6 +570,11 @@ __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restr
     }
     __syncthreads();
     // ---- weighted sum
+    if (has_pos) {  // the new V row, from LDS (row pos and the rows past the end, weight 0, that re-read it)
+#pragma unroll
+      for (int j = 0; j < KPP; ++j)
+        if (kp * KPP + j >= kpos) vv[j] = vnew[d];
+    }
 #pragma unroll
     for (int hh = 0; hh < GP; ++hh) o[hh] *= rs[hh];
 #pragma unroll
@@ -575,6 +588,15 @@ __global__ void __launch_bounds__(AD_THREADS) k_attn_decode(const float* __restr
         o[hh] = fma(pk.y, v1, o[hh]);
       }
     }
+  };
+  load(j0, min(AD_KEYS, j1 - j0));
+  prep();
+  __syncthreads();
+  sub_chunk(j0, min(AD_KEYS, j1 - j0));
+  for (int t0 = j0 + AD_KEYS; t0 < j1; t0 += AD_KEYS) {
+    load(t0, min(AD_KEYS, j1 - t0));
+    __syncthreads();  // sc and rs of the previous sub-chunk consumed
+    sub_chunk(t0, min(AD_KEYS, j1 - t0));
   }
   // ---- the key parts, summed in order; m and l from the head's wave
   if (kp > 0) {
@@ -709,26 +731,33 @@ int attn_decode_ranges(int n_ctx, int* keys_per_range) {
 }
 
 template <int HD>
-static void launch_attn_decode_hd(int gp, dim3 grid, hipStream_t s, const float* q, const float* k_region,
-                                  const float* v_region, const int32_t* pos_dev, int n_head, int n_head_kv, int kpr,
-                                  double* part) {
-  auto k = gp == 8 ? k_attn_decode<HD, 8> : gp == 4 ? k_attn_decode<HD, 4> : gp == 2 ? k_attn_decode<HD, 2>
-                                                                                     : k_attn_decode<HD, 1>;
-  hipLaunchKernelGGL(k, grid, dim3(AD_THREADS), 0, s, q, k_region, v_region, pos_dev, n_head, n_head_kv, kpr, part);
+static void launch_attn_decode_hd(int gp, dim3 grid, hipStream_t s, const float* q, float* k_region, float* v_region,
+                                  const int32_t* pos_dev, int n_head, int n_head_kv, int kpr, double* part,
+                                  int fin, const double2* rope, const float* q_norm, const float* k_norm,
+                                  float eps) {
+  auto k = gp == 4 ? k_attn_decode<HD, 4> : gp == 2 ? k_attn_decode<HD, 2> : k_attn_decode<HD, 1>;
+  hipLaunchKernelGGL(k, grid, dim3(AD_THREADS), 0, s, q, k_region, v_region, pos_dev, n_head, n_head_kv, kpr, part,
+                     fin, rope, q_norm, k_norm, eps);
 }
 
-int launch_attn_decode(const float* q, const float* k_region, const float* v_region, const int32_t* pos_dev,
-                       int n_ctx, int n_head, int n_head_kv, int head_dim, double* part, hipStream_t s) {
+int launch_attn_decode(const float* q, float* k_region, float* v_region, const int32_t* pos_dev, int n_ctx,
+                       int n_head, int n_head_kv, int head_dim, double* part, const AttnFinish* fin, hipStream_t s) {
   int kpr = 0;
   const int n_range = attn_decode_ranges(n_ctx, &kpr);
   const int G = n_head / n_head_kv, n_hb = (G + AD_HB - 1) / AD_HB;
   int gp = 1;  // the head block, rounded up to a power of two
   while (gp < G && gp < AD_HB) gp *= 2;
   const dim3 grid(n_head_kv * n_hb, n_range);
+  const double2* rope = fin ? reinterpret_cast<const double2*>(fin->rope) : nullptr;
+  const float* qn = fin ? fin->q_norm : nullptr;
+  const float* kn = fin ? fin->k_norm : nullptr;
+  const float eps = fin ? fin->eps : 0.0f;
   if (head_dim == 64)
-    launch_attn_decode_hd<64>(gp, grid, s, q, k_region, v_region, pos_dev, n_head, n_head_kv, kpr, part);
+    launch_attn_decode_hd<64>(gp, grid, s, q, k_region, v_region, pos_dev, n_head, n_head_kv, kpr, part, fin != nullptr,
+                              rope, qn, kn, eps);
   else if (head_dim == 128)
-    launch_attn_decode_hd<128>(gp, grid, s, q, k_region, v_region, pos_dev, n_head, n_head_kv, kpr, part);
+    launch_attn_decode_hd<128>(gp, grid, s, q, k_region, v_region, pos_dev, n_head, n_head_kv, kpr, part,
+                               fin != nullptr, rope, qn, kn, eps);
   else
     return set_error(MI_ERR_UNSUPPORTED, "attention decode: head_dim %d", head_dim);
   MI_LAUNCH_CHECK("k_attn_decode");
