@@ -241,6 +241,8 @@ def main():
                           "quantize_plus_gemm_ms": round(p_ms, 4)})
             del xw, ac, as_, wc, wsc, gws, out
 
+    box = box_probe(dev)  # right after the GPU work, before the GPU idles through the CPU baseline
+
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     cpu = None
     if not args.no_cpu_baseline:
@@ -261,9 +263,17 @@ def main():
         "roofline": roofline,
         "gemm_sweep": sweep,
         "cpu_baseline": cpu,
+        "box_probe": box,
         "load_s": round(load_s, 2),
     }
     print(json.dumps(line), flush=True)
+
+
+def box_probe(dev):
+    """The register-only int8 MFMA probe, run right after the timed region: its share of the peak
+    tracks the clock the GPU ran at, which differs by several percent between hosts."""
+    r = probe_rates(dev, only=["mfma_i8"])["mfma_i8"]
+    return {"mfma_i8_tops": r["rate"], "int8_peak_frac": r["int8_peak_frac"]}
 
 
 def slots_bench(args, cfg, model, ids, load_s):
@@ -364,6 +374,7 @@ def decode_bench(args, cfg, model, ids, pos, load_s):
     context = p0 + n + args.warmup + args.steps / 2.0  # mean attended positions over the timed steps
     nbytes = decode_step_bytes(cfg, context)
     gbs = nbytes / (ms / 1e3) / 1e9
+    box = box_probe(model.device)
     cpu = None if args.no_cpu_baseline else cpu_baseline_decode(cfg)
     line = {
         "metric": "decode tokens/sec (one token per step after the prompt), 1 GPU",
@@ -381,6 +392,7 @@ def decode_bench(args, cfg, model, ids, pos, load_s):
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "algorithmic_bytes_per_step": round(nbytes), "mean_context": context},
         "cpu_baseline": cpu,
+        "box_probe": box,
         "load_s": round(load_s, 2),
     }
     print(json.dumps(line), flush=True)

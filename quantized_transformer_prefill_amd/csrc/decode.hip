@@ -86,8 +86,8 @@ enum { GV_IN_Q8 = 0, GV_IN_NORM = 1 };
 
 // The one-row-per-wave instances (the Q|K|V rows: 288 workgroups at the 7B shape; the output and
 // down projections) are held to 64 registers, so that two workgroups fit a CU.
-template <int RPW, int EPI, int PRO, int TH>
-__global__ void __launch_bounds__(TH, (RPW == 1 && EPI != GV_SWIGLU) ? 8 : 1) k_gemv_q8(const float* __restrict__ x, const float* __restrict__ gamma,
+template <int RPW, int EPI, int PRO>
+__global__ void __launch_bounds__(GV_THREADS, (RPW == 1 && EPI != GV_SWIGLU) ? 8 : 1) k_gemv_q8(const float* __restrict__ x, const float* __restrict__ gamma,
                                                        float eps, const int8_t* __restrict__ xq,
                                                        const uint16_t* __restrict__ xs, int K,
                                                        const int8_t* __restrict__ w_codes,
@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(TH, (RPW == 1 && EPI != GV_SWIGLU) ? 8 : 1) k_
                                                        const float* __restrict__ bias, const float* residual,
                                                        float* out, int8_t* __restrict__ q_codes,
                                                        uint16_t* __restrict__ q_scales) {
-  constexpr int WAVES = TH / 64;
+  constexpr int TH = GV_THREADS, WAVES = TH / 64;
   constexpr int NV = (GV_NORM_K / 4 + TH - 1) / TH;  // float4s of the row per thread (norm prologue)
   constexpr int RWG = RPW * WAVES;  // weight rows per group
   // 64-chunk steps of K per load batch; two batches are in flight (double buffered)
@@ -317,14 +317,11 @@ int launch_gemv_q8(const GemvArgs& g, hipStream_t s) {
   if (g.bias && g.epi != GV_F32) return set_error(MI_ERR_INVALID_ARG, "gemv: a bias needs the plain f32 epilogue");
   // enough workgroups to keep every CU busy, looping over row groups beyond that
   const int max_wg = GV_MAX_WG;
-  auto grid = [&](int rwg, int th) {
-    return dim3((unsigned)std::min((g.n + rwg - 1) / rwg, (2048 / th) * 256));
-  };
-#define GV_LAUNCH_T(RPW, EPI, NORM, TH)                                                                           \
-  hipLaunchKernelGGL((k_gemv_q8<RPW, EPI, NORM, TH>), grid(RPW * (TH / 64), TH), dim3(TH), lds, s, g.x, g.gamma, \
-                     g.eps, g.xq, g.xs, g.k, g.w_codes, g.w_scales, g.n, g.bias, g.residual, g.out, g.q_codes,      \
+  auto grid = [&](int rwg) { return dim3((unsigned)std::min((g.n + rwg - 1) / rwg, max_wg)); };
+#define GV_LAUNCH(RPW, EPI, NORM)                                                                          \
+  hipLaunchKernelGGL((k_gemv_q8<RPW, EPI, NORM>), grid(RPW * GV_WAVES), dim3(GV_THREADS), lds, s, g.x, g.gamma, \
+                     g.eps, g.xq, g.xs, g.k, g.w_codes, g.w_scales, g.n, g.bias, g.residual, g.out, g.q_codes,     \
                      g.q_scales)
-#define GV_LAUNCH(RPW, EPI, NORM) GV_LAUNCH_T(RPW, EPI, NORM, GV_THREADS)
   switch (g.epi) {
     case GV_RES:
     case GV_F32: {
@@ -350,7 +347,6 @@ int launch_gemv_q8(const GemvArgs& g, hipStream_t s) {
       return set_error(MI_ERR_INVALID_ARG, "gemv: epilogue %d", g.epi);
   }
 #undef GV_LAUNCH
-#undef GV_LAUNCH_T
   MI_LAUNCH_CHECK("k_gemv_q8");
   return MI_OK;
 }
