@@ -205,8 +205,9 @@ int mi_prefill_forward_slots(const mi_model* model, const int32_t* token_ids, co
  * 2.2, for attention over region rows 0..=position).  Computes exactly what mi_prefill_forward
  * computes for n_tokens = 1 -- which runs the same one-row kernels: HBM-bound exact Q8_0
  * matrix-vector products with the RMSNorms in their prologues and the bias / residual / SwiGLU
- * work in their epilogues, a per-head step for the QK norm, RoPE and the K/V store, and a
- * single-query attention split over fixed key ranges, whose ranges one more kernel merges.
+ * work in their epilogues, and a single-query attention split over fixed key ranges (which also
+ * applies the per-head QK norm and RoPE and stores the new K/V rows), whose ranges one more kernel
+ * merges.
  *   token_id, position  host values, 0 <= token_id < vocab, 0 <= position < n_ctx
  *   logits_out          device f32 [vocab]
  * Writes K/V row `position` of every layer.  Errors as mi_prefill_forward (nothing written).
