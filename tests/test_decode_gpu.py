@@ -185,20 +185,25 @@ def test_one_token_tail_merges_key_ranges_head_dim_128():
     assert_f32_match(gv[:, :end], vv[:, :end], max_ulp=64, max_frac_inexact=0.05, what="V regions")
 
 
-# n_ctx above 4096: the one-token attention's key ranges grow to 512 keys (10 ranges for 5120)
+# n_ctx above 4096: the one-token attention's key ranges grow to 128 keys, two sub-chunks of 64
+# (40 ranges for 5120)
 TINY_FAR = synth.ModelConfig(name="tiny_far_positions", n_layers=2, hidden=128, n_head=4, n_head_kv=2, head_dim=64,
                              ffn=192, vocab=700, n_tokens=20, n_ctx=5120, seed=23, qkv_bias=True)
+TINY_FAR_Q3 = synth.ModelConfig(name="tiny_far_qwen3", n_layers=2, hidden=256, n_head=8, n_head_kv=2, head_dim=128,
+                                ffn=384, vocab=700, n_tokens=20, n_ctx=5120, seed=31, qkv_bias=False, qk_norm=True,
+                                tied=False)
 
 
-def test_far_positions_over_long_context():
-    """A prompt at positions 5000..5019 of a 5120-row context (the rows below it hold the regions'
-    fill, read by both sides), then 3 decode steps: every key range of 512 keys carries keys, and
-    the merge combines 10 ranges.  Logits and regions against the oracle."""
+@pytest.mark.parametrize("cfg", [TINY_FAR, TINY_FAR_Q3], ids=lambda c: c.name)
+def test_far_positions_over_long_context(cfg):
+    """A prompt at positions 5040..5059 of a 5120-row context (the rows below it hold the regions'
+    fill, read by both sides), then 3 decode steps: every key range of 128 keys carries keys, the
+    range holding the position (4992..) spans two sub-chunks, and the merge combines 40 ranges.  Head dims
+    64 and 128 (with the QK norm).  Logits and regions against the oracle."""
     dev = need_gpu()
-    cfg = TINY_FAR
     m, w = load_pair(cfg, dev, max_tokens=cfg.n_tokens)
     _, ids = synth.gen_token_ids(cfg)
-    pos = np.arange(5000, 5000 + cfg.n_tokens, dtype=np.int32)
+    pos = np.arange(5040, 5040 + cfg.n_tokens, dtype=np.int32)
     kk, vv = oracle.new_kv_regions(cfg, cfg.n_ctx, fill=SENTINEL)
     got = m.forward(ids, pos).cpu().numpy().copy()
     want = oracle.prefill_forward(cfg, w, ids, pos, cfg.n_ctx, kk, vv)[0]
