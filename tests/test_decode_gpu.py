@@ -147,8 +147,8 @@ def test_headline_config_decode_matches_oracle():
     assert d <= 1e-3 and np.all(gk[:, end:] == SENTINEL)
 
 
-# head_dim 128 with keys spread over several of the one-token attention's key ranges (256 keys each
-# for n_ctx 800): the last prompt token sits at position 599, so its attention merges three ranges
+# head_dim 128 with keys spread over several of the one-token attention's key ranges (64 keys each
+# for n_ctx 800): the last prompt token sits at position 599, so its attention merges ten ranges
 TINY_Q3_LONG = synth.ModelConfig(name="tiny_qwen3_long", n_layers=2, hidden=256, n_head=4, n_head_kv=2,
                                  head_dim=128, ffn=384, vocab=1000, n_tokens=40, n_ctx=800, seed=17,
                                  qkv_bias=False, qk_norm=True, tied=True, prefix_tokens=560)
@@ -156,8 +156,8 @@ TINY_Q3_LONG = synth.ModelConfig(name="tiny_qwen3_long", n_layers=2, hidden=256,
 
 def test_one_token_tail_merges_key_ranges_head_dim_128():
     """The last prompt token of a prefill (n_out = 1) and the decode steps after it run the
-    one-token attention, whose key ranges are merged in the output projection's prologue: with
-    head_dim 128 and positions past 512 several ranges carry keys.  Logits and regions against the
+    one-token attention, whose key ranges are merged by one more kernel: with head_dim 128 and
+    positions past 512 several ranges carry keys.  Logits and regions against the
     oracle, for the prefill and for 3 decode steps at 600..602."""
     dev = need_gpu()
     cfg = TINY_Q3_LONG
