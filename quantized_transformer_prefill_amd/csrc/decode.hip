@@ -3,17 +3,18 @@
 // matmul is a matrix-vector product bound by HBM, and the attention has one query per head.
 //
 // k_gemv_q8: y[n] = sum_kb dx[kb] * dw[n][kb] * sum_32 qx * qw, one activation row.
-//  * 16 waves per workgroup, RPW weight rows per wave (up to 4 in flight at once); a lane takes
-//    16-byte chunks (half a block) of every row, sdot4 gives the integer half-block sums, lane
-//    pairs combine them to the block sum, and the exact f64 epilogue (block sum times dw, times
-//    dx, one rounding per block) accumulates per lane; the lanes' partial sums then reduce in f64.
+//  * 16 waves per workgroup, RPW weight rows per wave (up to 4 in flight at once, 2 for the SwiGLU
+//    rows); a lane takes 16-byte chunks (half a block) of every row, sdot4 gives the integer
+//    half-block sums, lane pairs combine them to the block sum, and the exact f64 epilogue (block
+//    sum times dw, times dx, one rounding per block) accumulates per lane; the lanes' partial sums
+//    then reduce in f64.
 //    The weight loads are double buffered: the next step's requests go out before this step's
 //    math, and are unconditional (clamped addresses) so that the wait for one buffer never
 //    includes the other's requests.
 //  * The activation row is staged in LDS as codes + f64 scales.  The workgroup can build it
 //    itself from the f32 residual stream (RMSNorm in f64, one rounding to f32, Q8_0 -- the same
 //    arithmetic as the prefill's k_rmsnorm_quant), so the decode step has no normalization
-//    kernels.  The weight loads of the first rows go out before this prologue.
+//    kernels.  The prologue's inputs, then the first weight loads, go out before it.
 //  * Epilogues: residual add (output projection, down projection), plain f32 with an optional
 //    bias (lm_head; the Q|K|V rows), SwiGLU + Q8_0 (a workgroup holds one interleaved group of 32
 //    gate and 32 up rows, i.e. one Q8_0 block of the SwiGLU output).  Every epilogue is per row,
@@ -39,7 +40,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int GV_THREADS = 1024;  // 16 waves
 constexpr int GV_WAVES = GV_THREADS / 64;
 constexpr int GV_NORM_K = 4096;                                  // widest row the norm prologue takes
-constexpr int GV_NV = (GV_NORM_K / 4 + GV_THREADS - 1) / GV_THREADS;  // float4s of the row per thread
 constexpr int GV_RPW_SWIGLU = 64 / GV_WAVES;                       // a SwiGLU group is 64 rows
 constexpr int GV_MAX_WG = (2048 / GV_THREADS) * 256;               // grid cap: two workgroups per CU
 
