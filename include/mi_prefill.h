@@ -98,9 +98,10 @@ typedef struct {
  * for several sequences, the attention tile table and region pointers).  The prefill page takes
  * token ids and positions as host slices that are only read during the call ("09", section 2.2,
  * the forward signature), so the call copies them into pinned host memory before it returns and
- * the transfer to the device runs asynchronously from there.  The stage is a ring of MI_STAGE_RING
- * pinned buffers, each guarded by a HIP event: a buffer is rewritten only after the transfer that
- * last read it has completed, so back-to-back calls never wait for the GPU unless they are
+ * the transfer to the device runs asynchronously from there: a small kernel, first on the call's
+ * stream, reads the pinned buffer (mapped, coherent) into the workspace.  The stage is a ring of
+ * MI_STAGE_RING pinned buffers, each guarded by a HIP event: a buffer is rewritten only after the
+ * transfer that last read it has completed, so back-to-back calls never wait for the GPU unless they are
  * MI_STAGE_RING calls ahead of it.  Created once per model (it allocates pinned host memory and
  * events; nothing on the device); not thread-safe, like the mi_model that refers to it.
  *   mi_stage_create   hp and max_tokens as for mi_prefill_workspace_bytes; *out NULL on error

@@ -131,13 +131,15 @@ static int check_hparams(const mi_hparams* hp) {
 // ---------------------------------------------------------------- pinned host staging
 // A ring of pinned host buffers, each a mirror of the workspace's staged part (ids, positions,
 // largest position, the several-sequence tables) with the same offsets, so one call fills a buffer
-// and sends it with a single asynchronous host-to-device copy.  The event recorded after that copy
-// tells when the buffer may be written again.
+// and a small kernel on the call's stream reads it into the workspace (zero-copy: no copy-engine
+// transfer in front of the forward's first kernel).  The event recorded after that kernel tells when
+// the buffer may be written again.
 struct mi_stage {
   mi_hparams hp{};
   int32_t max_tokens = 0;
   size_t bytes = 0;  // per buffer
   char* host[MI_STAGE_RING] = {};
+  const char* dev[MI_STAGE_RING] = {};  // the same buffers' device addresses
   hipEvent_t ev[MI_STAGE_RING] = {};
   bool pending[MI_STAGE_RING] = {};
   int next = 0;
@@ -175,7 +177,7 @@ static int stage_send(mi_stage* st, void* dev, size_t n, hipStream_t s, F fill) 
   }
   st->next = (i + 1) % MI_STAGE_RING;
   fill(st->host[i]);
-  MI_HIP(hipMemcpyAsync(dev, st->host[i], n, hipMemcpyHostToDevice, s));
+  if (int rc = launch_stage_in(dev, st->dev[i], n, s)) return rc;
   MI_HIP(hipEventRecord(st->ev[i], s));
   st->pending[i] = true;
   return MI_OK;
@@ -196,7 +198,9 @@ extern "C" int mi_stage_create(const mi_hparams* hp, int32_t max_tokens, mi_stag
   st->max_tokens = max_tokens;
   st->bytes = carve(*hp, max_tokens, nullptr).staged_bytes;
   for (int i = 0; i < MI_STAGE_RING; ++i) {
-    hipError_t e = hipHostMalloc((void**)&st->host[i], st->bytes, hipHostMallocDefault);
+    // mapped and coherent: a kernel reads it over the bus (launch_stage_in)
+    hipError_t e = hipHostMalloc((void**)&st->host[i], st->bytes, hipHostMallocMapped | hipHostMallocCoherent);
+    if (e == hipSuccess) e = hipHostGetDevicePointer((void**)&st->dev[i], st->host[i], 0);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&st->ev[i], hipEventDisableTiming);
     if (e != hipSuccess) {
       stage_free(st);
@@ -493,7 +497,7 @@ static int validate_tokens(const mi_hparams& hp, const int32_t* ids, const int32
 }
 
 // boundary staging: token ids, positions and the largest position copied into the next pinned
-// buffer of the stage (before the call returns), then one asynchronous copy to the workspace
+// buffer of the stage (before the call returns), then read into the workspace by one small kernel
 static int stage_tokens(mi_stage* st, const Ws& w, const int32_t* ids, const int32_t* pos, int32_t nt, int32_t max_pos,
                         hipStream_t s) {
   char* base = reinterpret_cast<char*>(w.ids);

@@ -169,6 +169,8 @@ int launch_swiglu_quant(const float* gate, const float* up, int64_t rows, int co
                         int8_t* codes, uint16_t* scales, hipStream_t s);
 int launch_embed(const int8_t* codes, const uint16_t* scales, int cols, const int32_t* ids, int n,
                  float* out, hipStream_t s);
+// bytes (a multiple of 4) from a pinned host buffer to device memory, read by a kernel
+int launch_stage_in(void* dst, const void* host_src, size_t bytes, hipStream_t s);
 // out[r] = x[rows[r]] for r < n (rows of cols floats; rows: device int32 [n])
 int launch_gather_rows(const float* x, int cols, const int32_t* rows, int n, float* out, hipStream_t s);
 int launch_qk_norm(float* x, int64_t ld, const float* gamma, int64_t rows, int n_heads, int head_dim,

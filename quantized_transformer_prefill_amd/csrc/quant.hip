@@ -230,6 +230,27 @@ int launch_swiglu_quant(const float* gate, const float* up, int64_t rows, int co
   return MI_OK;
 }
 
+// ---------------------------------------------------------------- staging from pinned host memory
+// words [0, n) of a pinned (device-mapped, coherent) host buffer -> device memory: the kernel reads
+// the host buffer over the bus itself, so the ids and positions of a call reach the device without
+// a copy-engine transfer (and the queue switch it costs) in front of the first kernel.
+__global__ void __launch_bounds__(256) k_stage_in(uint32_t* __restrict__ dst, const uint32_t* __restrict__ src,
+                                                  int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+int launch_stage_in(void* dst, const void* host_src, size_t bytes, hipStream_t s) {
+  if (bytes % 4) return set_error(MI_ERR_INVALID_ARG, "stage: %zu bytes is not a whole number of words", bytes);
+  const int64_t n = (int64_t)(bytes / 4);
+  if (n == 0) return MI_OK;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 256);
+  hipLaunchKernelGGL(k_stage_in, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<uint32_t*>(dst),
+                     reinterpret_cast<const uint32_t*>(host_src), n);
+  MI_LAUNCH_CHECK("k_stage_in");
+  return MI_OK;
+}
+
 // ---------------------------------------------------------------- embedding rows
 // out[t][c] = scale[id][c/32] * code[id][c]  (exact in f32).  One lane per 4 values.
 __global__ void __launch_bounds__(256) k_embed(const int8_t* __restrict__ codes,
