@@ -401,10 +401,7 @@ extern "C" int mi_sample(const float* logits, int32_t vocab, const int32_t* wind
   const int32_t* w = window + (n_window - nw);  // the last 64 count
   for (int i = 0; i < nw; ++i)
     if (w[i] < 0 || w[i] >= vocab) return set_error(MI_ERR_INVALID_ARG, "mi_sample: window id %d outside [0, %d)", w[i], vocab);
-  hipStream_t s = as_stream(stream);
-  int32_t* window_dev = (int32_t*)((char*)workspace + sampler_workspace_bytes() - 64 * sizeof(int32_t) - 256);
-  if (nw) MI_HIP(hipMemcpyAsync(window_dev, w, sizeof(int32_t) * nw, hipMemcpyHostToDevice, s));
-  return launch_sample(logits, vocab, window_dev, nw, *p, seed, step, workspace, token_out, s);
+  return launch_sample(logits, vocab, w, nw, *p, seed, step, workspace, token_out, as_stream(stream));
 }
 
 // ---------------------------------------------------------------- the forward

@@ -274,7 +274,8 @@ int launch_attn_merge(const double* part, int n_ctx, const int32_t* pos_dev, int
 
 // ---- sampler (sampler.hip)
 size_t sampler_workspace_bytes();
-int launch_sample(const float* logits, int vocab, const int32_t* window_dev, int n_window, const mi_sampler_params& p,
+// window: host ids [n_window <= 64], passed to the kernel by value
+int launch_sample(const float* logits, int vocab, const int32_t* window, int n_window, const mi_sampler_params& p,
                   uint64_t seed, uint64_t step, void* workspace, int32_t* token_out, hipStream_t s);
 
 }  // namespace mi

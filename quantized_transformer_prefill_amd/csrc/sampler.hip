@@ -52,12 +52,19 @@ __device__ void sp_sort(double* v, int* id, int n) {
     }
 }
 
+// the last (up to) 64 window ids, passed by value as a kernel argument: no host-to-device copy
+struct SampleWindow {
+  int32_t ids[64];
+};
+
 __global__ void __launch_bounds__(SP_THREADS) k_sample_slices(const float* __restrict__ logits, int vocab,
-                                                             const int32_t* __restrict__ window, int n_window,
+                                                             const SampleWindow win, int n_window,
                                                              SampleParamsDev p, double* __restrict__ cand_v,
                                                              int* __restrict__ cand_id) {
   __shared__ double v[SP_MAX_SLICE];
   __shared__ int id[SP_MAX_SLICE];
+  __shared__ int window[64];
+  if ((int)threadIdx.x < n_window) window[threadIdx.x] = win.ids[threadIdx.x];
   const int slice = (vocab + SP_SLICES - 1) / SP_SLICES;
   const int lo = blockIdx.x * slice, hi = min(lo + slice, vocab);
   int n = 1;
@@ -180,8 +187,10 @@ size_t sampler_workspace_bytes() {
   return (first + second) * (sizeof(double) + sizeof(int)) + 64 * sizeof(int32_t) + 256;
 }
 
-int launch_sample(const float* logits, int vocab, const int32_t* window_dev, int n_window, const mi_sampler_params& hp,
+int launch_sample(const float* logits, int vocab, const int32_t* window, int n_window, const mi_sampler_params& hp,
                   uint64_t seed, uint64_t step, void* workspace, int32_t* token_out, hipStream_t s) {
+  SampleWindow win{};
+  for (int i = 0; i < n_window && i < 64; ++i) win.ids[i] = window[i];
   SampleParamsDev p;
   p.repeat = hp.repeat_penalty;
   p.frequency = hp.frequency_penalty;
@@ -195,7 +204,7 @@ int launch_sample(const float* logits, int vocab, const int32_t* window_dev, int
   double* cv2 = cv + first;
   int* ci = reinterpret_cast<int*>(cv2 + second);
   int* ci2 = ci + first;
-  hipLaunchKernelGGL(k_sample_slices, dim3(SP_SLICES), dim3(SP_THREADS), 0, s, logits, vocab, window_dev, n_window, p,
+  hipLaunchKernelGGL(k_sample_slices, dim3(SP_SLICES), dim3(SP_THREADS), 0, s, logits, vocab, win, n_window, p,
                      cv, ci);
   MI_LAUNCH_CHECK("k_sample_slices");
   hipLaunchKernelGGL(k_sample_merge, dim3(SP_SLICES / SP_GROUP), dim3(SP_THREADS), 0, s, cv, ci, p.top_k, cv2, ci2);
