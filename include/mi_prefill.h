@@ -249,7 +249,8 @@ size_t mi_sampler_workspace_bytes(void);
  *   seed, step the draw's counter (step = the number of tokens sampled before in this sequence)
  *   token_out  device int32 [1]
  * Errors (MI_ERR_INVALID_ARG): bad sizes or parameters, window ids out of range; nothing is
- * written.  Enqueued on `stream`; the window is staged through `workspace`. */
+ * written.  Enqueued on `stream`; the window is read before the call returns (it goes to the first
+ * kernel as an argument), so the caller may reuse it at once. */
 int mi_sample(const float* logits, int32_t vocab, const int32_t* window, int32_t n_window,
               const mi_sampler_params* params, uint64_t seed, uint64_t step, void* workspace,
               size_t workspace_bytes, int32_t* token_out, void* stream);
