@@ -236,3 +236,32 @@ def test_decode_at_first_and_last_rows():
     gk, gv = m.kv_k.cpu().numpy(), m.kv_v.cpu().numpy()
     assert_f32_match(gk, kk, max_ulp=64, max_frac_inexact=0.05, what="K regions")
     assert_f32_match(gv, vv, max_ulp=64, max_frac_inexact=0.05, what="V regions")
+
+
+def test_back_to_back_steps_through_the_stage_ring():
+    """Ten decode steps enqueued without a host synchronization between them (more than the stage's
+    four pinned buffers, each read on the device by the first kernel of its call): the regions and
+    each step's logits (copied to a buffer of its own) equal the oracle's steps."""
+    dev = need_gpu()
+    cfg = TINY_Q3
+    m, w = load_pair(cfg, dev)
+    _, ids = synth.gen_token_ids(cfg)
+    n = 12
+    pos = np.arange(n, dtype=np.int32)
+    kk, vv = oracle.new_kv_regions(cfg, cfg.n_ctx, fill=SENTINEL)
+    m.forward(ids[:n], pos)
+    oracle.prefill_forward(cfg, w, ids[:n], pos, cfg.n_ctx, kk, vv)
+    toks = decode_tokens(cfg, 10)
+    outs = [torch.empty(cfg.vocab, dtype=torch.float32, device=dev) for _ in toks]
+    for i, tok in enumerate(toks):  # no synchronization in between
+        m.decode(int(tok), n + i, logits=outs[i])
+    torch.cuda.synchronize()
+    for i, tok in enumerate(toks):
+        want = oracle.prefill_forward(cfg, w, np.array([tok], np.int32), np.array([n + i], np.int32), cfg.n_ctx,
+                                      kk, vv)[0]
+        compare_logits(outs[i].cpu().numpy(), want, f"back-to-back step {i}")
+    gk, gv = m.kv_k.cpu().numpy(), m.kv_v.cpu().numpy()
+    end = n + len(toks)
+    assert np.all(gk[:, end:] == SENTINEL) and np.all(gv[:, end:] == SENTINEL), "stray KV writes"
+    assert_f32_match(gk[:, :end], kk[:, :end], max_ulp=64, max_frac_inexact=0.05, what="K regions")
+    assert_f32_match(gv[:, :end], vv[:, :end], max_ulp=64, max_frac_inexact=0.05, what="V regions")
