@@ -316,8 +316,13 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
       v4i fa[RG], fb[CG];
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
+        // odd lanes read the zero row, at a chunk that no real row of their 16-lane group uses in
+        // the same pass (the rows of one parity take chunks c ^ 0, 2, 4, 6 of a 64-bank row), so
+        // the read is a broadcast without a bank conflict; the 4 x 2 tile keeps chunk c, where the
+        // extra selects cost more than the conflicts (measured)
         const int r = a_lane ? a_rrow + rg * 16 : BM;
-        fa[rg] = *reinterpret_cast<const v4i*>(&sm.a[st][r][swz(r, 2 * jb + khalf)]);
+        const int ch = (a_lane || RG == 4) ? swz(r, 2 * jb + khalf) : (((2 * jb + khalf) ^ 1) << 4);
+        fa[rg] = *reinterpret_cast<const v4i*>(&sm.a[st][r][ch]);
       }
 #pragma unroll
       for (int cg = 0; cg < CG; ++cg)
