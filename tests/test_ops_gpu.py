@@ -99,6 +99,52 @@ def test_gemm_matches_oracle(m, k, n, use_bias, use_res, split):
     assert_f32_match(out.cpu().numpy(), want, what="gemm out")
 
 
+def _random_gemm_cases(n_cases, seed):
+    """Seeded random shapes: rows 1..1200, output columns a multiple of 32 up to 4096, K a multiple of
+    32 up to 3072 (odd and even block counts), the library's split or a forced one (1, 2, 3, 7)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n_cases):
+        m = int(rng.integers(1, 1201))
+        n = 32 * int(rng.integers(1, 129))
+        k = 32 * int(rng.integers(1, 97))
+        split = int(rng.choice([0, 0, 1, 2, 3, 7]))
+        cases.append((m, k, n, bool(rng.integers(2)), bool(rng.integers(2)), split))
+    return cases
+
+
+RANDOM_GEMM_CASES = _random_gemm_cases(16, 20261203)
+
+
+@pytest.mark.parametrize("m,k,n,use_bias,use_res,split", RANDOM_GEMM_CASES,
+                         ids=[f"m{c[0]}_k{c[1]}_n{c[2]}_s{c[5]}" for c in RANDOM_GEMM_CASES])
+def test_gemm_random_shapes_match_oracle(m, k, n, use_bias, use_res, split):
+    test_gemm_matches_oracle(m, k, n, use_bias, use_res, split)
+
+
+RANDOM_SWIGLU_CASES = [(m, k, 32 * max(1, n // 64)) for m, k, n, *_ in _random_gemm_cases(10, 20261204)]
+
+
+@pytest.mark.parametrize("m,k,f", RANDOM_SWIGLU_CASES, ids=[f"m{c[0]}_k{c[1]}_f{c[2]}" for c in RANDOM_SWIGLU_CASES])
+def test_gemm_swiglu_random_shapes_match_oracle(m, k, f):
+    dev = need_gpu()
+    say(f"gemm+swiglu m={m} k={k} ffn={f}")
+    x = synth.gen_normal(34, f"x{m}x{k}", (m, k), device=dev)
+    wg = synth.gen_normal(35, f"g{f}x{k}", (f, k), std=0.02, device=dev)
+    wu = synth.gen_normal(36, f"u{f}x{k}", (f, k), std=0.02, device=dev)
+    (gc, gs), (ogc, ogs) = q8_pair(wg)
+    (uc, us), (ouc, ous) = q8_pair(wu)
+    wgu_c = interleave_gate_up(gc, uc).contiguous()
+    wgu_s = interleave_gate_up(gs, us).contiguous()
+    xc, xs = B.quantize_q8_0(x)
+    wsp = torch.empty(max(B.lib().mi_gemm_q8_0_workspace_bytes(m, 2 * f, k), 8), dtype=torch.uint8, device=dev)
+    sc, ss = B.gemm_swiglu_q8_0(xc, xs, wgu_c, wgu_s, workspace=wsp)
+    xh = x.cpu().numpy()
+    s = ops.swiglu(ops.matmul_q8_0(xh, ogc, ogs), ops.matmul_q8_0(xh, ouc, ous))
+    oc, os_ = quantize_q8_0(s)
+    assert_codes_match(sc, ss, oc, os_, max_frac_code_diff=1e-4, what=f"swiglu codes m={m} k={k} f={f}")
+
+
 def test_gemm_in_place_residual():
     dev = need_gpu()
     x = outlier_acts(40, 896, 21, dev)
