@@ -303,8 +303,7 @@ def test_rope_kvstore_rows_and_values(nh, nkv, hd):
     np.testing.assert_array_equal(k.cpu().numpy(), k0)  # k itself is not modified
 
 
-# head_dim 128 takes the KV-head-shared kernel for 4..8 query heads per KV head (7 and 4 here) and
-# the per-head kernel otherwise (2 and 16)
+# GQA groups of 7, 7, 4, 1, 2 and 16 query heads per KV head; unsorted positions with gaps
 @pytest.mark.parametrize("nh,nkv,hd,n,n_ctx", [(14, 2, 64, 37, 300), (28, 4, 128, 21, 200), (32, 8, 128, 50, 700),
                                                (4, 4, 64, 1, 5), (4, 2, 128, 30, 100), (16, 1, 128, 20, 64)])
 def test_attention_matches_oracle(nh, nkv, hd, n, n_ctx):
@@ -315,6 +314,45 @@ def test_attention_matches_oracle(nh, nkv, hd, n, n_ctx):
     q = synth.gen_normal(91, "q", (n, nh * hd), std=0.6, device=dev)
     kr = synth.gen_normal(92, "k", (n_ctx, nkv * hd), std=0.6, device=dev)
     vr = synth.gen_normal(93, "v", (n_ctx, nkv * hd), device=dev)
+    out = B.attention_gqa(q, kr, vr, torch.as_tensor(pos, device=dev), int(pos.max()), nh, nkv, hd)
+    want = ops.attention_gqa(q.cpu().numpy(), kr.cpu().numpy(), vr.cpu().numpy(), pos, nh, nkv, hd)
+    assert_f32_match(out.cpu().numpy(), want, what="attention")
+
+
+def _random_attention_cases(n_cases, seed):
+    """Seeded random attention calls: head layouts with GQA groups of 1 to 12, head_dim 64 or 128, 1 to
+    300 queries over regions of up to 2000 rows, positions either a contiguous run at a random offset
+    or a random unsorted subset with gaps."""
+    rng = np.random.default_rng(seed)
+    layouts = [(14, 2), (28, 4), (32, 8), (16, 16), (12, 1), (8, 2)]
+    cases = []
+    for _ in range(n_cases):
+        nh, nkv = layouts[int(rng.integers(len(layouts)))]
+        hd = int(rng.choice([64, 128]))
+        n = int(rng.integers(1, 301))
+        n_ctx = int(rng.integers(n, 2001))
+        contiguous = bool(rng.integers(2))
+        cases.append((nh, nkv, hd, n, n_ctx, contiguous, int(rng.integers(1 << 30))))
+    return cases
+
+
+RANDOM_ATTENTION_CASES = _random_attention_cases(12, 20261205)
+
+
+@pytest.mark.parametrize("nh,nkv,hd,n,n_ctx,contiguous,seed", RANDOM_ATTENTION_CASES,
+                         ids=[f"h{c[0]}_{c[1]}_d{c[2]}_n{c[3]}_ctx{c[4]}_{'run' if c[5] else 'set'}"
+                              for c in RANDOM_ATTENTION_CASES])
+def test_attention_random_calls_match_oracle(nh, nkv, hd, n, n_ctx, contiguous, seed):
+    dev = need_gpu()
+    say(f"attention nh={nh} nkv={nkv} hd={hd} n={n} n_ctx={n_ctx} contiguous={contiguous}")
+    rng = np.random.default_rng(seed)
+    if contiguous:
+        pos = (int(rng.integers(0, n_ctx - n + 1)) + np.arange(n)).astype(np.int32)
+    else:
+        pos = rng.choice(n_ctx, size=n, replace=False).astype(np.int32)
+    q = synth.gen_normal(seed % 1000, "q", (n, nh * hd), std=0.6, device=dev)
+    kr = synth.gen_normal(seed % 1000 + 1, "k", (n_ctx, nkv * hd), std=0.6, device=dev)
+    vr = synth.gen_normal(seed % 1000 + 2, "v", (n_ctx, nkv * hd), device=dev)
     out = B.attention_gqa(q, kr, vr, torch.as_tensor(pos, device=dev), int(pos.max()), nh, nkv, hd)
     want = ops.attention_gqa(q.cpu().numpy(), kr.cpu().numpy(), vr.cpu().numpy(), pos, nh, nkv, hd)
     assert_f32_match(out.cpu().numpy(), want, what="attention")
