@@ -8,7 +8,7 @@ import oracle
 import synth
 from quantized_transformer_prefill_amd import binding as B
 from tests.gpu_util import assert_f32_match, need_gpu, say
-from tests.test_forward_gpu import SENTINEL, TINY_Q2, TINY_Q3, compare_logits, load_pair
+from tests.test_forward_gpu import SENTINEL, TINY_Q2, TINY_Q3, _random_tiny_configs, compare_logits, load_pair
 
 pytestmark = pytest.mark.gpu
 
@@ -81,6 +81,27 @@ def test_decode_matches_oracle(cfg):
     over 256); several steps, each attending to the prompt and the earlier steps."""
     dev = need_gpu()
     m, steps, kk, vv, end = prefill_then_decode(cfg, dev, 4)
+    for i, (got, want) in enumerate(steps):
+        compare_logits(got, want, f"{cfg.name} step {i} logits")
+        assert_f32_match(got, want, max_ulp=64, max_frac_inexact=0.05, what=f"{cfg.name} step {i} logits ulp")
+    gk, gv = m.kv_k.cpu().numpy(), m.kv_v.cpu().numpy()
+    assert np.all(gk[:, end:] == SENTINEL) and np.all(gv[:, end:] == SENTINEL), "stray KV writes"
+    assert_f32_match(gk[:, :end], kk[:, :end], max_ulp=64, max_frac_inexact=0.05, what="K regions")
+    assert_f32_match(gv[:, :end], vv[:, :end], max_ulp=64, max_frac_inexact=0.05, what="V regions")
+
+
+# random small models (other draws than the forward's), each with room for its decode steps
+RANDOM_DECODE = [c for c, _ in _random_tiny_configs(8, 20261207) if c.n_ctx >= c.prefix_tokens + c.n_tokens + 3]
+
+
+@pytest.mark.parametrize("cfg", RANDOM_DECODE,
+                         ids=[f"{c.name}_L{c.n_layers}_h{c.hidden}_{c.n_head}x{c.head_dim}_kv{c.n_head_kv}"
+                              f"_f{c.ffn}_t{c.n_tokens}_p{c.prefix_tokens}_ctx{c.n_ctx}" for c in RANDOM_DECODE])
+def test_decode_random_small_models_match_oracle(cfg):
+    """Three decode steps after the prompt of a random small model, every step's logits and the
+    regions against the oracle."""
+    dev = need_gpu()
+    m, steps, kk, vv, end = prefill_then_decode(cfg, dev, 3)
     for i, (got, want) in enumerate(steps):
         compare_logits(got, want, f"{cfg.name} step {i} logits")
         assert_f32_match(got, want, max_ulp=64, max_frac_inexact=0.05, what=f"{cfg.name} step {i} logits ulp")

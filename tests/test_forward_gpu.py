@@ -100,6 +100,59 @@ def test_forward_n_out_matches_oracle(cfg, n_outs):
         np.testing.assert_array_equal(got[-1], one)   # the last row is the n_out = 1 logits
 
 
+def _random_tiny_configs(n_cases, seed):
+    """Seeded random small models: 1-3 layers, hidden 64..512, head layouts with GQA groups of 1-8 at
+    head_dim 64 or 128, ffn 64..640, with or without Q/K/V bias and per-head QK norm, tied or separate
+    lm_head, a prompt of 1-80 tokens after a prefix of 0-30, n_ctx up to 200 rows; plus an n_out (1 in
+    about half the cases: the last layer's one-token tail)."""
+    rng = np.random.default_rng(seed)
+    layouts = [(4, 1), (4, 2), (4, 4), (8, 2), (8, 1), (6, 3)]
+    out = []
+    for i in range(n_cases):
+        nh, nkv = layouts[int(rng.integers(len(layouts)))]
+        n_tokens = int(rng.integers(1, 81))
+        prefix = int(rng.choice([0, 0, int(rng.integers(1, 31))]))
+        cfg = synth.ModelConfig(
+            name=f"rand{i}", n_layers=int(rng.integers(1, 4)), hidden=32 * int(rng.integers(2, 17)),
+            n_head=nh, n_head_kv=nkv, head_dim=int(rng.choice([64, 128])), ffn=32 * int(rng.integers(2, 21)),
+            vocab=int(rng.integers(200, 1500)), n_tokens=n_tokens,
+            n_ctx=prefix + n_tokens + int(rng.integers(0, 201 - n_tokens)), seed=int(rng.integers(1000)),
+            qkv_bias=bool(rng.integers(2)), qk_norm=bool(rng.integers(2)), tied=bool(rng.integers(2)),
+            prefix_tokens=prefix)
+        out.append((cfg, 1 if rng.integers(2) else int(rng.integers(1, n_tokens + 1))))
+    return out
+
+
+RANDOM_TINY = _random_tiny_configs(12, 20261206)
+
+
+@pytest.mark.parametrize("cfg,n_out", RANDOM_TINY,
+                         ids=[f"{c.name}_L{c.n_layers}_h{c.hidden}_{c.n_head}x{c.head_dim}_kv{c.n_head_kv}"
+                              f"_f{c.ffn}_t{c.n_tokens}_p{c.prefix_tokens}_o{o}" for c, o in RANDOM_TINY])
+def test_random_small_models_match_oracle(cfg, n_out):
+    """Whole forwards of random small models: the last n_out logits and every K/V region row against
+    the oracle, and nothing written past the prompt's rows."""
+    dev = need_gpu()
+    say(f"random forward {cfg}")
+    m, w = load_pair(cfg, dev)
+    pre_ids, ids = synth.gen_token_ids(cfg)
+    pre_pos, pos = synth.positions_for(cfg)
+    kk, vv = oracle.new_kv_regions(cfg, cfg.n_ctx, fill=SENTINEL)
+    if cfg.prefix_tokens:
+        m.forward(pre_ids, pre_pos)
+        oracle.prefill_forward(cfg, w, pre_ids, pre_pos, cfg.n_ctx, kk, vv)
+    got = m.forward_n(ids, pos, n_out).cpu().numpy()
+    want = oracle.prefill_forward(cfg, w, ids, pos, cfg.n_ctx, kk, vv, n_out=n_out)
+    compare_logits(got, want, f"{cfg.name} n_out={n_out} logits")
+    assert_f32_match(got, want, max_ulp=64, max_frac_inexact=0.05, what=f"{cfg.name} logits ulp")
+    gk, gv = m.kv_k.cpu().numpy(), m.kv_v.cpu().numpy()
+    used = np.arange(cfg.prefix_tokens + cfg.n_tokens)
+    free = np.arange(used.size, cfg.n_ctx)
+    assert np.all(gk[:, free] == SENTINEL) and np.all(gv[:, free] == SENTINEL), "stray KV writes"
+    assert_f32_match(gk[:, used], kk[:, used], max_ulp=64, max_frac_inexact=0.05, what="K regions")
+    assert_f32_match(gv[:, used], vv[:, used], max_ulp=64, max_frac_inexact=0.05, what="V regions")
+
+
 def test_forward_n_out_bounds():
     dev = need_gpu()
     cfg = synth.LAYER1
