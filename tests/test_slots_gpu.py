@@ -8,7 +8,7 @@ import oracle
 import synth
 from quantized_transformer_prefill_amd import binding as B
 from tests.gpu_util import assert_f32_match, need_gpu, say
-from tests.test_forward_gpu import SENTINEL, TINY_Q3, compare_logits, load_pair
+from tests.test_forward_gpu import SENTINEL, TINY_Q3, _random_tiny_configs, compare_logits, load_pair
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,36 @@ def test_slots_match_independent_oracle_calls(cfg):
         gk, gv = ks.k.cpu().numpy(), ks.v.cpu().numpy()
         assert_f32_match(gk, kk, max_ulp=64, max_frac_inexact=0.05, what=f"slot {i} K regions")
         assert_f32_match(gv, vv, max_ulp=64, max_frac_inexact=0.05, what=f"slot {i} V regions")
+
+
+RANDOM_SLOT_MODELS = [c for c, _ in _random_tiny_configs(4, 20261208)]
+
+
+@pytest.mark.parametrize("cfg", RANDOM_SLOT_MODELS,
+                         ids=[f"{c.name}_L{c.n_layers}_h{c.hidden}_{c.n_head}x{c.head_dim}_kv{c.n_head_kv}_ctx{c.n_ctx}"
+                              for c in RANDOM_SLOT_MODELS])
+def test_slots_random_match_independent_oracle_calls(cfg):
+    """2-6 sequences of random lengths, each a run of positions at a random offset in its own
+    regions (the rows before the run are unwritten), against the oracle's prefill of each alone."""
+    dev = need_gpu()
+    rng = np.random.default_rng(cfg.seed + 99)
+    n_slots = int(rng.integers(2, 7))
+    lens = [min(int(rng.integers(1, 25)), cfg.n_ctx) for _ in range(n_slots)]
+    say(f"slots {cfg.name}: lengths {lens}")
+    m, w = load_pair(cfg, dev, max_tokens=sum(lens))
+    sets = [m.new_kv_set(SENTINEL) for _ in range(n_slots)]
+    okv = [oracle.new_kv_regions(cfg, cfg.n_ctx, fill=SENTINEL) for _ in sets]
+    slots = []
+    for n in lens:
+        start = int(rng.integers(0, cfg.n_ctx - n + 1))
+        slots.append((rng.integers(0, cfg.vocab, n).astype(np.int32), (start + np.arange(n)).astype(np.int32)))
+    got = m.forward_slots([(a, b, ks) for (a, b), ks in zip(slots, sets)]).cpu().numpy()
+    for i, ((ids, pos), ks, (kk, vv)) in enumerate(zip(slots, sets, okv)):
+        want = oracle.prefill_forward(cfg, w, ids, pos, cfg.n_ctx, kk, vv)[0]
+        compare_logits(got[i], want, f"{cfg.name} slot {i} logits")
+        assert_f32_match(got[i], want, max_ulp=64, max_frac_inexact=0.05, what=f"slot {i} logits ulp")
+        assert_f32_match(ks.k.cpu().numpy(), kk, max_ulp=64, max_frac_inexact=0.05, what=f"slot {i} K regions")
+        assert_f32_match(ks.v.cpu().numpy(), vv, max_ulp=64, max_frac_inexact=0.05, what=f"slot {i} V regions")
 
 
 def test_one_slot_equals_forward():
