@@ -47,6 +47,44 @@ def test_sample_matches_oracle(pi):
     assert got == want
 
 
+def _random_sampler_cases(n_cases, seed):
+    """Seeded random calls: vocabularies of 1 to 262144 tokens (half log-uniform, half 100k and up), every parameter of the
+    chain drawn on or off (values f32-representable, as the C parameter block holds them), windows of
+    0 to 100 ids."""
+    rng = np.random.default_rng(seed)
+    f = lambda x: float(np.float32(x))
+    cases = []
+    for _ in range(n_cases):
+        vocab = int(rng.integers(100000, 262145)) if rng.integers(2) else int(np.exp(rng.uniform(0, np.log(262144))))
+        p = S.SamplerParams(
+            repeat_penalty=f(rng.uniform(0.5, 2.0)) if rng.integers(2) else 1.0,
+            frequency_penalty=f(rng.uniform(-1, 1)) if rng.integers(2) else 0.0,
+            presence_penalty=f(rng.uniform(-1, 1)) if rng.integers(2) else 0.0,
+            top_k=int(rng.integers(1, 65)),
+            top_p=f(rng.uniform(0.05, 1.0)) if rng.integers(2) else 1.0,
+            temperature=0.0 if rng.integers(10) == 0 else f(rng.uniform(0.1, 2.5)))
+        cases.append((max(vocab, 1), p, int(rng.integers(0, 101)), int(rng.integers(1 << 31))))
+    return cases
+
+
+RANDOM_SAMPLER_CASES = _random_sampler_cases(12, 20261209)
+
+
+@pytest.mark.parametrize("vocab,p,n_window,seed", RANDOM_SAMPLER_CASES,
+                         ids=[f"v{c[0]}_k{c[1].top_k}_w{c[2]}" for c in RANDOM_SAMPLER_CASES])
+def test_sample_random_calls_match_oracle(vocab, p, n_window, seed):
+    dev = need_gpu()
+    say(f"sample vocab={vocab} {p} window={n_window}")
+    rng = np.random.default_rng(seed)
+    logits = synthetic_logits(vocab, seed % 100000, scale=float(rng.uniform(0.1, 5.0)))
+    window = rng.integers(0, vocab, n_window).astype(np.int32)
+    ld = torch.as_tensor(logits, device=dev)
+    ws = torch.empty(B.lib().mi_sampler_workspace_bytes(), dtype=torch.uint8, device=dev)
+    got = [int(B.sample(ld, window, p, seed, step, workspace=ws).item()) for step in range(10)]
+    want = [S.sample(logits, window, p, seed, step) for step in range(10)]
+    assert got == want
+
+
 def test_sample_edge_cases():
     dev = need_gpu()
     p = S.SamplerParams(top_k=64, temperature=1.0, repeat_penalty=1.5, presence_penalty=0.5)
