@@ -314,8 +314,8 @@ def compare_regions(gk, gv, kk, vv, used, what):
 @pytest.mark.parametrize("name", ["qwen2p5_7b_pp2048", "qwen3_8b_chunk3072at1024"])
 def test_large_configs_full_size_properties(name):
     """The 7B- and 8B-shaped configurations at full size, in the launch configuration the bench
-    times (eager call and captured-graph replay), checked by properties that hold at any size (the
-    oracle comparison of the same configurations needs minutes of host time: the slow test above):
+    times (eager call and captured-graph replay), checked by properties that hold at any size (their
+    oracle comparison, minutes of host time, is test_zx_full_size_gpu.py, collected last):
     a repeated call and the graph replay give bit-identical logits and KV regions; rows no call
     wrote keep their sentinel; logits are finite; changing only the last token leaves every KV row
     at an earlier position bit-identical in every layer, and changes the last position's K row."""
