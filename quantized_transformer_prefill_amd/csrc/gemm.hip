@@ -16,9 +16,10 @@
 // * The VALU f64 epilogue (2 f64 FMAs per output per block) bounds this kernel, not the
 //   MFMA: half-used MFMAs cost nothing extra.
 //
-// Tiling: 256 threads = 4 waves (2 x 2).  Wave tile RG x CG MFMAs of 16 real rows x 32 columns:
-// 4 x 2 (workgroup 128 x 128) for large problems of >= 1024 rows, 2 x 2 (64 x 128) for other
-// large ones, 1 x 2 (32 x 128) and 1 x 1 (workgroup 32 x 64) for small ones.  A
+// Tiling: 256 threads = 4 waves (2 x 2, or 4 x 1 for the fused SwiGLU at few rows).  Wave tile
+// RG x CG MFMAs of 16 real rows x 32 columns: 4 x 2 (workgroup 128 x 128) for large problems of
+// >= 1024 rows, 2 x 2 (64 x 128) for other large ones, 1 x 2 (32 x 128, or 64 x 64 with the waves
+// stacked 4 x 1) and 1 x 1 (workgroup 32 x 64) for small ones.  A
 // stage of 4 blocks (128 K values) of codes and f64 scales goes through LDS, double-buffered,
 // with the next stage's global loads in flight while the current one computes.  Split-K writes f64 partials that a second kernel
 // reduces in a fixed order (deterministic).
@@ -53,10 +54,11 @@ __device__ __forceinline__ int swz(int row, int chunk) { return ((chunk ^ (row &
 //    blocks 2p (low half) and 2p+1 (high half) of the stage, moved 4 bytes per lane -- one
 //    transfer instruction covers 32 rows x 4 blocks;
 //  * otherwise word [block][row] holds one fp16 scale in its low half, moved 2 bytes per lane.
-template <int RG, int CG, int NS, bool SP>
+// WM: waves along the rows (2: a 2 x 2 arrangement; 4: the waves stacked 4 x 1)
+template <int RG, int CG, int NS, bool SP, int WM = 2>
 struct GemmTile {
-  static constexpr int BM = 2 * 16 * RG;   // real activation rows per workgroup
-  static constexpr int BN = 2 * 32 * CG;   // weight rows (output columns) per workgroup
+  static constexpr int BM = WM * 16 * RG;         // real activation rows per workgroup
+  static constexpr int BN = (4 / WM) * 32 * CG;   // weight rows (output columns) per workgroup
   int8_t a[NS][BM + 1][G_ROWB];   // row BM is all zeros
   int8_t b[NS][BN][G_ROWB];
   uint32_t as[NS][SP ? 2 * BM : G_KS * BM];
@@ -114,14 +116,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
 }
 
-template <int RG, int CG, int EPI, bool SPLIT, int NS, bool SP>
-__global__ void __launch_bounds__(G_THREADS, RG == 1 ? 3 : 2)
+template <int RG, int CG, int EPI, bool SPLIT, int NS, bool SP, int WM = 2>
+__global__ void __launch_bounds__(G_THREADS, WM == 4 ? 4 : (RG == 1 ? 3 : 2))
 k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales, int M,
           const int8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales, int N, int K,
           const float* __restrict__ bias, const float* residual, float* out, int64_t ld_out,
           int8_t* __restrict__ q_codes, uint16_t* __restrict__ q_scales,
           double* __restrict__ partial, int kb_per_split, int xcd_order, QkvEpi qe) {
-  using T = GemmTile<RG, CG, NS, SP>;
+  using T = GemmTile<RG, CG, NS, SP, WM>;
   constexpr int BM = T::BM, BN = T::BN;
   static_assert(!SP || NS == 2, "scale pairs: one wait for all of a stage's transfers");
   __shared__ __align__(16) T sm;
@@ -129,7 +131,7 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
   const int tid = threadIdx.x;
   if constexpr (EPI == EPI_SWIGLU_Q8) exp2_table_fill(exp_tab, tid);
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index held in an SGPR
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / (4 / WM), wn = wave % (4 / WM);
   // XCD-aware tile order.  Workgroups are dispatched round-robin over the 8 XCDs, each with its
   // own L2; workgroup L is given tile t so that every XCD owns one contiguous range of tiles, and
   // t walks the row tiles fastest, so the workgroups of an XCD share the weight tiles they read.
@@ -599,13 +601,15 @@ static GemmPlan plan_gemm(int m, int n, int k, bool swiglu, bool defer = false) 
   GemmPlan p{1, 1};
   const int tiles_big = ((m + 63) / 64) * ((n + 127) / 128);
   if (swiglu) {
-    // gate/up pairs live in column-group pairs: 2x2 or 1x2; prefer enough workgroups for 2 per CU
+    // gate/up pairs live in column-group pairs: 2x2 or 1x2 (waves 4 x 1); prefer enough workgroups for 2 per CU
     p.shape = tiles_big >= 1024 ? 1 : 2;
   } else if (tiles_big < 512) {
     p.shape = 0;
   }
-  const int tiles = p.shape == 1 ? tiles_big : p.shape == 2 ? ((m + 31) / 32) * ((n + 127) / 128)
-                                                           : ((m + 31) / 32) * ((n + 63) / 64);
+  // (the SwiGLU's 1 x 2 tiles are 64 x 64 workgroups, the others 32 x 128; see launch_gemm_q8)
+  const int tiles = p.shape == 1   ? tiles_big
+                    : p.shape == 2 ? (swiglu ? ((m + 63) / 64) * ((n + 63) / 64) : ((m + 31) / 32) * ((n + 127) / 128))
+                                   : ((m + 31) / 32) * ((n + 63) / 64);
   // Split K only for long reductions whose output tiles cannot fill the chip, keeping the f64
   // partials (written once, read once) at most 8 MB.
   const int target = 512;
@@ -644,28 +648,28 @@ size_t gemm_workspace_bytes(int m, int n, int k) {
   return s > 1 ? (size_t)s * m * n * sizeof(double) : 0;
 }
 
-template <int RG, int CG, int NS, bool SP>
+template <int RG, int CG, int NS, bool SP, int WM = 2>
 static void launch_tiles(const GemmArgs& g, int split, int kb_per, hipStream_t s) {
-  using T = GemmTile<RG, CG, NS, SP>;
+  using T = GemmTile<RG, CG, NS, SP, WM>;
   dim3 grid((g.n + T::BN - 1) / T::BN, (g.m + T::BM - 1) / T::BM, split);
   // XCD-aware order once the weights outgrow one XCD's 4 MB L2 several times over
   const int xcd = (int64_t)g.n * g.k > ((int64_t)16 << 20) ? 1 : 0;
   double* partial = reinterpret_cast<double*>(g.workspace);
   if (split > 1)
-    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, true, NS, SP>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
+    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, true, NS, SP, WM>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
                        g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
                        partial, kb_per, xcd, g.qkv);
   else if (g.qkv.pos)
-    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_QKV, false, NS, SP>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
+    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_QKV, false, NS, SP, WM>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
                        g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
                        nullptr, kb_per, xcd, g.qkv);
   else if (g.q_codes) {
     if constexpr (CG >= 2)
-      hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_SWIGLU_Q8, false, NS, SP>), grid, dim3(G_THREADS), 0, s, g.a_codes,
+      hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_SWIGLU_Q8, false, NS, SP, WM>), grid, dim3(G_THREADS), 0, s, g.a_codes,
                          g.a_scales, g.m, g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out,
                          g.q_codes, g.q_scales, nullptr, kb_per, xcd, g.qkv);
   } else
-    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, false, NS, SP>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
+    hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, false, NS, SP, WM>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
                        g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
                        nullptr, kb_per, xcd, g.qkv);
 }
@@ -693,13 +697,19 @@ int launch_gemm_q8(const GemmArgs& g, hipStream_t s) {
   split = (KB + kb_per - 1) / kb_per;
   // scale pairs: rows of an even number of blocks, scale planes 4-byte aligned
   const bool sp = KB % 2 == 0 && ((uintptr_t)g.a_scales & 3) == 0 && ((uintptr_t)g.w_scales & 3) == 0;
+  // The fused SwiGLU on 1 x 2 wave tiles stacks its waves 4 x 1 (64 x 64 workgroups: 35 KB of LDS and
+  // 126 registers, four workgroups per CU instead of three; measured 30.2 -> 28.8 us at 512 x 9728 x
+  // 896); the Q|K|V matmul keeps 32 x 128 (whole heads of 128 per tile).
+  const bool tall = p.shape == 2 && g.q_codes;
   if (sp && p.shape != 3) {  // (the 4x2 tile: more spills with pairs, measured no faster)
     if (p.shape == 1) launch_tiles<2, 2, G_NS_22, true>(g, split, kb_per, s);
+    else if (tall) launch_tiles<1, 2, G_NS_12, true, 4>(g, split, kb_per, s);
     else if (p.shape == 2) launch_tiles<1, 2, G_NS_12, true>(g, split, kb_per, s);
     else launch_tiles<1, 1, G_NS_11, true>(g, split, kb_per, s);
   } else {
     if (p.shape == 3) launch_tiles<4, 2, G_NS_22, false>(g, split, kb_per, s);
     else if (p.shape == 1) launch_tiles<2, 2, G_NS_22, false>(g, split, kb_per, s);
+    else if (tall) launch_tiles<1, 2, G_NS_12, false, 4>(g, split, kb_per, s);
     else if (p.shape == 2) launch_tiles<1, 2, G_NS_12, false>(g, split, kb_per, s);
     else launch_tiles<1, 1, G_NS_11, false>(g, split, kb_per, s);
   }
