@@ -206,7 +206,8 @@ def test_gemm_swiglu_matches_oracle():
     # 1x2 wave tiles for the first three, then 4x2 (128 x 128 workgroups) and 2x2 (64 x 128): the
     # library picks the one that fills the chip's workgroup slots in fewer rounds
     for m, k, f in [(100, 896, 320), (16, 3584, 512), (1, 896, 4864), (512, 256, 8192), (1100, 256, 3680),
-                    (1000, 160, 8192)]:  # the last: 4x2 tiles with a row tail and a 1-block K stage
+                    (1000, 160, 8192),   # 4x2 tiles with a row tail and a 1-block K stage
+                    (3, 64, 32), (70, 96, 32)]:  # one 32-wide SwiGLU block: a single column tile
         say(f"gemm+swiglu m={m} k={k} ffn={f}")
         x = synth.gen_normal(31, f"x{m}", (m, k), device=dev)
         wg = synth.gen_normal(32, f"g{f}", (f, k), std=0.02, device=dev)
