@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
     python bench.py --counter-run | --write-counters C F W OUT     (per-kernel counter summary)
+    python bench.py --write-wave-states DIR OUT                     (wave states of a --counter-run pass)
 
 A step is one forward over the whole 512-token prompt (all layers, the KV stores, the last-token
 lm_head) on seeded synthetic Q8_0 weights resident in HBM, launched as a replay of the captured
@@ -48,6 +49,8 @@ def parse():
                    help="launches for the per-kernel counters: two eager forwards, then the calibration kernel")
     p.add_argument("--write-counters", nargs=4, metavar=("COMPUTE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT"),
                    help="turn the three counter passes of --counter-run into a per-kernel summary (OUT)")
+    p.add_argument("--write-wave-states", nargs=2, metavar=("DIR", "OUT"),
+                   help="turn a --counter-run pass with the wave-state counters into a per-kernel summary (OUT)")
     p.add_argument("--write-kernel-summary", nargs=2, metavar=("TRACE_DIR", "OUT"),
                    help="turn a rocprofv3 --kernel-trace run of this benchmark into a per-forward kernel table "
                         "(OUT); --skip-forwards leaves out the first forwards, --trace-command records the command")
@@ -98,6 +101,10 @@ def main():
     if args.write_counters:
         import synth
         write_counters(synth.MODEL_CONFIGS[args.workload] if args.workload else synth.HEADLINE, *args.write_counters)
+        return
+    if args.write_wave_states:
+        import synth
+        write_wave_states(synth.MODEL_CONFIGS[args.workload] if args.workload else synth.HEADLINE, *args.write_wave_states)
         return
     if args.write_kernel_summary:
         import synth
@@ -782,6 +789,57 @@ def write_counters(cfg, cdir, fdir, wdir, out_path):
             f"{f64m / s_ / 1e12:.1f} | {fma64 / s_ / 1e12:.1f} ({100 * fma64 / s_ / 1e12 / F64_VALU_PEAK_TFLOPS:.0f}%) | "
             f"{100 * busy / (s_ * 2.4e9 * 1024):.0f}% | {100 * coex / busy if busy else 0:.0f}% | {ldsc:.3f} | "
             f"{hbm / 1e6:.2f} ({hbm / bytes_alg:.2f}x) | {hbm / s_ / 1e9:.0f} ({100 * hbm / s_ / 1e9 / HBM_PEAK_GBS:.0f}%) |")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+COUNTERS_WAVE = ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+                 "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_LDS"]
+
+
+def write_wave_states(cfg, d, out_path):
+    """Where a wave's life goes, per forward node, from one --counter-run pass with COUNTERS_WAVE:
+    waiting on a counter or barrier (SQ_WAIT_ANY), ready but not issued (SQ_WAIT_INST_ANY), issuing
+    (SQ_ACTIVE_INST_ANY), each as a share of SQ_WAVE_CYCLES; and the VALU, scalar and LDS issue
+    cycles per wave (the counters count in units of 4 cycles)."""
+    tab, _ = _dispatch_table(d)
+
+    def by_node(node):
+        groups = {}
+        for did, (n, g, vals) in tab.items():
+            prev = _short(tab[did - 1][0]) if did - 1 in tab else None
+            if _classify(_short(n), prev) == node:
+                groups.setdefault(g, []).append(vals)
+        return groups
+
+    run = f"python3 bench.py --workload {cfg.name} --counter-run"
+    lines = [f"# Wave states per kernel: {cfg.description} ({cfg.name})", "",
+             "Commands (repository root on the GPU host; run from /tmp with TMPDIR=/tmp):", "",
+             "    rocprofv3 --pmc " + " ".join(COUNTERS_WAVE) + " --output-format csv -d out/cnt_wave -o p -- " + run,
+             f"    python3 bench.py --workload {cfg.name} --write-wave-states out/cnt_wave "
+             f"profiles/wave_states_{cfg.name}.md", "",
+             "Per kernel: the group of launches at the full prompt, medians over its launches.  Shares of the "
+             "summed wave cycles (SQ_WAVE_CYCLES): waiting on a counter or the barrier (SQ_WAIT_ANY), ready but "
+             "not issued (SQ_WAIT_INST_ANY), issuing (SQ_ACTIVE_INST_ANY).  Issue cycles per wave: "
+             "SQ_ACTIVE_INST_VALU, _SCA, _LDS x 4 / SQ_WAVES (the counters count in units of 4 cycles).", "",
+             "| kernel | launches | waves | cycles per wave | waiting | ready, not issued | issuing | "
+             "VALU cycles per wave | scalar cycles per wave | LDS cycles per wave |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    med = lambda xs: float(np.median(xs)) if xs else float("nan")
+    for node, (label, _, _) in _forward_kernels(cfg).items():
+        groups = by_node(node)
+        if not groups:
+            continue
+        _, disp = max(groups.items(), key=lambda kv: len(kv[1]))
+        cv = lambda c: med([v.get(c, float("nan")) for v in disp])
+        waves, wc = cv("SQ_WAVES"), cv("SQ_WAVE_CYCLES")
+        share = lambda c: 100.0 * cv(c) / wc if wc else float("nan")
+        per = lambda c: 4.0 * cv(c) / waves if waves else float("nan")
+        lines.append(f"| {label.replace('|', chr(92) + '|')} | {len(disp)} | {waves:.0f} | {4.0 * wc / waves:.0f} | "
+                     f"{share('SQ_WAIT_ANY'):.0f}% | {share('SQ_WAIT_INST_ANY'):.0f}% | {share('SQ_ACTIVE_INST_ANY'):.0f}% | "
+                     f"{per('SQ_ACTIVE_INST_VALU'):.0f} | {per('SQ_ACTIVE_INST_SCA'):.0f} | "
+                     f"{per('SQ_ACTIVE_INST_LDS'):.0f} |")
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
