@@ -49,6 +49,9 @@ def parse():
                    help="launches for the per-kernel counters: two eager forwards, then the calibration kernel")
     p.add_argument("--write-counters", nargs=4, metavar=("COMPUTE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT"),
                    help="turn the three counter passes of --counter-run into a per-kernel summary (OUT)")
+    p.add_argument("--k-sweep", action="store_true",
+                   help="time the fused gate|up matmul of the workload's shape at K = 128 .. 3584 and fit a fixed "
+                        "plus per-stage (128 K values) cost; prints its own JSON line")
     p.add_argument("--write-wave-states", nargs=2, metavar=("DIR", "OUT"),
                    help="turn a --counter-run pass with the wave-state counters into a per-kernel summary (OUT)")
     p.add_argument("--write-kernel-summary", nargs=2, metavar=("TRACE_DIR", "OUT"),
@@ -129,6 +132,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.probes:
         print(json.dumps({"probes": probe_rates(dev)}), flush=True)
+        return
+    if args.k_sweep:
+        print(json.dumps({"k_sweep": k_sweep(cfg, dev)}), flush=True)
         return
     if args.traffic_run:
         traffic_run(cfg, dev)
@@ -505,6 +511,33 @@ def dominant_kernel(cfg, dev, w_gate_up=None):
     wsp = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=dev)
     gu_codes, gu_scales = w_gate_up
     return (lambda: B.gemm_swiglu_q8_0(xc, xs, gu_codes, gu_scales, workspace=wsp)), (M, 2 * F, H)
+
+
+def k_sweep(cfg, dev):
+    """The fused gate|up matmul + SwiGLU + Q8_0 at the workload's M and N = 2 x ffn with K = 128 ..
+    3584 (1 .. 28 stages of 128), 200 launches each, and the least-squares fit time = fixed + stages
+    x per-stage: how much of a launch grows with the reduction and how much does not."""
+    import torch
+
+    import synth
+    from quantized_transformer_prefill_amd import binding as B
+    from quantized_transformer_prefill_amd.model import interleave_gate_up
+
+    M, F = cfg.n_tokens, cfg.ffn
+    pts = []
+    for K in (128, 256, 512, 896, 1792, 3584):
+        g = B.quantize_q8_0(synth.gen_normal(2, f"ks.g{K}", (F, K), std=0.02, device=dev))
+        u = B.quantize_q8_0(synth.gen_normal(3, f"ks.u{K}", (F, K), std=0.02, device=dev))
+        wc, ws = interleave_gate_up(g[0], u[0]).contiguous(), interleave_gate_up(g[1], u[1]).contiguous()
+        xc, xs = B.quantize_q8_0(synth.gen_normal(1, f"ks.x{K}", (M, K), device=dev))
+        wsp = torch.empty(max(B.lib().mi_gemm_q8_0_workspace_bytes(M, 2 * F, K), 8), dtype=torch.uint8, device=dev)
+        us = 1e3 * timed_loop(lambda: B.gemm_swiglu_q8_0(xc, xs, wc, ws, workspace=wsp), 200, torch)
+        pts.append((K // 128, round(us, 3)))
+    st = np.array([p[0] for p in pts], float)
+    t = np.array([p[1] for p in pts], float)
+    per, fixed = np.polyfit(st, t, 1)
+    return {"shape_mn": [M, 2 * F], "stages_us": pts, "fixed_us": round(float(fixed), 2),
+            "per_stage_us": round(float(per), 3), "command": f"python3 bench.py --workload {cfg.name} --k-sweep"}
 
 
 def traffic_run(cfg, dev):
