@@ -19,8 +19,9 @@
 // Tiling: 256 threads = 4 waves (2 x 2, or 4 x 1 for the fused SwiGLU at few rows).  Wave tile
 // RG x CG MFMAs of 16 real rows x 32 columns: 4 x 2 (workgroup 128 x 128) for large problems of
 // >= 1024 rows, 2 x 2 (64 x 128) for other large ones, 1 x 2 (32 x 128, or 64 x 64 with the waves
-// stacked 4 x 1) and 1 x 1 (workgroup 32 x 64) for small ones.  A
-// stage of 4 blocks (128 K values) of codes and f64 scales goes through LDS, double-buffered,
+// stacked 4 x 1) and 1 x 1 (workgroup 32 x 64) for small ones; 1 x 1 tiles of long reductions
+// that cannot fill the chip run two groups of 4 waves per workgroup, each over half of the K range,
+// their f64 sums added in LDS before the epilogue.  A stage of 4 blocks (128 K values) of codes and f64 scales goes through LDS, double-buffered,
 // with the next stage's global loads in flight while the current one computes.  Split-K writes f64 partials that a second kernel
 // reduces in a fixed order (deterministic).
 #include <mutex>
@@ -116,8 +117,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
 }
 
-template <int RG, int CG, int EPI, bool SPLIT, int NS, bool SP, int WM = 2>
-__global__ void __launch_bounds__(G_THREADS, WM == 4 ? 4 : (RG == 1 ? 3 : 2))
+// KW: groups of 4 waves that split the workgroup's K range between them and add their f64 sums in
+// LDS before the epilogue (2: more waves per output tile when the tiles cannot fill the chip)
+template <int RG, int CG, int EPI, bool SPLIT, int NS, bool SP, int WM = 2, int KW = 1>
+__global__ void __launch_bounds__(G_THREADS * KW, KW == 2 ? 2 : (WM == 4 ? 4 : (RG == 1 ? 3 : 2)))
 k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales, int M,
           const int8_t* __restrict__ w_codes, const uint16_t* __restrict__ w_scales, int N, int K,
           const float* __restrict__ bias, const float* residual, float* out, int64_t ld_out,
@@ -126,11 +129,14 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
   using T = GemmTile<RG, CG, NS, SP, WM>;
   constexpr int BM = T::BM, BN = T::BN;
   static_assert(!SP || NS == 2, "scale pairs: one wait for all of a stage's transfers");
-  __shared__ __align__(16) T sm;
+  static_assert(KW == 1 || (KW == 2 && EPI == EPI_F32 && WM == 2), "K groups: plain f32 / partial epilogue");
+  __shared__ __align__(16) T sm_all[KW];
   __shared__ double exp_tab[EPI == EPI_SWIGLU_Q8 ? 64 : 1];  // 2^(j/64) for the SiLU
   const int tid = threadIdx.x;
   if constexpr (EPI == EPI_SWIGLU_Q8) exp2_table_fill(exp_tab, tid);
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index held in an SGPR
+  const int lane = tid & 63, wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index held in an SGPR
+  const int kgrp = wave_all >> 2, wave = wave_all & 3;  // K group, wave within it
+  T& sm = sm_all[kgrp];
   const int wm = wave / (4 / WM), wn = wave % (4 / WM);
   // XCD-aware tile order.  Workgroups are dispatched round-robin over the 8 XCDs, each with its
   // own L2; workgroup L is given tile t so that every XCD owns one contiguous range of tiles, and
@@ -145,8 +151,15 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
   const int n0 = ((t / gy) % gx) * BN, m0 = (t % gy) * BM;
   const int kz = t / (gx * gy);  // K split
   const int KB = K / QK;
-  const int kb0 = kz * kb_per_split;
-  const int kb1 = min(KB, kb0 + kb_per_split);
+  int kb0 = kz * kb_per_split;
+  int kb1 = min(KB, kb0 + kb_per_split);
+  // K groups: the first takes the first half of the slice's stages (rounded up), the second the rest
+  const int ns_it = KW == 1 ? (kb1 - kb0 + G_KS - 1) / G_KS : ((kb1 - kb0 + G_KS - 1) / G_KS + 1) / 2;
+  if constexpr (KW == 2) {
+    const int mid = min(kb1, kb0 + ns_it * G_KS);
+    if (kgrp == 0) kb1 = mid;
+    else kb0 = mid;
+  }
 
   // QKV epilogue of the smallest tile: the positions and (cos, sin) of this thread's RoPE pairs
   // are requested now, so they arrive while the K loop runs
@@ -171,8 +184,9 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
   }
 
   // zero row for the dummy MFMA rows (every ring slot)
-  if (tid < NS * G_ROWB / 16)
-    *reinterpret_cast<v4i*>(&sm.a[tid / (G_ROWB / 16)][BM][(tid % (G_ROWB / 16)) * 16]) = v4i{0, 0, 0, 0};
+  if ((tid & (G_THREADS - 1)) < NS * G_ROWB / 16)
+    *reinterpret_cast<v4i*>(&sm.a[(tid & (G_THREADS - 1)) / (G_ROWB / 16)][BM][((tid & (G_THREADS - 1)) % (G_ROWB / 16)) * 16]) =
+        v4i{0, 0, 0, 0};
 
   // ---- codes: global -> LDS directly (global_load_lds_dwordx4).  One wave instruction moves 64
   // chunks of 16 bytes = 8 whole LDS rows; lane l lands at row 8q + (l >> 3), position l & 7,
@@ -380,14 +394,39 @@ k_gemm_q8(const int8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_sca
       qcs[k] = reinterpret_cast<const double2*>(qe.rope)[qpos[k] * half + i];
     }
   }
-  for (int s = 0; s < ns; ++s) {
+  // (with two K groups the second may have one stage less: it skips its last iteration's work but
+  // keeps the barriers)
+  for (int s = 0; s < ns_it; ++s) {
     const bool more = s + NS - 1 < ns;
     if (more) issue(kb0 + (s + NS - 1) * G_KS, (s + NS - 1) % NS);
-    compute(s % NS, min(G_KS, kb1 - kb0 - s * G_KS));
+    if (KW == 1 || s < ns) compute(s % NS, min(G_KS, kb1 - kb0 - s * G_KS));
     // stage s + 1 has landed once at most the later stages' transfers are outstanding
     if (more) wait_vmcnt<(NS - 2) * L_OPS>();
     else wait_vmcnt<0>();
     __syncthreads();
+  }
+  if constexpr (KW == 2) {
+    // the second group's sums go through its (now idle) LDS ring to the first group, which adds
+    // them to its own in a fixed order and runs the epilogue alone
+    constexpr int NACC = RG * CG * 8;
+    static_assert(sizeof(T) >= sizeof(double) * NACC * 64 * 4, "K-group sums in LDS");
+    double* red = reinterpret_cast<double*>(&sm_all[1]);
+    if (kgrp == 1) {
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int cg = 0; cg < CG; ++cg)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) red[(wave * NACC + (rg * CG + cg) * 8 + j) * 64 + lane] = acc[rg][cg][j];
+    }
+    __syncthreads();
+    if (kgrp == 1) return;
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int cg = 0; cg < CG; ++cg)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[rg][cg][j] += red[(wave * NACC + (rg * CG + cg) * 8 + j) * 64 + lane];
   }
 
   // ---- epilogue.  Lane holds, for each (rg, cg, j): real row, column.
@@ -648,13 +687,24 @@ size_t gemm_workspace_bytes(int m, int n, int k) {
   return s > 1 ? (size_t)s * m * n * sizeof(double) : 0;
 }
 
-template <int RG, int CG, int NS, bool SP, int WM = 2>
+template <int RG, int CG, int NS, bool SP, int WM = 2, int KW = 1>
 static void launch_tiles(const GemmArgs& g, int split, int kb_per, hipStream_t s) {
   using T = GemmTile<RG, CG, NS, SP, WM>;
   dim3 grid((g.n + T::BN - 1) / T::BN, (g.m + T::BM - 1) / T::BM, split);
   // XCD-aware order once the weights outgrow one XCD's 4 MB L2 several times over
   const int xcd = (int64_t)g.n * g.k > ((int64_t)16 << 20) ? 1 : 0;
   double* partial = reinterpret_cast<double*>(g.workspace);
+  if constexpr (KW == 2) {
+    if (split > 1)
+      hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, true, NS, SP, WM, 2>), grid, dim3(2 * G_THREADS), 0, s, g.a_codes,
+                         g.a_scales, g.m, g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out,
+                         g.q_codes, g.q_scales, partial, kb_per, xcd, g.qkv);
+    else
+      hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, false, NS, SP, WM, 2>), grid, dim3(2 * G_THREADS), 0, s, g.a_codes,
+                         g.a_scales, g.m, g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out,
+                         g.q_codes, g.q_scales, nullptr, kb_per, xcd, g.qkv);
+    return;
+  }
   if (split > 1)
     hipLaunchKernelGGL((k_gemm_q8<RG, CG, EPI_F32, true, NS, SP, WM>), grid, dim3(G_THREADS), 0, s, g.a_codes, g.a_scales, g.m,
                        g.w_codes, g.w_scales, g.n, g.k, g.bias, g.residual, g.out, g.ld_out, g.q_codes, g.q_scales,
@@ -701,16 +751,24 @@ int launch_gemm_q8(const GemmArgs& g, hipStream_t s) {
   // 126 registers, four workgroups per CU instead of three; measured 30.2 -> 28.8 us at 512 x 9728 x
   // 896); the Q|K|V matmul keeps 32 x 128 (whole heads of 128 per tile).
   const bool tall = p.shape == 2 && g.q_codes;
+  // Plain f32 (or partial) outputs on 1 x 1 tiles too few to give every CU two workgroups, with at
+  // least 8 stages per slice: two K groups of 4 waves per workgroup, which double the waves working
+  // on the chip's few tiles (measured: 512 x 896 x 4864 22.2 -> 21.0 us, 0.5B forward -0.7%; with 4
+  // to 7 stages per slice no gain or slower).
+  const int wgs = ((g.m + 31) / 32) * ((g.n + 63) / 64) * split;
+  const bool kgroups = p.shape == 0 && !g.qkv.pos && !g.q_codes && wgs <= 512 && kb_per >= 8 * G_KS;
   if (sp && p.shape != 3) {  // (the 4x2 tile: more spills with pairs, measured no faster)
     if (p.shape == 1) launch_tiles<2, 2, G_NS_22, true>(g, split, kb_per, s);
     else if (tall) launch_tiles<1, 2, G_NS_12, true, 4>(g, split, kb_per, s);
     else if (p.shape == 2) launch_tiles<1, 2, G_NS_12, true>(g, split, kb_per, s);
+    else if (kgroups) launch_tiles<1, 1, G_NS_11, true, 2, 2>(g, split, kb_per, s);
     else launch_tiles<1, 1, G_NS_11, true>(g, split, kb_per, s);
   } else {
     if (p.shape == 3) launch_tiles<4, 2, G_NS_22, false>(g, split, kb_per, s);
     else if (p.shape == 1) launch_tiles<2, 2, G_NS_22, false>(g, split, kb_per, s);
     else if (tall) launch_tiles<1, 2, G_NS_12, false, 4>(g, split, kb_per, s);
     else if (p.shape == 2) launch_tiles<1, 2, G_NS_12, false>(g, split, kb_per, s);
+    else if (kgroups) launch_tiles<1, 1, G_NS_11, false, 2, 2>(g, split, kb_per, s);
     else launch_tiles<1, 1, G_NS_11, false>(g, split, kb_per, s);
   }
   MI_LAUNCH_CHECK("k_gemm_q8");
